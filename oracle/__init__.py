@@ -1,0 +1,44 @@
+"""CPU oracle for exact scaled-dot-product attention — TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python binding)
+never imports, links or calls anything here, and this package imports nothing
+from the product path: the two share no code.
+
+Everything here is plain float64 numpy (or pure-Python floats) written to be
+checked against the pages by eye, not to be fast.  Pages cited (title, address):
+
+  [A100]  "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型（含A100环境配置）"
+          http://www.cyqw.cn/news/1153354
+  [PT29]  "PyTorch-CUDA-v2.9镜像中使用FlashAttention提升训练速度"
+          http://www.yongjin360.com/news/212413
+  [FA37]  "Flash Attention 3.7 核心原理与实战：加速Transformer模型训练与推理"
+          http://www.hmyw.cn/news/56989
+  [VRAM]  "显存神技：必学FlashAttention！"
+          https://gitcode.csdn.net/69e6287b0a2f6a37c5a11aee.html
+
+Modules
+  attention  the definition: materialise S and P per (batch, head) in float64
+             (forward, backward, row-sampled forward) — pinned
+  brute      a scalar pure-Python evaluation of the unshifted softmax formula,
+             used only to pin ``attention`` on tiny shapes — pinned (by the
+             closed forms and by ``attention``)
+  online     the tiled running-max / running-sum recurrence in the pages'
+             order — pinned against ``attention``
+  pool       a process pool over (batch, head) for timing the oracle on a
+             bounded sample
+
+Every function has at least one pin in ``tests/test_oracle*.py`` that does not
+re-type its formula; no function is "parity unpinned".
+"""
+from .attention import (allowed_mask, attention_forward, attention_backward,
+                        attention_forward_rows, attention_forward_bh, attention_backward_bh,
+                        allowed_pairs, score_matrix_nbytes)
+from .online import attention_forward_online
+from .brute import attention_forward_brute
+
+__all__ = [
+    "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
+    "attention_forward_bh", "attention_backward_bh", "allowed_pairs", "score_matrix_nbytes",
+    "attention_forward_online", "attention_forward_brute",
+]

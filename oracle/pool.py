@@ -1,0 +1,65 @@
+"""Run the oracle over many (batch, head) slices in a process pool — test infrastructure.
+
+Used to time the oracle as a CPU baseline.  Each worker evaluates whole heads with
+``attention.attention_forward`` / ``attention_backward`` and one BLAS thread, so the
+pool size is the number of cores the oracle uses.  The pool is created with the
+``fork`` start method; callers create it before any GPU work in the process.
+"""
+from __future__ import annotations
+
+import multiprocessing as mp
+import os
+import time
+
+from . import attention
+
+_SHARED = {}
+
+
+def _init(arrays, scale, causal, window):
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    _SHARED.update(arrays=arrays, scale=scale, causal=causal, window=window)
+
+
+def _one_head(task):
+    kind, b, h = task
+    a = _SHARED["arrays"]
+    s, c, w = _SHARED["scale"], _SHARED["causal"], _SHARED["window"]
+    o, lse = attention.attention_forward(a["q"][b, h], a["k"][b, h], a["v"][b, h], s, c, w)
+    if kind == "fwd":
+        return (b, h, o, lse)
+    dq, dk, dv = attention.attention_backward(a["q"][b, h], a["k"][b, h], a["v"][b, h],
+                                              a["do"][b, h], s, c, w)
+    return (b, h, o, lse, dq, dk, dv)
+
+
+def available_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def run_heads(arrays, heads, scale, causal, window, backward=False, workers=None):
+    """Evaluate the listed (b, h) heads; returns (results, seconds, workers_used).
+
+    ``arrays`` maps "q", "k", "v" (and "do" when ``backward``) to float64 [B, H, N, d].
+    The timed interval covers the pool's work only, not its start-up.
+    """
+    workers = max(1, min(workers or available_cores(), len(heads)))
+    kind = "fwdbwd" if backward else "fwd"
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_init, initargs=(arrays, scale, causal, window)) as pool:
+        pool.map(_noop, range(workers))           # start every worker before timing
+        t0 = time.perf_counter()
+        res = pool.map(_one_head, [(kind, b, h) for b, h in heads], chunksize=1)
+        dt = time.perf_counter() - t0
+    return res, dt, workers
+
+
+def _noop(_):
+    return None

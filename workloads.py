@@ -1,0 +1,105 @@
+"""Seeded synthetic workloads shared by the oracle checks, the GPU tests and the benchmark.
+
+This module draws random inputs and names shapes; it holds none of the attention
+arithmetic.  Every tensor is ``numpy.random.default_rng(seed).standard_normal``
+in float32, drawn in the order Q, K, V, dO with shape ``[B, H, N, d]`` (C order),
+then rounded on the CPU to the working dtype by torch (round to nearest even).
+The GPU receives exactly those rounded bytes and the oracle upcasts the same
+rounded values to float64, so both sides see identical inputs.
+
+Shapes follow the pages' own examples: the SDPA example shape (B=2, H=8, N=1024,
+d=64) of "Flash Attention 3.7 核心原理与实战" §3.2, the memory example
+(B=32, H=16, N=2048, d=64) of "告别OOM和训练慢…（含A100环境配置）" §1, and the
+long-sequence / causal training settings those pages discuss.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str               # "f16" | "bf16" | "f32" (f32: source values, cast per test)
+    causal: bool
+    window: tuple            # (left, right); -1 means unbounded
+    seed: int
+    backward: bool = False
+    scale: float = field(default=float("nan"))
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d) if math.isnan(self.scale) else self.scale
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+# The five workloads.  Seeds are fixed once and never tuned after seeing results.
+TINY = Workload("tiny_b1h2n128d64", 1, 2, 128, 64, "f32", False, (-1, -1), seed=1)
+BERT = Workload("sdpa_b2h8n1024d64_f16", 2, 8, 1024, 64, "f16", False, (-1, -1), seed=2)
+CAUSAL = Workload("causal_b32h16n2048d64_bf16", 32, 16, 2048, 64, "bf16", True, (-1, -1), seed=3)
+LONG_4K = Workload("window_b2h8n4096d128_bf16", 2, 8, 4096, 128, "bf16", True, (1024, 0), seed=41)
+LONG_8K = Workload("window_b2h8n8192d128_bf16", 2, 8, 8192, 128, "bf16", True, (1024, 0), seed=42)
+TRAIN = Workload("train_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=5,
+                 backward=True)
+
+ALL = (TINY, BERT, CAUSAL, LONG_4K, LONG_8K, TRAIN)
+BY_NAME = {w.name: w for w in ALL}
+
+
+def draw_f32(shape, seed: int, count: int):
+    """``count`` standard-normal float32 arrays of ``shape`` from one seeded stream."""
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(shape, dtype=np.float32) for _ in range(count)]
+
+
+def round_to(x_f32: np.ndarray, dtype: str):
+    """Round float32 values to ``dtype`` on the CPU with torch (RNE).
+
+    Returns ``(torch_cpu_tensor_in_dtype, float64_numpy_of_the_rounded_values)``.
+    """
+    import torch
+
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    t = torch.from_numpy(np.ascontiguousarray(x_f32)).to(tdt)
+    return t, t.to(torch.float64).numpy()
+
+
+def make_inputs(w: Workload, dtype: str | None = None, shape=None, seed=None, with_grad=None):
+    """Seeded inputs for workload ``w``.
+
+    Returns a dict with torch CPU tensors ``q, k, v`` (and ``do`` when the workload
+    has a backward pass) in the working dtype, and their float64 numpy copies
+    ``q64, k64, v64 (, do64)`` holding exactly the rounded values.
+    """
+    dtype = dtype or w.dtype
+    shape = tuple(shape or w.shape)
+    seed = w.seed if seed is None else seed
+    with_grad = w.backward if with_grad is None else with_grad
+    names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    out = {}
+    for name, arr in zip(names, draw_f32(shape, seed, len(names))):
+        t, a64 = round_to(arr, dtype)
+        out[name] = t
+        out[name + "64"] = a64
+    return out
+
+
+def random_case(shape, dtype: str, seed: int, with_grad: bool = False, scale_inputs: float = 1.0):
+    """Seeded N(0, scale_inputs^2) inputs of an arbitrary shape (edge-case tests)."""
+    names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    out = {}
+    for name, arr in zip(names, draw_f32(tuple(shape), seed, len(names))):
+        t, a64 = round_to(arr * np.float32(scale_inputs), dtype)
+        out[name] = t
+        out[name + "64"] = a64
+    return out
