@@ -1,0 +1,15 @@
+"""Fused exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+
+    import exact_attention_125_amd as fa
+    o, lse = fa.fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1))
+    dq, dk, dv = fa.bwd(do, q, k, v, o, lse, ...)
+    o = fa.attention(q, k, v, causal=True)           # autograd-aware
+
+q, k, v: contiguous [batch, heads, seqlen, head_dim] float16 / bfloat16 GPU tensors,
+head_dim 64 or 128.  The work runs in the HIP kernels of ``libfa.so`` (C ABI in
+include/fa.h); importing this package fails if that library has not been built.
+"""
+from ._lib import FaError, bwd, bwd_workspace_size, fwd, lib  # noqa: F401
+from .autograd import attention  # noqa: F401
+
+__all__ = ["fwd", "bwd", "attention", "bwd_workspace_size", "FaError", "lib"]

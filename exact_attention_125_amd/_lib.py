@@ -1,0 +1,151 @@
+"""ctypes binding of ``libfa.so`` (include/fa.h) — argument marshalling only.
+
+Tensors are torch tensors on the GPU; torch provides device memory and the current HIP
+stream, nothing else.  Every step of the computation runs in the library's HIP kernels.
+If the library is missing this module raises on import: there is no fallback path.
+
+Argument names follow the ``flash_attn_fn(q, k, v, dropout_p, softmax_scale, causal,
+window_size, alibi_slopes)`` call listed in "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型
+（含A100环境配置）" §4.2 (dropout and ALiBi are not supported) and the (batch, num_heads,
+seq_len, head_dim) layout of the SDPA call in "Flash Attention 3.7 核心原理与实战：加速
+Transformer模型训练与推理" §3.2.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F16, FA_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
+    4: "FA_ERR_BAD_DTYPE", 5: "FA_ERR_BAD_WINDOW", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_BAD_SCALE",
+    8: "FA_ERR_WORKSPACE", 9: "FA_ERR_HIP", 10: "FA_ERR_ALIAS",
+}
+
+# Every function include/fa.h declares, with its ctypes signature.
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_version": (_I, []),
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                    _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_last_error_detail": (ctypes.c_char_p, []),
+}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, lib):
+        self.status = status
+        msg = lib.fa_status_string(status).decode()
+        detail = lib.fa_last_error_detail().decode()
+        super().__init__(msg + (f" ({detail})" if detail else ""))
+
+
+def load(path: str = LIB_PATH):
+    """Load the library and attach signatures.  Raises if it is not built."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m exact_attention_125_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status, _lib)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float16 or bfloat16")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensors(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if t.device != ref.device:
+            raise ValueError("tensors must be on the same device")
+        if t.dtype != ref.dtype:
+            raise ValueError("q, k, v (and o, dout) must share one dtype")
+        if t.dim() != 4 or tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"expected [B, H, N, d] tensors of one shape, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _resolve(q, softmax_scale, window_size):
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    return scale, wl, wr
+
+
+def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None,
+        return_lse=True):
+    """Forward pass.  Returns ``(o, lse)`` (``lse`` None when ``return_lse`` is False)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, N, d = q.shape
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if not return_lse:
+        lse = None
+    _check(_lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                       _dtype_code(q), scale, int(bool(causal)), wl, wr, _stream(q.device)))
+    return o, lse
+
+
+def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
+        dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass.  Returns ``(dq, dk, dv)``."""
+    import torch
+    _check_tensors(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = _lib.fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(_lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(),
+                       B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
+                       _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_workspace_size(B, H, N, d) -> int:
+    return int(_lib.fa_bwd_workspace_size(B, H, N, d))

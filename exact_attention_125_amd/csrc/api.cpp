@@ -1,0 +1,163 @@
+// C ABI entry points (include/fa.h): argument validation, then kernel launch.
+//
+// Validation runs entirely on the host before any HIP call, so an invalid call enqueues
+// nothing and every error path can be exercised without a GPU.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr long kMaxRowElems = 1L << 30;   // N * d limit (32-bit byte offsets inside a head)
+constexpr long kMaxRows = 1L << 31;       // B * H * N limit
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of shape, head dim, dtype, window and scale.  Sets *empty when the call has
+// no work (some dimension is zero).
+fa_status check_common(int B, int H, int N, int d, fa_dtype dtype, float scale, int wl, int wr,
+                       bool* empty) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if ((long)N * d >= kMaxRowElems) return FA_ERR_BAD_SHAPE;
+  if ((long)B * H * (long)N >= kMaxRows) return FA_ERR_BAD_SHAPE;
+  if (wl < -1 || wr < -1) return FA_ERR_BAD_WINDOW;
+  if (!std::isfinite(scale)) return FA_ERR_BAD_SCALE;
+  *empty = (B == 0 || H == 0 || N == 0);
+  return FA_OK;
+}
+
+fa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_error = hipGetErrorString(e);
+  return FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: batch, heads or seqlen negative or too large";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head_dim must be 64 or 128";
+    case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be FA_F16 or FA_BF16";
+    case FA_ERR_BAD_WINDOW: return "FA_ERR_BAD_WINDOW: window bounds must be >= -1";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: pointers must be 16-byte aligned";
+    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: softmax_scale must be finite";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output buffer is also an input buffer";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_last_error_detail(void) { return g_last_error.c_str(); }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
+                 int causal, int window_left, int window_right, void* stream) {
+  bool empty = false;
+  fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
+                              window_right, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return FA_ERR_MISALIGNED;
+  if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k ||
+      (const void*)lse == v || (void*)lse == o)
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = batch;
+  p.H = heads;
+  p.N = seqlen;
+  p.D = head_dim;
+  p.bf16 = dtype == FA_BF16;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  g_last_error.clear();
+  return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
+  bool empty = false;
+  if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)
+    return 0;
+  if (empty) return 0;
+  return (size_t)batch * heads * seqlen * sizeof(float);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int batch, int heads, int seqlen, int head_dim,
+                 fa_dtype dtype, float softmax_scale, int causal, int window_left,
+                 int window_right, void* stream) {
+  bool empty = false;
+  fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
+                              window_right, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+  const size_t need = fa_bwd_workspace_size(batch, heads, seqlen, head_dim);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ins[] = {q, k, v, o, dout, lse, workspace};
+  void* outs[] = {dq, dk, dv};
+  for (const void* p : ins)
+    if (!aligned16(p)) return FA_ERR_MISALIGNED;
+  for (const void* p : outs)
+    if (!aligned16(p)) return FA_ERR_MISALIGNED;
+  for (void* out : outs) {
+    for (const void* in : ins)
+      if (out == in) return FA_ERR_ALIAS;
+  }
+  if (dq == dk || dq == dv || dk == dv) return FA_ERR_ALIAS;
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.B = batch;
+  p.H = heads;
+  p.N = seqlen;
+  p.D = head_dim;
+  p.bf16 = dtype == FA_BF16;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  g_last_error.clear();
+  return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

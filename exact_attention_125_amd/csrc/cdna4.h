@@ -1,0 +1,190 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, MFMA wrappers, buffer
+// loads, the LDS tile layout and cross-lane helpers.  Shared by the forward and backward
+// kernels.
+//
+// Lane layouts used throughout (wave64, verified on the device with integer matrices):
+//   v_mfma_f32_32x32x16_{bf16,f16}:  C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[m = l%32][k = 8*(l/32) + e], e = 0..7   (one 16-byte register quad)
+//     B: lane l holds B[k = 8*(l/32) + e][n = l%32]
+//     C: lane l holds C[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32], i = 0..15
+//   ds_read_b64_tr_b16: inside each 16-lane group, the 16 lanes' 8-byte reads form four
+//     rows of 16 elements (lanes 4r..4r+3 supply row r); lane t of the group receives
+//     element t of rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------- MFMA
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(i16x8 a, i16x8 b, f32x16 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two fp32 values -> two 16-bit values of the input type, round to nearest even.
+template <bool BF16>
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  if constexpr (BF16) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(unsigned, r);
+  } else {
+    f16x2 r = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(unsigned, r);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_float(unsigned short bits) {
+  if constexpr (BF16) {
+    return __uint_as_float(((unsigned)bits) << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+}
+
+// ---------------------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes).  Loads past the end return zeros, which
+// is how tails of the sequence are read without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------- LDS tiles
+// A K or V tile is stored row-major, one row per key, D 16-bit elements per row, split in
+// 16-byte chunks.  The chunk index is XOR-swizzled with a function of the row so that the
+// three access patterns (16-byte row writes, 16-byte MFMA operand reads of 16 rows at one
+// chunk, and 8-byte transposing reads of 4 rows x 4 chunks) spread over all banks.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 64) {
+    int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  } else {
+    int x = row & 15;
+    return ((x & 3) << 2) | (x >> 2);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int tile_offset(int row, int chunk) {  // bytes
+  return row * (D * 2) + ((chunk ^ chunk_swizzle<D>(row)) << 4);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char FA_LDS* base, int off) {
+  return *reinterpret_cast<const u32x4 FA_LDS*>(base + off);
+}
+
+__device__ __forceinline__ void lds_write16(char FA_LDS* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4 FA_LDS*>(base + off) = v;
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char FA_LDS* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<i16x4 FA_LDS*>(const_cast<char FA_LDS*>(base) + off));
+}
+
+// ---------------------------------------------------------------------------- cross-lane
+// The partner of lane l is lane l ^ 32.  permlane32_swap(x, x) leaves {x[l], x[l^32]} in
+// some order in every lane, so a symmetric combine of the pair is the wave-wide result.
+__device__ __forceinline__ float max_with_partner(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float min_with_partner(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_with_partner(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------- masks
+// Key j is visible to query i iff (!causal || j <= i) && (wl < 0 || j >= i - wl)
+// && (wr < 0 || j <= i + wr), and j < N.
+struct Mask {
+  int n, causal, wl, wr;
+  __device__ __forceinline__ bool visible(int i, int j) const {
+    bool ok = j < n;
+    if (causal) ok = ok && (j <= i);
+    if (wl >= 0) ok = ok && (j >= i - wl);
+    if (wr >= 0) ok = ok && (j <= i + wr);
+    return ok;
+  }
+  // Key range [lo, hi) that queries [q_first, q_last] can see at all.
+  __device__ __forceinline__ void key_range(int q_first, int q_last, int& lo, int& hi) const {
+    lo = wl >= 0 ? max(0, q_first - wl) : 0;
+    hi = n;
+    if (causal) hi = min(hi, q_last + 1);
+    if (wr >= 0) hi = min(hi, q_last + wr + 1);
+  }
+  // Whether every (i, j) in [q_first, q_last] x [j0, j1) is visible.
+  __device__ __forceinline__ bool all_visible(int q_first, int q_last, int j0, int j1) const {
+    bool ok = j1 <= n;
+    if (causal) ok = ok && (j1 - 1 <= q_first);
+    if (wl >= 0) ok = ok && (j0 >= q_last - wl);
+    if (wr >= 0) ok = ok && (j1 - 1 <= q_first + wr);
+    return ok;
+  }
+  // Query range [lo, hi) that keys [k_first, k_last] are visible to (for key-owned passes).
+  __device__ __forceinline__ void query_range(int k_first, int k_last, int& lo, int& hi) const {
+    lo = 0;
+    hi = n;
+    if (causal) lo = max(lo, k_first);
+    if (wr >= 0) lo = max(lo, k_first - wr);
+    if (wl >= 0) hi = min(hi, k_last + wl + 1);
+  }
+};
+
+// ---------------------------------------------------------------------------- grid order
+// The hardware hands consecutive workgroup ids to the 8 XCDs in turn (id % 8), and each
+// XCD has its own L2.  Map ids so that all tiles of one (batch, head) run on one XCD and
+// reuse that head's K/V from the same L2, walking each head's tiles in the given order.
+__device__ __forceinline__ void xcd_tile_order(int id, int n_bh, int n_tiles, int& bh, int& tile) {
+  if ((n_bh & 7) == 0) {
+    int xcd = id & 7;
+    int slot = id >> 3;
+    bh = (slot / n_tiles) * 8 + xcd;
+    tile = slot % n_tiles;
+  } else {
+    bh = id / n_tiles;
+    tile = id % n_tiles;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// Internal interface between the validating C-ABI layer (api.cpp) and the kernel
+// launchers (fwd.hip, bwd.hip).  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // may be null
+  int B, H, N, D;
+  bool bf16;
+  float scale;         // softmax scale
+  int causal;
+  int window_left;     // -1 = unbounded
+  int window_right;    // -1 = unbounded (ignored when causal)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // workspace: rowsum(dO * O), [B, H, N] fp32
+  int B, H, N, D;
+  bool bf16;
+  float scale;
+  int causal;
+  int window_left;
+  int window_right;
+};
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fa

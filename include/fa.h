@@ -1,0 +1,120 @@
+/*
+ * fa.h — C ABI of the fused exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes, per (batch b, head h), with queries i and keys j in [0, N):
+ *
+ *     S_ij  = softmax_scale * <Q_i, K_j>            (scaled dot products)
+ *     S_ij  = -inf where key j is hidden from query i (causal / sliding window)
+ *     O_i   = sum_j softmax_j(S_i) V_j
+ *     LSE_i = ln sum_j exp(S_ij)                    (natural log, over visible keys)
+ *
+ * This is the formula softmax(QK^T / sqrt(d_k)) V of the page "PyTorch-CUDA-v2.9镜像中使用
+ * FlashAttention提升训练速度" (section "FlashAttention：不只是更快的 Attention"), computed the
+ * way the page "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型（含A100环境配置）"
+ * describes in §2.1 (tiling) and §2.2 (running max / running sum, keeping only the
+ * normalisation statistics for the backward pass): one fused kernel, the N x N score
+ * matrix never reaches device memory.  The argument set is the one of that page's §4.2
+ * (softmax_scale, causal, window_size) and of the SDPA call of "Flash Attention 3.7 核心原理与
+ * 实战：加速Transformer模型训练与推理" §3.2 ((batch, num_heads, seq_len, head_dim) tensors).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] arrays of
+ *             `dtype` elements (last dimension contiguous, no padding).  LSE and the
+ *             backward workspace are dense [B, H, N] float32.
+ *  Memory     Every pointer is a device pointer the caller allocated (hipMalloc or any
+ *             allocator handing out device memory).  The library allocates nothing and
+ *             keeps no per-call state; it never takes ownership.  Array pointers must be
+ *             16-byte aligned.  Outputs must not be the same buffer as an input.
+ *  Shapes     B, H, N >= 0 (a zero makes the call a no-op that returns FA_OK; pointers
+ *             may then be NULL).  head_dim (d) must be 64 or 128.  N * d must be below
+ *             2^30 and B * H * N below 2^31.
+ *  Masks      causal != 0 hides keys j > i.  window_left / window_right >= 0 hide keys
+ *             j < i - window_left / j > i + window_right (bounds inclusive); -1 means
+ *             unbounded; values below -1 are rejected.  Causal and window combine (AND).
+ *  Scale      any finite float (0 gives the plain mean over visible keys).  Callers who
+ *             want the default use 1/sqrt(head_dim).
+ *  Precision  inputs fp16 or bf16; products accumulate in fp32; the probabilities are
+ *             rounded once to the input type (round to nearest even) before the P·V
+ *             product; O (and dQ, dK, dV) are rounded to the input type at the end.
+ *  Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *             enqueue work and return; the caller orders and synchronises.
+ *  Errors     Arguments are validated on the host before any HIP call; an invalid call
+ *             returns its status and enqueues nothing.  A failed launch returns
+ *             FA_ERR_HIP (details from fa_last_error_detail()).  There is no silent
+ *             fallback to another algorithm or device.
+ *  Results    are deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,            /* a required pointer is NULL                        */
+  FA_ERR_BAD_SHAPE = 2,           /* negative or too large B, H, N                     */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3,/* head_dim not in {64, 128}                          */
+  FA_ERR_BAD_DTYPE = 4,           /* dtype not FA_F16 / FA_BF16                         */
+  FA_ERR_BAD_WINDOW = 5,          /* window bound below -1                              */
+  FA_ERR_MISALIGNED = 6,          /* a pointer is not 16-byte aligned                   */
+  FA_ERR_BAD_SCALE = 7,           /* softmax_scale is NaN or infinite                   */
+  FA_ERR_WORKSPACE = 8,           /* backward workspace NULL or smaller than required   */
+  FA_ERR_HIP = 9,                 /* the HIP runtime reported an error                  */
+  FA_ERR_ALIAS = 10               /* an output buffer is also an input buffer           */
+} fa_status;
+
+typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Version of this ABI (major * 100 + minor). */
+int fa_version(void);
+
+/* Forward pass.
+ *   q, k, v  in:  [B, H, N, d] dtype
+ *   o        out: [B, H, N, d] dtype
+ *   lse      out: [B, H, N] float32, ln sum_j exp(S_ij) per query (may be NULL when the
+ *            caller needs no backward pass; the backward pass requires it)
+ * Every query has at least its own key visible (the diagonal), so O and LSE are always
+ * finite for finite inputs. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream);
+
+/* Bytes of device workspace fa_bwd needs for this shape (the per-query rowsum(dO * O)
+ * term, float32 [B, H, N]).  Returns 0 for invalid or empty shapes. */
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim);
+
+/* Backward pass by recomputation: P is rebuilt tile by tile from Q, K and the saved LSE
+ * (the forward's own output), so neither S nor P is ever stored — the recomputation
+ * the page "PyTorch-CUDA-v2.9镜像中使用FlashAttention提升训练速度" names as its third
+ * technique ("3. 重计算策略（Recomputation）").
+ *   q, k, v, o, dout  in:  [B, H, N, d] dtype (o and lse from fa_fwd on the same inputs)
+ *   lse               in:  [B, H, N] float32
+ *   dq, dk, dv        out: [B, H, N, d] dtype, gradients of sum(dout * o)
+ *   workspace         scratch of at least fa_bwd_workspace_size() bytes, 16-byte aligned;
+ *                     its contents on entry do not matter and are clobbered.
+ * Masks and scale must be those of the forward call. */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Text of the last HIP error seen by this thread (empty if none); valid until the next
+ * call on this thread. */
+const char* fa_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

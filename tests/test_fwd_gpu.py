@@ -1,0 +1,184 @@
+"""Forward parity on the GPU: the HIP kernels through the C ABI against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import (LSE_TOL, O_TOL, check_forward, say, to64, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_125_amd as fa
+    return fa
+
+
+def run(fa, inp, scale, causal, window, return_lse=True):
+    import torch
+    q, k, v = (to_dev(inp[n]) for n in "qkv")
+    o, lse = fa.fwd(q, k, v, scale, causal, window, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def sampled_rows(n, rng, extra=8):
+    base = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, n // 2, n - 130, n - 129, n - 2, n - 1}
+    base |= set(rng.integers(0, n, extra).tolist())
+    return sorted(r for r in base if 0 <= r < n)
+
+
+# --------------------------------------------------------------------------- the workloads
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiny_workload(fa, dtype):
+    w = W.TINY
+    inp = W.make_inputs(w, dtype=dtype)
+    say(f"[tiny] {w.name} as {dtype}")
+    o, lse = run(fa, inp, w.softmax_scale, w.causal, w.window)
+    err = check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], w.softmax_scale, w.causal,
+                        w.window, dtype, label=w.name)
+    say(f"[tiny] max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}")
+
+
+def test_bert_workload(fa):
+    w = W.BERT
+    inp = W.make_inputs(w)
+    say(f"[bert] {w.name}")
+    o, lse = run(fa, inp, w.softmax_scale, w.causal, w.window)
+    err = check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], w.softmax_scale, w.causal,
+                        w.window, w.dtype, label=w.name)
+    say(f"[bert] max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}")
+
+
+@pytest.mark.parametrize("w", [W.CAUSAL, W.LONG_4K, W.LONG_8K, W.TRAIN], ids=lambda w: w.name)
+def test_large_workload_sampled(fa, w):
+    """Full-size launch; the oracle checks whole heads at both ends of the batch plus sampled
+    rows of every head, and every output is checked for properties that hold at any size."""
+    import torch
+    inp = W.make_inputs(w, with_grad=False)
+    say(f"[large] {w.name} shape={w.shape} causal={w.causal} window={w.window}")
+    o, lse = run(fa, inp, w.softmax_scale, w.causal, w.window)
+    B, H, N, d = w.shape
+    rng = np.random.default_rng(w.seed + 1000)
+    full_heads = [(0, 0), (B - 1, H - 1)]
+    # whole heads (chunks of rows to bound memory)
+    for b, h in full_heads:
+        for r0 in range(0, N, 1024):
+            rows = list(range(r0, min(N, r0 + 1024)))
+            check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], w.softmax_scale, w.causal,
+                          w.window, w.dtype, heads=[(b, h)], rows=rows, label=w.name)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    err = check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], w.softmax_scale, w.causal,
+                        w.window, w.dtype, heads=heads,
+                        rows=lambda b, h: sampled_rows(N, rng), label=w.name)
+    say(f"[large] {w.name} sampled max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}")
+    # properties of every output: finite; O a convex combination of V rows (|O| <= max|V|);
+    # LSE at least the query's own (always visible) diagonal score.
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    vmax = inp["v"].abs().amax(dim=2, keepdim=True).to(torch.float32)
+    assert (o.cpu().float().abs() <= vmax + 1e-2).all()
+    diag = (inp["q"].float() * inp["k"].float()).sum(-1) * w.softmax_scale
+    assert (lse.cpu() >= diag - 1e-3).all()
+
+
+# --------------------------------------------------------------------------- edge cases
+EDGE_MASKS = [
+    (False, (-1, -1)), (True, (-1, -1)), (False, (0, 0)), (True, (0, 0)), (False, (3, 5)),
+    (True, (40, -1)), (False, (0, 70)), (False, (100, 0)), (True, (1024, 0)),
+    (False, (5000, 5000)),
+]
+
+
+@pytest.mark.parametrize("n", [1, 17, 63, 64, 65, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_edge_shapes(fa, n, d, dtype):
+    B, H = (1, 3) if n % 2 else (2, 4)       # n_bh = 3 (not a multiple of 8) or 8
+    inp = W.random_case((B, H, n, d), dtype, seed=1000 + n + d)
+    scale = 1.0 / math.sqrt(d)
+    for causal, window in EDGE_MASKS:
+        say(f"[edge] n={n} d={d} {dtype} causal={causal} window={window}")
+        o, lse = run(fa, inp, scale, causal, window)
+        check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], scale, causal, window, dtype,
+                      label=f"n={n} d={d} {dtype} causal={causal} window={window}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, None, 0.5])
+def test_scales(fa, scale):
+    inp = W.random_case((1, 2, 300, 64), "bf16", seed=77)
+    s = 1 / 8 if scale is None else scale
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (20, 9))]:
+        o, lse = run(fa, inp, scale, causal, window)
+        check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], s, causal, window, "bf16",
+                      label=f"scale={scale}")
+
+
+def test_peaked_scores(fa):
+    # large |q.k| (near one-hot softmax rows) stresses the running-max rescaling
+    inp = W.random_case((1, 2, 500, 128), "f16", seed=78)
+    import torch
+    q = inp["q"] * 6
+    inp2 = dict(inp, q=q, q64=q.to(torch.float64).numpy())
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (True, (64, 0))]:
+        o, lse = run(fa, inp2, 0.25, causal, window)
+        check_forward(o, lse, inp2["q64"], inp2["k64"], inp2["v64"], 0.25, causal, window, "f16",
+                      label="peaked")
+
+
+def test_q_equals_k_equals_v(fa):
+    # the demo configuration of "显存神技：必学FlashAttention！" §三 (k and v cloned from q)
+    inp = W.random_case((2, 8, 512, 64), "f16", seed=79)
+    same = dict(q=inp["q"], k=inp["q"], v=inp["q"], q64=inp["q64"], k64=inp["q64"],
+                v64=inp["q64"])
+    o, lse = run(fa, same, None, False, (-1, -1))
+    check_forward(o, lse, same["q64"], same["k64"], same["v64"], 1 / 8, False, (-1, -1), "f16",
+                  label="q=k=v")
+
+
+def test_deterministic_and_lse_optional(fa):
+    import torch
+    inp = W.random_case((2, 8, 777, 128), "bf16", seed=80)
+    o1, l1 = run(fa, inp, None, True, (100, 0))
+    o2, l2 = run(fa, inp, None, True, (100, 0))
+    o3, none = run(fa, inp, None, True, (100, 0), return_lse=False)
+    assert none is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_guard_bands_untouched(fa):
+    import torch
+    B, H, N, d = 1, 3, 130, 64
+    inp = W.random_case((B, H, N, d), "f16", seed=81)
+    q, k, v = (to_dev(inp[n]) for n in "qkv")
+    pad = 4096
+    obuf = torch.full((pad + B * H * N * d + pad,), 7.0, device="cuda", dtype=torch.float16)
+    lbuf = torch.full((pad + B * H * N + pad,), 7.0, device="cuda", dtype=torch.float32)
+    o = obuf[pad:pad + B * H * N * d].view(B, H, N, d)
+    lse = lbuf[pad:pad + B * H * N].view(B, H, N)
+    fa.fwd(q, k, v, None, True, (-1, -1), out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (obuf[:pad] == 7).all() and (obuf[-pad:] == 7).all()
+    assert (lbuf[:pad] == 7).all() and (lbuf[-pad:] == 7).all()
+    check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], 1 / 8, True, (-1, -1), "f16",
+                  label="guard")
+
+
+def test_empty(fa):
+    import torch
+    q = torch.empty((2, 3, 0, 64), device="cuda", dtype=torch.float16)
+    o, lse = fa.fwd(q, q, q)
+    assert o.shape == q.shape and lse.shape == (2, 3, 0)
+
+
+def test_errors_surface(fa):
+    import torch
+    q = torch.zeros((1, 1, 8, 96), device="cuda", dtype=torch.float16)
+    with pytest.raises(fa.FaError, match="UNSUPPORTED_HEAD_DIM"):
+        fa.fwd(q, q, q)
+    q = torch.zeros((1, 1, 8, 64), device="cuda", dtype=torch.float16)
+    with pytest.raises(fa.FaError, match="BAD_WINDOW"):
+        fa.fwd(q, q, q, window_size=(-3, 0))
