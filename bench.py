@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch of synthetic input: the fused
+forward (fa_fwd) followed by the recomputing backward (delta, dK/dV and dQ kernels).
+The default workload is B=8, H=16, N=4096, d=64, causal, bf16, with Q, K, V, dO drawn
+N(0, 1) from a fixed seed.  Inputs are resident in device memory before timing starts.
+
+Prints ONE JSON line:
+  value         whole-step TFLOP/s: algorithmic FLOPs (4 d per visible (query, key) pair
+                forward, 10 d backward, per (batch, head)) over the wall time of K steps
+                bracketed by device synchronisation
+  roofline      the kernel with the largest share of the step: its algorithmic FLOPs per
+                launch over its average duration (HIP events on the launch stream)
+                against the published dense bf16/fp16 MFMA peak of 2516.6 TFLOP/s
+  cpu_baseline  the float64 CPU oracle, timed on a bounded sample of the same workload
+                (a subset of the (batch, head) slices), on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "bwd.hip", "api.cpp", "launch.h")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.TRAIN.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the forward kernel alone (default: forward + backward)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=0,
+                    help="(batch, head) slices the oracle times (default: 2 per core)")
+    return ap.parse_args()
+
+
+def allowed_pairs(n, causal, window):
+    """Visible (query, key) pairs of one head: closed forms of the mask's row counts."""
+    wl, wr = window
+    total = 0
+    # row i sees keys max(0, i - wl) .. min(n - 1, i + wr') with wr' = 0 if causal
+    right = 0 if causal else wr
+    for i in range(n):
+        lo = max(0, i - wl) if wl >= 0 else 0
+        hi = min(n - 1, i + right) if right >= 0 else n - 1
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def flops(w, pairs):
+    fwd = 4.0 * w.d * w.B * w.H * pairs
+    return {"fwd": fwd, "bwd": 10.0 * w.d * w.B * w.H * pairs,
+            # algorithmic share of each backward kernel: dK/dV does 4 of the 5 products,
+            # dQ does 1 (its 2 recomputed products are not counted)
+            "dkdv": 8.0 * w.d * w.B * w.H * pairs, "dq": 2.0 * w.d * w.B * w.H * pairs}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_125_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    ent = rec.get(f"{workload}/{kernel}")
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_heads):
+    """Time the oracle on a subset of the workload's heads (before any GPU use)."""
+    from oracle import pool
+    inp = W.make_inputs(w)
+    arrays = {"q": inp["q64"], "k": inp["k64"], "v": inp["v64"]}
+    if w.backward:
+        arrays["do"] = inp["do64"]
+    cores = pool.available_cores()
+    n_heads = sample_heads or min(w.B * w.H, 2 * cores)
+    heads = [(i // w.H, i % w.H) for i in range(n_heads)]
+    _, secs, used = pool.run_heads(arrays, heads, w.softmax_scale, w.causal, w.window,
+                                   backward=w.backward, workers=cores)
+    pairs = allowed_pairs(w.N, w.causal, w.window)
+    per_head = (4.0 + (10.0 if w.backward else 0.0)) * w.d * pairs
+    return {"value": round(per_head * n_heads / secs / 1e12, 6), "unit": "TFLOP/s",
+            "cores": used, "kind": "oracle",
+            "sample": f"{n_heads} of {w.B * w.H} (batch, head) slices of {w.name}, "
+                      f"{'forward+backward' if w.backward else 'forward'}, float64 numpy, "
+                      f"{secs:.2f} s wall, one process and one BLAS thread per core"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the attention path needs no collectives and runs per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    w = W.BY_NAME[args.workload]
+    backward = w.backward and not args.forward_only
+
+    # CPU baseline first: the oracle's process pool forks before this process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w if backward else W.Workload(**{**w.__dict__, "backward": False}),
+                           args.cpu_sample_heads)
+        print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    import torch
+    import exact_attention_125_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    inp = W.make_inputs(w, with_grad=backward)
+    q, k, v = (inp[n].to("cuda") for n in "qkv")
+    do = inp["do"].to("cuda") if backward else None
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, device="cuda", dtype=torch.float32)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(fa.bwd_workspace_size(w.B, w.H, w.N, w.d), 16), device="cuda",
+                     dtype=torch.uint8)
+    scale, causal, window = w.softmax_scale, w.causal, w.window
+    stages = [("fwd", None)] + ([("delta", fa._lib.BWD_DELTA), ("dkdv", fa._lib.BWD_DKDV),
+                                 ("dq", fa._lib.BWD_DQ)] if backward else [])
+
+    def step(events=None):
+        for idx, (name, st) in enumerate(stages):
+            if events is not None:
+                events[idx][0].record()
+            if st is None:
+                fa.fwd(q, k, v, scale, causal, window, out=o, lse=lse)
+            else:
+                fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv,
+                       workspace=ws, stages=st)
+            if events is not None:
+                events[idx][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in stages] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kernel_ms = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+                 / args.steps for i, (name, _) in enumerate(stages)}
+    pairs = allowed_pairs(w.N, w.causal, w.window)
+    fl = flops(w, pairs)
+    step_flops = fl["fwd"] + (fl["bwd"] if backward else 0.0)
+    ms = wall / args.steps * 1e3
+    value = step_flops / (ms * 1e-3) / 1e12
+    nominal = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+
+    kernels = {}
+    for name, t in kernel_ms.items():
+        kf = {"fwd": fl["fwd"], "dkdv": fl["dkdv"], "dq": fl["dq"]}.get(name)
+        entry = {"ms": round(t, 4)}
+        if kf is not None:
+            entry["tflops"] = round(kf / (t * 1e-3) / 1e12, 2)
+            entry["frac"] = round(entry["tflops"] / PEAK_TFLOPS, 4)
+        else:   # delta: bandwidth kernel, reads O and dO, writes fp32 delta
+            nbytes = 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+            entry["gbs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+    dominant = max((n for n in kernel_ms if n != "delta"), key=lambda n: kernel_ms[n])
+    dom_flops = {"fwd": fl["fwd"], "dkdv": fl["dkdv"], "dq": fl["dq"]}[dominant]
+    achieved = dom_flops / (kernel_ms[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dominant, w.name)}
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s on 1 MI355X (fraction of dense bf16 MFMA peak in "
+                  "roofline)" if backward else "attention fwd TFLOP/s on 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
+                   "head_dim": w.d, "causal": w.causal, "window": list(w.window),
+                   "pass": "fwd+bwd" if backward else "fwd", "visible_pairs_per_head": pairs,
+                   "flops_per_step": step_flops,
+                   "nominal_flops_per_step": nominal * (3.5 if backward else 1.0)},
+        "kernels": kernels,
+        "fwd_tflops": kernels["fwd"]["tflops"], "fwd_frac_of_peak": kernels["fwd"]["frac"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,8 +22,9 @@ FA_F16, FA_BF16 = 0, 1
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA_ERR_BAD_DTYPE", 5: "FA_ERR_BAD_WINDOW", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_BAD_SCALE",
-    8: "FA_ERR_WORKSPACE", 9: "FA_ERR_HIP", 10: "FA_ERR_ALIAS",
+    8: "FA_ERR_WORKSPACE", 9: "FA_ERR_HIP", 10: "FA_ERR_ALIAS", 11: "FA_ERR_BAD_STAGES",
 }
+BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 # Every function include/fa.h declares, with its ctypes signature.
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -33,6 +34,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                     _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_bwd_stages": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                           _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -49,7 +52,7 @@ class FaError(RuntimeError):
 def load(path: str = LIB_PATH):
     """Load the library and attach signatures.  Raises if it is not built."""
     if not os.path.exists(path):
-        raise ImportError(f"{path} not found: build it with `python -m exact_attention_125_amd.build`")
+        raise ImportError(f"{path} not found: build it with `python exact_attention_125_amd/build.py`")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -127,8 +130,10 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
 
 
 def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
-        dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass.  Returns ``(dq, dk, dv)``."""
+        dq=None, dk=None, dv=None, workspace=None, stages=BWD_ALL):
+    """Backward pass.  Returns ``(dq, dk, dv)``.  ``stages`` (a mask of BWD_DELTA, BWD_DKDV,
+    BWD_DQ) runs a subset of the three kernels; later stages need the earlier ones' results
+    in the same ``workspace`` and outputs."""
     import torch
     _check_tensors(q, k, v, o, dout)
     B, H, N, d = q.shape
@@ -139,11 +144,11 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
     need = _lib.fa_bwd_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    _check(_lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                       workspace.numel() * workspace.element_size(),
-                       B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
-                       _stream(q.device)))
+    _check(_lib.fa_bwd_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(),
+                              B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
+                              int(stages), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -1,6 +1,7 @@
 """Build the HIP library ``libfa.so`` in-tree for gfx950 with hipcc.
 
-    python -m exact_attention_125_amd.build          # or build() from Python
+    python exact_attention_125_amd/build.py   (runs without importing the package, whose
+                                              import needs the built library)
 
 Every source under ``csrc/`` is compiled to an object in ``_build/`` (in parallel) and
 linked into ``exact_attention_125_amd/libfa.so``.  All device code is compiled with packed
@@ -21,6 +22,7 @@ ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

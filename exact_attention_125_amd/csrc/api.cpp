@@ -62,6 +62,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output buffer is also an input buffer";
+    case FA_ERR_BAD_STAGES: return "FA_ERR_BAD_STAGES: stage mask empty or unknown bits set";
   }
   return "unknown fa_status";
 }
@@ -71,6 +72,7 @@ const char* fa_last_error_detail(void) { return g_last_error.c_str(); }
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                  int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
                  int causal, int window_left, int window_right, void* stream) {
+  g_last_error.clear();
   bool empty = false;
   fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
                               window_right, &empty);
@@ -99,7 +101,6 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.causal = causal != 0;
   p.window_left = window_left;
   p.window_right = window_right;
-  g_last_error.clear();
   return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -111,12 +112,14 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   return (size_t)batch * heads * seqlen * sizeof(float);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                 size_t workspace_bytes, int batch, int heads, int seqlen, int head_dim,
-                 fa_dtype dtype, float softmax_scale, int causal, int window_left,
-                 int window_right, void* stream) {
+fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
+                        int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, unsigned stages, void* stream) {
+  g_last_error.clear();
   bool empty = false;
+  if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_BAD_STAGES;
   fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
                               window_right, &empty);
   if (st != FA_OK) return st;
@@ -156,8 +159,17 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.causal = causal != 0;
   p.window_left = window_left;
   p.window_right = window_right;
-  g_last_error.clear();
-  return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+  return hip_status(fa::launch_bwd(p, stages, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int batch, int heads, int seqlen, int head_dim,
+                 fa_dtype dtype, float softmax_scale, int causal, int window_left,
+                 int window_right, void* stream) {
+  return fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, batch,
+                       heads, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
+                       window_right, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@
 // (read as l_new = exp(m_old - m_new) l_old + sum exp(s - m_new), with O rescaled by the
 // same factor and divided by l once at the end), and the per-query-block loop of
 // "Flash Attention 3.7 核心原理与实战：加速Transformer模型训练与推理" §3.1.
+#include <type_traits>
+
 #include "cdna4.h"
 #include "launch.h"
 
@@ -129,11 +131,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int tr_key = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int stage = (t - t_begin) & 1;
-    const char FA_LDS* kt = lds + stage * 2 * kTileBytes;
-    const char FA_LDS* vt = kt + kTileBytes;
-    if (t + 1 < t_end) load_tile(t + 1);
+  // One key tile.  MASKED selects the variant for tiles that straddle an edge; the common
+  // variant has no per-element work beyond the softmax itself.
+  auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 
     // ---- S^T = K Q^T: two 32-key blocks x 32 queries
     f32x16 s[2];
@@ -147,11 +148,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    // ---- mask the tiles that straddle an edge
-    const int j0 = t * kBc;
-    const bool full = mk.all_visible(q0, q_last, j0, j0 + kBc);
     unsigned vis_bits = 0xffffffffu;
-    if (!full) {
+    if constexpr (MASKED) {
       const float sentinel = c >= 0.f ? NEG_INF : __builtin_inff();
       vis_bits = 0;
 #pragma unroll
@@ -161,11 +159,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
           const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
           const bool ok = mk.visible(qi, j);
           vis_bits |= (ok ? 1u : 0u) << (16 * mb + i);
-          if (!ok) s[mb][i] = sentinel;
+          s[mb][i] = ok ? s[mb][i] : sentinel;
         }
     }
 
-    // ---- online softmax update (base 2, scale folded into the FMA)
+    // ---- row extreme of the raw scores (max, or min for a negative scale)
     float ext;
     if (c >= 0.f) {
       ext = NEG_INF;
@@ -183,30 +181,40 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       ext = min_with_partner(ext);
     }
     const float m_tile = __builtin_isinf(ext) ? NEG_INF : ext * c;
-    const float m_new = fmaxf(m_run, m_tile);
-    const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    const float neg_m = -m_use;
 
+    // ---- running max: the reference moves to the exact row max whenever it grows, so the
+    // largest probability of a row is exactly 1 (representable in every input type).  O
+    // and l are rescaled only when some row of the wave actually grew.
+    const float m_new = fmaxf(m_run, m_tile);
+    if (__any(m_new > m_run)) {
+      // alpha = 1 for rows that did not grow (also rows with no visible key yet, where
+      // m_run - m_new would be -inf - -inf); 0 for a row's first visible key
+      const float alpha = m_new > m_run ? exp2_fast(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDb; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == NEG_INF ? 0.f : -m_run;
+
+    // P = 2^(s*c - m); l accumulates the unrounded values in fp32 (the logsumexp keeps full
+    // precision), P itself is rounded once to the input type for the P.V product.
     unsigned pk[2][8];
-    float rowsum = 0.f;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float p0 = exp2_fast(__builtin_fmaf(s[mb][i], c, neg_m));
         float p1 = exp2_fast(__builtin_fmaf(s[mb][i + 1], c, neg_m));
-        if (!full) {
+        if constexpr (MASKED) {
           p0 = (vis_bits >> (16 * mb + i)) & 1u ? p0 : 0.f;
           p1 = (vis_bits >> (16 * mb + i + 1)) & 1u ? p1 : 0.f;
         }
-        rowsum += p0 + p1;
+        part[(i >> 1) & 3] += p0 + p1;
         pk[mb][i >> 1] = pack2<BF16>(p0, p1);
       }
-    l_run = l_run * alpha + rowsum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) oacc[db] *= alpha;
+    l_run += (part[0] + part[1]) + (part[2] + part[3]);
 
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -223,7 +231,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         oacc[db] = mfma32x32x16<BF16>(vop, __builtin_bit_cast(i16x8, pb), oacc[db]);
       }
     }
+  };
 
+  for (int t = t_begin; t < t_end; ++t) {
+    const int stage = (t - t_begin) & 1;
+    const char FA_LDS* kt = lds + stage * 2 * kTileBytes;
+    const char FA_LDS* vt = kt + kTileBytes;
+    if (t + 1 < t_end) load_tile(t + 1);
+    const int j0 = t * kBc;
+    if (mk.all_visible(q0, q_last, j0, j0 + kBc))
+      tile(std::false_type{}, kt, vt, j0);
+    else
+      tile(std::true_type{}, kt, vt, j0);
     if (t + 1 < t_end) store_tile(stage ^ 1);
     __syncthreads();
   }

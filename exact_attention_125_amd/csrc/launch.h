@@ -41,6 +41,9 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// Backward stages, run in this order on one stream: delta = rowsum(dO * O) into the
+// workspace, then dK/dV, then dQ (both read delta).
+constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u;
+hipError_t launch_bwd(const BwdParams& p, unsigned stages, hipStream_t stream);
 
 }  // namespace fa

@@ -65,7 +65,8 @@ typedef enum fa_status {
   FA_ERR_BAD_SCALE = 7,           /* softmax_scale is NaN or infinite                   */
   FA_ERR_WORKSPACE = 8,           /* backward workspace NULL or smaller than required   */
   FA_ERR_HIP = 9,                 /* the HIP runtime reported an error                  */
-  FA_ERR_ALIAS = 10               /* an output buffer is also an input buffer           */
+  FA_ERR_ALIAS = 10,              /* an output buffer is also an input buffer           */
+  FA_ERR_BAD_STAGES = 11          /* fa_bwd_stages: empty mask or unknown stage bits     */
 } fa_status;
 
 typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -105,6 +106,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
                  float softmax_scale, int causal, int window_left, int window_right,
                  void* stream);
+
+/* The backward pass is three kernels.  fa_bwd runs all of them; fa_bwd_stages runs the
+ * subset in `stages` (a bitwise OR of the values below), for callers that time or schedule
+ * them one by one.  Same arguments as fa_bwd.  The stages depend on each other through the
+ * workspace and the outputs: a call for a later stage must follow (on the same stream, with
+ * the same arguments and workspace) the calls for every earlier stage.
+ *   FA_BWD_DELTA  workspace <- rowsum(dout * o) per query (float32 [B, H, N])
+ *   FA_BWD_DKDV   dk, dv    (reads workspace)
+ *   FA_BWD_DQ     dq        (reads workspace) */
+typedef enum fa_bwd_stage {
+  FA_BWD_DELTA = 1,
+  FA_BWD_DKDV = 2,
+  FA_BWD_DQ = 4,
+  FA_BWD_ALL = 7
+} fa_bwd_stage;
+
+fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        unsigned stages, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

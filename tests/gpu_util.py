@@ -5,6 +5,15 @@ Tolerances (fixed before any GPU run):
   LSE   max |LSE_gpu - LSE_oracle| <= 1e-3
   grads ||g_gpu - g_oracle||_2 / ||g_oracle||_2 <= 2e-2 for each of dQ, dK, dV
 The oracle is float64 on exactly the rounded fp16/bf16 input values.
+
+Stress inputs (softmax rows far more peaked than N(0,1) inputs at scale 1/sqrt(d) give)
+are checked against a bound derived from the arithmetic instead of the fixed one.  The
+kernel rounds each probability once to the input type and rounds O once at the end, so
+per element
+  |O_gpu - O_oracle| <= u * (sum_j P_ij |V_jc| + |O_ic|) + 1e-5,
+with u the unit roundoff of the input type (2^-8 bf16, 2^-11 fp16); the sum is the
+oracle evaluated with |V| as values.  On peaked rows with |O| >= 2 this bound exceeds
+the fixed bf16 tolerance: such outputs are limited by the bf16 format itself.
 """
 from __future__ import annotations
 
@@ -13,6 +22,7 @@ import sys
 import numpy as np
 
 O_TOL = {"f16": 2e-3, "bf16": 1e-2}
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 LSE_TOL = 1e-3
 GRAD_REL_L2 = 2e-2
 
@@ -37,9 +47,10 @@ def to64(t):
 
 
 def check_forward(o_gpu, lse_gpu, q64, k64, v64, scale, causal, window, dtype, heads=None,
-                  rows=None, label=""):
+                  rows=None, label="", derived_bound=False):
     """Compare GPU outputs to the oracle on the listed heads ((b, h) pairs) and rows
-    (None = all).  Returns (max |dO|, max |dLSE|)."""
+    (None = all).  Returns (max |dO|, max |dLSE|).  ``derived_bound`` switches the O check
+    from the fixed tolerance to the rounding bound in the module docstring."""
     import oracle
     B, H, N, _ = q64.shape
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
@@ -54,14 +65,23 @@ def check_forward(o_gpu, lse_gpu, q64, k64, v64, scale, causal, window, dtype, h
         worst_o = max(worst_o, float(do.max()))
         if lse is not None:
             worst_l = max(worst_l, float(np.abs(lse[b, h][r] - rl).max()))
-        if do.max() > O_TOL[dtype]:
-            i, c = np.unravel_index(np.argmax(do), do.shape)
+        if derived_bound:
+            wabs, _ = oracle.attention_forward_rows(q64[b, h], k64[b, h], np.abs(v64[b, h]), scale,
+                                                    causal, window, rows=r)
+            bound = UNIT_ROUNDOFF[dtype] * (wabs + np.abs(ro)) + 1e-5
+        else:
+            bound = np.full(ro.shape, O_TOL[dtype])
+        if np.any(do > bound):
+            i, c = np.unravel_index(np.argmax(do - bound), do.shape)
             raise AssertionError(
                 f"{label} O mismatch at b={b} h={h} row={r[i]} col={c}: gpu={o[b, h][r[i], c]} "
-                f"oracle={ro[i, c]} |d|={do.max():.3e} > {O_TOL[dtype]}")
+                f"oracle={ro[i, c]} |d|={do[i, c]:.3e} > {bound[i, c]:.3e}")
     assert worst_l <= LSE_TOL, f"{label} LSE mismatch {worst_l:.3e} > {LSE_TOL}"
     return worst_o, worst_l
 
 
-def rel_l2(a, b):
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+def rel_l2(a, b, floor=1e-300):
+    """||a - b|| / ||b||.  Where the true gradient vanishes (every row sees one key, so the
+    softmax has zero derivative and dQ = dK = 0 exactly) the ratio is undefined; callers then
+    pass ``floor`` = 1e-3 * ||dO|| so that rounding noise of fp32 accumulation counts as zero."""
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), floor))

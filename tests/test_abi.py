@@ -32,7 +32,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
-                            "fa_status_string", "fa_last_error_detail"])
+                            "fa_bwd_stages", "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
     from exact_attention_125_amd import _lib
@@ -109,6 +109,16 @@ def test_backward_specific(lib):
     assert bwd(lib, dv=DO) == 10
     assert bwd(lib, dk=DQ) == 10
     assert bwd(lib, ws=DK) == 10
+
+
+def test_stage_mask_rejections(lib):
+    args = [Q, K, V, O, DO, L, DQ, DK, DV, WS, 1 << 20, 2, 3, 100, 64, 1, 0.125, 0, -1, -1]
+    assert lib.fa_bwd_stages(*args, 0, None) == 11
+    assert lib.fa_bwd_stages(*args, 8, None) == 11
+    assert lib.fa_bwd_stages(*args, 0xFFFFFFFF, None) == 11
+    bad = list(args)
+    bad[14] = 96      # head dim checked for every stage mask
+    assert lib.fa_bwd_stages(*bad, 2, None) == 3
 
 
 def test_workspace_size(lib):

@@ -107,14 +107,16 @@ def test_edge_shapes(fa, n, d, dtype):
                       label=f"n={n} d={d} {dtype} causal={causal} window={window}")
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.3, None, 0.5])
+@pytest.mark.parametrize("scale", [0.0, -0.125, None, -0.3, 0.5])
 def test_scales(fa, scale):
+    # |scale| above 1/sqrt(d) sharpens the softmax beyond the workloads' statistics: those
+    # cases are checked against the derived rounding bound (tests/gpu_util.py)
     inp = W.random_case((1, 2, 300, 64), "bf16", seed=77)
     s = 1 / 8 if scale is None else scale
     for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (20, 9))]:
         o, lse = run(fa, inp, scale, causal, window)
         check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], s, causal, window, "bf16",
-                      label=f"scale={scale}")
+                      label=f"scale={scale}", derived_bound=abs(s) > 1 / 8)
 
 
 def test_peaked_scores(fa):
@@ -126,7 +128,7 @@ def test_peaked_scores(fa):
     for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (True, (64, 0))]:
         o, lse = run(fa, inp2, 0.25, causal, window)
         check_forward(o, lse, inp2["q64"], inp2["k64"], inp2["v64"], 0.25, causal, window, "f16",
-                      label="peaked")
+                      label="peaked", derived_bound=True)
 
 
 def test_q_equals_k_equals_v(fa):
