@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -32,6 +34,16 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------- compile-time loop
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, for bodies that need i as a constant.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------- MFMA
 template <bool BF16>
@@ -77,6 +89,42 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// ---------------------------------------------------------------------------- async copy
+// 16 bytes per lane from a buffer resource straight into LDS, without passing through
+// registers: lane l of the wave writes [lds + 16 l, lds + 16 l + 16).  `lds` must be the
+// same in every lane of the wave.  Out-of-range offsets write zeros and touch no memory.
+// The copy is counted by vmcnt; the consumer waits with wait_vmcnt and a barrier.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, char FA_LDS* lds,
+                                                  int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void FA_LDS*)lds, 16, byte_off, 0, 0, 0);
+}
+
+// s_waitcnt immediates (vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+// The same wait as a scheduling fence: nothing is moved across it.  Values read with
+// lds_read_tr_nowait look available to the compiler right after the read is issued, so
+// their consumers must be kept behind the wait explicitly.
+__device__ __forceinline__ void wait_lgkmcnt0_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_lgkmcnt0();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that the compiler neither reorders work across nor pads with waits of
+// its own: callers state the waits they need (wait_vmcnt / wait_lgkmcnt0) before it.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------- LDS tiles
 // A K or V tile is stored row-major, one row per key, D 16-bit elements per row, split in
 // 16-byte chunks.  The chunk index is XOR-swizzled with a function of the row so that the
@@ -110,6 +158,29 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char FA_LDS* base, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<i16x4 FA_LDS*>(const_cast<char FA_LDS*>(base) + off));
 }
+
+// The same transposing read issued as inline assembly, for kernels that manage LDS waits
+// themselves: the compiler does not see it as an LDS access, so it neither waits for
+// outstanding global->LDS copies before it (it would wait for all of them) nor waits for its
+// result.  The caller must s_waitcnt lgkmcnt(0) before using the value.  `addr` is an LDS
+// byte address, OFF an immediate byte offset.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_read_tr_nowait(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+__device__ __forceinline__ unsigned lds_addr(const char FA_LDS* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Empty statements that make a value be computed before this point (the compiler may not
+// sink it past a barrier into the phase that uses it).  They emit no instruction.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // ---------------------------------------------------------------------------- cross-lane
 // The partner of lane l is lane l ^ 32.  permlane32_swap(x, x) leaves {x[l], x[l^32]} in

@@ -1,26 +1,46 @@
 // Fused attention forward for gfx950.
 //
-// One workgroup owns one tile of Br = 128 query rows of one (batch, head); each of its four
-// waves owns 32 of those rows.  The key/value sequence streams through LDS in tiles of
-// Bc = 64 keys, double-buffered: while the waves work on tile t, the loads of tile t+1 are
-// already in flight into registers, and land in the other LDS buffer afterwards.  Per tile:
+// One workgroup owns Br = 32 * QB * WAVES query rows of one (batch, head); each wave owns
+// 32 * QB of them (QB query blocks of 32).  The key/value sequence streams through LDS in
+// tiles of Bc = 64 keys, double-buffered: while the waves work on tile t, the loads of tile
+// t+1 are in flight into registers and land in the other LDS buffer afterwards.  Per tile
+// and wave:
 //
-//   S^T = K Q^T        32x32x16 MFMAs, K from LDS (A operand), Q^T kept in registers
-//   mask               only on tiles that straddle a causal/window/sequence edge; tiles
-//                      that are hidden entirely are never visited
-//   online softmax     running max m and running sum l per query, in base 2 with the
-//                      scale folded into one FMA (x*scale*log2e - m)
-//   O^T += V^T P^T     32x32x16 MFMAs, V^T read from LDS with transposing reads, P^T taken
-//                      straight from the S^T accumulators (no LDS round trip)
+//   S^T = K Q^T        32x32x16 MFMAs; each K operand read from LDS feeds QB MFMAs (one
+//                      per query block), Q^T stays in registers for the whole loop
+//   mask               only on tiles that straddle a causal/window/sequence edge for this
+//                      wave; tiles hidden from all of the wave's queries are skipped
+//   online softmax     a per-query reference m (base 2, scale folded into one FMA
+//                      x*c - m); P = 2^(x*c - m), l += P in fp32, P rounded once to the
+//                      input type
+//   O^T += V^T P^T     32x32x16 MFMAs, V^T read from LDS with transposing reads (each
+//                      feeds QB MFMAs), P^T taken straight from the S^T accumulators
 //
 // Computing the transposed score block puts one query in each lane (keys spread over the
 // lane's registers and its partner lane l^32), so row max and row sum are in-lane
-// reductions plus one permlane32 swap, and the rescale of O^T by exp(m_old - m_new) is a
-// per-lane scalar.  The method follows the tiling of "告别OOM和训练慢：用Flash Attention加速
-// 你的PyTorch大模型（含A100环境配置）" §2.1 and its running-max / running-sum update of §2.2
-// (read as l_new = exp(m_old - m_new) l_old + sum exp(s - m_new), with O rescaled by the
-// same factor and divided by l once at the end), and the per-query-block loop of
-// "Flash Attention 3.7 核心原理与实战：加速Transformer模型训练与推理" §3.1.
+// reductions plus one permlane32 swap, and rescaling O^T is a per-lane scalar multiply.
+//
+// The method is the tiling of "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型（含A100环境
+// 配置）" §2.1 with the running-max / running-sum update of its §2.2 (read as
+// l_new = exp(m_old - m_new) l_old + sum exp(s - m_new), O rescaled by the same factor and
+// divided by l once at the end), looping over key blocks per query block as "Flash
+// Attention 3.7 核心原理与实战：加速Transformer模型训练与推理" §3.1 describes.
+//
+// The reference m of a query is the exact maximum of its first visible tile.  A later tile
+// whose maximum exceeds m by g > 0 moves m to that exact maximum (rescaling O and l) unless
+// the new largest probability 2^g is small against the mass already summed (2^g * 16 <= l)
+// and g <= kTau.  The softmax does not depend on the shift (the safe-softmax argument of the
+// same §2.2), so the result is the same up to rounding; probabilities stay at most 2^kTau,
+// which every input type represents.  Rows dominated by a few keys still get their exact
+// maximum (a probability of exactly 1, exact in every input type), while on long rows the
+// O/l rescale, a multiply per accumulator, disappears from almost every tile.  The
+// logsumexp is m + log2(l) whatever m is.
+//
+// A negative softmax scale is handled exactly by flipping the sign bits of Q in registers
+// (s * scale = (-q).k * |scale|), so the kernel only ever needs row maxima.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "cdna4.h"
@@ -30,9 +50,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBr = 32 * kWaves;   // query rows per workgroup
-constexpr int kBc = 64;            // keys per K/V tile
+constexpr int kBc = 64;           // keys per K/V tile
+constexpr float kTau = 8.0f;      // largest lag (base 2) of the reference behind a row max
 
 struct FwdArgs {
   const char* q;
@@ -43,25 +62,29 @@ struct FwdArgs {
   int n;          // sequence length
   int n_bh;       // batch * heads
   int n_qt;       // query tiles per head
-  float c;        // softmax_scale * log2(e)
+  float c;        // |softmax_scale| * log2(e)
+  unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
   int causal, wl, wr;
 };
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+template <int D, bool BF16, int WAVES, int QB>
+__global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kBr = 32 * QB * WAVES;
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kBc * kRowBytes;
-  constexpr int kChunks = D / 8;                    // 16-byte chunks per row
-  constexpr int kLoads = kBc * kChunks / 256;       // chunks per thread per tile
-  constexpr int kKs = D / 16;                       // MFMA k-steps over the head dim
-  constexpr int kDb = D / 32;                       // 32-wide blocks of the head dim
+  constexpr int kChunks = D / 8;                      // 16-byte chunks per row
+  constexpr int kLoads = kBc * kChunks / kThreads;    // chunks per thread per tile (K or V)
+  constexpr int kKs = D / 16;                         // MFMA k-steps over the head dim
+  constexpr int kDb = D / 32;                         // 32-wide blocks of the head dim
+  static_assert(kBc * kChunks % kThreads == 0, "tile must split evenly over the threads");
 
   __shared__ __attribute__((aligned(16))) char lds_raw[2 * 2 * kTileBytes];
   char FA_LDS* lds = (char FA_LDS*)(lds_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -76,25 +99,36 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const auto rk = make_rsrc(a.k + head, head_bytes);
   const auto rv = make_rsrc(a.v + head, head_bytes);
 
-  // Q^T as the B operand: lane holds query (q0 + 32 wave + l32), head-dim chunk 2 ks + hi.
-  const int qi = q0 + 32 * wave + l32;
-  i16x8 qreg[kKs];
+  // This wave's queries: block qb holds query wq0 + 32 qb + l32 in lane l.
+  const int wq0 = q0 + 32 * QB * wave;
+  const int wq1 = wq0 + 32 * QB - 1;
+
+  // Q^T as the B operand: lane holds query (wq0 + 32 qb + l32), head-dim chunk 2 ks + hi.
+  i16x8 qreg[QB][kKs];
 #pragma unroll
-  for (int ks = 0; ks < kKs; ++ks)
-    qreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, qi * kRowBytes + (2 * ks + hi) * 16));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      u32x4 x = buffer_load16(rq, (wq0 + 32 * qb + l32) * kRowBytes + (2 * ks + hi) * 16);
+      x ^= a.q_sign;
+      qreg[qb][ks] = __builtin_bit_cast(i16x8, x);
+    }
 
   const Mask mk{n, a.causal, a.wl, a.wr};
-  const int q_last = q0 + kBr - 1;
   int key_lo, key_hi;
-  mk.key_range(q0, min(q_last, n - 1), key_lo, key_hi);
+  mk.key_range(q0, min(q0 + kBr - 1, n - 1), key_lo, key_hi);
   const int t_begin = key_lo / kBc;
   const int t_end = (key_hi + kBc - 1) / kBc;
+  // The keys this wave's own queries can see (tiles outside are skipped by this wave).
+  int wkey_lo, wkey_hi;
+  mk.key_range(wq0, min(wq1, n - 1), wkey_lo, wkey_hi);
+  const bool wave_has_rows = wq0 < n;
 
   u32x4 kbuf[kLoads], vbuf[kLoads];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + kThreads * i;
       const int off = (t * kBc + c / kChunks) * kRowBytes + (c % kChunks) * 16;
       kbuf[i] = buffer_load16(rk, off);
       vbuf[i] = buffer_load16(rv, off);
@@ -105,7 +139,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     char FA_LDS* vt = kt + kTileBytes;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + kThreads * i;
       const int off = tile_offset<D>(c / kChunks, c % kChunks);
       lds_write16(kt, off, kbuf[i]);
       lds_write16(vt, off, vbuf[i]);
@@ -114,11 +148,16 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
   const float c = a.c;
   const float NEG_INF = -__builtin_inff();
-  float m_run = NEG_INF;   // running max of the scaled scores, base-2 units
-  float l_run = 0.f;       // running sum of 2^(s*c - m_run) over this lane's keys
-  f32x16 oacc[kDb];
+  float m_ref[QB];      // reference of the exponent per query, base-2 units
+  float l_run[QB];      // sum of 2^(s*c - m_ref) over this lane's keys
+  f32x16 oacc[kDb][QB];
 #pragma unroll
-  for (int db = 0; db < kDb; ++db) oacc[db] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = NEG_INF;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDb; ++db) oacc[db][qb] = f32x16{};
+  }
 
   if (t_begin < t_end) {
     load_tile(t_begin);
@@ -131,96 +170,103 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int tr_key = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
 
-  // One key tile.  MASKED selects the variant for tiles that straddle an edge; the common
-  // variant has no per-element work beyond the softmax itself.
+  // One key tile for this wave.  MASKED selects the variant for tiles that straddle an
+  // edge; the common variant has no per-element work beyond the softmax itself.
   auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0) {
     constexpr bool MASKED = decltype(masked_tag)::value;
 
-    // ---- S^T = K Q^T: two 32-key blocks x 32 queries
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const i16x8 kop = __builtin_bit_cast(i16x8, lds_read16(kt, tile_offset<D>(32 * mb + l32, 2 * ks + hi)));
-        s[mb] = mfma32x32x16<BF16>(kop, qreg[ks], s[mb]);
-      }
-    }
-
-    unsigned vis_bits = 0xffffffffu;
-    if constexpr (MASKED) {
-      const float sentinel = c >= 0.f ? NEG_INF : __builtin_inff();
-      vis_bits = 0;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const bool ok = mk.visible(qi, j);
-          vis_bits |= (ok ? 1u : 0u) << (16 * mb + i);
-          s[mb][i] = ok ? s[mb][i] : sentinel;
-        }
-    }
-
-    // ---- row extreme of the raw scores (max, or min for a negative scale)
-    float ext;
-    if (c >= 0.f) {
-      ext = NEG_INF;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ext = fmaxf(ext, s[mb][i]);
-      ext = max_with_partner(ext);
-    } else {
-      ext = __builtin_inff();
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ext = fminf(ext, s[mb][i]);
-      ext = min_with_partner(ext);
-    }
-    const float m_tile = __builtin_isinf(ext) ? NEG_INF : ext * c;
-
-    // ---- running max: the reference moves to the exact row max whenever it grows, so the
-    // largest probability of a row is exactly 1 (representable in every input type).  O
-    // and l are rescaled only when some row of the wave actually grew.
-    const float m_new = fmaxf(m_run, m_tile);
-    if (__any(m_new > m_run)) {
-      // alpha = 1 for rows that did not grow (also rows with no visible key yet, where
-      // m_run - m_new would be -inf - -inf); 0 for a row's first visible key
-      const float alpha = m_new > m_run ? exp2_fast(m_run - m_new) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < kDb; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = m_run == NEG_INF ? 0.f : -m_run;
-
-    // P = 2^(s*c - m); l accumulates the unrounded values in fp32 (the logsumexp keeps full
-    // precision), P itself is rounded once to the input type for the P.V product.
-    unsigned pk[2][8];
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T: two 32-key blocks x QB query blocks
+    f32x16 s[2][QB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p0 = exp2_fast(__builtin_fmaf(s[mb][i], c, neg_m));
-        float p1 = exp2_fast(__builtin_fmaf(s[mb][i + 1], c, neg_m));
-        if constexpr (MASKED) {
-          p0 = (vis_bits >> (16 * mb + i)) & 1u ? p0 : 0.f;
-          p1 = (vis_bits >> (16 * mb + i + 1)) & 1u ? p1 : 0.f;
-        }
-        part[(i >> 1) & 3] += p0 + p1;
-        pk[mb][i >> 1] = pack2<BF16>(p0, p1);
+      for (int qb = 0; qb < QB; ++qb) s[mb][qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const i16x8 kop =
+            __builtin_bit_cast(i16x8, lds_read16(kt, tile_offset<D>(32 * mb + l32, 2 * ks + hi)));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[mb][qb] = mfma32x32x16<BF16>(kop, qreg[qb][ks], s[mb][qb]);
       }
-    l_run += (part[0] + part[1]) + (part[2] + part[3]);
+
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = wq0 + 32 * qb + l32;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            s[mb][qb][i] = mk.visible(qi, j) ? s[mb][qb][i] : NEG_INF;
+          }
+      }
+    }
+
+    // ---- tile maximum per query; move the reference where the new maximum matters.
+    // Both lanes of a query (l and l^32) see the same m_tile and the same full-row sum, so
+    // they always take the same decision.
+    float m_tile[QB];
+    bool move[QB];
+    bool move_any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ext = s[0][qb][0];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = (mb == 0 ? 1 : 0); i < 16; ++i) ext = fmaxf(ext, s[mb][qb][i]);
+      ext = max_with_partner(ext);
+      m_tile[qb] = __builtin_isinf(ext) ? NEG_INF : ext * c;
+      // g = +inf on a row's first visible tile (m_ref = -inf); NaN or -inf (no visible key
+      // in this tile) compares false
+      const float g = m_tile[qb] - m_ref[qb];
+      const float l_row = sum_with_partner(l_run[qb]);   // all lanes take part
+      const bool heavy = exp2_fast(g + 4.f) > l_row;
+      move[qb] = (g > 0.f) & ((g > kTau) | heavy);   // no short-circuit branches
+      move_any |= move[qb];
+    }
+    if (__any(move_any)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool grow = move[qb];
+        // the first visible tile of a row has m_ref = -inf: alpha = 0 (nothing to keep)
+        const float alpha = grow ? exp2_fast(m_ref[qb] - m_tile[qb]) : 1.f;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDb; ++db) oacc[db][qb] *= alpha;
+        m_ref[qb] = grow ? m_tile[qb] : m_ref[qb];
+      }
+    }
+
+    // ---- P = 2^(s*c - m); l accumulates the unrounded values in fp32 (the logsumexp keeps
+    // full precision), P itself is rounded once to the input type for the P.V product.
+    unsigned pk[QB][2][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = m_ref[qb] == NEG_INF ? 0.f : -m_ref[qb];
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float p0 = exp2_fast(__builtin_fmaf(s[mb][qb][i], c, neg_m));
+          float p1 = exp2_fast(__builtin_fmaf(s[mb][qb][i + 1], c, neg_m));
+          if constexpr (MASKED) {   // hidden scores are -inf; also right for c == 0
+            p0 = s[mb][qb][i] == NEG_INF ? 0.f : p0;
+            p1 = s[mb][qb][i + 1] == NEG_INF ? 0.f : p1;
+          }
+          part[(i >> 1) & 3] += p0 + p1;
+          pk[qb][mb][i >> 1] = pack2<BF16>(p0, p1);
+        }
+      l_run[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+    }
 
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 pb = {pk[kk >> 1][4 * (kk & 1) + 0], pk[kk >> 1][4 * (kk & 1) + 1],
-                        pk[kk >> 1][4 * (kk & 1) + 2], pk[kk >> 1][4 * (kk & 1) + 3]};
       const int key_a = 16 * kk + tr_key;
 #pragma unroll
       for (int db = 0; db < kDb; ++db) {
@@ -228,7 +274,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         const i16x4 lo = lds_read_tr(vt, tile_offset<D>(key_a, chunk) + tr_byte);
         const i16x4 hi4 = lds_read_tr(vt, tile_offset<D>(key_a + 8, chunk) + tr_byte);
         const i16x8 vop = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma32x32x16<BF16>(vop, __builtin_bit_cast(i16x8, pb), oacc[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4 pb = {pk[qb][kk >> 1][4 * (kk & 1) + 0], pk[qb][kk >> 1][4 * (kk & 1) + 1],
+                            pk[qb][kk >> 1][4 * (kk & 1) + 2], pk[qb][kk >> 1][4 * (kk & 1) + 3]};
+          oacc[db][qb] = mfma32x32x16<BF16>(vop, __builtin_bit_cast(i16x8, pb), oacc[db][qb]);
+        }
       }
     }
   };
@@ -239,35 +290,42 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     const char FA_LDS* vt = kt + kTileBytes;
     if (t + 1 < t_end) load_tile(t + 1);
     const int j0 = t * kBc;
-    if (mk.all_visible(q0, q_last, j0, j0 + kBc))
-      tile(std::false_type{}, kt, vt, j0);
-    else
-      tile(std::true_type{}, kt, vt, j0);
+    if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo) {
+      if (mk.all_visible(wq0, wq1, j0, j0 + kBc))
+        tile(std::false_type{}, kt, vt, j0);
+      else
+        tile(std::true_type{}, kt, vt, j0);
+    }
     if (t + 1 < t_end) store_tile(stage ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
-  const float l_tot = sum_with_partner(l_run);
-  if (qi < n) {
-    const float inv = 1.f / l_tot;
-    char* orow = a.o + head + (long)qi * kRowBytes;
 #pragma unroll
-    for (int db = 0; db < kDb; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = wq0 + 32 * qb + l32;
+    const float l_tot = sum_with_partner(l_run[qb]);
+    if (qi < n) {
+      const float inv = 1.f / l_tot;
+      char* orow = a.o + head + (long)qi * kRowBytes;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = 32 * db + 8 * g + 4 * hi;
-        u32x2 w = {pack2<BF16>(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                   pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
-      }
-    if (a.lse != nullptr && hi == 0)
-      a.lse[(long)bh * n + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+      for (int db = 0; db < kDb; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * db + 8 * g + 4 * hi;
+          u32x2 w = {pack2<BF16>(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv),
+                     pack2<BF16>(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
+        }
+      if (a.lse != nullptr && hi == 0)
+        a.lse[(long)bh * n + qi] = (m_ref[qb] + __builtin_log2f(l_tot)) * kLn2;
+    }
   }
 }
 
-template <int D, bool BF16>
-hipError_t launch(const FwdParams& p, hipStream_t stream) {
+template <int D, bool BF16, int WAVES, int QB>
+hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
+  constexpr int kBr = 32 * QB * WAVES;
   FwdArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -277,18 +335,47 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   a.n = p.N;
   a.n_bh = p.B * p.H;
   a.n_qt = (p.N + kBr - 1) / kBr;
-  a.c = (float)((double)p.scale * 1.4426950408889634);
+  a.c = (float)(std::fabs((double)p.scale) * 1.4426950408889634);
+  a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
   a.causal = p.causal;
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;   // causal is a right bound of 0
   const long blocks = (long)a.n_bh * a.n_qt;
-  hipLaunchKernelGGL((fwd_kernel<D, BF16>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+// Four waves of 32 query rows per workgroup: 128-row workgroups, twice as many as the
+// 8-wave kernel's, for grids too small to fill the chip with those.
+template <int D, bool BF16>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  return launch_cfg<D, BF16, 4, 1>(p, stream);
+}
+
+// Kernel requested through the environment (FA_FWD_KERNEL = "main" or "basic"), 0 if unset.
+// A tuning and testing knob, read once per process and ignored unless set.
+int env_kernel_choice() {
+  static const int v = [] {
+    const char* e = std::getenv("FA_FWD_KERNEL");
+    if (e == nullptr) return 0;
+    if (std::strcmp(e, "main") == 0) return 1;
+    if (std::strcmp(e, "basic") == 0) return 2;
+    return 0;
+  }();
+  return v;
 }
 
 }  // namespace
 
+// The 8-wave kernel (256 rows per query tile, one workgroup per CU) needs at least one
+// query tile per CU to fill the chip; smaller grids run the four-wave kernel, whose 128-row
+// workgroups are twice as many.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+  const long pp_blocks = (long)p.B * p.H * ((p.N + 255) / 256);
+  int choice = env_kernel_choice();
+  if (choice == 0) choice = pp_blocks >= 256 ? 1 : 2;
+  if (choice == 1) return launch_fwd_main(p, stream);
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
   return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }

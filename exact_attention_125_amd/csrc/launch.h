@@ -41,6 +41,10 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+// The 8-wave forward (256 query rows per workgroup, direct global->LDS copies, two-phase
+// software pipeline), for grids that fill the chip; launch_fwd chooses between it and the
+// four-wave kernel of fwd.hip.
+hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream);
 // Backward stages, run in this order on one stream: delta = rowsum(dO * O) into the
 // workspace, then dK/dV, then dQ (both read delta).
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u;
