@@ -34,7 +34,10 @@ import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "bwd.hip", "api.cpp", "launch.h")
+KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "api.cpp", "launch.h")
+# rocprofv3 kernel names -> the bench's kernel keys
+KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_kernel", "fwd"), ("delta_kernel", "delta"),
+               ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"))
 
 
 def parse():
@@ -47,7 +50,13 @@ def parse():
                     help="time the forward kernel alone (default: forward + backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
-                    help="(batch, head) slices the oracle times (default: 2 per core)")
+                    help="(batch, head) slices the oracle times (default: all of them)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB device to device three "
+                         "times (a plain copy kernel of known traffic, for HBM counter scaling)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench made with --copy-calibration-mib; writes profiles/hbm_traffic.json")
     return ap.parse_args()
 
 
@@ -95,28 +104,89 @@ def measured_traffic(kernel, workload):
 
 
 def cpu_baseline(w, sample_heads):
-    """Time the oracle on a subset of the workload's heads (before any GPU use)."""
+    """Time the oracle on the workload's (batch, head) slices, all of them by default
+    (before any GPU use)."""
     from oracle import pool
     inp = W.make_inputs(w)
     arrays = {"q": inp["q64"], "k": inp["k64"], "v": inp["v64"]}
     if w.backward:
         arrays["do"] = inp["do64"]
     cores = pool.available_cores()
-    n_heads = sample_heads or min(w.B * w.H, 2 * cores)
+    n_heads = min(sample_heads or w.B * w.H, w.B * w.H)
     heads = [(i // w.H, i % w.H) for i in range(n_heads)]
     _, secs, used = pool.run_heads(arrays, heads, w.softmax_scale, w.causal, w.window,
-                                   backward=w.backward, workers=cores)
+                                   backward=w.backward, workers=cores, keep=False)
     pairs = allowed_pairs(w.N, w.causal, w.window)
     per_head = (4.0 + (10.0 if w.backward else 0.0)) * w.d * pairs
     return {"value": round(per_head * n_heads / secs / 1e12, 6), "unit": "TFLOP/s",
             "cores": used, "kind": "oracle",
             "sample": f"{n_heads} of {w.B * w.H} (batch, head) slices of {w.name}, "
-                      f"{'forward+backward' if w.backward else 'forward'}, float64 numpy, "
+                      f"{'forward+backward' if w.backward else 'forward'}, float64 numpy "
+                      f"materialising S and P, "
                       f"{secs:.2f} s wall, one process and one BLAS thread per core"}
+
+
+def kernel_key(name):
+    for pat, key in KERNEL_KEYS:
+        if pat in name:
+            return key
+    return None
+
+
+def pmc_summary(fetch_dir, write_dir, workload, calib_mib):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two rocprofv3 --pmc
+    runs, scaled by what the same counters read for the plain copy kernel of known size."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        per = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    name = r["Kernel_Name"]
+                    key = kernel_key(name) or ("copy" if "copy" in name.lower() else None)
+                    if key is None:
+                        continue
+                    per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                    per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    expected_kib = calib_mib * 1024.0
+    f_fac = expected_kib / fetch["copy"] if fetch.get("copy") else None
+    w_fac = expected_kib / write["copy"] if write.get("copy") else None
+    out = {}
+    for key in sorted(set(fetch) | set(write)):
+        if key == "copy":
+            continue
+        fk, wk = fetch.get(key), write.get(key)
+        ent = {"fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_scale": f_fac, "write_scale": w_fac,
+               "copy_fetch_kib_raw": fetch.get("copy"), "copy_write_kib_raw": write.get("copy"),
+               "copy_mib": calib_mib, "source_digest": source_digest()}
+        if fk is not None and wk is not None and f_fac and w_fac:
+            ent["bytes_per_launch"] = round((fk * f_fac + wk * w_fac) * 1024.0)
+        out[f"{workload}/{key}"] = ent
+    return out
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        w = W.BY_NAME[args.workload]
+        path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+        rec = {}
+        if os.path.exists(path):
+            with open(path, encoding="utf-8") as f:
+                rec = json.load(f)
+        rec.update(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], w.name,
+                               args.copy_calibration_mib or 256))
+        with open(path, "w", encoding="utf-8") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+        print(json.dumps({k: v for k, v in rec.items() if k.startswith(w.name + "/")}, indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
@@ -161,6 +231,15 @@ def main():
                        workspace=ws, stages=st)
             if events is not None:
                 events[idx][1].record()
+
+    if args.copy_calibration_mib:
+        # contents do not matter: only the bytes moved are counted
+        src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -354,16 +354,13 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 }
 
 // Kernel requested through the environment (FA_FWD_KERNEL = "main" or "basic"), 0 if unset.
-// A tuning and testing knob, read once per process and ignored unless set.
+// A tuning and testing knob, read at every call and ignored unless set.
 int env_kernel_choice() {
-  static const int v = [] {
-    const char* e = std::getenv("FA_FWD_KERNEL");
-    if (e == nullptr) return 0;
-    if (std::strcmp(e, "main") == 0) return 1;
-    if (std::strcmp(e, "basic") == 0) return 2;
-    return 0;
-  }();
-  return v;
+  const char* e = std::getenv("FA_FWD_KERNEL");
+  if (e == nullptr) return 0;
+  if (std::strcmp(e, "main") == 0) return 1;
+  if (std::strcmp(e, "basic") == 0) return 2;
+  return 0;
 }
 
 }  // namespace

@@ -14,6 +14,13 @@ per element
 with u the unit roundoff of the input type (2^-8 bf16, 2^-11 fp16); the sum is the
 oracle evaluated with |V| as values.  On peaked rows with |O| >= 2 this bound exceeds
 the fixed bf16 tolerance: such outputs are limited by the bf16 format itself.
+
+Edge shapes (short windows, few keys per row) use ``rounding="edge"``: an element passes
+if it is within the fixed tolerance, or within the derived bound and at most one step of
+the output type away from the correctly rounded oracle value.  The fixed tolerance is
+absolute while a bf16 step is 2^-7 |O| for |O| in [1, 2) and 2^-6 |O| above, so for |O|
+beyond about 2.5 a single rounding decision already approaches it.  The workloads use the
+fixed tolerance only.
 """
 from __future__ import annotations
 
@@ -46,11 +53,33 @@ def to64(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+def round_to_dtype(x64, dtype):
+    """float64 values rounded to the input type (RNE), back as float64."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x64)).to(torch_dtype(dtype))
+    return t.to(torch.float64).numpy()
+
+
+def ulp_distance(got, ref64, dtype):
+    """Steps of the output type between ``got`` (already in that type) and the correctly
+    rounded oracle value."""
+    import torch
+    r = round_to_dtype(ref64, dtype)
+    gi = torch.from_numpy(np.ascontiguousarray(got)).to(torch_dtype(dtype)).view(torch.int16)
+    ri = torch.from_numpy(np.ascontiguousarray(r)).to(torch_dtype(dtype)).view(torch.int16)
+    # map sign-magnitude to a monotone integer line
+    def mono(t):
+        t = t.to(torch.int32)
+        return torch.where(t < 0, -(t & 0x7FFF), t)
+    return (mono(gi) - mono(ri)).abs().numpy()
+
+
 def check_forward(o_gpu, lse_gpu, q64, k64, v64, scale, causal, window, dtype, heads=None,
-                  rows=None, label="", derived_bound=False):
+                  rows=None, label="", derived_bound=False, rounding="fixed"):
     """Compare GPU outputs to the oracle on the listed heads ((b, h) pairs) and rows
     (None = all).  Returns (max |dO|, max |dLSE|).  ``derived_bound`` switches the O check
-    from the fixed tolerance to the rounding bound in the module docstring."""
+    from the fixed tolerance to the rounding bound in the module docstring; ``rounding=
+    "edge"`` applies the edge-shape rule described there."""
     import oracle
     B, H, N, _ = q64.shape
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
@@ -65,12 +94,23 @@ def check_forward(o_gpu, lse_gpu, q64, k64, v64, scale, causal, window, dtype, h
         worst_o = max(worst_o, float(do.max()))
         if lse is not None:
             worst_l = max(worst_l, float(np.abs(lse[b, h][r] - rl).max()))
-        if derived_bound:
+        if derived_bound or rounding == "edge":
             wabs, _ = oracle.attention_forward_rows(q64[b, h], k64[b, h], np.abs(v64[b, h]), scale,
                                                     causal, window, rows=r)
-            bound = UNIT_ROUNDOFF[dtype] * (wabs + np.abs(ro)) + 1e-5
+            derived = UNIT_ROUNDOFF[dtype] * (wabs + np.abs(ro)) + 1e-5
+        if derived_bound:
+            bound = derived
         else:
             bound = np.full(ro.shape, O_TOL[dtype])
+        if rounding == "edge" and np.any(do > bound):
+            over = do > bound
+            steps = ulp_distance(o[b, h][r], ro, dtype)
+            ok = over & (do <= derived) & (steps <= 1)
+            if ok.any():
+                say(f"{label}: {int(ok.sum())} element(s) of b={b} h={h} over {O_TOL[dtype]} "
+                    f"within one {dtype} step of the rounded oracle (max |O| "
+                    f"{float(np.abs(ro[ok]).max()):.3f}): representation-limited")
+            bound = np.where(ok, np.inf, bound)
         if np.any(do > bound):
             i, c = np.unravel_index(np.argmax(do - bound), do.shape)
             raise AssertionError(

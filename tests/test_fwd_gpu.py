@@ -1,5 +1,6 @@
 """Forward parity on the GPU: the HIP kernels through the C ABI against the float64 oracle."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -18,12 +19,27 @@ def fa():
     return fa
 
 
-def run(fa, inp, scale, causal, window, return_lse=True):
+def run(fa, inp, scale, causal, window, return_lse=True, kernel=None):
+    """Forward through the C ABI.  ``kernel`` ("main" / "basic") forces the library's kernel
+    choice through its FA_FWD_KERNEL knob; None keeps the library's own heuristic."""
     import torch
     q, k, v = (to_dev(inp[n]) for n in "qkv")
-    o, lse = fa.fwd(q, k, v, scale, causal, window, return_lse=return_lse)
-    torch.cuda.synchronize()
+    old = os.environ.get("FA_FWD_KERNEL")
+    if kernel is not None:
+        os.environ["FA_FWD_KERNEL"] = kernel
+    try:
+        o, lse = fa.fwd(q, k, v, scale, causal, window, return_lse=return_lse)
+        torch.cuda.synchronize()
+    finally:
+        if kernel is not None:
+            if old is None:
+                os.environ.pop("FA_FWD_KERNEL", None)
+            else:
+                os.environ["FA_FWD_KERNEL"] = old
     return o, lse
+
+
+KERNELS = ["main", "basic"]   # the two forward kernels; the default choice is covered too
 
 
 def sampled_rows(n, rng, extra=8):
@@ -93,42 +109,46 @@ EDGE_MASKS = [
 ]
 
 
-@pytest.mark.parametrize("n", [1, 17, 63, 64, 65, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("n", [1, 17, 63, 64, 65, 127, 128, 129, 200, 257, 513, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_edge_shapes(fa, n, d, dtype):
+def test_edge_shapes(fa, n, d, dtype, kernel):
     B, H = (1, 3) if n % 2 else (2, 4)       # n_bh = 3 (not a multiple of 8) or 8
     inp = W.random_case((B, H, n, d), dtype, seed=1000 + n + d)
     scale = 1.0 / math.sqrt(d)
     for causal, window in EDGE_MASKS:
-        say(f"[edge] n={n} d={d} {dtype} causal={causal} window={window}")
-        o, lse = run(fa, inp, scale, causal, window)
+        say(f"[edge] {kernel} n={n} d={d} {dtype} causal={causal} window={window}")
+        o, lse = run(fa, inp, scale, causal, window, kernel=kernel)
         check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], scale, causal, window, dtype,
-                      label=f"n={n} d={d} {dtype} causal={causal} window={window}")
+                      label=f"{kernel} n={n} d={d} {dtype} causal={causal} window={window}",
+                      rounding="edge")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("scale", [0.0, -0.125, None, -0.3, 0.5])
-def test_scales(fa, scale):
+def test_scales(fa, scale, kernel):
     # |scale| above 1/sqrt(d) sharpens the softmax beyond the workloads' statistics: those
     # cases are checked against the derived rounding bound (tests/gpu_util.py)
     inp = W.random_case((1, 2, 300, 64), "bf16", seed=77)
     s = 1 / 8 if scale is None else scale
     for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (20, 9))]:
-        o, lse = run(fa, inp, scale, causal, window)
+        o, lse = run(fa, inp, scale, causal, window, kernel=kernel)
         check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], s, causal, window, "bf16",
-                      label=f"scale={scale}", derived_bound=abs(s) > 1 / 8)
+                      label=f"{kernel} scale={scale}", derived_bound=abs(s) > 1 / 8)
 
 
-def test_peaked_scores(fa):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_peaked_scores(fa, kernel):
     # large |q.k| (near one-hot softmax rows) stresses the running-max rescaling
     inp = W.random_case((1, 2, 500, 128), "f16", seed=78)
     import torch
     q = inp["q"] * 6
     inp2 = dict(inp, q=q, q64=q.to(torch.float64).numpy())
     for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (True, (64, 0))]:
-        o, lse = run(fa, inp2, 0.25, causal, window)
+        o, lse = run(fa, inp2, 0.25, causal, window, kernel=kernel)
         check_forward(o, lse, inp2["q64"], inp2["k64"], inp2["v64"], 0.25, causal, window, "f16",
-                      label="peaked", derived_bound=True)
+                      label=f"{kernel} peaked", derived_bound=True)
 
 
 def test_q_equals_k_equals_v(fa):
@@ -141,14 +161,30 @@ def test_q_equals_k_equals_v(fa):
                   label="q=k=v")
 
 
-def test_deterministic_and_lse_optional(fa):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_deterministic_and_lse_optional(fa, kernel):
     import torch
     inp = W.random_case((2, 8, 777, 128), "bf16", seed=80)
-    o1, l1 = run(fa, inp, None, True, (100, 0))
-    o2, l2 = run(fa, inp, None, True, (100, 0))
-    o3, none = run(fa, inp, None, True, (100, 0), return_lse=False)
+    o1, l1 = run(fa, inp, None, True, (100, 0), kernel=kernel)
+    o2, l2 = run(fa, inp, None, True, (100, 0), kernel=kernel)
+    o3, none = run(fa, inp, None, True, (100, 0), return_lse=False, kernel=kernel)
     assert none is None
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_causal_pairing_and_many_tiles(fa):
+    """A causal launch large enough for the main kernel to pair query tiles (and a windowed
+    one, which it does not pair), checked on rows of every query tile of several heads."""
+    import numpy as np
+    for (B, H, N, d, causal, window, seed) in [(2, 64, 1536, 64, True, (-1, -1), 82),
+                                               (2, 64, 1536, 128, True, (300, 0), 83),
+                                               (1, 128, 1100, 64, False, (-1, -1), 84)]:
+        inp = W.random_case((B, H, N, d), "bf16", seed=seed)
+        o, lse = run(fa, inp, None, causal, window)
+        rows = sorted(set(list(range(0, N, 97)) + [N - 1, 255, 256, 511, 512]))
+        heads = [(0, 0), (B - 1, H - 1), (0, H // 2), (B - 1, 3)]
+        check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], 1 / math.sqrt(d), causal, window,
+                      "bf16", heads=heads, rows=rows, label=f"pairing N={N} d={d}")
 
 
 def test_guard_bands_untouched(fa):
