@@ -109,7 +109,7 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)
     return 0;
   if (empty) return 0;
-  return (size_t)batch * heads * seqlen * sizeof(float);
+  return 2 * (size_t)batch * heads * seqlen * sizeof(float);   // -LSE / sigma, then -delta
 }
 
 fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
@@ -149,7 +149,7 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.delta = static_cast<float*>(workspace);
+  p.stats = static_cast<float*>(workspace);
   p.B = batch;
   p.H = heads;
   p.N = seqlen;

@@ -20,6 +20,9 @@
 //                 dQ^T += K^T dS^T with K^T read transposed from LDS
 // Each score tile is laid out so that the accumulator registers of S / dP are directly the
 // MFMA operand that P / dS feed, as in the forward kernel.
+#include <cstdlib>
+#include <cstring>
+
 #include "cdna4.h"
 #include "launch.h"
 
@@ -37,17 +40,19 @@ struct BwdArgs {
   char* dq;
   char* dk;
   char* dv;
-  float* delta;
+  float* stats;   // [B*H*N] -LSE / sigma, then [B*H*N] -delta
   int n;
   int n_bh;
   int n_tiles;
-  float c;        // softmax_scale * log2(e)
+  float c;        // sigma * log2(e)
+  float sigma;    // softmax_scale kept away from zero (softmax_sigma)
   float scale;    // softmax_scale
   int causal, wl, wr;
 };
 
 // ---------------------------------------------------------------------------- delta
-// One thread per query row: delta = sum_c dO[c] * O[c] with both rounded inputs in fp32.
+// One thread per query row: delta = sum_c dO[c] * O[c] with both rounded inputs in fp32,
+// stored next to log2(e) * LSE (the exponent offset the recomputation of P needs).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, long rows) {
   const long r = (long)blockIdx.x * 256 + threadIdx.x;
@@ -66,7 +71,8 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, long rows) {
              to_float<BF16>((unsigned short)(gv[w] >> 16));
     }
   }
-  a.delta[r] = acc;
+  a.stats[r] = -a.lse[r] / a.sigma;
+  a.stats[rows + r] = -acc;
 }
 
 // ---------------------------------------------------------------------------- dK, dV
@@ -98,8 +104,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const auto rk = make_rsrc(a.k + head, head_bytes);
   const auto rv = make_rsrc(a.v + head, head_bytes);
   const auto rg = make_rsrc(a.dout + head, head_bytes);
-  const float* lse = a.lse + (long)bh * n;
-  const float* delta = a.delta + (long)bh * n;
+  const long rows = (long)a.n_bh * n;
+  const float* lse2 = a.stats + (long)bh * n;
+  const float* delta = a.stats + rows + (long)bh * n;
 
   // K^T and V^T as B operands: lane holds key (k0 + l32), head-dim chunk 2 ks + hi.
   const int k_first = kt * kKvRows;
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
     const int q = s * kQStep + tid;
     if (tid < kQStep && q < n) {
-      lse_buf = lse[q] * kLog2e;
+      lse_buf = lse2[q];
       delta_buf = delta[q];
     } else {
       lse_buf = 0.f;
@@ -201,13 +208,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e;
-        float pe = exp2_fast(__builtin_fmaf(sc[i], c, -l2[e]));
+        float pe = exp2_fast(__builtin_fmaf(sc[i], c, c * l2[e]));
         if (!full) {
           const int qq = q0 + 8 * g + 4 * hi + e;
           pe = (qq < n && mk.visible(qq, key)) ? pe : 0.f;
         }
         p[e] = pe;
-        d[e] = pe * (dp[i] - de[e]);
+        d[e] = pe * (dp[i] + de[e]);
       }
       pk[2 * g] = pack2<BF16>(p[0], p[1]);
       pk[2 * g + 1] = pack2<BF16>(p[2], p[3]);
@@ -298,8 +305,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     greg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, qi * kRowBytes + (2 * ks + hi) * 16));
   }
   const bool row_ok = qi < n;
-  const float lse2 = row_ok ? a.lse[(long)bh * n + qi] * kLog2e : 0.f;
-  const float dlt = row_ok ? a.delta[(long)bh * n + qi] : 0.f;
+  const long rows = (long)a.n_bh * n;
+  const float mrow = row_ok ? a.stats[(long)bh * n + qi] : 0.f;        // -LSE / sigma
+  const float ndlt = row_ok ? a.stats[rows + (long)bh * n + qi] : 0.f;  // -delta
 
   const Mask mk{n, a.causal, a.wl, a.wr};
   const int q_last = q0 + kDqRows - 1;
@@ -333,6 +341,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < kDb; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
+  const float cm = c * mrow;   // -log2(e) LSE
 
   if (t_begin < t_end) {
     load_tile(t_begin);
@@ -374,12 +383,12 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
         float d2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float p = exp2_fast(__builtin_fmaf(sc[mb][i + e], c, -lse2));
+          float p = exp2_fast(__builtin_fmaf(sc[mb][i + e], c, cm));
           if (!full) {
             const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
             p = (row_ok && mk.visible(qi, j)) ? p : 0.f;
           }
-          d2[e] = p * (dp[mb][i + e] - dlt);
+          d2[e] = p * (dp[mb][i + e] + ndlt);
         }
         dsk[mb][i >> 1] = pack2<BF16>(d2[0], d2[1]);
       }
@@ -419,6 +428,16 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   }
 }
 
+// Backward kernel requested through the environment (FA_BWD_KERNEL = "main" or "basic"),
+// 0 if unset.  A tuning and testing knob, read at every call and ignored unless set.
+int env_bwd_choice() {
+  const char* e = std::getenv("FA_BWD_KERNEL");
+  if (e == nullptr) return 0;
+  if (std::strcmp(e, "main") == 0) return 1;
+  if (std::strcmp(e, "basic") == 0) return 2;
+  return 0;
+}
+
 BwdArgs make_args(const BwdParams& p) {
   BwdArgs a;
   a.q = static_cast<const char*>(p.q);
@@ -430,11 +449,12 @@ BwdArgs make_args(const BwdParams& p) {
   a.dq = static_cast<char*>(p.dq);
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
-  a.delta = p.delta;
+  a.stats = p.stats;
   a.n = p.N;
   a.n_bh = p.B * p.H;
   a.n_tiles = 0;
-  a.c = (float)((double)p.scale * 1.4426950408889634);
+  a.sigma = softmax_sigma(p.scale);
+  a.c = (float)((double)a.sigma * 1.4426950408889634);
   a.scale = p.scale;
   a.causal = p.causal;
   a.wl = p.window_left;
@@ -451,7 +471,9 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        stream, a, rows);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  if (stages & kBwdDkDv) {
+  if ((stages & kBwdDkDv) && env_bwd_choice() != 2) {
+    if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
+  } else if (stages & kBwdDkDv) {
     a.n_tiles = (a.n + kKvRows - 1) / kKvRows;
     hipLaunchKernelGGL((dkdv_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256),
                        0, stream, a);

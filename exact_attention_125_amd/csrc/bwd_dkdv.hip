@@ -1,0 +1,534 @@
+// dK and dV for gfx950 by recomputation: key-owned workgroups, one wave per SIMD.
+//
+// A workgroup of 4 waves owns KWG keys of one (batch, head); each wave owns KW = 32 KB of
+// them (KB = 2 blocks of 32 keys at head dim 64, 1 at 128).  The queries that can see those
+// keys stream through LDS in steps of 32.  Per step s and wave:
+//
+//   S_s  = Q_s K^T + m_s       C[query][key] layout: A = Q_s rows from LDS, B = K^T, and
+//                              the per-query m = -LSE / sigma as the initial accumulator
+//   dP_s = dO_s V^T - delta_s  A = dO_s rows from LDS, B = V^T, -delta initial accumulator
+//   P_s  = 2^(c S_s)           c = sigma log2(e); masked on edge steps (VALU)
+//   dS_s = P_s dP_s            (VALU)
+//   dV^T += dO_s^T P_s         A = dO_s^T by transposing LDS reads, B = P_s taken from the S
+//                              accumulator registers
+//   dK^T += Q_s^T dS_s         A = Q_s^T by transposing LDS reads, B = dS_s
+//
+// Every A operand read from LDS feeds KB MFMAs, one per key block, which keeps LDS issue
+// below one instruction per MFMA.  K^T, V^T and the dK^T, dV^T accumulators live in the
+// accumulation registers (AGPRs) for the whole kernel, touched only by MFMAs; the VGPRs hold
+// the per-step working set.  The step is software-pipelined in two phases, each pairing MFMA
+// work with independent VALU work:
+//
+//   phase 1   dV_s, then S_{s+1}   (MFMA)  with  dS_s     (VALU)
+//   phase 2   dK_s, then dP_{s+1}  (MFMA)  with  P_{s+1}  (VALU)
+//
+// so that the MFMA results the next phase's VALU reads come last in their phase, and the
+// LDS operands of each half are read one half ahead.  Q and dO tiles and the per-query
+// statistics arrive by direct global->LDS copies into a ring of kNS stages, kPD steps ahead,
+// published by one workgroup barrier per step.  Step s reads tiles s and s+1 and writes tile
+// s+kPD into the stage of tile s-1; the copies of tile s+2 must have landed, in every wave,
+// before the barrier that ends step s.
+//
+// The MFMAs are issued as inline assembly (cdna4.h), so the register dependencies the
+// compiler would resolve for the builtins are kept apart by the order written here: VALU
+// reads an MFMA result only in the phase after the one that produced it, the products those
+// reads need come first in their phase, and the statistics registers an MFMA reads as its
+// initial accumulator stay untouched until the phase ends.
+//
+// The gradients are the derivative of softmax(scale Q K^T + mask) V recomputed tile by
+// tile from the saved logsumexp, the recomputation of "PyTorch-CUDA-v2.9镜像中使用
+// FlashAttention提升训练速度" ("3. 重计算策略（Recomputation）") and of "告别OOM和训练慢：用Flash
+// Attention加速你的PyTorch大模型（含A100环境配置）" §2.2 (only the normalisation statistics are
+// kept): dV = P^T dO, dS = P (dO V^T - delta), dK = scale dS^T Q.
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "cdna4.h"
+#include "launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves, one per SIMD
+constexpr int kBQ = 32;         // queries per step
+constexpr int kPD = 4;          // query tiles copied ahead
+constexpr int kNS = kPD + 1;    // LDS ring stages
+
+struct DkdvArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* dout;
+  const float* mrow;     // [B*H*N] -LSE / sigma
+  const float* ndelta;   // [B*H*N] -rowsum(dO * O)
+  char* dk;
+  char* dv;
+  int n;
+  int n_bh;
+  int n_tiles;           // key tiles of KWG keys per head
+  float c;               // sigma * log2(e)
+  float scale;
+  int causal, wl, wr;
+  int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
+};
+
+template <int D>
+struct DShape {
+  static constexpr int KB = D == 64 ? 2 : 1;       // 32-key blocks per wave
+  static constexpr int KW = 32 * KB;               // keys per wave
+  static constexpr int KWG = 4 * KW;               // keys per workgroup
+  static constexpr int KS = D / 16;                // k-steps over the head dim
+  static constexpr int DB = D / 32;                // 32-dim blocks of dK^T, dV^T
+  static constexpr int RB = D * 2;                 // bytes per row
+  static constexpr int QTILE = kBQ * RB;           // bytes of a Q or dO tile
+  static constexpr int STAGE = 2 * QTILE + 256;    // Q tile, dO tile, 32 + 32 statistics
+  static constexpr int CPT = QTILE / (16 * kThreads);   // 16-byte chunks per thread per tile
+  static_assert(QTILE % (16 * kThreads) == 0, "tiles split evenly over the threads");
+};
+
+__device__ __forceinline__ f32x16 join4(const f32x4 (&v)[4]) {
+  const f32x8 lo = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  const f32x8 hi = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+// f(c) for c = B .. E-1, unrolled at compile time (c selects registers)
+template <int B, int E, typename F>
+__device__ __forceinline__ void slices(F&& f) {
+  if constexpr (B < E) {
+    f(B);
+    slices<B + 1, E>(f);
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
+  using S = DShape<D>;
+  constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
+  constexpr int STAGE = S::STAGE, CPT = S::CPT;
+
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * STAGE];
+  char FA_LDS* ring = (char FA_LDS*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, kt;
+  xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, kt);
+  const int n = a.n;
+  const long head = (long)bh * n * RB;
+  const int head_bytes = n * RB;
+  const auto rq = make_rsrc(a.q + head, head_bytes);
+  const auto rk = make_rsrc(a.k + head, head_bytes);
+  const auto rv = make_rsrc(a.v + head, head_bytes);
+  const auto rg = make_rsrc(a.dout + head, head_bytes);
+  const auto rm = make_rsrc(a.mrow + (long)bh * n, n * 4);
+  const auto rd = make_rsrc(a.ndelta + (long)bh * n, n * 4);
+  const Mask mk{n, a.causal, a.wl, a.wr};
+  const float c_scale = a.c;
+
+  // ---- this wave's keys: K^T and V^T as B operands (lane: key kw0 + 32 kb + l32, dims of
+  // chunk 2 ks + hi), zero beyond the sequence
+  const int k_first = kt * S::KWG;
+  const int kw0 = k_first + S::KW * wave;
+  i16x8 kreg[KB][KS], vreg[KB][KS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = (kw0 + 32 * kb + l32) * RB + (2 * ks + hi) * 16;
+      kreg[kb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rk, off));
+      vreg[kb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rv, off));
+    }
+  f32x16 dk[KB][DB], dv[KB][DB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk[kb][db] = f32x16{};
+      dv[kb][db] = f32x16{};
+    }
+  // into the AGPRs here; the wait states after separate those writes from the first product
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kreg[kb][ks]), "+a"(vreg[kb][ks]));
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[kb][db]), "+a"(dv[kb][db]));
+  asm volatile("s_nop 7" ::: "memory");
+
+  // ---- query steps that can see the workgroup's keys
+  int q_lo, q_hi;
+  mk.query_range(k_first, min(k_first + S::KWG, n) - 1, q_lo, q_hi);
+  const int s_begin = q_lo / kBQ;
+  const int NSTEP = q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - s_begin : 0;
+
+  // ---- per-lane constants
+  const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+  const int tr_row = (tg >> 1) * 4 + tr;
+  const int tr_byte = (tq & 1) * 8;
+  // LDS addresses of this lane's reads, kept per ring stage and moved on by one stage per
+  // step (tile, statistics and 16-row offsets are immediates):
+  //   row_a[ks]   A operand rows of a tile (query l32, chunk 2 ks + hi), stage of tile s+1
+  //   st_a        the 16 statistics of this lane's accumulator rows, stage of tile s+1
+  //   tr_a[h][db] transposed halves (rows tr_row + 8 h, dim block db), stage of tile s until
+  //               its Q^T is read, then of tile s+1
+  const unsigned ring_a = lds_addr(ring);
+  unsigned row_a[KS], st_a, tr_a[2][DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) row_a[ks] = ring_a + tile_offset<D>(l32, 2 * ks + hi);
+  st_a = ring_a + 2 * QTILE + 64 * hi;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      tr_a[h][db] = ring_a + tile_offset<D>(tr_row + 8 * h, 4 * db + 2 * (tg & 1) + (tq >> 1)) + tr_byte;
+  // byte distance from the stage of tile t to that of tile t+1
+  auto stage_step = [&](int t) __attribute__((always_inline)) {
+    return (t % kNS) == kNS - 1 ? -(kNS - 1) * STAGE : STAGE;
+  };
+  auto advance_rows = [&](int t) __attribute__((always_inline)) {   // stage of t -> of t+1
+    const int dlt = stage_step(t);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) row_a[ks] += dlt;
+    st_a += dlt;
+  };
+  auto advance_tr = [&](int t) __attribute__((always_inline)) {
+    const int dlt = stage_step(t);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) tr_a[h][db] += dlt;
+  };
+  int cp_src[CPT];              // global offset inside a tile of this thread's chunks
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int p = 16 * (tid + kThreads * i);
+    const int r = p / RB;
+    cp_src[i] = r * RB + ((((p % RB) / 16) ^ chunk_swizzle<D>(r))) * 16;
+  }
+  // statistics: lane L < 8 of wave 0 copies the 4 values of queries 4 sigma(L) .. +3 to LDS
+  // slot L, sigma(L) = 2L (L < 4) or 2(L-4)+1, so that lanes of half hi find the 16 values of
+  // their accumulator rows 8 g + 4 hi + 0..3 (g = 0..3) contiguous at slot 4 hi
+  const int st_src = 16 * (lane < 4 ? 2 * lane : 2 * (lane - 4) + 1);
+
+  // ---- copies of query tile t (relative step) into stage t % kNS: Q, dO, and the 32 m and
+  // 32 -delta values; past the last step they read beyond the buffers (zero fills, no
+  // traffic) so every step issues the same copies
+  auto issue_copies = [&](int t) __attribute__((always_inline)) {
+    const int q0 = (s_begin + t) * kBQ;
+    const int off = t < NSTEP ? q0 * RB : head_bytes;
+    char FA_LDS* st = ring + (t % kNS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      buffer_load16_lds(rq, st + 4096 * i + 1024 * wave, cp_src[i] + off);
+      buffer_load16_lds(rg, st + QTILE + 4096 * i + 1024 * wave, cp_src[i] + off);
+    }
+    if (wave == 0) {
+      const int so = t < NSTEP ? q0 * 4 : n * 4;
+      if (lane < 8) {
+        buffer_load16_lds(rm, st + 2 * QTILE, so + st_src);
+        buffer_load16_lds(rd, st + 2 * QTILE + 128, so + st_src);
+      }
+    }
+  };
+  // this wave's copies of tiles up to s+2 have landed (loads complete in order), leaving
+  // those of tiles s+3 .. s+kPD in flight; wave 0 also issues the two statistics copies
+  static_assert(kPD >= 2, "the ring holds the two tiles a step reads");
+  auto wait_copies = [&]() __attribute__((always_inline)) {
+    if (wave == 0)
+      wait_vmcnt<(kPD - 2) * (2 * CPT + 2)>();
+    else
+      wait_vmcnt<(kPD - 2) * 2 * CPT>();
+  };
+
+  // ---- operand registers.  All LDS reads in the steps are issued as inline assembly the
+  // compiler does not track (it would otherwise wait for every copy in flight into the ring
+  // before each read); the waits are explicit fences, counted in LDS reads.  The values look
+  // available to the compiler at once, so every piece stays in the register it was read into
+  // and is joined with others only where an MFMA uses it, behind the fence.
+  i16x8 qa[KS], ga[KS];             // Q, dO rows of a tile (A operands of S, dP)
+  // Q^T, dO^T of a tile (A operands of dK, dV) per 16 queries, as the two 4-element halves
+  // the transposing reads return
+  i16x4 qt_lo[2][DB], qt_hi[2][DB], gt_lo[2][DB], gt_hi[2][DB];
+  f32x4 mv[4], ndv[4];              // m and -delta of accumulator rows (initial S, dP)
+  f32x16 sacc[KB], dpacc[KB], pv[KB];
+  unsigned pk[KB][8], dsk[KB][8];
+  constexpr int kRowReads = KS + 4;         // LDS reads of one rows-and-statistics group
+  constexpr int kTrReads = 2 * 2 * DB;      // transposing reads of one tile
+  constexpr int kTrWait = kTrReads < 15 ? kTrReads : 15;
+
+  // rows (Q at TOFF 0, dO at QTILE) and statistics group WHICH (m, -delta) of the tile
+  // row_a / st_a point at
+  auto read_rows = [&](auto toff, auto which, i16x8 (&rows)[KS], f32x4 (&stv)[4])
+                       __attribute__((always_inline)) {
+    constexpr int TOFF = decltype(toff)::value, WHICH = decltype(which)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      rows[ks] = __builtin_bit_cast(i16x8, lds_read16_nowait<TOFF>(row_a[ks]));
+    static_for<4>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int g = decltype(gc)::value;
+      stv[g] = __builtin_bit_cast(f32x4, lds_read16_nowait<128 * WHICH + 16 * g>(st_a));
+    });
+  };
+  // transposed halves of the tile tr_a points at (Q^T at TOFF 0, dO^T at QTILE)
+  auto read_tr = [&](auto toff, i16x4 (&dlo)[2][DB], i16x4 (&dhi)[2][DB])
+                     __attribute__((always_inline)) {
+    constexpr int TOFF = decltype(toff)::value;
+    static_for<2>([&](auto kkc) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kkc)::value;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dlo[kk][db] = lds_read_tr_nowait<TOFF + kk * 16 * RB>(tr_a[0][db]);
+        dhi[kk][db] = lds_read_tr_nowait<TOFF + kk * 16 * RB>(tr_a[1][db]);
+      }
+    });
+  };
+  using Z = std::integral_constant<int, 0>;
+  using O = std::integral_constant<int, 1>;
+  using QT = std::integral_constant<int, QTILE>;
+
+  // ---- the four products, one MFMA at a time (m indexes the MFMAs of one product)
+  constexpr int NM = KS * KB;       // MFMAs of S or dP
+  constexpr int NG = 2 * DB * KB;   // MFMAs of dV or dK
+  static_assert(NM == 8 && NG == 8, "phases interleave 16 MFMAs");
+  auto mfma_s = [&](auto mc) __attribute__((always_inline)) {        // S = Q K^T + m
+    constexpr int m = decltype(mc)::value, ks = m / KB, kb = m % KB;
+    if constexpr (ks == 0) mfma_bagpr_init<BF16>(sacc[kb], qa[ks], kreg[kb][ks], join4(mv));
+    else mfma_bagpr_acc<BF16>(sacc[kb], qa[ks], kreg[kb][ks]);
+  };
+  auto mfma_dp = [&](auto mc) __attribute__((always_inline)) {       // dP = dO V^T - delta
+    constexpr int m = decltype(mc)::value, ks = m / KB, kb = m % KB;
+    if constexpr (ks == 0) mfma_bagpr_init<BF16>(dpacc[kb], ga[ks], vreg[kb][ks], join4(ndv));
+    else mfma_bagpr_acc<BF16>(dpacc[kb], ga[ks], vreg[kb][ks]);
+  };
+  auto mfma_dv = [&](auto mc) __attribute__((always_inline)) {       // dV^T += dO^T P
+    constexpr int m = decltype(mc)::value, kk = m / (DB * KB), db = (m / KB) % DB, kb = m % KB;
+    const u32x4 b = {pk[kb][4 * kk], pk[kb][4 * kk + 1], pk[kb][4 * kk + 2], pk[kb][4 * kk + 3]};
+    const i16x8 op = __builtin_shufflevector(gt_lo[kk][db], gt_hi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7);
+    mfma_agpr_acc<BF16>(dv[kb][db], op, __builtin_bit_cast(i16x8, b));
+  };
+  auto mfma_dk = [&](auto mc) __attribute__((always_inline)) {       // dK^T += Q^T dS
+    constexpr int m = decltype(mc)::value, kk = m / (DB * KB), db = (m / KB) % DB, kb = m % KB;
+    const u32x4 b = {dsk[kb][4 * kk], dsk[kb][4 * kk + 1], dsk[kb][4 * kk + 2], dsk[kb][4 * kk + 3]};
+    const i16x8 op = __builtin_shufflevector(qt_lo[kk][db], qt_hi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7);
+    mfma_agpr_acc<BF16>(dk[kb][db], op, __builtin_bit_cast(i16x8, b));
+  };
+
+  // ---- the VALU work in slices of two accumulator elements (c = 8 kb + g: elements 2g, 2g+1)
+  constexpr int NSL = 8 * KB;
+  // P = 2^(c S) for query 8 (i/4) + 4 hi + i%4 of the step
+  auto p_slice = [&](int c) __attribute__((always_inline)) {
+    const int kb = c >> 3, g = c & 7;
+    pv[kb][2 * g] = exp2_fast(sacc[kb][2 * g] * c_scale);
+    pv[kb][2 * g + 1] = exp2_fast(sacc[kb][2 * g + 1] * c_scale);
+    pk[kb][g] = pack2<BF16>(pv[kb][2 * g], pv[kb][2 * g + 1]);
+  };
+  // On steps that hold hidden pairs, zero them afterwards: a branch around VALU work only, so
+  // every step issues the same MFMAs.  Hidden entries were evaluated from scores the mask
+  // discards and may be infinite; they are replaced, not scaled.  Rows past the sequence need
+  // no mask: their dO and -delta are zero fills, so they add nothing to dV and their dS is 0;
+  // keys past the sequence are not stored.  So only the band dlo <= q - key <= dhi is tested:
+  // q - key - dlo = u + 8 (i/4) + i%4 with u per lane, compared unsigned against dhi - dlo.
+  auto mask_step = [&](int t) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");   // keeps the caller's branch: not worth running every step
+    const int q0 = (s_begin + t) * kBQ;
+    const unsigned span = (unsigned)(a.dhi - a.dlo);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int u = q0 + 4 * hi - (kw0 + 32 * kb + l32) - a.dlo;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pv[kb][i] = (unsigned)(u + 8 * (i >> 2) + (i & 3)) <= span ? pv[kb][i] : 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) pk[kb][g] = pack2<BF16>(pv[kb][2 * g], pv[kb][2 * g + 1]);
+    }
+  };
+  // dS = P (dP - delta)
+  auto ds_slice = [&](int c) __attribute__((always_inline)) {
+    const int kb = c >> 3, g = c & 7;
+    dsk[kb][g] = pack2<BF16>(pv[kb][2 * g] * dpacc[kb][2 * g], pv[kb][2 * g + 1] * dpacc[kb][2 * g + 1]);
+  };
+  auto edge_step = [&](int t) __attribute__((always_inline)) {   // some pair outside the band
+    const int q0 = (s_begin + t) * kBQ;
+    return q0 - (kw0 + S::KW - 1) < a.dlo || q0 + kBQ - 1 - kw0 > a.dhi;
+  };
+
+  // ---- phases: each MFMA followed by its share of the phase's VALU slices, with a
+  // scheduling fence after each pair so that the issue order is the written one
+  auto pin_phase1 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) pin(dsk[kb][g]);
+    asm volatile("" ::"v"(mv[0]), "v"(mv[1]), "v"(mv[2]), "v"(mv[3]));   // read by this phase's
+                                                                           // products: kept until here
+  };
+  auto pin_phase2 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pin(pv[kb]);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) pin(pk[kb][g]);
+    }
+    asm volatile("" ::"v"(ndv[0]), "v"(ndv[1]), "v"(ndv[2]), "v"(ndv[3]));
+  };
+  // Every step computes S, dP and P of the following tile; after the last step that tile is
+  // the zero fill past the sequence and its values go unused.  One MFMA sequence per phase,
+  // with no branch around any of it, keeps each accumulator in one set of registers.
+  // phase 1: dV_s, S_{s+1} | dS_s
+  auto phase1 = [&]() __attribute__((always_inline)) {
+    static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m == NG) wait_lgkmcnt_fence<kTrWait>();   // Q rows and m have landed
+      if constexpr (m < NG) mfma_dv(std::integral_constant<int, m>{});
+      else mfma_s(std::integral_constant<int, m - NG>{});
+      slices<m * NSL / (NG + NM), (m + 1) * NSL / (NG + NM)>(ds_slice);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pin_phase1();
+  };
+  // phase 2: dK_s, dP_{s+1} | P_{s+1}.  The slices start after the second MFMA: S_{s+1} was
+  // the last product of phase 1.
+  auto phase2 = [&]() __attribute__((always_inline)) {
+    static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m == NG) wait_lgkmcnt_fence<kTrWait>();   // dO rows and -delta have landed
+      if constexpr (m < NG) mfma_dk(std::integral_constant<int, m>{});
+      else mfma_dp(std::integral_constant<int, m - NG>{});
+      constexpr int W = NG + NM - 2;
+      if constexpr (m >= 2) slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(p_slice);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pin_phase2();
+  };
+
+  // ---- prologue: tiles 0..kPD-1, then S_0, dP_0, P_0 and the dO^T operand of step 0
+  for (int t = 0; t < kPD; ++t) issue_copies(t);
+  wait_vmcnt<0>();
+  wg_barrier();
+  if (NSTEP > 0) {
+    read_rows(Z{}, Z{}, qa, mv);
+    read_rows(QT{}, O{}, ga, ndv);
+    wait_lgkmcnt0_fence();
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_dp(mc); });
+    // the products' results are read by VALU below
+    asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pin(sacc[kb]);
+      pin(dpacc[kb]);
+    }
+    asm volatile("" ::"v"(mv[0]), "v"(mv[1]), "v"(mv[2]), "v"(mv[3]));
+    asm volatile("" ::"v"(ndv[0]), "v"(ndv[1]), "v"(ndv[2]), "v"(ndv[3]));
+    slices<0, NSL>(p_slice);
+    if (edge_step(0)) mask_step(0);
+    pin_phase2();
+    read_tr(QT{}, gt_lo, gt_hi);
+  }
+  advance_rows(0);   // rows: tile 1; transposed: tile 0
+  wait_lgkmcnt0_fence();
+
+  // ---- steps: one barrier each
+  for (int s = 0; s < NSTEP; ++s) {
+    issue_copies(s + kPD);
+    // operands of the rest of this phase and of phase 2's first half
+    read_rows(Z{}, Z{}, qa, mv);      // tile s+1
+    read_tr(Z{}, qt_lo, qt_hi);       // tile s
+    advance_tr(s);
+    phase1();
+    wait_lgkmcnt0_fence();
+    // operands of the rest of this phase and of the next phase 1's first half
+    read_rows(QT{}, O{}, ga, ndv);    // tile s+1
+    read_tr(QT{}, gt_lo, gt_hi);      // tile s+1
+    advance_rows(s + 1);
+    phase2();
+    if (s + 1 < NSTEP && edge_step(s + 1)) {
+      mask_step(s + 1);
+      pin_phase2();
+    }
+    wait_lgkmcnt0();
+    wait_copies();
+    wg_barrier();
+  }
+  wait_vmcnt<0>();   // no copy may land after the workgroup ends
+
+  // ---- epilogue: lane holds key kw0 + 32 kb + l32, dims 32 db + 8 g + 4 hi + 0..3.  The
+  // accumulators were last written by products; keep their reads the required distance away.
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[kb][db]), "+a"(dv[kb][db]));
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + 32 * kb + l32;
+    if (key < n) {
+      char* dkrow = a.dk + head + (long)key * RB;
+      char* dvrow = a.dv + head + (long)key * RB;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * db + 8 * g + 4 * hi;
+          u32x2 wk = {pack2<BF16>(dk[kb][db][4 * g + 0] * sc, dk[kb][db][4 * g + 1] * sc),
+                      pack2<BF16>(dk[kb][db][4 * g + 2] * sc, dk[kb][db][4 * g + 3] * sc)};
+          u32x2 wv = {pack2<BF16>(dv[kb][db][4 * g + 0], dv[kb][db][4 * g + 1]),
+                      pack2<BF16>(dv[kb][db][4 * g + 2], dv[kb][db][4 * g + 3])};
+          *reinterpret_cast<u32x2*>(dkrow + dim * 2) = wk;
+          *reinterpret_cast<u32x2*>(dvrow + dim * 2) = wv;
+        }
+    }
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch(const BwdParams& p, hipStream_t stream) {
+  using S = DShape<D>;
+  DkdvArgs a;
+  a.q = static_cast<const char*>(p.q);
+  a.k = static_cast<const char*>(p.k);
+  a.v = static_cast<const char*>(p.v);
+  a.dout = static_cast<const char*>(p.dout);
+  const long rows = (long)p.B * p.H * p.N;
+  a.mrow = p.stats;
+  a.ndelta = p.stats + rows;
+  a.dk = static_cast<char*>(p.dk);
+  a.dv = static_cast<char*>(p.dv);
+  a.n = p.N;
+  a.n_bh = p.B * p.H;
+  a.n_tiles = (p.N + S::KWG - 1) / S::KWG;
+  a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
+  a.scale = p.scale;
+  a.causal = p.causal;
+  a.wl = p.window_left;
+  a.wr = p.causal ? 0 : p.window_right;
+  // a window of kUnbounded or more is no bound: every i - j of a sequence the library takes
+  // (N < 2^24) lies inside it, and dhi - dlo stays below 2^32
+  constexpr int kUnbounded = 1 << 30;
+  const int wr = p.window_right < 0 ? kUnbounded : std::min(p.window_right, kUnbounded);
+  const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
+  a.dlo = p.causal ? 0 : -wr;
+  a.dhi = wl;
+  const long blocks = (long)a.n_bh * a.n_tiles;
+  hipLaunchKernelGGL((dkdv_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream) {
+  if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+}
+
+}  // namespace fa

@@ -26,6 +26,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +56,49 @@ __device__ __forceinline__ f32x16 mfma32x32x16(i16x8 a, i16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+}
+
+// The same product issued as inline assembly with the accumulator, or the B operand, held
+// in accumulation registers (AGPRs).  A kernel whose working set needs both register files
+// uses these: the compiler places every builtin MFMA of a kernel in one form.  The compiler
+// does not see them as matrix instructions, so their callers keep register dependencies
+// apart themselves: no VALU write of an operand within a few wait states before the
+// product, no other access to its result within kMfmaResultWait wait states after it (back
+// to back accumulation into the same registers is resolved by the hardware).
+constexpr int kMfmaResultWait = 20;   // wait states, a margin over what a 32x32x16 product needs
+
+// acc (AGPRs) += a * b
+template <bool BF16>
+__device__ __forceinline__ void mfma_agpr_acc(f32x16& acc, const i16x8& a, const i16x8& b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// d (VGPRs) = a * b_agpr
+template <bool BF16>
+__device__ __forceinline__ void mfma_bagpr_first(f32x16& d, const i16x8& a, const i16x8& b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+// d (VGPRs) = a * b_agpr + c
+template <bool BF16>
+__device__ __forceinline__ void mfma_bagpr_init(f32x16& d, const i16x8& a, const i16x8& b,
+                                                const f32x16& c) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+// d (VGPRs) += a * b_agpr
+template <bool BF16>
+__device__ __forceinline__ void mfma_bagpr_acc(f32x16& d, const i16x8& a, const i16x8& b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 // Two fp32 values -> two 16-bit values of the input type, round to nearest even.
@@ -170,6 +214,25 @@ __device__ __forceinline__ i16x4 lds_read_tr_nowait(unsigned addr) {
   i16x4 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
+}
+
+// A 16-byte LDS read issued the same way (no compiler-inserted waits before or after it).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_nowait(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N) as a scheduling fence: at most N LDS reads still in flight.  LDS reads
+// complete in issue order, so this waits for every read but the N latest.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt_fence() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ unsigned lds_addr(const char FA_LDS* p) {

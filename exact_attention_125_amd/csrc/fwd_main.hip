@@ -187,7 +187,9 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     f32x16 sb[2][MB];
     unsigned pk[MB][8];
     i16x8 kop[MB][KS];
-    i16x8 vop[KK][DB];
+    // V^T operands as the two halves the transposing reads return, joined where the MFMA
+    // uses them (after the wait), so no copy of them can run before the data has landed
+    i16x4 vlo[KK][DB], vhi[KK][DB];
 
     auto edge = [&](int t) __attribute__((always_inline)) {
       const int j0 = (t_begin + t) * BC;
@@ -216,9 +218,8 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
         constexpr int kk = decltype(kkc)::value;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const i16x4 lo = lds_read_tr_nowait<kk * 16 * RB>(va[0][db]);
-          const i16x4 hi4 = lds_read_tr_nowait<kk * 16 * RB>(va[1][db]);
-          vop[kk][db] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          vlo[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(va[0][db]);
+          vhi[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(va[1][db]);
         }
       });
     };
@@ -239,7 +240,8 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
                           pk[kk >> 1][4 * (kk & 1) + 2], pk[kk >> 1][4 * (kk & 1) + 3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          oacc[db] = mfma32x32x16<BF16>(vop[kk][db], __builtin_bit_cast(i16x8, pb), oacc[db]);
+          oacc[db] = mfma32x32x16<BF16>(__builtin_shufflevector(vlo[kk][db], vhi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7),
+                                        __builtin_bit_cast(i16x8, pb), oacc[db]);
       }
     };
     // hidden scores -> -inf (edge tiles only)

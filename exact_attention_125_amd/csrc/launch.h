@@ -31,7 +31,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;        // workspace: rowsum(dO * O), [B, H, N] fp32
+  float* stats;        // workspace, 2 x [B, H, N] fp32: -LSE / sigma, then -rowsum(dO * O)
   int B, H, N, D;
   bool bf16;
   float scale;
@@ -45,9 +45,21 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 // software pipeline), for grids that fill the chip; launch_fwd chooses between it and the
 // four-wave kernel of fwd.hip.
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream);
-// Backward stages, run in this order on one stream: delta = rowsum(dO * O) into the
-// workspace, then dK/dV, then dQ (both read delta).
+// Backward stages, run in this order on one stream: the row statistics (log2(e) * LSE and
+// delta = rowsum(dO * O)) into the workspace, then dK/dV, then dQ (both read them).
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u;
 hipError_t launch_bwd(const BwdParams& p, unsigned stages, hipStream_t stream);
+
+// The backward passes evaluate P = exp(scale s - LSE) as 2^(c (s + m)) with c = sigma log2(e)
+// and the per-row m = -LSE / sigma, where sigma is the scale moved away from zero (a zero
+// scale leaves every score weight equal, which sigma = 1e-30 reproduces to fp32 rounding).
+inline float softmax_sigma(float scale) {
+  constexpr float kTiny = 1e-30f;
+  if (scale >= 0.f) return scale < kTiny ? kTiny : scale;
+  return scale > -kTiny ? -kTiny : scale;
+}
+// dK/dV with key-owned workgroups of one wave per SIMD (bwd_dkdv.hip); launch_bwd chooses
+// between it and the four-wave kernel of bwd.hip.
+hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -20,8 +20,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  Layout     Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] arrays of
- *             `dtype` elements (last dimension contiguous, no padding).  LSE and the
- *             backward workspace are dense [B, H, N] float32.
+ *             `dtype` elements (last dimension contiguous, no padding).  LSE is a dense
+ *             [B, H, N] float32 array; the backward workspace holds two of them.
  *  Memory     Every pointer is a device pointer the caller allocated (hipMalloc or any
  *             allocator handing out device memory).  The library allocates nothing and
  *             keeps no per-call state; it never takes ownership.  Array pointers must be
@@ -86,8 +86,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float softmax_scale, int causal, int window_left, int window_right,
                  void* stream);
 
-/* Bytes of device workspace fa_bwd needs for this shape (the per-query rowsum(dO * O)
- * term, float32 [B, H, N]).  Returns 0 for invalid or empty shapes. */
+/* Bytes of device workspace fa_bwd needs for this shape: two float32 [B, H, N] arrays of
+ * per-query statistics (-LSE / sigma and -rowsum(dO * O), where sigma is softmax_scale moved
+ * at least 1e-30 away from zero), 8 bytes per query row.  Returns 0
+ * for invalid or empty shapes. */
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim);
 
 /* Backward pass by recomputation: P is rebuilt tile by tile from Q, K and the saved LSE
@@ -112,7 +114,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * them one by one.  Same arguments as fa_bwd.  The stages depend on each other through the
  * workspace and the outputs: a call for a later stage must follow (on the same stream, with
  * the same arguments and workspace) the calls for every earlier stage.
- *   FA_BWD_DELTA  workspace <- rowsum(dout * o) per query (float32 [B, H, N])
+ *   FA_BWD_DELTA  workspace <- -lse / sigma and -rowsum(dout * o) per query
  *   FA_BWD_DKDV   dk, dv    (reads workspace)
  *   FA_BWD_DQ     dq        (reads workspace) */
 typedef enum fa_bwd_stage {

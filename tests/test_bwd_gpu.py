@@ -1,6 +1,7 @@
 """Backward parity on the GPU: dQ, dK, dV from the recomputing kernels (C ABI) against the
 float64 oracle's derivative, each within 2e-2 relative L2 per tensor."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -19,22 +20,37 @@ def fa():
     return fa
 
 
-def run(fa, inp, scale, causal, window, stages=None):
+def run(fa, inp, scale, causal, window, stages=None, kernel=None):
+    """Forward then backward through the C ABI.  ``kernel`` ("main" / "basic") forces the
+    library's dK/dV kernel through its FA_BWD_KERNEL knob; None keeps the default."""
     import torch
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, scale, causal, window)
-    if stages is None:
-        grads = fa.bwd(do, q, k, v, o, lse, scale, causal, window)
-    else:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        ws = torch.empty(max(fa.bwd_workspace_size(*q.shape), 16), device="cuda",
-                         dtype=torch.uint8)
-        for st in stages:
-            fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv, workspace=ws,
-                   stages=st)
-        grads = (dq, dk, dv)
-    torch.cuda.synchronize()
+    old = os.environ.get("FA_BWD_KERNEL")
+    if kernel is not None:
+        os.environ["FA_BWD_KERNEL"] = kernel
+    try:
+        if stages is None:
+            grads = fa.bwd(do, q, k, v, o, lse, scale, causal, window)
+        else:
+            dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+            ws = torch.empty(max(fa.bwd_workspace_size(*q.shape), 16), device="cuda",
+                             dtype=torch.uint8)
+            for st in stages:
+                fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv,
+                       workspace=ws, stages=st)
+            grads = (dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        if kernel is not None:
+            if old is None:
+                os.environ.pop("FA_BWD_KERNEL", None)
+            else:
+                os.environ["FA_BWD_KERNEL"] = old
     return grads
+
+
+KERNELS = ["main", "basic"]   # the two dK/dV kernels; the default choice is covered too
 
 
 def check_grads(grads, inp, scale, causal, window, heads=None, label=""):
@@ -73,8 +89,12 @@ def test_train_workload_backward(fa):
     w = W.TRAIN
     inp = W.make_inputs(w)
     say(f"[train] {w.name}")
-    grads = run(fa, inp, w.softmax_scale, w.causal, w.window)
     B, H = w.B, w.H
+    basic = run(fa, inp, w.softmax_scale, w.causal, w.window, kernel="basic")
+    check_grads(basic, inp, w.softmax_scale, w.causal, w.window, heads=[(B - 1, H - 1)],
+                label=w.name + " basic dK/dV kernel")
+    del basic
+    grads = run(fa, inp, w.softmax_scale, w.causal, w.window)
     check_grads(grads, inp, w.softmax_scale, w.causal, w.window,
                 heads=[(0, 0), (B - 1, H - 1), (3, 7), (5, 2)], label=w.name)
     dq, dk, dv = grads
@@ -93,34 +113,52 @@ MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (0, 0)), (False, (7, 3)),
          (True, (50, -1)), (False, (0, 40)), (True, (1024, 0))]
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("n", [1, 17, 64, 65, 129, 200, 513])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_edge_shapes_backward(fa, n, d, dtype):
+def test_edge_shapes_backward(fa, n, d, dtype, kernel):
     B, H = (1, 3) if n % 2 else (2, 4)
     inp = W.random_case((B, H, n, d), dtype, seed=2000 + n + d, with_grad=True)
     scale = 1.0 / math.sqrt(d)
     for causal, window in MASKS:
-        grads = run(fa, inp, scale, causal, window)
+        grads = run(fa, inp, scale, causal, window, kernel=kernel)
         check_grads(grads, inp, scale, causal, window,
-                    label=f"n={n} d={d} {dtype} causal={causal} window={window}")
+                    label=f"{kernel} n={n} d={d} {dtype} causal={causal} window={window}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("scale", [0.0, -0.25, 0.6])
-def test_scales_backward(fa, scale):
+def test_scales_backward(fa, scale, kernel):
     inp = W.random_case((1, 2, 300, 64), "bf16", seed=90, with_grad=True)
     for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (20, 9))]:
-        grads = run(fa, inp, scale, causal, window)
-        check_grads(grads, inp, scale, causal, window, label=f"scale={scale}")
+        grads = run(fa, inp, scale, causal, window, kernel=kernel)
+        check_grads(grads, inp, scale, causal, window, label=f"{kernel} scale={scale}")
 
 
-def test_stages_match_single_call_and_are_deterministic(fa):
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_key_tiles_backward(fa, d, kernel):
+    """Sequences spanning many key tiles and query steps of either dK/dV kernel, with a
+    ragged tail, under each mask family."""
+    inp = W.random_case((1, 2, 1500, d), "bf16", seed=95 + d, with_grad=True)
+    scale = 1.0 / math.sqrt(d)
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (300, 77)),
+                           (True, (700, -1))]:
+        grads = run(fa, inp, scale, causal, window, kernel=kernel)
+        check_grads(grads, inp, scale, causal, window,
+                    label=f"{kernel} n=1500 d={d} causal={causal} window={window}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_stages_match_single_call_and_are_deterministic(fa, d, kernel):
     import torch
-    inp = W.random_case((2, 4, 333, 128), "bf16", seed=91, with_grad=True)
-    a = run(fa, inp, None, True, (-1, -1))
-    b = run(fa, inp, None, True, (-1, -1))
-    c = run(fa, inp, None, True, (-1, -1), stages=[1, 2, 4])
-    d = run(fa, inp, None, True, (-1, -1), stages=[1, 6])
+    inp = W.random_case((2, 4, 333, d), "bf16", seed=91, with_grad=True)
+    a = run(fa, inp, None, True, (-1, -1), kernel=kernel)
+    b = run(fa, inp, None, True, (-1, -1), kernel=kernel)
+    c = run(fa, inp, None, True, (-1, -1), stages=[1, 2, 4], kernel=kernel)
+    d = run(fa, inp, None, True, (-1, -1), stages=[1, 6], kernel=kernel)
     for x, y, z, u in zip(a, b, c, d):
         assert torch.equal(x, y) and torch.equal(x, z) and torch.equal(x, u)
 
