@@ -34,11 +34,11 @@ import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "bwd_dkdv.hip", "api.cpp",
-                  "launch.h")
+KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip",
+                  "api.cpp", "launch.h")
 # rocprofv3 kernel names -> the bench's kernel keys
 KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_kernel", "fwd"), ("delta_kernel", "delta"),
-               ("dkdv_main_kernel", "dkdv"),
+               ("dkdv_main_kernel", "dkdv"), ("dq_main_kernel", "dq"),
                ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"))
 
 

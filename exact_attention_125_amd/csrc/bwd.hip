@@ -479,7 +479,9 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  if (stages & kBwdDq) {
+  if ((stages & kBwdDq) && env_bwd_choice() != 2) {
+    if (hipError_t e = launch_dq_main(p, stream); e != hipSuccess) return e;
+  } else if (stages & kBwdDq) {
     a.n_tiles = (a.n + kDqRows - 1) / kDqRows;
     hipLaunchKernelGGL((dq_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256), 0,
                        stream, a);

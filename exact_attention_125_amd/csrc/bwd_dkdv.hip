@@ -157,12 +157,18 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kreg[kb][ks]), "+a"(vreg[kb][ks]));
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(kreg[kb][ks]);
+      in_agpr(vreg[kb][ks]);
+    }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[kb][db]), "+a"(dv[kb][db]));
-  asm volatile("s_nop 7" ::: "memory");
+    for (int db = 0; db < DB; ++db) {
+      in_agpr(dk[kb][db]);
+      in_agpr(dv[kb][db]);
+    }
+  mfma_operand_wait();
 
   // ---- query steps that can see the workgroup's keys
   int q_lo, q_hi;
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   // keys past the sequence are not stored.  So only the band dlo <= q - key <= dhi is tested:
   // q - key - dlo = u + 8 (i/4) + i%4 with u per lane, compared unsigned against dhi - dlo.
   auto mask_step = [&](int t) __attribute__((always_inline)) {
-    asm volatile("" ::: "memory");   // keeps the caller's branch: not worth running every step
+    keep_branch();   // not worth running on every step
     const int q0 = (s_begin + t) * kBQ;
     const unsigned span = (unsigned)(a.dhi - a.dlo);
 #pragma unroll
@@ -368,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int g = 0; g < 8; ++g) pin(dsk[kb][g]);
-    asm volatile("" ::"v"(mv[0]), "v"(mv[1]), "v"(mv[2]), "v"(mv[3]));   // read by this phase's
-                                                                           // products: kept until here
+#pragma unroll
+    for (int g = 0; g < 4; ++g) keep(mv[g]);   // read by this phase's products: kept until here
   };
   auto pin_phase2 = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -378,7 +384,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
 #pragma unroll
       for (int g = 0; g < 8; ++g) pin(pk[kb][g]);
     }
-    asm volatile("" ::"v"(ndv[0]), "v"(ndv[1]), "v"(ndv[2]), "v"(ndv[3]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) keep(ndv[g]);
   };
   // Every step computes S, dP and P of the following tile; after the last step that tile is
   // the zero fill past the sequence and its values go unused.  One MFMA sequence per phase,
@@ -421,14 +428,17 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
     static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
     static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_dp(mc); });
     // the products' results are read by VALU below
-    asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+    mfma_result_wait();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       pin(sacc[kb]);
       pin(dpacc[kb]);
     }
-    asm volatile("" ::"v"(mv[0]), "v"(mv[1]), "v"(mv[2]), "v"(mv[3]));
-    asm volatile("" ::"v"(ndv[0]), "v"(ndv[1]), "v"(ndv[2]), "v"(ndv[3]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      keep(mv[g]);
+      keep(ndv[g]);
+    }
     slices<0, NSL>(p_slice);
     if (edge_step(0)) mask_step(0);
     pin_phase2();
@@ -463,11 +473,14 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
 
   // ---- epilogue: lane holds key kw0 + 32 kb + l32, dims 32 db + 8 g + 4 hi + 0..3.  The
   // accumulators were last written by products; keep their reads the required distance away.
-  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+  mfma_result_wait();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[kb][db]), "+a"(dv[kb][db]));
+    for (int db = 0; db < DB; ++db) {
+      in_agpr(dk[kb][db]);
+      in_agpr(dv[kb][db]);
+    }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw0 + 32 * kb + l32;

@@ -1,0 +1,451 @@
+// dQ for gfx950 by recomputation: query-owned workgroups, one wave per SIMD.
+//
+// A workgroup of 4 waves owns QWG queries of one (batch, head); each wave owns QW = 32 QB of
+// them (QB = 2 blocks of 32 queries at head dim 64, 1 at 128), one query per lane and block.
+// The keys those queries can see stream through LDS in steps of 32.  Per step s and wave
+// (C[key][query] layouts, so a lane's accumulator entries all belong to its query):
+//
+//   S_s^T  = K_s Q^T             A = K_s rows from LDS, B = Q^T
+//   dP_s^T = V_s dO^T - delta    A = V_s rows from LDS, B = dO^T; -delta of the lane's query
+//                                as the initial accumulator
+//   P_s    = 2^(c S_s + c m)     c = sigma log2(e), m = -LSE / sigma of the lane's query
+//   dS_s   = P_s dP_s
+//   dQ^T  += K_s^T dS_s^T        A = K_s^T by transposing LDS reads, B = dS_s from the
+//                                accumulator registers
+//
+// Q^T, dO^T and the dQ^T accumulators live in the accumulation registers (AGPRs) for the
+// whole kernel, touched only by MFMAs.  The step is software-pipelined in two phases:
+//
+//   phase 1   dQ_{s-1}, then dP_s   (MFMA)  with  P_s    (VALU)
+//   phase 2   S_{s+1}               (MFMA)  with  dS_s   (VALU)
+//
+// K and V tiles arrive by direct global->LDS copies into a ring of kNS stages, kPD steps
+// ahead, published by one workgroup barrier per step.  Step s reads V_s and K_s^T from the
+// stage of tile s and K_{s+1} from that of tile s+1, and writes tile s+kPD into the stage of
+// tile s-1.  As in the dK/dV kernel, the MFMAs are inline assembly with register
+// dependencies kept apart by the written order, and all LDS reads in the steps are untracked
+// with counted waits.
+//
+// dQ = scale dS K, the query-side derivative of softmax(scale Q K^T + mask) V recomputed from
+// the saved logsumexp: the recomputation of "PyTorch-CUDA-v2.9镜像中使用FlashAttention提升训练
+// 速度" ("3. 重计算策略（Recomputation）") and of "告别OOM和训练慢：用Flash Attention加速你的
+// PyTorch大模型（含A100环境配置）" §2.2.
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "cdna4.h"
+#include "launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves, one per SIMD
+constexpr int kBK = 32;         // keys per step
+constexpr int kPD = 4;          // key tiles copied ahead
+constexpr int kNS = kPD + 1;    // LDS ring stages
+
+struct DqArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* dout;
+  const float* mrow;     // [B*H*N] -LSE / sigma
+  const float* ndelta;   // [B*H*N] -rowsum(dO * O)
+  char* dq;
+  int n;
+  int n_bh;
+  int n_tiles;           // query tiles of QWG queries per head
+  float c;               // sigma * log2(e)
+  float scale;
+  int causal, wl, wr;
+  int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
+};
+
+template <int D>
+struct QShape {
+  static constexpr int QB = D == 64 ? 2 : 1;       // 32-query blocks per wave
+  static constexpr int QW = 32 * QB;               // queries per wave
+  static constexpr int QWG = 4 * QW;               // queries per workgroup
+  static constexpr int KS = D / 16;                // k-steps over the head dim
+  static constexpr int DB = D / 32;                // 32-dim blocks of dQ^T
+  static constexpr int RB = D * 2;                 // bytes per row
+  static constexpr int KTILE = kBK * RB;           // bytes of a K or V tile
+  static constexpr int STAGE = 2 * KTILE;          // K tile, V tile
+  static constexpr int CPT = KTILE / (16 * kThreads);   // 16-byte chunks per thread per tile
+  static_assert(KTILE % (16 * kThreads) == 0, "tiles split evenly over the threads");
+};
+
+// f(c) for c = B .. E-1, unrolled at compile time (c selects registers)
+template <int B, int E, typename F>
+__device__ __forceinline__ void dq_slices(F&& f) {
+  if constexpr (B < E) {
+    f(B);
+    dq_slices<B + 1, E>(f);
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
+  using S = QShape<D>;
+  constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
+  constexpr int STAGE = S::STAGE, CPT = S::CPT;
+
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * STAGE];
+  char FA_LDS* ring = (char FA_LDS*)lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, tile;
+  xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, tile);
+  const int qt = a.n_tiles - 1 - tile;   // longest (latest) query tiles first under a causal mask
+  const int n = a.n;
+  const long head = (long)bh * n * RB;
+  const int head_bytes = n * RB;
+  const auto rq = make_rsrc(a.q + head, head_bytes);
+  const auto rk = make_rsrc(a.k + head, head_bytes);
+  const auto rv = make_rsrc(a.v + head, head_bytes);
+  const auto rg = make_rsrc(a.dout + head, head_bytes);
+  const Mask mk{n, a.causal, a.wl, a.wr};
+  const float c_scale = a.c;
+
+  // ---- this wave's queries: Q^T and dO^T as B operands (lane: query qw0 + 32 qb + l32, dims
+  // of chunk 2 ks + hi), zero beyond the sequence; their statistics as lane scalars
+  const int q_first = qt * S::QWG;
+  const int qw0 = q_first + S::QW * wave;
+  i16x8 qreg[QB][KS], greg[QB][KS];
+  float cm[QB];        // c m = -log2(e) LSE
+  f32x16 ndv[QB];      // -delta, the initial accumulator of dP
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + 32 * qb + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = q * RB + (2 * ks + hi) * 16;
+      qreg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, off));
+      greg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, off));
+    }
+    const bool ok = q < n;
+    const long r = (long)bh * n + (ok ? q : 0);
+    cm[qb] = ok ? c_scale * a.mrow[r] : 0.f;
+    const float nd = ok ? a.ndelta[r] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndv[qb][i] = nd;
+  }
+  f32x16 dqacc[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqacc[qb][db] = f32x16{};
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(qreg[qb][ks]);
+      in_agpr(greg[qb][ks]);
+    }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) in_agpr(dqacc[qb][db]);
+  mfma_operand_wait();
+
+  // ---- key steps the workgroup's queries can see
+  int k_lo, k_hi;
+  mk.key_range(q_first, min(q_first + S::QWG, n) - 1, k_lo, k_hi);
+  const int s_begin = k_lo / kBK;
+  const int NSTEP = k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
+
+  // ---- per-lane LDS addresses, moved on by one ring stage per step:
+  //   vrow_a[ks]  A operand rows (key l32, chunk 2 ks + hi) in the stage of tile s (V at +KTILE)
+  //   krow_a[ks]  the same rows in the stage of tile s+1 (K)
+  //   tr_a[h][db] transposed halves (rows tr_row + 8 h, dim block db) in the stage of tile s
+  const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+  const int tr_row = (tg >> 1) * 4 + tr;
+  const int tr_byte = (tq & 1) * 8;
+  const unsigned ring_a = lds_addr(ring);
+  unsigned vrow_a[KS], krow_a[KS], tr_a[2][DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    vrow_a[ks] = ring_a + tile_offset<D>(l32, 2 * ks + hi);
+    krow_a[ks] = vrow_a[ks] + STAGE;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      tr_a[h][db] = ring_a + tile_offset<D>(tr_row + 8 * h, 4 * db + 2 * (tg & 1) + (tq >> 1)) + tr_byte;
+  auto stage_step = [&](int t) __attribute__((always_inline)) {   // stage of t -> of t+1
+    return (t % kNS) == kNS - 1 ? -(kNS - 1) * STAGE : STAGE;
+  };
+  int cp_src[CPT];              // global offset inside a tile of this thread's chunks
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int p = 16 * (tid + kThreads * i);
+    const int r = p / RB;
+    cp_src[i] = r * RB + ((((p % RB) / 16) ^ chunk_swizzle<D>(r))) * 16;
+  }
+
+  // ---- copies of key tile t (relative step) into stage t % kNS; past the last step they
+  // read beyond the buffers (zero fills, no traffic) so every step issues the same copies
+  auto issue_copies = [&](int t) __attribute__((always_inline)) {
+    const int off = t < NSTEP ? (s_begin + t) * kBK * RB : head_bytes;
+    char FA_LDS* st = ring + (t % kNS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      buffer_load16_lds(rk, st + 4096 * i + 1024 * wave, cp_src[i] + off);
+      buffer_load16_lds(rv, st + KTILE + 4096 * i + 1024 * wave, cp_src[i] + off);
+    }
+  };
+  // this wave's copies of tiles up to s+2 have landed, those of s+3 .. s+kPD in flight
+  static_assert(kPD >= 2, "the ring holds the two tiles a step reads");
+
+  // ---- operand registers (untracked LDS reads; joined with others only at the MFMA)
+  i16x8 ka[KS], va[KS];             // K_{s+1}, V_s rows (A operands of S^T, dP^T)
+  i16x4 kt_lo[2][DB], kt_hi[2][DB]; // K^T halves of a tile (A operand of dQ^T)
+  f32x16 sacc[QB], dpacc[QB], pv[QB];
+  unsigned dsk[QB][8];
+  constexpr int kTrReads = 2 * 2 * DB;
+  (void)kTrReads;
+
+  auto read_rows = [&](const unsigned (&addr)[KS], auto toff, i16x8 (&rows)[KS])
+                       __attribute__((always_inline)) {
+    constexpr int TOFF = decltype(toff)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      rows[ks] = __builtin_bit_cast(i16x8, lds_read16_nowait<TOFF>(addr[ks]));
+  };
+  auto read_kt = [&]() __attribute__((always_inline)) {
+    static_for<2>([&](auto kkc) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kkc)::value;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        kt_lo[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[0][db]);
+        kt_hi[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[1][db]);
+      }
+    });
+  };
+  using Z = std::integral_constant<int, 0>;
+  using KT = std::integral_constant<int, KTILE>;
+
+  // ---- the three products, one MFMA at a time
+  constexpr int NM = KS * QB;       // MFMAs of S^T or dP^T
+  constexpr int NG = 2 * DB * QB;   // MFMAs of dQ^T
+  static_assert(NM == 8 && NG == 8, "phases interleave 16 + 8 MFMAs");
+  auto mfma_s = [&](auto mc) __attribute__((always_inline)) {        // S^T = K Q^T
+    constexpr int m = decltype(mc)::value, ks = m / QB, qb = m % QB;
+    if constexpr (ks == 0) mfma_bagpr_first<BF16>(sacc[qb], ka[ks], qreg[qb][ks]);
+    else mfma_bagpr_acc<BF16>(sacc[qb], ka[ks], qreg[qb][ks]);
+  };
+  auto mfma_dp = [&](auto mc) __attribute__((always_inline)) {       // dP^T = V dO^T - delta
+    constexpr int m = decltype(mc)::value, ks = m / QB, qb = m % QB;
+    if constexpr (ks == 0) mfma_bagpr_init<BF16>(dpacc[qb], va[ks], greg[qb][ks], ndv[qb]);
+    else mfma_bagpr_acc<BF16>(dpacc[qb], va[ks], greg[qb][ks]);
+  };
+  auto mfma_dq = [&](auto mc) __attribute__((always_inline)) {       // dQ^T += K^T dS^T
+    constexpr int m = decltype(mc)::value, kk = m / (DB * QB), db = (m / QB) % DB, qb = m % QB;
+    const u32x4 b = {dsk[qb][4 * kk], dsk[qb][4 * kk + 1], dsk[qb][4 * kk + 2], dsk[qb][4 * kk + 3]};
+    const i16x8 op = __builtin_shufflevector(kt_lo[kk][db], kt_hi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7);
+    mfma_agpr_acc<BF16>(dqacc[qb][db], op, __builtin_bit_cast(i16x8, b));
+  };
+
+  // ---- VALU slices of two accumulator elements (c = 8 qb + g: elements 2g, 2g+1)
+  constexpr int NSL = 8 * QB;
+  auto p_slice = [&](int c) __attribute__((always_inline)) {     // P = 2^(c S + c m)
+    const int qb = c >> 3, g = c & 7;
+    pv[qb][2 * g] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g], c_scale, cm[qb]));
+    pv[qb][2 * g + 1] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g + 1], c_scale, cm[qb]));
+  };
+  auto ds_slice = [&](int c) __attribute__((always_inline)) {    // dS = P (dP - delta)
+    const int qb = c >> 3, g = c & 7;
+    dsk[qb][g] = pack2<BF16>(pv[qb][2 * g] * dpacc[qb][2 * g], pv[qb][2 * g + 1] * dpacc[qb][2 * g + 1]);
+  };
+  // Hidden pairs of band-edge steps are zeroed after P is formed (a branch around VALU only).
+  // Keys past the sequence need no mask (their K rows are zero fills, so they add nothing to
+  // dQ); queries past it are not stored.  q - key - dlo = u - (8 (i/4) + i%4), u per lane.
+  auto mask_step = [&](int t) __attribute__((always_inline)) {
+    keep_branch();   // not worth running on every step
+    const int k0 = (s_begin + t) * kBK;
+    const unsigned span = (unsigned)(a.dhi - a.dlo);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int u = qw0 + 32 * qb + l32 - k0 - 4 * hi - a.dlo;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pv[qb][i] = (unsigned)(u - 8 * (i >> 2) - (i & 3)) <= span ? pv[qb][i] : 0.f;
+    }
+  };
+  auto edge_step = [&](int t) __attribute__((always_inline)) {   // some pair outside the band
+    const int k0 = (s_begin + t) * kBK;
+    return qw0 - (k0 + kBK - 1) < a.dlo || qw0 + S::QW - 1 - k0 > a.dhi;
+  };
+  auto pin_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) pin(pv[qb]);
+  };
+  auto pin_ds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) pin(dsk[qb][g]);
+  };
+
+  // phase 1: dQ_{s-1}, dP_s | P_s.  P slices start after the second MFMA: S_s was the last
+  // product of the step before.
+  auto phase1 = [&]() __attribute__((always_inline)) {
+    static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m == NG) wait_lgkmcnt_fence<KS>();   // V rows have landed (K rows may not)
+      if constexpr (m < NG) mfma_dq(std::integral_constant<int, m>{});
+      else mfma_dp(std::integral_constant<int, m - NG>{});
+      constexpr int W = NG + NM - 2;
+      if constexpr (m >= 2) dq_slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(p_slice);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pin_p();
+  };
+  // phase 2: S_{s+1} | dS_s.  dS slices start after the second MFMA: dP_s was the last
+  // product of phase 1.
+  auto phase2 = [&]() __attribute__((always_inline)) {
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      mfma_s(mc);
+      constexpr int W = NM - 2;
+      if constexpr (m >= 2) dq_slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(ds_slice);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pin_ds();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) keep(ndv[qb]);   // dP's initial value
+  };
+
+  // ---- prologue: tiles 0..kPD-1, S_0; dQ_{-1} adds zeros (zero dS and K^T operands)
+  for (int t = 0; t < kPD; ++t) issue_copies(t);
+  wait_vmcnt<0>();
+  wg_barrier();
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) dsk[qb][g] = 0u;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) kt_lo[kk][db] = kt_hi[kk][db] = i16x4{};
+  if (NSTEP > 0) {
+    read_rows(vrow_a, Z{}, ka);        // K_0 (stage 0)
+    wait_lgkmcnt0_fence();
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
+  }
+  pin_ds();
+  mfma_result_wait();   // S_0 is read by VALU in step 0
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) pin(sacc[qb]);
+
+  // ---- steps: one barrier each
+  for (int s = 0; s < NSTEP; ++s) {
+    issue_copies(s + kPD);
+    read_rows(vrow_a, KT{}, va);      // V_s
+    read_rows(krow_a, Z{}, ka);       // K_{s+1}
+    phase1();
+    if (edge_step(s)) {
+      mask_step(s);
+      pin_p();
+    }
+    wait_lgkmcnt0_fence();
+    read_kt();                        // K_s^T, for dQ_s in the next step
+    phase2();
+    // next stage: V and K^T rows move to tile s+1, K rows to tile s+2
+    {
+      const int d0 = stage_step(s), d1 = stage_step(s + 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        vrow_a[ks] += d0;
+        krow_a[ks] += d1;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) tr_a[h][db] += d0;
+    }
+    wait_lgkmcnt0();
+    wait_vmcnt<(kPD - 2) * 2 * CPT>();
+    wg_barrier();
+  }
+  // dQ of the last step
+  if (NSTEP > 0) {
+    static_for<NG>([&](auto mc) __attribute__((always_inline)) {
+      mfma_dq(mc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  wait_vmcnt<0>();   // no copy may land after the workgroup ends
+
+  // ---- epilogue: lane holds query qw0 + 32 qb + l32, dims 32 db + 8 g + 4 hi + 0..3
+  mfma_result_wait();
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) in_agpr(dqacc[qb][db]);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + 32 * qb + l32;
+    if (q < n) {
+      char* row = a.dq + head + (long)q * RB;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = 32 * db + 8 * g + 4 * hi;
+          u32x2 w = {pack2<BF16>(dqacc[qb][db][4 * g + 0] * sc, dqacc[qb][db][4 * g + 1] * sc),
+                     pack2<BF16>(dqacc[qb][db][4 * g + 2] * sc, dqacc[qb][db][4 * g + 3] * sc)};
+          *reinterpret_cast<u32x2*>(row + dim * 2) = w;
+        }
+    }
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch(const BwdParams& p, hipStream_t stream) {
+  using S = QShape<D>;
+  DqArgs a;
+  a.q = static_cast<const char*>(p.q);
+  a.k = static_cast<const char*>(p.k);
+  a.v = static_cast<const char*>(p.v);
+  a.dout = static_cast<const char*>(p.dout);
+  const long rows = (long)p.B * p.H * p.N;
+  a.mrow = p.stats;
+  a.ndelta = p.stats + rows;
+  a.dq = static_cast<char*>(p.dq);
+  a.n = p.N;
+  a.n_bh = p.B * p.H;
+  a.n_tiles = (p.N + S::QWG - 1) / S::QWG;
+  a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
+  a.scale = p.scale;
+  a.causal = p.causal;
+  a.wl = p.window_left;
+  a.wr = p.causal ? 0 : p.window_right;
+  // a window of kUnbounded or more is no bound (see the dK/dV kernel)
+  constexpr int kUnbounded = 1 << 30;
+  const int wr = p.window_right < 0 ? kUnbounded : std::min(p.window_right, kUnbounded);
+  const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
+  a.dlo = p.causal ? 0 : -wr;
+  a.dhi = wl;
+  const long blocks = (long)a.n_bh * a.n_tiles;
+  hipLaunchKernelGGL((dq_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream) {
+  if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+}
+
+}  // namespace fa

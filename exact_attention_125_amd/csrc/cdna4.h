@@ -244,6 +244,21 @@ __device__ __forceinline__ unsigned lds_addr(const char FA_LDS* p) {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+// Moves x into accumulation registers (AGPRs) at this point; used for values that only
+// register-placed MFMAs read or write afterwards.
+__device__ __forceinline__ void in_agpr(i16x8& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void in_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+// Wait states between register-placed MFMAs and other accesses to their registers:
+// kMfmaResultWait after a product before its result is read, a few before a product reads a
+// register a VALU instruction wrote.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
+__device__ __forceinline__ void mfma_operand_wait() { asm volatile("s_nop 7" ::: "memory"); }
+// An empty statement the compiler may not speculate: placed in a branch's body, it keeps the
+// branch (the body is not turned into selects that run on every path).
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+// Keeps x in its registers, unchanged, up to this point (its registers are not reused before).
+__device__ __forceinline__ void keep(const f32x16& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(const f32x4& x) { asm volatile("" ::"v"(x)); }
 
 // ---------------------------------------------------------------------------- cross-lane
 // The partner of lane l is lane l ^ 32.  permlane32_swap(x, x) leaves {x[l], x[l^32]} in

@@ -61,5 +61,7 @@ inline float softmax_sigma(float scale) {
 // dK/dV with key-owned workgroups of one wave per SIMD (bwd_dkdv.hip); launch_bwd chooses
 // between it and the four-wave kernel of bwd.hip.
 hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream);
+// dQ with query-owned workgroups of one wave per SIMD (bwd_dq.hip).
+hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -22,7 +22,7 @@ def fa():
 
 def run(fa, inp, scale, causal, window, stages=None, kernel=None):
     """Forward then backward through the C ABI.  ``kernel`` ("main" / "basic") forces the
-    library's dK/dV kernel through its FA_BWD_KERNEL knob; None keeps the default."""
+    library's dK/dV and dQ kernels through its FA_BWD_KERNEL knob; None keeps the default."""
     import torch
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, scale, causal, window)
@@ -50,7 +50,7 @@ def run(fa, inp, scale, causal, window, stages=None, kernel=None):
     return grads
 
 
-KERNELS = ["main", "basic"]   # the two dK/dV kernels; the default choice is covered too
+KERNELS = ["main", "basic"]   # the two kernel sets (dK/dV, dQ); the default is covered too
 
 
 def check_grads(grads, inp, scale, causal, window, heads=None, label=""):
@@ -92,7 +92,7 @@ def test_train_workload_backward(fa):
     B, H = w.B, w.H
     basic = run(fa, inp, w.softmax_scale, w.causal, w.window, kernel="basic")
     check_grads(basic, inp, w.softmax_scale, w.causal, w.window, heads=[(B - 1, H - 1)],
-                label=w.name + " basic dK/dV kernel")
+                label=w.name + " basic kernels")
     del basic
     grads = run(fa, inp, w.softmax_scale, w.causal, w.window)
     check_grads(grads, inp, w.softmax_scale, w.causal, w.window,
@@ -139,7 +139,7 @@ def test_scales_backward(fa, scale, kernel):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("d", [64, 128])
 def test_many_key_tiles_backward(fa, d, kernel):
-    """Sequences spanning many key tiles and query steps of either dK/dV kernel, with a
+    """Sequences spanning many key and query tiles of either kernel set, with a
     ragged tail, under each mask family."""
     inp = W.random_case((1, 2, 1500, d), "bf16", seed=95 + d, with_grad=True)
     scale = 1.0 / math.sqrt(d)
