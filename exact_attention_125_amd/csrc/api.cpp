@@ -109,7 +109,7 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)
     return 0;
   if (empty) return 0;
-  return 2 * (size_t)batch * heads * seqlen * sizeof(float);   // -LSE / sigma, then -delta
+  return (size_t)batch * heads * fa::stat_blocks(seqlen) * 2 * fa::kStatRows * sizeof(float);
 }
 
 fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,

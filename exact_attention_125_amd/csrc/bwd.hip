@@ -20,6 +20,7 @@
 //                 dQ^T += K^T dS^T with K^T read transposed from LDS
 // Each score tile is laid out so that the accumulator registers of S / dP are directly the
 // MFMA operand that P / dS feed, as in the forward kernel.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -40,7 +41,7 @@ struct BwdArgs {
   char* dq;
   char* dk;
   char* dv;
-  float* stats;   // [B*H*N] -LSE / sigma, then [B*H*N] -delta
+  float* stats;   // per-query statistics in 32-query blocks (stat_index)
   int n;
   int n_bh;
   int n_tiles;
@@ -51,28 +52,39 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------- delta
-// One thread per query row: delta = sum_c dO[c] * O[c] with both rounded inputs in fp32,
-// stored next to log2(e) * LSE (the exponent offset the recomputation of P needs).
+// One thread per query slot of the padded statistics blocks: delta = sum_c dO[c] * O[c] with
+// both rounded inputs in fp32, stored negated next to m = -LSE / sigma (the exponent offset
+// the recomputation of P needs); slots past the sequence get zeros.
+// Grid: x over a head's padded query slots, y (with a stride loop) over (batch, head).
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, long rows) {
-  const long r = (long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const u32x4* o = reinterpret_cast<const u32x4*>(a.o + r * D * 2);
-  const u32x4* g = reinterpret_cast<const u32x4*>(a.dout + r * D * 2);
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 ov = o[c], gv = g[c];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += to_float<BF16>((unsigned short)(ov[w] & 0xffff)) *
-             to_float<BF16>((unsigned short)(gv[w] & 0xffff));
-      acc += to_float<BF16>((unsigned short)(ov[w] >> 16)) *
-             to_float<BF16>((unsigned short)(gv[w] >> 16));
+__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= stat_blocks(a.n) * kStatRows) return;
+  for (long bh = blockIdx.y; bh < a.n_bh; bh += gridDim.y) {
+    float* out = a.stats + stat_index(bh, a.n, q);
+    if (q >= a.n) {
+      out[0] = 0.f;
+      out[kStatRows] = 0.f;
+      continue;
     }
+    const long r = bh * a.n + q;
+    const u32x4* o = reinterpret_cast<const u32x4*>(a.o + r * D * 2);
+    const u32x4* g = reinterpret_cast<const u32x4*>(a.dout + r * D * 2);
+    float acc = 0.f;
+  #pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 ov = o[c], gv = g[c];
+  #pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc += to_float<BF16>((unsigned short)(ov[w] & 0xffff)) *
+               to_float<BF16>((unsigned short)(gv[w] & 0xffff));
+        acc += to_float<BF16>((unsigned short)(ov[w] >> 16)) *
+               to_float<BF16>((unsigned short)(gv[w] >> 16));
+      }
+    }
+    out[0] = -a.lse[r] / a.sigma;
+    out[kStatRows] = -acc;
   }
-  a.stats[r] = -a.lse[r] / a.sigma;
-  a.stats[rows + r] = -acc;
 }
 
 // ---------------------------------------------------------------------------- dK, dV
@@ -104,9 +116,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const auto rk = make_rsrc(a.k + head, head_bytes);
   const auto rv = make_rsrc(a.v + head, head_bytes);
   const auto rg = make_rsrc(a.dout + head, head_bytes);
-  const long rows = (long)a.n_bh * n;
-  const float* lse2 = a.stats + (long)bh * n;
-  const float* delta = a.stats + rows + (long)bh * n;
 
   // K^T and V^T as B operands: lane holds key (k0 + l32), head-dim chunk 2 ks + hi.
   const int k_first = kt * kKvRows;
@@ -137,8 +146,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
     const int q = s * kQStep + tid;
     if (tid < kQStep && q < n) {
-      lse_buf = lse2[q];
-      delta_buf = delta[q];
+      lse_buf = a.stats[stat_index(bh, n, q)];
+      delta_buf = a.stats[stat_index(bh, n, q) + kStatRows];
     } else {
       lse_buf = 0.f;
       delta_buf = 0.f;
@@ -305,9 +314,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     greg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, qi * kRowBytes + (2 * ks + hi) * 16));
   }
   const bool row_ok = qi < n;
-  const long rows = (long)a.n_bh * n;
-  const float mrow = row_ok ? a.stats[(long)bh * n + qi] : 0.f;        // -LSE / sigma
-  const float ndlt = row_ok ? a.stats[rows + (long)bh * n + qi] : 0.f;  // -delta
+  const float mrow = row_ok ? a.stats[stat_index(bh, n, qi)] : 0.f;               // -LSE / sigma
+  const float ndlt = row_ok ? a.stats[stat_index(bh, n, qi) + kStatRows] : 0.f;   // -delta
 
   const Mask mk{n, a.causal, a.wl, a.wr};
   const int q_last = q0 + kDqRows - 1;
@@ -466,9 +474,9 @@ template <int D, bool BF16>
 hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
   BwdArgs a = make_args(p);
   if (stages & kBwdDelta) {
-    const long rows = (long)a.n_bh * a.n;
-    hipLaunchKernelGGL((delta_kernel<D, BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, a, rows);
+    const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
+    const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
+    hipLaunchKernelGGL((delta_kernel<D, BF16>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   if ((stages & kBwdDkDv) && env_bwd_choice() != 2) {

@@ -22,12 +22,12 @@
 //   phase 1   dV_s, then S_{s+1}   (MFMA)  with  dS_s     (VALU)
 //   phase 2   dK_s, then dP_{s+1}  (MFMA)  with  P_{s+1}  (VALU)
 //
-// so that the MFMA results the next phase's VALU reads come last in their phase, and the
-// LDS operands of each half are read one half ahead.  Q and dO tiles and the per-query
-// statistics arrive by direct global->LDS copies into a ring of kNS stages, kPD steps ahead,
-// published by one workgroup barrier per step.  Step s reads tiles s and s+1 and writes tile
-// s+kPD into the stage of tile s-1; the copies of tile s+2 must have landed, in every wave,
-// before the barrier that ends step s.
+// so that the MFMA results the next phase's VALU reads come last in their phase.  Each phase
+// also issues, one per MFMA, the LDS reads of the next phase's operands.  Q and dO tiles and
+// the per-query statistics arrive by direct global->LDS copies into a ring of kNS stages, kPD
+// steps ahead, published by one workgroup barrier per step.  Step s reads tiles s, s+1 and
+// s+2 and writes tile s+kPD into the stage of tile s-1; the copies of tile s+3 must have
+// landed, in every wave, before the barrier that ends step s.
 //
 // The MFMAs are issued as inline assembly (cdna4.h), so the register dependencies the
 // compiler would resolve for the builtins are kept apart by the order written here: VALU
@@ -53,7 +53,7 @@ namespace {
 
 constexpr int kThreads = 256;   // 4 waves, one per SIMD
 constexpr int kBQ = 32;         // queries per step
-constexpr int kPD = 4;          // query tiles copied ahead
+constexpr int kPD = 5;          // query tiles copied ahead
 constexpr int kNS = kPD + 1;    // LDS ring stages
 
 struct DkdvArgs {
@@ -61,8 +61,7 @@ struct DkdvArgs {
   const char* k;
   const char* v;
   const char* dout;
-  const float* mrow;     // [B*H*N] -LSE / sigma
-  const float* ndelta;   // [B*H*N] -rowsum(dO * O)
+  const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dk;
   char* dv;
   int n;
@@ -83,7 +82,7 @@ struct DShape {
   static constexpr int DB = D / 32;                // 32-dim blocks of dK^T, dV^T
   static constexpr int RB = D * 2;                 // bytes per row
   static constexpr int QTILE = kBQ * RB;           // bytes of a Q or dO tile
-  static constexpr int STAGE = 2 * QTILE + 256;    // Q tile, dO tile, 32 + 32 statistics
+  static constexpr int STAGE = 2 * QTILE + 1024;   // Q tile, dO tile, statistics (see copy_stats)
   static constexpr int CPT = QTILE / (16 * kThreads);   // 16-byte chunks per thread per tile
   static_assert(QTILE % (16 * kThreads) == 0, "tiles split evenly over the threads");
 };
@@ -127,8 +126,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const auto rk = make_rsrc(a.k + head, head_bytes);
   const auto rv = make_rsrc(a.v + head, head_bytes);
   const auto rg = make_rsrc(a.dout + head, head_bytes);
-  const auto rm = make_rsrc(a.mrow + (long)bh * n, n * 4);
-  const auto rd = make_rsrc(a.ndelta + (long)bh * n, n * 4);
+  const int stat_bytes = stat_blocks(n) * 2 * kStatRows * 4;
+  const auto rs = make_rsrc(a.stats + (long)bh * stat_blocks(n) * 2 * kStatRows, stat_bytes);
   const Mask mk{n, a.causal, a.wl, a.wr};
   const float c_scale = a.c;
 
@@ -181,11 +180,12 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const int tr_row = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
   // LDS addresses of this lane's reads, kept per ring stage and moved on by one stage per
-  // step (tile, statistics and 16-row offsets are immediates):
-  //   row_a[ks]   A operand rows of a tile (query l32, chunk 2 ks + hi), stage of tile s+1
-  //   st_a        the 16 statistics of this lane's accumulator rows, stage of tile s+1
-  //   tr_a[h][db] transposed halves (rows tr_row + 8 h, dim block db), stage of tile s until
-  //               its Q^T is read, then of tile s+1
+  // phase of step s (tile, statistics and 16-row offsets are immediates):
+  //   row_a[ks]   A operand rows of a tile (query l32, chunk 2 ks + hi): tile s+1 in phase 1,
+  //               tile s+2 in phase 2
+  //   st_a        the 16 statistics of this lane's accumulator rows, likewise
+  //   tr_a[h][db] transposed halves (rows tr_row + 8 h, dim block db): tile s in phase 1,
+  //               tile s+1 in phase 2
   const unsigned ring_a = lds_addr(ring);
   unsigned row_a[KS], st_a, tr_a[2][DB];
 #pragma unroll
@@ -220,39 +220,46 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
     const int r = p / RB;
     cp_src[i] = r * RB + ((((p % RB) / 16) ^ chunk_swizzle<D>(r))) * 16;
   }
-  // statistics: lane L < 8 of wave 0 copies the 4 values of queries 4 sigma(L) .. +3 to LDS
-  // slot L, sigma(L) = 2L (L < 4) or 2(L-4)+1, so that lanes of half hi find the 16 values of
-  // their accumulator rows 8 g + 4 hi + 0..3 (g = 0..3) contiguous at slot 4 hi
-  const int st_src = 16 * (lane < 4 ? 2 * lane : 2 * (lane - 4) + 1);
+  // statistics of a 32-query tile, one 256-byte block (m, then -delta): lane L < 16 of wave 0
+  // copies 16 bytes to LDS slot L (m for L < 8, -delta for 8 <= L < 16): the values of queries
+  // 4 sig(L % 8) .. +3 with sig(j) = 2j (j < 4) or 2(j-4)+1, so that lanes of half hi find the
+  // 16 values of their accumulator rows 8 g + 4 hi + 0..3 (g = 0..3) contiguous at slot 4 hi
+  // (of the m or -delta half).  Lanes 16..63 read past the buffer and write zeros to slots
+  // 16..63, which keeps the copy one full-wave instruction.
+  const int jl = lane & 7;
+  const int st_src = lane < 16 ? 128 * (lane >> 3) + 16 * (jl < 4 ? 2 * jl : 2 * (jl - 4) + 1)
+                               : stat_bytes;
 
-  // ---- copies of query tile t (relative step) into stage t % kNS: Q, dO, and the 32 m and
-  // 32 -delta values; past the last step they read beyond the buffers (zero fills, no
-  // traffic) so every step issues the same copies
-  auto issue_copies = [&](int t) __attribute__((always_inline)) {
-    const int q0 = (s_begin + t) * kBQ;
-    const int off = t < NSTEP ? q0 * RB : head_bytes;
+  // ---- copies of query tile t (relative step) into stage t % kNS: Q and dO (every wave its
+  // share), and the statistics block (wave 0); past the last step they read beyond the
+  // buffers (zero fills, no traffic) so every step issues the same copies
+  auto copy_tiles = [&](int t) __attribute__((always_inline)) {
+    const int off = t < NSTEP ? (s_begin + t) * kBQ * RB : head_bytes;
     char FA_LDS* st = ring + (t % kNS) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       buffer_load16_lds(rq, st + 4096 * i + 1024 * wave, cp_src[i] + off);
       buffer_load16_lds(rg, st + QTILE + 4096 * i + 1024 * wave, cp_src[i] + off);
     }
+  };
+  auto copy_stats = [&](int t) __attribute__((always_inline)) {
     if (wave == 0) {
-      const int so = t < NSTEP ? q0 * 4 : n * 4;
-      if (lane < 8) {
-        buffer_load16_lds(rm, st + 2 * QTILE, so + st_src);
-        buffer_load16_lds(rd, st + 2 * QTILE + 128, so + st_src);
-      }
+      const int off = t < NSTEP ? (s_begin + t) * 2 * kStatRows * 4 : stat_bytes;
+      buffer_load16_lds(rs, ring + (t % kNS) * STAGE + 2 * QTILE, st_src + off);
     }
   };
-  // this wave's copies of tiles up to s+2 have landed (loads complete in order), leaving
-  // those of tiles s+3 .. s+kPD in flight; wave 0 also issues the two statistics copies
-  static_assert(kPD >= 2, "the ring holds the two tiles a step reads");
+  auto issue_copies = [&](int t) __attribute__((always_inline)) {
+    copy_stats(t);
+    copy_tiles(t);
+  };
+  // this wave's copies of tiles up to s+3 have landed (loads complete in order), leaving
+  // those of tiles s+4 .. s+kPD in flight; wave 0 also issues the two statistics copies
+  static_assert(kPD >= 3, "the ring holds the three tiles a step reads");
   auto wait_copies = [&]() __attribute__((always_inline)) {
     if (wave == 0)
-      wait_vmcnt<(kPD - 2) * (2 * CPT + 2)>();
+      wait_vmcnt<(kPD - 3) * (2 * CPT + 1)>();
     else
-      wait_vmcnt<(kPD - 2) * 2 * CPT>();
+      wait_vmcnt<(kPD - 3) * 2 * CPT>();
   };
 
   // ---- operand registers.  All LDS reads in the steps are issued as inline assembly the
@@ -267,12 +274,12 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   f32x4 mv[4], ndv[4];              // m and -delta of accumulator rows (initial S, dP)
   f32x16 sacc[KB], dpacc[KB], pv[KB];
   unsigned pk[KB][8], dsk[KB][8];
-  constexpr int kRowReads = KS + 4;         // LDS reads of one rows-and-statistics group
   constexpr int kTrReads = 2 * 2 * DB;      // transposing reads of one tile
-  constexpr int kTrWait = kTrReads < 15 ? kTrReads : 15;
+  constexpr int NR = kTrReads + KS + 4;     // LDS reads a phase issues for the next
+  static_assert(KS + 4 <= 15 && NR / 2 <= 15, "counted waits fit lgkmcnt");
 
   // rows (Q at TOFF 0, dO at QTILE) and statistics group WHICH (m, -delta) of the tile
-  // row_a / st_a point at
+  // row_a / st_a point at (the prologue's reads)
   auto read_rows = [&](auto toff, auto which, i16x8 (&rows)[KS], f32x4 (&stv)[4])
                        __attribute__((always_inline)) {
     constexpr int TOFF = decltype(toff)::value, WHICH = decltype(which)::value;
@@ -284,7 +291,25 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
       stv[g] = __builtin_bit_cast(f32x4, lds_read16_nowait<128 * WHICH + 16 * g>(st_a));
     });
   };
-  // transposed halves of the tile tr_a points at (Q^T at TOFF 0, dO^T at QTILE)
+  // read r of a phase's list: r < kTrReads a transposed half of the tile tr_a points at (at
+  // TROFF), then KS rows and 4 statistics vectors of the tile row_a / st_a point at (rows at
+  // ROFF, statistics group WHICH)
+  auto read_one = [&](auto rc, auto troff, auto roff, auto which, i16x4 (&dlo)[2][DB],
+                      i16x4 (&dhi)[2][DB], i16x8 (&rows)[KS], f32x4 (&stv)[4])
+                      __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value, TROFF = decltype(troff)::value;
+    constexpr int ROFF = decltype(roff)::value, WHICH = decltype(which)::value;
+    if constexpr (r < kTrReads) {
+      constexpr int kk = r / (2 * DB), db = (r / 2) % DB;
+      if constexpr (r % 2 == 0) dlo[kk][db] = lds_read_tr_nowait<TROFF + kk * 16 * RB>(tr_a[0][db]);
+      else dhi[kk][db] = lds_read_tr_nowait<TROFF + kk * 16 * RB>(tr_a[1][db]);
+    } else if constexpr (r < kTrReads + KS) {
+      rows[r - kTrReads] = __builtin_bit_cast(i16x8, lds_read16_nowait<ROFF>(row_a[r - kTrReads]));
+    } else {
+      constexpr int g = r - kTrReads - KS;
+      stv[g] = __builtin_bit_cast(f32x4, lds_read16_nowait<128 * WHICH + 16 * g>(st_a));
+    }
+  };
   auto read_tr = [&](auto toff, i16x4 (&dlo)[2][DB], i16x4 (&dhi)[2][DB])
                      __attribute__((always_inline)) {
     constexpr int TOFF = decltype(toff)::value;
@@ -390,34 +415,51 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   // Every step computes S, dP and P of the following tile; after the last step that tile is
   // the zero fill past the sequence and its values go unused.  One MFMA sequence per phase,
   // with no branch around any of it, keeps each accumulator in one set of registers.
-  // phase 1: dV_s, S_{s+1} | dS_s
-  auto phase1 = [&]() __attribute__((always_inline)) {
+  //
+  // Counted waits: a phase starts when the transposed halves the previous phase read have
+  // landed (its KS + 4 rows and statistics reads may still be in flight) and runs its second
+  // product once those have landed too (its own first NR / 2 reads may still be in flight).
+  //
+  // phase 1 of step s: dV_s, S_{s+1} | dS_s; reads Q_s^T, dO_{s+1} rows, -delta_{s+1}; copies
+  // of tile s + kPD
+  auto phase1 = [&](int s) __attribute__((always_inline)) {
+    wait_lgkmcnt_fence<KS + 4>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (m == NG) wait_lgkmcnt_fence<kTrWait>();   // Q rows and m have landed
+      if constexpr (m == NG) wait_lgkmcnt_fence<NR / 2>();   // Q_{s+1} rows and m have landed
       if constexpr (m < NG) mfma_dv(std::integral_constant<int, m>{});
       else mfma_s(std::integral_constant<int, m - NG>{});
       slices<m * NSL / (NG + NM), (m + 1) * NSL / (NG + NM)>(ds_slice);
+      static_for<(m + 1) * NR / (NG + NM) - m * NR / (NG + NM)>([&](auto jc) __attribute__((always_inline)) {
+        read_one(std::integral_constant<int, m * NR / (NG + NM) + decltype(jc)::value>{}, Z{}, QT{}, O{},
+                 qt_lo, qt_hi, ga, ndv);
+      });
+      if constexpr (m == 1) copy_tiles(s + kPD);
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_phase1();
   };
-  // phase 2: dK_s, dP_{s+1} | P_{s+1}.  The slices start after the second MFMA: S_{s+1} was
-  // the last product of phase 1.
+  // phase 2 of step s: dK_s, dP_{s+1} | P_{s+1}; reads dO_{s+1}^T, Q_{s+2} rows, m_{s+2}.  The
+  // slices start after the second MFMA: S_{s+1} was the last product of phase 1.
   auto phase2 = [&]() __attribute__((always_inline)) {
+    wait_lgkmcnt_fence<KS + 4>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (m == NG) wait_lgkmcnt_fence<kTrWait>();   // dO rows and -delta have landed
+      if constexpr (m == NG) wait_lgkmcnt_fence<NR / 2>();   // dO_{s+1} rows and -delta have landed
       if constexpr (m < NG) mfma_dk(std::integral_constant<int, m>{});
       else mfma_dp(std::integral_constant<int, m - NG>{});
       constexpr int W = NG + NM - 2;
       if constexpr (m >= 2) slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(p_slice);
+      static_for<(m + 1) * NR / (NG + NM) - m * NR / (NG + NM)>([&](auto jc) __attribute__((always_inline)) {
+        read_one(std::integral_constant<int, m * NR / (NG + NM) + decltype(jc)::value>{}, QT{}, Z{}, Z{},
+                 gt_lo, gt_hi, qa, mv);
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_phase2();
   };
 
-  // ---- prologue: tiles 0..kPD-1, then S_0, dP_0, P_0 and the dO^T operand of step 0
+  // ---- prologue: tiles 0..kPD-1, then S_0, dP_0, P_0 and the operands of step 0's phase 1
   for (int t = 0; t < kPD; ++t) issue_copies(t);
   wait_vmcnt<0>();
   wg_barrier();
@@ -442,33 +484,28 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
     slices<0, NSL>(p_slice);
     if (edge_step(0)) mask_step(0);
     pin_phase2();
-    read_tr(QT{}, gt_lo, gt_hi);
   }
-  advance_rows(0);   // rows: tile 1; transposed: tile 0
+  read_tr(QT{}, gt_lo, gt_hi);       // dO_0^T
+  advance_rows(0);
+  read_rows(Z{}, Z{}, qa, mv);       // Q_1 rows, m_1
   wait_lgkmcnt0_fence();
+  // from here: tr_a at tile s, row_a / st_a at tile s+1 when step s begins
 
   // ---- steps: one barrier each
   for (int s = 0; s < NSTEP; ++s) {
-    issue_copies(s + kPD);
-    // operands of the rest of this phase and of phase 2's first half
-    read_rows(Z{}, Z{}, qa, mv);      // tile s+1
-    read_tr(Z{}, qt_lo, qt_hi);       // tile s
-    advance_tr(s);
-    phase1();
-    wait_lgkmcnt0_fence();
-    // operands of the rest of this phase and of the next phase 1's first half
-    read_rows(QT{}, O{}, ga, ndv);    // tile s+1
-    read_tr(QT{}, gt_lo, gt_hi);      // tile s+1
-    advance_rows(s + 1);
+    copy_stats(s + kPD);             // before the phase: its branch stays out of the MFMA sequence
+    phase1(s);
+    advance_tr(s);                   // tile s   -> s+1
+    advance_rows(s + 1);             // tile s+1 -> s+2
     phase2();
     if (s + 1 < NSTEP && edge_step(s + 1)) {
       mask_step(s + 1);
       pin_phase2();
     }
-    wait_lgkmcnt0();
     wait_copies();
     wg_barrier();
   }
+  wait_lgkmcnt0();
   wait_vmcnt<0>();   // no copy may land after the workgroup ends
 
   // ---- epilogue: lane holds key kw0 + 32 kb + l32, dims 32 db + 8 g + 4 hi + 0..3.  The
@@ -512,9 +549,7 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.k = static_cast<const char*>(p.k);
   a.v = static_cast<const char*>(p.v);
   a.dout = static_cast<const char*>(p.dout);
-  const long rows = (long)p.B * p.H * p.N;
-  a.mrow = p.stats;
-  a.ndelta = p.stats + rows;
+  a.stats = p.stats;
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
   a.n = p.N;

@@ -51,8 +51,7 @@ struct DqArgs {
   const char* k;
   const char* v;
   const char* dout;
-  const float* mrow;     // [B*H*N] -LSE / sigma
-  const float* ndelta;   // [B*H*N] -rowsum(dO * O)
+  const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dq;
   int n;
   int n_bh;
@@ -131,9 +130,9 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
       greg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, off));
     }
     const bool ok = q < n;
-    const long r = (long)bh * n + (ok ? q : 0);
-    cm[qb] = ok ? c_scale * a.mrow[r] : 0.f;
-    const float nd = ok ? a.ndelta[r] : 0.f;
+    const long r = stat_index(bh, n, ok ? q : 0);
+    cm[qb] = ok ? c_scale * a.stats[r] : 0.f;
+    const float nd = ok ? a.stats[r + kStatRows] : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ndv[qb][i] = nd;
   }
@@ -418,9 +417,7 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.k = static_cast<const char*>(p.k);
   a.v = static_cast<const char*>(p.v);
   a.dout = static_cast<const char*>(p.dout);
-  const long rows = (long)p.B * p.H * p.N;
-  a.mrow = p.stats;
-  a.ndelta = p.stats + rows;
+  a.stats = p.stats;
   a.dq = static_cast<char*>(p.dq);
   a.n = p.N;
   a.n_bh = p.B * p.H;

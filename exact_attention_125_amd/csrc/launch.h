@@ -31,7 +31,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* stats;        // workspace, 2 x [B, H, N] fp32: -LSE / sigma, then -rowsum(dO * O)
+  float* stats;        // workspace: per-query statistics in 32-query blocks (stat_index)
   int B, H, N, D;
   bool bf16;
   float scale;
@@ -53,6 +53,16 @@ hipError_t launch_bwd(const BwdParams& p, unsigned stages, hipStream_t stream);
 // The backward passes evaluate P = exp(scale s - LSE) as 2^(c (s + m)) with c = sigma log2(e)
 // and the per-row m = -LSE / sigma, where sigma is the scale moved away from zero (a zero
 // scale leaves every score weight equal, which sigma = 1e-30 reproduces to fp32 rounding).
+// Backward workspace layout: for each (batch, head) and each block of 32 queries, 64 floats:
+// m = -LSE / sigma of the block's 32 queries, then their -rowsum(dO * O); zero for query
+// slots past N.  A block's statistics are one contiguous 256-byte run, copied as one piece.
+constexpr int kStatRows = 32;
+__host__ __device__ inline int stat_blocks(int n) { return (n + kStatRows - 1) / kStatRows; }
+// index of m of query q of head bh (add kStatRows for its -delta)
+__host__ __device__ inline long stat_index(long bh, int n, int q) {
+  return (bh * stat_blocks(n) + q / kStatRows) * (2 * kStatRows) + q % kStatRows;
+}
+
 inline float softmax_sigma(float scale) {
   constexpr float kTiny = 1e-30f;
   if (scale >= 0.f) return scale < kTiny ? kTiny : scale;

@@ -86,10 +86,11 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float softmax_scale, int causal, int window_left, int window_right,
                  void* stream);
 
-/* Bytes of device workspace fa_bwd needs for this shape: two float32 [B, H, N] arrays of
- * per-query statistics (-LSE / sigma and -rowsum(dO * O), where sigma is softmax_scale moved
- * at least 1e-30 away from zero), 8 bytes per query row.  Returns 0
- * for invalid or empty shapes. */
+/* Bytes of device workspace fa_bwd needs for this shape: float32 per-query statistics,
+ * -LSE / sigma and -rowsum(dO * O) (sigma is softmax_scale moved at least 1e-30 away from
+ * zero), stored per (batch, head) in blocks of 32 queries (32 of each, 256 bytes per block,
+ * the last block padded with zeros): 8 * B * H * ceil(N / 32) * 32 bytes.  Returns 0 for
+ * invalid or empty shapes. */
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim);
 
 /* Backward pass by recomputation: P is rebuilt tile by tile from Q, K and the saved LSE

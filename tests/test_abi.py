@@ -102,7 +102,7 @@ def test_backward_specific(lib):
     assert bwd(lib, dk=0) == 1
     assert bwd(lib, ws=0) == 8
     need = lib.fa_bwd_workspace_size(2, 3, 100, 64)
-    assert need == 2 * 2 * 3 * 100 * 4
+    assert need == 2 * 3 * 4 * 32 * 8   # 100 queries fill 4 blocks of 32
     assert bwd(lib, ws_bytes=need - 1) == 8
     assert bwd(lib, ws=WS + 4) == 6
     assert bwd(lib, dq=Q) == 10
@@ -122,7 +122,8 @@ def test_stage_mask_rejections(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.fa_bwd_workspace_size(8, 16, 4096, 64) == 2 * 8 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_size(8, 16, 4096, 64) == 8 * 16 * 4096 * 8
+    assert lib.fa_bwd_workspace_size(1, 1, 33, 128) == 2 * 32 * 8
     assert lib.fa_bwd_workspace_size(0, 16, 4096, 64) == 0
     assert lib.fa_bwd_workspace_size(1, 1, 10, 96) == 0
     assert lib.fa_bwd_workspace_size(-1, 1, 10, 64) == 0
