@@ -67,6 +67,8 @@ struct DkdvArgs {
   int n;
   int n_bh;
   int n_tiles;           // key tiles of KWG keys per head
+  int n_units;           // workgroups per head: n_tiles, or ceil(n_tiles / 2) when paired
+  int paired;            // a workgroup takes key tiles t and n_tiles - 1 - t
   float c;               // sigma * log2(e)
   float scale;
   int causal, wl, wr;
@@ -102,14 +104,12 @@ __device__ __forceinline__ void slices(F&& f) {
   }
 }
 
+// dK, dV of key tile kt of head bh (the whole workgroup)
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
+__device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int bh, int kt) {
   using S = DShape<D>;
   constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
-
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * STAGE];
-  char FA_LDS* ring = (char FA_LDS*)lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,8 +117,6 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, kt;
-  xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, kt);
   const int n = a.n;
   const long head = (long)bh * n * RB;
   const int head_bytes = n * RB;
@@ -541,6 +539,22 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   }
 }
 
+// Under a causal mask (no left window) the number of query steps falls linearly with the key
+// tile, so tiles t and n_tiles - 1 - t together take the same time for every t: paired, the
+// workgroups are of equal length and fill the chip evenly.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * DShape<D>::STAGE];
+  char FA_LDS* ring = (char FA_LDS*)lds_raw;
+  int bh, t;
+  xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, t);
+  const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
+    dkdv_tile<D, BF16>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch(const BwdParams& p, hipStream_t stream) {
   using S = DShape<D>;
@@ -567,7 +581,10 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
   a.dlo = p.causal ? 0 : -wr;
   a.dhi = wl;
-  const long blocks = (long)a.n_bh * a.n_tiles;
+  const int half = (a.n_tiles + 1) / 2;
+  a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
+  a.n_units = a.paired ? half : a.n_tiles;
+  const long blocks = (long)a.n_bh * a.n_units;
   hipLaunchKernelGGL((dkdv_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

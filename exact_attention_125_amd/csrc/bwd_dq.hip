@@ -19,12 +19,13 @@
 //   phase 1   dQ_{s-1}, then dP_s   (MFMA)  with  P_s    (VALU)
 //   phase 2   S_{s+1}               (MFMA)  with  dS_s   (VALU)
 //
-// K and V tiles arrive by direct global->LDS copies into a ring of kNS stages, kPD steps
-// ahead, published by one workgroup barrier per step.  Step s reads V_s and K_s^T from the
-// stage of tile s and K_{s+1} from that of tile s+1, and writes tile s+kPD into the stage of
-// tile s-1.  As in the dK/dV kernel, the MFMAs are inline assembly with register
-// dependencies kept apart by the written order, and all LDS reads in the steps are untracked
-// with counted waits.
+// and each phase issues, between its MFMAs, the LDS reads of later operands: phase 1 (in
+// its second half, once dQ_{s-1} has taken its operands) the K_{s+1} rows and K_s^T halves,
+// phase 2 the V_{s+1} rows.  K and V tiles arrive by direct global->LDS copies into a ring of
+// kNS stages, kPD steps ahead, published by one workgroup barrier per step.  Step s reads
+// tiles s and s+1 and writes tile s+kPD into the stage of tile s-1.  As in the dK/dV kernel,
+// the MFMAs are inline assembly with register dependencies kept apart by the written order,
+// and all LDS reads in the steps are untracked with counted waits.
 //
 // dQ = scale dS K, the query-side derivative of softmax(scale Q K^T + mask) V recomputed from
 // the saved logsumexp: the recomputation of "PyTorch-CUDA-v2.9镜像中使用FlashAttention提升训练
@@ -56,6 +57,8 @@ struct DqArgs {
   int n;
   int n_bh;
   int n_tiles;           // query tiles of QWG queries per head
+  int n_units;           // workgroups per head: n_tiles, or ceil(n_tiles / 2) when paired
+  int paired;            // a workgroup takes query tiles t and n_tiles - 1 - t
   float c;               // sigma * log2(e)
   float scale;
   int causal, wl, wr;
@@ -85,14 +88,12 @@ __device__ __forceinline__ void dq_slices(F&& f) {
   }
 }
 
+// dQ of query tile qt of head bh (the whole workgroup)
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
+__device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int bh, int qt) {
   using S = QShape<D>;
   constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
-
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * STAGE];
-  char FA_LDS* ring = (char FA_LDS*)lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,9 +101,6 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, tile;
-  xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, tile);
-  const int qt = a.n_tiles - 1 - tile;   // longest (latest) query tiles first under a causal mask
   const int n = a.n;
   const long head = (long)bh * n * RB;
   const int head_bytes = n * RB;
@@ -161,19 +159,16 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   const int NSTEP = k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
 
   // ---- per-lane LDS addresses, moved on by one ring stage per step:
-  //   vrow_a[ks]  A operand rows (key l32, chunk 2 ks + hi) in the stage of tile s (V at +KTILE)
-  //   krow_a[ks]  the same rows in the stage of tile s+1 (K)
+  //   row_a[ks]   A operand rows (key l32, chunk 2 ks + hi) in the stage of tile s+1 (K at
+  //               +0, V at +KTILE)
   //   tr_a[h][db] transposed halves (rows tr_row + 8 h, dim block db) in the stage of tile s
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
   const int tr_row = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
   const unsigned ring_a = lds_addr(ring);
-  unsigned vrow_a[KS], krow_a[KS], tr_a[2][DB];
+  unsigned row_a[KS], tr_a[2][DB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    vrow_a[ks] = ring_a + tile_offset<D>(l32, 2 * ks + hi);
-    krow_a[ks] = vrow_a[ks] + STAGE;
-  }
+  for (int ks = 0; ks < KS; ++ks) row_a[ks] = ring_a + tile_offset<D>(l32, 2 * ks + hi);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -203,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   };
   // this wave's copies of tiles up to s+2 have landed, those of s+3 .. s+kPD in flight
   static_assert(kPD >= 2, "the ring holds the two tiles a step reads");
+  auto copy_tiles = issue_copies;
 
   // ---- operand registers (untracked LDS reads; joined with others only at the MFMA)
   i16x8 ka[KS], va[KS];             // K_{s+1}, V_s rows (A operands of S^T, dP^T)
@@ -210,7 +206,9 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   f32x16 sacc[QB], dpacc[QB], pv[QB];
   unsigned dsk[QB][8];
   constexpr int kTrReads = 2 * 2 * DB;
-  (void)kTrReads;
+  constexpr int NR1 = KS + kTrReads;        // reads of phase 1's second half: K rows, K^T
+  constexpr int kTrWait = kTrReads < 15 ? kTrReads : 15;
+  static_assert(KS <= 15, "counted waits fit lgkmcnt");
 
   auto read_rows = [&](const unsigned (&addr)[KS], auto toff, i16x8 (&rows)[KS])
                        __attribute__((always_inline)) {
@@ -219,15 +217,16 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       rows[ks] = __builtin_bit_cast(i16x8, lds_read16_nowait<TOFF>(addr[ks]));
   };
-  auto read_kt = [&]() __attribute__((always_inline)) {
-    static_for<2>([&](auto kkc) __attribute__((always_inline)) {
-      constexpr int kk = decltype(kkc)::value;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        kt_lo[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[0][db]);
-        kt_hi[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[1][db]);
-      }
-    });
+  // read r of phase 1's list: K_{s+1} rows (r < KS), then the K_s^T halves
+  auto read_one = [&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    if constexpr (r < KS) {
+      ka[r] = __builtin_bit_cast(i16x8, lds_read16_nowait<0>(row_a[r]));
+    } else {
+      constexpr int t = r - KS, kk = t / (2 * DB), db = (t / 2) % DB;
+      if constexpr (t % 2 == 0) kt_lo[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[0][db]);
+      else kt_hi[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(tr_a[1][db]);
+    }
   };
   using Z = std::integral_constant<int, 0>;
   using KT = std::integral_constant<int, KTILE>;
@@ -294,28 +293,43 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
       for (int g = 0; g < 8; ++g) pin(dsk[qb][g]);
   };
 
-  // phase 1: dQ_{s-1}, dP_s | P_s.  P slices start after the second MFMA: S_s was the last
-  // product of the step before.
-  auto phase1 = [&]() __attribute__((always_inline)) {
+  // phase 1 of step s: dQ_{s-1}, dP_s | P_s.  P slices start after the second MFMA: S_s was
+  // the last product of the step before.  It starts once the K_{s-1}^T halves have landed
+  // (the V_s rows may still be in flight) and runs dP_s once they have too.
+  auto phase1 = [&](int s) __attribute__((always_inline)) {
+    wait_lgkmcnt_fence<KS>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (m == NG) wait_lgkmcnt_fence<KS>();   // V rows have landed (K rows may not)
+      if constexpr (m == NG) wait_lgkmcnt_fence<0>();   // V_s rows have landed
       if constexpr (m < NG) mfma_dq(std::integral_constant<int, m>{});
       else mfma_dp(std::integral_constant<int, m - NG>{});
       constexpr int W = NG + NM - 2;
       if constexpr (m >= 2) dq_slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(p_slice);
+      if constexpr (m >= NG) {
+        constexpr int h = m - NG;
+        static_for<(h + 1) * NR1 / NM - h * NR1 / NM>([&](auto jc) __attribute__((always_inline)) {
+          read_one(std::integral_constant<int, h * NR1 / NM + decltype(jc)::value>{});
+        });
+      }
+      if constexpr (m == 1) copy_tiles(s + kPD);
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_p();
   };
-  // phase 2: S_{s+1} | dS_s.  dS slices start after the second MFMA: dP_s was the last
-  // product of phase 1.
+  // phase 2 of step s: S_{s+1} | dS_s; reads the V_{s+1} rows.  It starts once the K_{s+1}
+  // rows have landed (the K_s^T halves may still be in flight).  dS slices start after the
+  // second MFMA: dP_s was the last product of phase 1.
   auto phase2 = [&]() __attribute__((always_inline)) {
+    wait_lgkmcnt_fence<kTrWait>();
     static_for<NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
       mfma_s(mc);
       constexpr int W = NM - 2;
       if constexpr (m >= 2) dq_slices<(m - 2) * NSL / W, (m - 1) * NSL / W>(ds_slice);
+      static_for<(m + 1) * KS / NM - m * KS / NM>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int ks = m * KS / NM + decltype(jc)::value;
+        va[ks] = __builtin_bit_cast(i16x8, lds_read16_nowait<KTILE>(row_a[ks]));
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_ds();
@@ -323,7 +337,8 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
     for (int qb = 0; qb < QB; ++qb) keep(ndv[qb]);   // dP's initial value
   };
 
-  // ---- prologue: tiles 0..kPD-1, S_0; dQ_{-1} adds zeros (zero dS and K^T operands)
+  // ---- prologue: tiles 0..kPD-1, S_0 and the V_0 rows; dQ_{-1} adds zeros (zero dS and
+  // K^T operands)
   for (int t = 0; t < kPD; ++t) issue_copies(t);
   wait_vmcnt<0>();
   wg_barrier();
@@ -335,46 +350,39 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int db = 0; db < DB; ++db) kt_lo[kk][db] = kt_hi[kk][db] = i16x4{};
-  if (NSTEP > 0) {
-    read_rows(vrow_a, Z{}, ka);        // K_0 (stage 0)
-    wait_lgkmcnt0_fence();
-    static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
-  }
+  read_rows(row_a, Z{}, ka);           // K_0
+  read_rows(row_a, KT{}, va);          // V_0
+  wait_lgkmcnt0_fence();
+  if (NSTEP > 0) static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
   pin_ds();
   mfma_result_wait();   // S_0 is read by VALU in step 0
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) pin(sacc[qb]);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) row_a[ks] += stage_step(0);   // rows: tile 1
 
   // ---- steps: one barrier each
   for (int s = 0; s < NSTEP; ++s) {
-    issue_copies(s + kPD);
-    read_rows(vrow_a, KT{}, va);      // V_s
-    read_rows(krow_a, Z{}, ka);       // K_{s+1}
-    phase1();
+    phase1(s);
     if (edge_step(s)) {
       mask_step(s);
       pin_p();
     }
-    wait_lgkmcnt0_fence();
-    read_kt();                        // K_s^T, for dQ_s in the next step
     phase2();
-    // next stage: V and K^T rows move to tile s+1, K rows to tile s+2
+    // next stage: rows move to tile s+2, transposed halves to tile s+1
     {
       const int d0 = stage_step(s), d1 = stage_step(s + 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        vrow_a[ks] += d0;
-        krow_a[ks] += d1;
-      }
+      for (int ks = 0; ks < KS; ++ks) row_a[ks] += d1;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) tr_a[h][db] += d0;
     }
-    wait_lgkmcnt0();
     wait_vmcnt<(kPD - 2) * 2 * CPT>();
     wg_barrier();
   }
+  wait_lgkmcnt0_fence();
   // dQ of the last step
   if (NSTEP > 0) {
     static_for<NG>([&](auto mc) __attribute__((always_inline)) {
@@ -409,6 +417,23 @@ __global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
   }
 }
 
+// Under a causal mask (no left window) the number of key steps grows linearly with the query
+// tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
+// latest (longest) tiles go first.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE];
+  char FA_LDS* ring = (char FA_LDS*)lds_raw;
+  int bh, t;
+  xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, t);
+  t = a.n_tiles - 1 - t;
+  const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
+    dq_tile<D, BF16>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch(const BwdParams& p, hipStream_t stream) {
   using S = QShape<D>;
@@ -433,7 +458,10 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
   a.dlo = p.causal ? 0 : -wr;
   a.dhi = wl;
-  const long blocks = (long)a.n_bh * a.n_tiles;
+  const int half = (a.n_tiles + 1) / 2;
+  a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
+  a.n_units = a.paired ? half : a.n_tiles;
+  const long blocks = (long)a.n_bh * a.n_units;
   hipLaunchKernelGGL((dq_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

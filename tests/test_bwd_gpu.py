@@ -190,3 +190,17 @@ def test_guard_bands_backward(fa):
     for b in bufs:
         assert (b[:pad] == 5).all() and (b[-pad:] == 5).all()
     check_grads(views, inp, 1 / 8, True, (-1, -1), label="guard")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_tile_pairing_backward(fa, d):
+    """Grids large enough that the causal dK/dV and dQ kernels pair tile t with tile
+    n_tiles-1-t (96 heads, N=1100: 5 key tiles of 256 at d=64, 9 of 128 at d=128, so the middle
+    tile pairs with itself); heads at both ends and inside against the oracle."""
+    import torch
+    inp = W.random_case((1, 96, 1100, d), "bf16", seed=97 + d, with_grad=True)
+    grads = run(fa, inp, None, True, (-1, -1))
+    for g in grads:
+        assert torch.isfinite(g).all()
+    check_grads(grads, inp, 1 / math.sqrt(d), True, (-1, -1), heads=[(0, 0), (0, 47), (0, 95)],
+                label=f"pairing d={d}")
