@@ -5,11 +5,14 @@
 
 Every source under ``csrc/`` is compiled to an object in ``_build/`` (in parallel) and
 linked into ``exact_attention_125_amd/libfa.so``.  All device code is compiled with packed
-fp32 instructions disabled.
+fp32 instructions disabled.  The device code of the kernels that issue MFMAs and LDS reads as
+inline assembly is also compiled to assembly and checked (``isa_check.py``); a finding fails
+the build.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import importlib.util
 import os
 import subprocess
 import sys
@@ -51,11 +54,32 @@ def _compile(src: str) -> str:
     return obj
 
 
+# sources whose MFMAs are inline assembly (full check) and whose LDS reads are (LDS check)
+ASM_MFMA = ("bwd_dkdv.hip", "bwd_dq.hip")
+ASM_LDS = ("fwd_main.hip",)
+
+
+def _isa_check_module():
+    spec = importlib.util.spec_from_file_location("fa_isa_check", os.path.join(PKG, "isa_check.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _check(item):
+    name, mfma = item
+    _isa_check_module().check_sources([os.path.join(CSRC, name)], COMMON, _hipcc(), BUILD, mfma=mfma)
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    checks = [(n, True) for n in ASM_MFMA] + [(n, False) for n in ASM_LDS]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(checks))) as ex:
+        pending = [ex.submit(_check, c) for c in checks]
         objs = list(ex.map(_compile, srcs))
+        for f in pending:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
