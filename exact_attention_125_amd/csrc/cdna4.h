@@ -259,6 +259,7 @@ __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
 // Keeps x in its registers, unchanged, up to this point (its registers are not reused before).
 __device__ __forceinline__ void keep(const f32x16& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void keep(const f32x4& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(const u32x4& x) { asm volatile("" ::"v"(x)); }
 
 // ---------------------------------------------------------------------------- cross-lane
 // The partner of lane l is lane l ^ 32.  permlane32_swap(x, x) leaves {x[l], x[l^32]} in

@@ -58,8 +58,8 @@ namespace {
 
 constexpr int kThreads = 512;      // 8 waves
 constexpr int kBr = 256;           // query rows per query tile (32 per wave)
-constexpr int kPD = 4;             // key tiles copied ahead
-constexpr int kNS = kPD + 1;       // LDS ring stages, K and V each
+constexpr int kPD = 3;             // key tiles copied ahead
+constexpr int kNS = kPD + 1;       // LDS ring stages, K and V each (the loop is unrolled over them)
 constexpr float kTau = 8.0f;
 constexpr float kNoRef = -1e30f;   // reference of a row with no visible key yet
 
@@ -88,18 +88,22 @@ struct Shape {
   static constexpr int KK = BC / 16;             // 16-key steps of P V
   static constexpr int RB = D * 2;               // bytes per row
   static constexpr int TILE = BC * RB;           // bytes per K or V tile
-  static_assert(TILE == 16 * kThreads, "one 16-byte chunk per thread per tile");
+  static constexpr int CPT = TILE / (16 * kThreads);   // 16-byte copies per thread per tile
+  static_assert(CPT * 16 * kThreads == TILE, "whole 16-byte chunks per thread");
   static_assert(kPD >= 2, "the phase-1 wait keeps one iteration of copies in flight");
+  static_assert((kNS - 1) * TILE + (KK - 1) * 16 * RB < 65536 &&
+                (kNS - 1) * TILE + (MB - 1) * 32 * RB < 65536, "operand offsets fit the ds immediate");
 };
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
+  constexpr int TILE = S::TILE, CPT = S::CPT;
 
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * S::TILE];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE];
   char FA_LDS* kring = (char FA_LDS*)lds_raw;
-  char FA_LDS* vring = kring + kNS * S::TILE;
+  char FA_LDS* vring = kring + kNS * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,20 +132,21 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
   const int tr_key = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
-  // LDS offsets inside a stage, independent of the stage: K operand of k-step ks (row l32,
-  // chunk 2 ks + hi; the 32-key block mb adds 32 rows) and V^T operand halves h (rows
-  // tr_key + 8 h) of dim block db (the 16-key step kk adds 16 rows).  The swizzle of a row
-  // depends only on bits that adding 32 or 16 rows leaves alone.
-  int kb[KS];
+  // LDS addresses of the operands in ring stage 0; stage st, the 32-key block mb (K) and the
+  // 16-key step kk (V) add immediate offsets (st TILE, 32 mb RB, 16 kk RB): the swizzle of a
+  // row depends only on bits that adding 16 or 32 rows leaves alone.  K operand of k-step ks:
+  // row l32, chunk 2 ks + hi.  V^T operand half h of dim block db: rows tr_key + 8 h.
+  unsigned ka[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kb[ks] = tile_offset<D>(l32, 2 * ks + hi);
-  unsigned vb[2][DB];
+  for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_addr(kring) + tile_offset<D>(l32, 2 * ks + hi);
+  unsigned va[2][DB];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      vb[h][db] = tile_offset<D>(tr_key + 8 * h, 4 * db + 2 * (tg & 1) + (tq >> 1)) + tr_byte;
-  // async copies: thread tid fills physical 16-byte chunk tid of each tile
+      va[h][db] = lds_addr(vring) + tile_offset<D>(tr_key + 8 * h, 4 * db + 2 * (tg & 1) + (tq >> 1)) + tr_byte;
+  // async copies: thread tid fills physical 16-byte chunks tid + kThreads j of each tile;
+  // chunk tid + kThreads j lies 16 kThreads j / RB rows below chunk tid, which keeps its swizzle
   const int cp_row = (16 * tid) / RB;
   const int cp_src = cp_row * RB + ((((16 * tid) % RB) / 16) ^ chunk_swizzle<D>(cp_row)) * 16;
 
@@ -154,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     const int wq0 = q0 + 32 * stripe;
     const int qi = wq0 + l32;
 
+    // Q^T operands, read once (B operand of every S^T product)
     i16x8 qreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -170,100 +176,105 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     const int row_lo = mk.wl >= 0 ? max(0, qi - mk.wl) : 0;
     const int row_hi = min(n - 1, mk.causal ? qi : (mk.wr >= 0 ? qi + mk.wr : n - 1));
 
-    auto issue_copies = [&](int tk, int tv) __attribute__((always_inline)) {
+    // ring stage of a tile is its index mod kNS; ST is that stage where the caller knows it
+    auto issue_copies = [&](int tk, int tv, int st_k, int st_v) __attribute__((always_inline)) {
       // tiles past the last one read beyond the buffer: zero fills, no memory traffic
-      const int ok = tk < T ? (t_begin + tk) * BC * RB : head_bytes;
-      const int ov = tv < T ? (t_begin + tv) * BC * RB : head_bytes;
-      buffer_load16_lds(rk, kring + (tk % kNS) * S::TILE + 1024 * wave, cp_src + ok);
-      buffer_load16_lds(rv, vring + (tv % kNS) * S::TILE + 1024 * wave, cp_src + ov);
+      const int ok = tk < T ? (t_begin + tk) * TILE : head_bytes;
+      const int ov = tv < T ? (t_begin + tv) * TILE : head_bytes;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        buffer_load16_lds(rk, kring + st_k * TILE + 16 * kThreads * j + 1024 * wave, cp_src + 16 * kThreads * j + ok);
+        buffer_load16_lds(rv, vring + st_v * TILE + 16 * kThreads * j + 1024 * wave, cp_src + 16 * kThreads * j + ov);
+      }
     };
 
     // ---- per-wave state of this query tile
-    f32x16 oacc[DB];
+    f32x16 oacc[DB];                 // O^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m_ref = kNoRef, l_run = 0.f, alpha = 1.f;
     bool moved = false;
     f32x16 sb[2][MB];
     unsigned pk[MB][8];
-    i16x8 kop[MB][KS];
+    u32x4 kop[MB][KS];
     // V^T operands as the two halves the transposing reads return, joined where the MFMA
     // uses them (after the wait), so no copy of them can run before the data has landed
     i16x4 vlo[KK][DB], vhi[KK][DB];
 
+    // Key tiles t_in_lo <= t <= t_in_hi show every key to every query of this wave (the
+    // conditions of Mask::all_visible solved for the tile index once, so that the per-tile
+    // test is two scalar compares).  Shifts by log2(BC) are floor divisions, also below 0.
+    constexpr int SH = BC == 64 ? 6 : 5;
+    static_assert((1 << SH) == BC, "tile width is a power of two");
+    int t_in_hi = (n >> SH) - 1;                                          // j1 <= n
+    if (mk.causal) t_in_hi = min(t_in_hi, (wq0 - BC + 1) >> SH);        // j1 - 1 <= q_first
+    if (mk.wr >= 0) t_in_hi = min(t_in_hi, (wq0 + mk.wr - BC + 1) >> SH);
+    const int t_in_lo = (mk.wl >= 0 ? -((mk.wl - wq0 - 31) >> SH) : 0) - t_begin;  // j0 >= q_last - wl
+    t_in_hi -= t_begin;
     auto edge = [&](int t) __attribute__((always_inline)) {
-      const int j0 = (t_begin + t) * BC;
-      return !mk.all_visible(wq0, wq0 + 31, j0, j0 + BC);
+      return t < t_in_lo || t > t_in_hi;
     };
 
-    // ---- the pieces of work
-    auto read_k = [&](int t) __attribute__((always_inline)) {
-      const char FA_LDS* kt = kring + (t % kNS) * S::TILE;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          kop[mb][ks] = __builtin_bit_cast(i16x8, lds_read16(kt + kb[ks], 32 * mb * RB));
+    // ---- the pieces of work.  Operand reads are untracked (waited for with lgkmcnt fences);
+    // ST is the ring stage as a constant, so every address is a register plus an immediate.
+    auto read_k = [&](auto stc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value;
+      static_for<KS>([&](auto ksc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ksc)::value;
+        static_for<MB>([&](auto mbc) __attribute__((always_inline)) {
+          constexpr int mb = decltype(mbc)::value;
+          kop[mb][ks] = lds_read16_nowait<ST * TILE + 32 * mb * RB>(ka[ks]);
+        });
+      });
     };
-    // V^T operands, read without compiler-inserted waits (see lds_read_tr_nowait); they are
-    // used only after a wait_lgkmcnt0.
-    auto read_v = [&](int t) __attribute__((always_inline)) {
-      const unsigned base = lds_addr(vring) + (t % kNS) * S::TILE;
-      unsigned va[2][DB];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) va[h][db] = base + vb[h][db];
+    auto read_v = [&](auto stc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value;
       static_for<KK>([&](auto kkc) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          vlo[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(va[0][db]);
-          vhi[kk][db] = lds_read_tr_nowait<kk * 16 * RB>(va[1][db]);
+          vlo[kk][db] = lds_read_tr_nowait<ST * TILE + kk * 16 * RB>(va[0][db]);
+          vhi[kk][db] = lds_read_tr_nowait<ST * TILE + kk * 16 * RB>(va[1][db]);
         }
       });
     };
-    auto gemm0 = [&](auto xb) __attribute__((always_inline)) {
-      constexpr int X = decltype(xb)::value;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sb[X][mb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          sb[X][mb] = mfma32x32x16<BF16>(kop[mb][ks], qreg[ks], sb[X][mb]);
+    // V^T * P^T products of one 16-key step into O^T
+    auto pv = [&](auto ec) __attribute__((always_inline)) {
+      constexpr int e = decltype(ec)::value, kk = e / DB, db = e % DB;
+      const u32x4 pb = {pk[kk >> 1][4 * (kk & 1) + 0], pk[kk >> 1][4 * (kk & 1) + 1],
+                        pk[kk >> 1][4 * (kk & 1) + 2], pk[kk >> 1][4 * (kk & 1) + 3]};
+      oacc[db] = mfma32x32x16<BF16>(__builtin_shufflevector(vlo[kk][db], vhi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7),
+                                    __builtin_bit_cast(i16x8, pb), oacc[db]);
     };
-    auto gemm1 = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 pb = {pk[kk >> 1][4 * (kk & 1) + 0], pk[kk >> 1][4 * (kk & 1) + 1],
-                          pk[kk >> 1][4 * (kk & 1) + 2], pk[kk >> 1][4 * (kk & 1) + 3]};
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[db] = mfma32x32x16<BF16>(__builtin_shufflevector(vlo[kk][db], vhi[kk][db], 0, 1, 2, 3, 4, 5, 6, 7),
-                                        __builtin_bit_cast(i16x8, pb), oacc[db]);
-      }
+    // K Q^T product e of S^T (k-step e / MB, 32-key block e % MB)
+    auto qk = [&](auto xb, auto ec) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value, e = decltype(ec)::value, ks = e / MB, mb = e % MB;
+      sb[X][mb] = mfma32x32x16<BF16>(__builtin_bit_cast(i16x8, kop[mb][ks]), qreg[ks],
+                                     ks == 0 ? f32x16{} : sb[X][mb]);
     };
-    // hidden scores -> -inf (edge tiles only)
+    // hidden scores -> -inf (edge tiles only): key j is visible iff j - row_lo, as an unsigned
+    // number, is at most row_hi - row_lo
     auto mask = [&](auto xb, int t) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
-      const int base = (t_begin + t) * BC + 4 * hi;
+      const unsigned u0 = (unsigned)((t_begin + t) * BC + 4 * hi - row_lo);
+      const unsigned width = (unsigned)(row_hi - row_lo);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = base + 32 * mb + 8 * (r >> 2) + (r & 3);
-          sb[X][mb][r] = (j >= row_lo && j <= row_hi) ? sb[X][mb][r] : NEG_INF;
+          const unsigned u = u0 + (unsigned)(32 * mb + 8 * (r >> 2) + (r & 3));
+          sb[X][mb][r] = u <= width ? sb[X][mb][r] : NEG_INF;
         }
     };
-    // row max, reference update, x = s*c - m (in place)
-    auto alu0 = [&](auto xb) __attribute__((always_inline)) {
-      constexpr int X = decltype(xb)::value;
-      float ext = sb[X][0][0];
+    // ALU0 of S_X: row max, reference update, x = s*c - m (in place)
+    // running row max over elements [LO, HI) (LO == 0 starts it)
+    auto row_max = [&](auto xb, auto lo_c, auto hi_c, float& ext) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value, LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+      if constexpr (LO == 0) ext = sb[X][0][0];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = (mb == 0 ? 1 : 0); r < 16; ++r) ext = fmaxf(ext, sb[X][mb][r]);
+      for (int e = LO == 0 ? 1 : LO; e < HI; ++e) ext = fmaxf(ext, sb[X][e / 16][e % 16]);
+    };
+    auto update_ref = [&](float ext) __attribute__((always_inline)) {
       ext = max_with_partner(ext);
       const float m_tile = ext * c;                     // -inf when no key of the tile shows
       const float g = m_tile - m_ref;                   // +huge on a row's first visible tile
@@ -274,142 +285,231 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
       l_run *= alpha;
       m_ref = move ? m_tile : m_ref;
       moved = move;
+    };
+    auto shift = [&](auto xb, auto lo_c, auto hi_c) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value, LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
       const float neg_m = -m_ref;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sb[X][mb][r] = __builtin_fmaf(sb[X][mb][r], c, neg_m);
+      for (int e = LO; e < HI; ++e) sb[X][e / 16][e % 16] = __builtin_fmaf(sb[X][e / 16][e % 16], c, neg_m);
     };
-    // P = 2^x, l += P (fp32), P rounded to the input type
+    using Z = std::integral_constant<int, 0>;
+    using NE = std::integral_constant<int, MB * 16>;
+    auto alu0 = [&](auto xb) __attribute__((always_inline)) {
+      float ext;
+      row_max(xb, Z{}, NE{}, ext);
+      update_ref(ext);
+      shift(xb, Z{}, NE{});
+    };
+    // ALU1 of S_Y, pair pp of its elements: P = 2^x (exp_pair), then l += P (fp32, in four
+    // partial sums) and P rounded to the input type (sum_pair)
+    auto exp_pair = [&](auto yb, auto ppc, float (&p)[2]) __attribute__((always_inline)) {
+      constexpr int Y = decltype(yb)::value, pp = decltype(ppc)::value;
+      constexpr int mb = pp / 8, r = 2 * (pp % 8);
+      p[0] = exp2_fast(sb[Y][mb][r]);
+      p[1] = exp2_fast(sb[Y][mb][r + 1]);
+    };
+    auto sum_pair = [&](auto ppc, const float (&p)[2], float (&part)[4]) __attribute__((always_inline)) {
+      constexpr int pp = decltype(ppc)::value;
+      constexpr int mb = pp / 8, r = 2 * (pp % 8), slot = pp & 3;
+      if constexpr (pp < 4)
+        part[slot] = p[0] + p[1];
+      else
+        part[slot] += p[0] + p[1];
+      pk[mb][r >> 1] = pack2<BF16>(p[0], p[1]);
+    };
     auto alu1 = [&](auto yb) __attribute__((always_inline)) {
-      constexpr int Y = decltype(yb)::value;
       float part[4];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(sb[Y][mb][r]);
-          const float p1 = exp2_fast(sb[Y][mb][r + 1]);
-          const int slot = (r >> 1) & 3;
-          part[slot] = (mb == 0 && r < 8) ? p0 + p1 : part[slot] + (p0 + p1);
-          pk[mb][r >> 1] = pack2<BF16>(p0, p1);
-        }
+      static_for<MB * 8>([&](auto ppc) __attribute__((always_inline)) {
+        float p[2];
+        exp_pair(yb, ppc, p);
+        sum_pair(ppc, p, part);
+      });
       l_run += (part[0] + part[1]) + (part[2] + part[3]);
     };
     auto rescale = [&]() __attribute__((always_inline)) {
       if (__any(moved)) {
+        keep_branch();                  // rare: not to be turned into multiplies by 1 on every tile
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       }
       moved = false;
     };
 
-    // ---- phases
+    // ---- phases.  Each MFMA is followed by its share of the phase's VALU work, and a
+    // scheduling barrier keeps that order: the MFMA runs while the VALU work issues, and the
+    // exponentials are spread evenly instead of being bunched.
     auto compute_a = [&](auto xb, auto yb) __attribute__((always_inline)) {   // GEMM0 + ALU1
-      gemm0(xb);
-      alu1(yb);
-#pragma unroll
-      for (int e = 0; e < MB * KS; ++e) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, (MB * 40) / (MB * KS), 0);
-      }
+      constexpr int NP = (MB * 8) / (MB * KS);                                  // pairs per MFMA
+      static_assert(NP * MB * KS == MB * 8, "pairs split evenly over the MFMAs");
+      // slot e: product e, the exponentials of its pairs, and the sums and conversions of the
+      // previous slot's pairs (so that no instruction waits for an exponential just issued)
+      float part[4], p[2][NP][2];
+      static_for<MB * KS + 1>([&](auto ec) __attribute__((always_inline)) {
+        constexpr int e = decltype(ec)::value;
+        if constexpr (e < MB * KS) {
+          qk(xb, ec);
+          static_for<NP>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int j = decltype(pc)::value;
+            exp_pair(yb, std::integral_constant<int, e * NP + j>{}, p[e & 1][j]);
+          });
+        }
+        if constexpr (e > 0) {
+          static_for<NP>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int j = decltype(pc)::value;
+            sum_pair(std::integral_constant<int, (e - 1) * NP + j>{}, p[(e - 1) & 1][j], part);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      l_run += (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 8; ++r) pin(pk[mb][r]);
       pin(l_run);
     };
-    auto compute_b = [&](auto xb) __attribute__((always_inline)) {            // GEMM1 + ALU0
-      gemm1();
-      alu0(xb);
-#pragma unroll
-      for (int e = 0; e < KK * DB; ++e) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, (MB * 32 + 16) / (KK * DB), 0);
-      }
+    // GEMM1 + ALU0: the row max under the first MFMAs, the reference update under the next,
+    // the shift spread over the rest
+    auto compute_b = [&](auto xb) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
+      constexpr int NM = KK * DB, NX = NM / 2 - 1;   // NX MFMA slots for the row max
+      static_assert(NM >= 8, "ALU0 spread needs eight MFMA slots");
+      float ext;
+      static_for<NM>([&](auto ec) __attribute__((always_inline)) {
+        constexpr int e = decltype(ec)::value;
+        pv(ec);
+        if constexpr (e < NX) {
+          constexpr int LO = (NE::value * e) / NX, HI = (NE::value * (e + 1)) / NX;
+          row_max(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{}, ext);
+        } else if constexpr (e == NX) {
+          update_ref(ext);
+        } else {
+          constexpr int J = e - NX - 1, NJ = NM - NX - 1;
+          constexpr int LO = (NE::value * J) / NJ, HI = (NE::value * (J + 1)) / NJ;
+          shift(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) pin(sb[X][mb]);
       pin(l_run);
       pin(m_ref);
       pin(alpha);
     };
+    // The scheduler would otherwise sink the operand reads below the phase's interleaved
+    // MFMA/VALU groups, right in front of the wait for them, leaving their latency exposed.
+    // K operands of the next tile stay in their registers until the read that fills them is
+    // waited for, also where the next tile is never computed (the reads are untracked)
+    auto keep_kop = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) keep(kop[mb][ks]);
+    };
+    auto issue_reads_now = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+    };
     auto mask_if_edge = [&](auto xb, int t) __attribute__((always_inline)) {
       if (edge(t)) mask(xb, t);
     };
 
-    // Iteration i; X holds S_{i+1}, Y holds S_i.  Copies: each wave issues its chunk of
-    // K_{i+kPD+1} and V_{i+kPD} at the start of iteration i into ring stage (tile % kNS); at
-    // the end of phase 1 it waits until only the current iteration's copies are
-    // outstanding, and the barrier that ends the iteration publishes everything older.
-    // Tile t is first read in iteration t-2 (K) or t (V), after that barrier of iteration
-    // t-3 or earlier; a stage is rewritten only in the iteration after the barrier that
-    // follows the last read of its previous tile (iteration t-2 for K, t for V).
-    auto iteration = [&](auto xb, auto yb, int i) __attribute__((always_inline)) {
-      issue_copies(i + kPD + 1, i + kPD);
-      read_v(i);
-      compute_a(xb, yb);                 // GEMM0_{i+1} + ALU1_i
-      wait_vmcnt<2 * (kPD - 2)>();
+    // Iteration i, ring stage U = i mod kNS; buffer (i+1) mod 2 receives S_{i+1}, buffer i mod 2
+    // holds S_i.  Copies: each wave issues its chunks of K_{i+kPD+1} (stage U) and V_{i+kPD}
+    // (stage U-1) at the start of iteration i; at the end of phase 1 it waits until only the
+    // current iteration's copies are outstanding, and the barrier that ends the iteration
+    // publishes everything older.  Tile t is first read in iteration t-2 (K) or t (V), after
+    // that barrier of iteration t-3 or earlier; a stage is rewritten only in the iteration
+    // after the barrier that follows the last read of its previous tile (iteration t-2 for K,
+    // t for V).  The phase-1 fence also covers the K operand reads of the previous iteration,
+    // the end-of-iteration wait the V^T reads of phase 1 and the K reads of phase 2.
+    auto iteration = [&](auto uc, int i) __attribute__((always_inline)) {
+      constexpr int U = decltype(uc)::value;
+      using XB = std::integral_constant<int, (U + 1) & 1>;
+      using YB = std::integral_constant<int, U & 1>;
+      issue_copies(i + kPD + 1, i + kPD, U, (U + kNS - 1) % kNS);
+      read_v(std::integral_constant<int, U>{});
+      issue_reads_now();
+      compute_a(XB{}, YB{});             // GEMM0_{i+1} + ALU1_i
+      wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();             // V_i operands have landed (GEMM1_i stays below)
-      mask_if_edge(xb, i + 1);
-      read_k(i + 2);
-      compute_b(xb);                     // GEMM1_i + ALU0_{i+1}
+      mask_if_edge(XB{}, i + 1);
+      read_k(std::integral_constant<int, (U + 2) % kNS>{});
+      issue_reads_now();
+      compute_b(XB{});                   // GEMM1_i + ALU0_{i+1}
       rescale();
       wait_lgkmcnt0();
+      keep_kop();                        // no register of an in-flight read is reused before the wait
       wg_barrier();
     };
     // first iteration (i = -1): only S_0 and its row statistics
     auto iteration_first = [&]() __attribute__((always_inline)) {
       using X = std::integral_constant<int, 0>;
-      issue_copies(kPD, kPD - 1);
-      gemm0(X{});
-      wait_vmcnt<2 * (kPD - 2)>();
-      mask_if_edge(X{}, 0);
-      read_k(1);
+      issue_copies(kPD, kPD - 1, kPD % kNS, (kPD - 1) % kNS);
+      static_for<MB * KS>([&](auto ec) __attribute__((always_inline)) { qk(X{}, ec); });
+      wait_vmcnt<2 * CPT * (kPD - 2)>();
+      if (edge(0)) mask(X{}, 0);
+      read_k(std::integral_constant<int, 1>{});
+      issue_reads_now();
       alu0(X{});
       rescale();
       wait_lgkmcnt0();
       wg_barrier();
     };
-    // last iteration (i = T-1): only P_{T-1} and its product with V_{T-1}
-    auto iteration_last = [&](auto yb) __attribute__((always_inline)) {
-      issue_copies(T + kPD, T + kPD - 1);   // beyond the sequence: zero fills, uniform vmcnt
-      read_v(T - 1);
-      alu1(yb);
-      wait_vmcnt<2 * (kPD - 2)>();
+    // last iteration (i = T-1, ring stage U): only P_{T-1} and its product with V_{T-1}
+    auto iteration_last = [&](auto uc) __attribute__((always_inline)) {
+      constexpr int U = decltype(uc)::value;
+      using YB = std::integral_constant<int, U & 1>;
+      // beyond the sequence: zero fills, uniform vmcnt
+      issue_copies(T + kPD, T + kPD - 1, U, (U + kNS - 1) % kNS);
+      read_v(std::integral_constant<int, U>{});
+      issue_reads_now();
+      alu1(YB{});
+      wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();
-      gemm1();
+      static_for<KK * DB>([&](auto ec) __attribute__((always_inline)) { pv(ec); });
       wg_barrier();
     };
 
     // ---- prologue: copies of K_0..K_{kPD-1} and V_0..V_{kPD-2}, all waited for
 #pragma unroll
-    for (int t = 0; t < kPD - 1; ++t) issue_copies(t, t);
+    for (int t = 0; t < kPD - 1; ++t) issue_copies(t, t, t % kNS, t % kNS);
     {
       const int tk = kPD - 1;
-      const int ok = tk < T ? (t_begin + tk) * BC * RB : head_bytes;
-      buffer_load16_lds(rk, kring + (tk % kNS) * S::TILE + 1024 * wave, cp_src + ok);
+      const int ok = tk < T ? (t_begin + tk) * TILE : head_bytes;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        buffer_load16_lds(rk, kring + (tk % kNS) * TILE + 16 * kThreads * j + 1024 * wave, cp_src + 16 * kThreads * j + ok);
     }
     wait_vmcnt<0>();
     wg_barrier();
-    read_k(0);
+    read_k(std::integral_constant<int, 0>{});
+    wait_lgkmcnt0_fence();
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
+    using U0 = std::integral_constant<int, 0>;
+    using U1 = std::integral_constant<int, 1>;
+    using U2 = std::integral_constant<int, 2>;
+    using U3 = std::integral_constant<int, 3>;
+    static_assert(kNS == 4, "the loop is unrolled over four ring stages");
     iteration_first();
     int i = 0;
-    for (; i + 2 <= T - 1; i += 2) {
-      iteration(I1{}, I0{}, i);        // i even: S_{i+1} -> buffer 1
-      iteration(I0{}, I1{}, i + 1);    // i+1 odd: S_{i+2} -> buffer 0
+    for (; i + kNS <= T - 1; i += kNS) {
+      iteration(U0{}, i);
+      iteration(U1{}, i + 1);
+      iteration(U2{}, i + 2);
+      iteration(U3{}, i + 3);
     }
-    if (i < T - 1) {
-      iteration(I1{}, I0{}, i);
-      ++i;
-    }
-    if (i & 1)
-      iteration_last(I1{});
+    const int rem = T - 1 - i;         // 0 .. kNS-1 iterations left, then the last
+    if (rem > 0) iteration(U0{}, i);
+    if (rem > 1) iteration(U1{}, i + 1);
+    if (rem > 2) iteration(U2{}, i + 2);
+    if (rem == 0)
+      iteration_last(U0{});
+    else if (rem == 1)
+      iteration_last(U1{});
+    else if (rem == 2)
+      iteration_last(U2{});
     else
-      iteration_last(I0{});
+      iteration_last(U3{});
     wait_vmcnt<0>();                   // no copy may land after this tile is done
 
     // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
