@@ -238,6 +238,19 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
         }
       });
     };
+    // single operand reads by flat index, for spreading them over a phase's MFMA slots
+    auto read_k_one = [&](auto stc, auto fc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value, f = decltype(fc)::value, ks = f / MB, mb = f % MB;
+      kop[mb][ks] = lds_read16_nowait<ST * TILE + 32 * mb * RB>(ka[ks]);
+    };
+    auto read_v_one = [&](auto stc, auto fc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value, f = decltype(fc)::value;
+      constexpr int kk = f / (2 * DB), db = (f / 2) % DB, h = f % 2;
+      if constexpr (h == 0)
+        vlo[kk][db] = lds_read_tr_nowait<ST * TILE + kk * 16 * RB>(va[0][db]);
+      else
+        vhi[kk][db] = lds_read_tr_nowait<ST * TILE + kk * 16 * RB>(va[1][db]);
+    };
     // V^T * P^T products of one 16-key step into O^T
     auto pv = [&](auto ec) __attribute__((always_inline)) {
       constexpr int e = decltype(ec)::value, kk = e / DB, db = e % DB;
@@ -338,9 +351,12 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     // ---- phases.  Each MFMA is followed by its share of the phase's VALU work, and a
     // scheduling barrier keeps that order: the MFMA runs while the VALU work issues, and the
     // exponentials are spread evenly instead of being bunched.
-    auto compute_a = [&](auto xb, auto yb) __attribute__((always_inline)) {   // GEMM0 + ALU1
+    // GEMM0 + ALU1, and the V^T operand reads of ring stage stv spread over its MFMA slots
+    auto compute_a = [&](auto xb, auto yb, auto stv) __attribute__((always_inline)) {
       constexpr int NP = (MB * 8) / (MB * KS);                                  // pairs per MFMA
       static_assert(NP * MB * KS == MB * 8, "pairs split evenly over the MFMAs");
+      constexpr int NR = 2 * KK * DB, RPS = NR / (MB * KS);                     // reads per slot
+      static_assert(RPS * MB * KS == NR, "reads split evenly over the MFMAs");
       // slot e: product e, the exponentials of its pairs, and the sums and conversions of the
       // previous slot's pairs (so that no instruction waits for an exponential just issued)
       float part[4], p[2][NP][2];
@@ -348,6 +364,9 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
         constexpr int e = decltype(ec)::value;
         if constexpr (e < MB * KS) {
           qk(xb, ec);
+          static_for<RPS>([&](auto rc) __attribute__((always_inline)) {
+            read_v_one(stv, std::integral_constant<int, e * RPS + decltype(rc)::value>{});
+          });
           static_for<NP>([&](auto pc) __attribute__((always_inline)) {
             constexpr int j = decltype(pc)::value;
             exp_pair(yb, std::integral_constant<int, e * NP + j>{}, p[e & 1][j]);
@@ -370,14 +389,18 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     };
     // GEMM1 + ALU0: the row max under the first MFMAs, the reference update under the next,
     // the shift spread over the rest
-    auto compute_b = [&](auto xb) __attribute__((always_inline)) {
+    // (with the K operand reads of ring stage stk spread over its MFMA slots)
+    auto compute_b = [&](auto xb, auto stk) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
       constexpr int NM = KK * DB, NX = NM / 2 - 1;   // NX MFMA slots for the row max
       static_assert(NM >= 8, "ALU0 spread needs eight MFMA slots");
+      constexpr int NR = MB * KS;                     // K reads, at most one per slot from slot 0
+      static_assert(NR <= NM, "one K read per MFMA slot");
       float ext;
       static_for<NM>([&](auto ec) __attribute__((always_inline)) {
         constexpr int e = decltype(ec)::value;
         pv(ec);
+        if constexpr (e < NR) read_k_one(stk, ec);
         if constexpr (e < NX) {
           constexpr int LO = (NE::value * e) / NX, HI = (NE::value * (e + 1)) / NX;
           row_max(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{}, ext);
@@ -420,22 +443,19 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
     // publishes everything older.  Tile t is first read in iteration t-2 (K) or t (V), after
     // that barrier of iteration t-3 or earlier; a stage is rewritten only in the iteration
     // after the barrier that follows the last read of its previous tile (iteration t-2 for K,
-    // t for V).  The phase-1 fence also covers the K operand reads of the previous iteration,
-    // the end-of-iteration wait the V^T reads of phase 1 and the K reads of phase 2.
+    // t for V).  The phase-1 fence covers the V^T reads of phase 1, the end-of-iteration wait
+    // the K reads of phase 2.
     auto iteration = [&](auto uc, int i) __attribute__((always_inline)) {
       constexpr int U = decltype(uc)::value;
       using XB = std::integral_constant<int, (U + 1) & 1>;
       using YB = std::integral_constant<int, U & 1>;
       issue_copies(i + kPD + 1, i + kPD, U, (U + kNS - 1) % kNS);
-      read_v(std::integral_constant<int, U>{});
       issue_reads_now();
-      compute_a(XB{}, YB{});             // GEMM0_{i+1} + ALU1_i
+      compute_a(XB{}, YB{}, std::integral_constant<int, U>{});   // GEMM0_{i+1} + ALU1_i, V_i reads
       wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();             // V_i operands have landed (GEMM1_i stays below)
       mask_if_edge(XB{}, i + 1);
-      read_k(std::integral_constant<int, (U + 2) % kNS>{});
-      issue_reads_now();
-      compute_b(XB{});                   // GEMM1_i + ALU0_{i+1}
+      compute_b(XB{}, std::integral_constant<int, (U + 2) % kNS>{});   // GEMM1_i + ALU0_{i+1}, K_{i+2} reads
       rescale();
       wait_lgkmcnt0();
       keep_kop();                        // no register of an in-flight read is reused before the wait
