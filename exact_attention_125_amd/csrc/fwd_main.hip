@@ -1,8 +1,10 @@
 // Fused attention forward for gfx950: the kernel for grids that fill the chip.
 //
-// A workgroup of 8 waves owns tiles of 256 query rows of one (batch, head), 32 rows per
-// wave.  The key/value sequence is processed in tiles of BC keys (64 for head dim 64, 32
-// for 128).  Per key tile j each wave does
+// A workgroup of 4 waves owns tiles of 128 query rows of one (batch, head), 32 rows per
+// wave; two workgroups share a CU, so each SIMD runs one wave of each.  The two waves of a
+// SIMD then meet no common barrier, and neither idles while the other finishes a step.  The
+// key/value sequence is processed in tiles of BC keys (64 for head dim 64, 32 for 128).  Per
+// key tile j each wave does
 //
 //   GEMM0  S_j^T = K_j Q^T                  MFMA 32x32x16, Q^T in registers, K from LDS
 //   ALU0   row max of S_j, reference update, x = s*c - m                  (VALU)
@@ -17,17 +19,19 @@
 // The loop is software-pipelined in two phases per key tile, with the score registers
 // double buffered (S_{j+1} is produced while P_j is being formed):
 //
-//   phase 1  V_j operands LDS -> registers (issued first, land under the compute);
-//            GEMM0_{j+1} interleaved with ALU1_j
-//   phase 2  edge mask of S_{j+1}; K_{j+2} operands LDS -> registers;
-//            GEMM1_j interleaved with ALU0_{j+1}; O rescaled where a reference moved
+//   phase 1  GEMM0_{j+1} interleaved with ALU1_j and the reads of the V_j operands
+//            (LDS -> registers, landing under the compute)
+//   phase 2  edge mask of S_{j+1}; GEMM1_j interleaved with ALU0_{j+1} and the reads of the
+//            K_{j+2} operands; O rescaled where a reference moved
 //
-// sched_group_barrier interleaves each phase's MFMAs with its VALU work, and empty asm
-// statements keep each phase's VALU results from being sunk into the next phase.  K and V
-// tiles arrive by direct global->LDS copies (no registers, no LDS write instructions) into
-// rings of kNS stages, issued kPD tiles ahead; the 16-byte chunks are placed so that the
-// LDS layout is the XOR-swizzled one the operand reads expect (no bank conflicts).  One
-// workgroup barrier per key tile publishes the copies and guards ring reuse.
+// Scheduling barriers interleave each phase's MFMAs with its VALU work and operand reads, and
+// empty asm statements keep each phase's VALU results from being sunk into the next phase.
+// K and V tiles arrive by direct global->LDS copies (no registers, no LDS write
+// instructions) into rings of kNS stages, issued kPD tiles ahead; the 16-byte chunks are
+// placed so that the LDS layout is the XOR-swizzled one the operand reads expect (no bank
+// conflicts).  The loop is unrolled over the ring stages, so every operand address is a
+// register plus an immediate.  One workgroup barrier per key tile publishes the copies and
+// guards ring reuse.
 //
 // Under a causal mask with no left window bound the work of a query tile grows with its
 // index; there a workgroup processes two query tiles, qt and n_qt - 1 - qt, so that every
@@ -56,8 +60,9 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 512;      // 8 waves
-constexpr int kBr = 256;           // query rows per query tile (32 per wave)
+constexpr int kWaves = 4;          // one per SIMD: two workgroups share a CU
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;   // query rows per query tile (32 per wave)
 constexpr int kPD = 3;             // key tiles copied ahead
 constexpr int kNS = kPD + 1;       // LDS ring stages, K and V each (the loop is unrolled over them)
 constexpr float kTau = 8.0f;
@@ -96,7 +101,7 @@ struct Shape {
 };
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
   constexpr int TILE = S::TILE, CPT = S::CPT;
@@ -123,9 +128,9 @@ __global__ __launch_bounds__(kThreads) void fwd_main_kernel(MainArgs a) {
   const float c = a.c;
   const float NEG_INF = -__builtin_inff();
 
-  // The two waves of a SIMD (w and w + 4) own neighbouring 32-row stripes, so under a
-  // causal mask they have nearly the same number of visible keys.
-  const int stripe = 2 * (wave & 3) + (wave >> 2);
+  // With 8 waves, the two waves of a SIMD (w and w + 4) own neighbouring 32-row stripes, so
+  // under a causal mask they have nearly the same number of visible keys.
+  const int stripe = kWaves == 8 ? 2 * (wave & 3) + (wave >> 2) : wave;
 
   // ---- per-lane constants
   // transposing-read coordinates (see cdna4.h): 16-lane group, row, quad
