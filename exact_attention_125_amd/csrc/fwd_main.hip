@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     f32x16 oacc[DB];                 // O^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float m_ref = kNoRef, l_run = 0.f, alpha = 1.f;
+    float m_ref = kNoRef, m_prev = kNoRef, l_run = 0.f;
     bool moved = false;
     f32x16 sb[2][MB];
     unsigned pk[MB][8];
@@ -299,8 +299,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       const float l_row = sum_with_partner(l_run);      // both lanes of a row decide alike
       const bool heavy = exp2_fast(g + 4.f) > l_row;
       const bool move = (g > 0.f) & ((g > kTau) | heavy);
-      alpha = move ? exp2_fast(m_ref - m_tile) : 1.f;   // 0 on a row's first visible tile
-      l_run *= alpha;
+      m_prev = m_ref;
       m_ref = move ? m_tile : m_ref;
       moved = move;
     };
@@ -344,9 +343,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       });
       l_run += (part[0] + part[1]) + (part[2] + part[3]);
     };
+    // O and l follow a moved reference (rare): alpha = 2^(m_old - m_new), 1 where the row's
+    // reference stayed, 0 on a row's first visible tile
     auto rescale = [&]() __attribute__((always_inline)) {
       if (__any(moved)) {
-        keep_branch();                  // rare: not to be turned into multiplies by 1 on every tile
+        keep_branch();                  // not to be turned into multiplies by 1 on every tile
+        const float alpha = exp2_fast(m_prev - m_ref);
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       }
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // (with the K operand reads of ring stage stk spread over its MFMA slots)
     auto compute_b = [&](auto xb, auto stk) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
-      constexpr int NM = KK * DB, NX = NM / 2 - 1;   // NX MFMA slots for the row max
+      constexpr int NM = KK * DB, NX = 2;            // NX MFMA slots for the row max
       static_assert(NM >= 8, "ALU0 spread needs eight MFMA slots");
       constexpr int NR = MB * KS;                     // K reads, at most one per slot from slot 0
       static_assert(NR <= NM, "one K read per MFMA slot");
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       for (int mb = 0; mb < MB; ++mb) pin(sb[X][mb]);
       pin(l_run);
       pin(m_ref);
-      pin(alpha);
+      pin(m_prev);
     };
     // The scheduler would otherwise sink the operand reads below the phase's interleaved
     // MFMA/VALU groups, right in front of the wait for them, leaving their latency exposed.

@@ -187,6 +187,21 @@ def test_causal_pairing_and_many_tiles(fa):
                       "bf16", heads=heads, rows=rows, label=f"pairing N={N} d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rem", [0, 1, 2, 3])
+def test_key_tile_count_remainders(fa, d, rem):
+    """The main kernel's key loop runs in groups of four tiles and then 0-3 single tiles before
+    the last one: sequences whose tile count leaves each remainder, with a ragged last tile,
+    without and with a causal mask."""
+    bc = 64 if d == 64 else 32                      # keys per tile of the main kernel
+    n = bc * (4 * 2 + rem + 1) - 5
+    inp = W.random_case((1, 2, n, d), "bf16", seed=300 + 10 * d + rem)
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (2 * bc + 3, 0))]:
+        o, lse = run(fa, inp, None, causal, window, kernel="main")
+        check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], 1 / math.sqrt(d), causal, window,
+                      "bf16", label=f"remainder {rem} n={n} d={d} causal={causal} window={window}")
+
+
 def test_guard_bands_untouched(fa):
     import torch
     B, H, N, d = 1, 3, 130, 64
