@@ -12,6 +12,10 @@ Prints ONE JSON line:
   value         whole-step TFLOP/s: algorithmic FLOPs (4 d per visible (query, key) pair
                 forward, 10 d backward, per (batch, head)) over the wall time of K steps
                 bracketed by device synchronisation
+  kernels       per kernel: mean, median and minimum duration over the K timed steps (HIP
+                events on the launch stream, caches warm from the previous step), and the
+                mean and median of a second pass of K steps each preceded by a write of
+                --flush-mib MiB that evicts L2 and the infinity cache ("cold")
   roofline      the kernel with the largest share of the step: its algorithmic FLOPs per
                 launch over its average duration (HIP events on the launch stream)
                 against the published dense bf16/fp16 MFMA peak of 2516.6 TFLOP/s
@@ -24,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -45,8 +50,10 @@ KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_kernel", "fwd"), ("delta_kernel
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="bytes written before each step of the cold pass (0: no cold pass)")
     ap.add_argument("--workload", default=W.TRAIN.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward kernel alone (default: forward + backward)")
@@ -257,8 +264,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    kernel_ms = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
-                 / args.steps for i, (name, _) in enumerate(stages)}
+    per_step = {name: [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+                for i, (name, _) in enumerate(stages)}
+    kernel_ms = {name: sum(t) / len(t) for name, t in per_step.items()}
+
+    # cold pass (not part of `value`): each step after a write that evicts L2 and the
+    # infinity cache, so K, V (and Q, dO) come from HBM again
+    cold = None
+    if args.flush_mib > 0:
+        flush = torch.empty(args.flush_mib << 20, device="cuda", dtype=torch.uint8)
+        cev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                for _ in stages] for _ in range(args.steps)]
+        for s in range(args.steps):
+            flush.fill_(s & 0xFF)
+            step(cev[s])
+        torch.cuda.synchronize()
+        cold = {name: [cev[s][i][0].elapsed_time(cev[s][i][1]) for s in range(args.steps)]
+                for i, (name, _) in enumerate(stages)}
+        del flush
     pairs = allowed_pairs(w.N, w.causal, w.window)
     fl = flops(w, pairs)
     step_flops = fl["fwd"] + (fl["bwd"] if backward else 0.0)
@@ -269,10 +292,16 @@ def main():
     kernels = {}
     for name, t in kernel_ms.items():
         kf = {"fwd": fl["fwd"], "dkdv": fl["dkdv"], "dq": fl["dq"]}.get(name)
-        entry = {"ms": round(t, 4)}
+        entry = {"ms": round(t, 4), "median_ms": round(statistics.median(per_step[name]), 4),
+                 "min_ms": round(min(per_step[name]), 4)}
+        if cold is not None:
+            entry["cold_ms"] = round(sum(cold[name]) / len(cold[name]), 4)
+            entry["cold_median_ms"] = round(statistics.median(cold[name]), 4)
         if kf is not None:
             entry["tflops"] = round(kf / (t * 1e-3) / 1e12, 2)
             entry["frac"] = round(entry["tflops"] / PEAK_TFLOPS, 4)
+            if cold is not None:
+                entry["cold_tflops"] = round(kf / (entry["cold_ms"] * 1e-3) / 1e12, 2)
         else:   # delta: bandwidth kernel, reads O and dO, writes fp32 delta
             nbytes = 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
             entry["gbs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
