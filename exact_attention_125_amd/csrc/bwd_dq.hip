@@ -1,7 +1,9 @@
-// dQ for gfx950 by recomputation: query-owned workgroups, one wave per SIMD.
+// dQ for gfx950 by recomputation: query-owned workgroups of one wave per SIMD.
 //
-// A workgroup of 4 waves owns QWG queries of one (batch, head); each wave owns QW = 32 QB of
-// them (QB = 2 blocks of 32 queries at head dim 64, 1 at 128), one query per lane and block.
+// A workgroup of 4 waves owns QWG queries of one (batch, head); each wave owns QW = 32 of
+// them, one query per lane.  At head dim 64 the working set fits in half of a SIMD's registers,
+// so two workgroups share a CU and each SIMD issues the VALU work of two waves (a single wave
+// issues VALU instructions at half the rate the SIMD can retire them); at 128 one does.
 // The keys those queries can see stream through LDS in steps of 32.  Per step s and wave
 // (C[key][query] layouts, so a lane's accumulator entries all belong to its query):
 //
@@ -42,7 +44,7 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves, one per SIMD
+constexpr int kThreads = 256;   // 4 waves, one per SIMD per workgroup
 constexpr int kBK = 32;         // keys per step
 constexpr int kPD = 4;          // key tiles copied ahead
 constexpr int kNS = kPD + 1;    // LDS ring stages
@@ -67,7 +69,7 @@ struct DqArgs {
 
 template <int D>
 struct QShape {
-  static constexpr int QB = D == 64 ? 2 : 1;       // 32-query blocks per wave
+  static constexpr int QB = 1;                     // 32-query blocks per wave
   static constexpr int QW = 32 * QB;               // queries per wave
   static constexpr int QWG = 4 * QW;               // queries per workgroup
   static constexpr int KS = D / 16;                // k-steps over the head dim
@@ -234,7 +236,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // ---- the three products, one MFMA at a time
   constexpr int NM = KS * QB;       // MFMAs of S^T or dP^T
   constexpr int NG = 2 * DB * QB;   // MFMAs of dQ^T
-  static_assert(NM == 8 && NG == 8, "phases interleave 16 + 8 MFMAs");
+  static_assert(NM == NG && NM >= 4, "phases interleave products of equal length");
   auto mfma_s = [&](auto mc) __attribute__((always_inline)) {        // S^T = K Q^T
     constexpr int m = decltype(mc)::value, ks = m / QB, qb = m % QB;
     if constexpr (ks == 0) mfma_bagpr_first<BF16>(sacc[qb], ka[ks], qreg[qb][ks]);
@@ -421,7 +423,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 // tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
 // latest (longest) tiles go first.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void dq_main_kernel(DqArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
   int bh, t;
