@@ -35,9 +35,9 @@
 //
 // Under a causal mask with no left window bound the work of a query tile grows with its
 // index; there a workgroup processes two query tiles, qt and n_qt - 1 - qt, so that every
-// workgroup has the same amount of work (when that still leaves a workgroup per CU).  Every wave computes every key tile the
-// workgroup visits; tiles hidden from some or all of a wave's queries go through the mask
-// and contribute P = 0.
+// workgroup has the same amount of work (when that still leaves a workgroup per CU).  Every
+// wave computes every key tile the workgroup visits; tiles hidden from some or all of a
+// wave's queries go through the mask and contribute P = 0.
 //
 // The arithmetic follows the tiling of "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型
 // （含A100环境配置）" §2.1 with the running max / running sum of its §2.2 (read as
@@ -46,7 +46,7 @@
 // Attention 3.7 核心原理与实战：加速Transformer模型训练与推理" §3.1 describes.  The reference m of a
 // row is the exact maximum of its first visible tile and moves to a later tile's exact
 // maximum when that one is not negligible against the mass already summed (2^g * 16 > l) or
-// exceeds m by more than 2^kTau; the softmax does not depend on the shift (the safe-softmax
+// exceeds m by more than kTau (base-2 units); the softmax does not depend on the shift (the safe-softmax
 // argument of the same §2.2), rows dominated by a few keys keep a largest probability of
 // exactly 1, and probabilities stay below 2^kTau.  l is summed in fp32 from unrounded
 // probabilities; P is rounded once to the input type; LSE = ln 2 * (m + log2 l).
