@@ -132,7 +132,8 @@ def cpu_baseline(w, sample_heads):
             "sample": f"{n_heads} of {w.B * w.H} (batch, head) slices of {w.name}, "
                       f"{'forward+backward' if w.backward else 'forward'}, float64 numpy "
                       f"materialising S and P, "
-                      f"{secs:.2f} s wall, one process and one BLAS thread per core"}
+                      f"{secs:.2f} s wall, one process and one BLAS thread ({pool.blas_info()}) "
+                      f"per core"}
 
 
 def kernel_key(name):

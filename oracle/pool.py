@@ -46,6 +46,19 @@ def _eval_head(kind, b, h):
     return (b, h, o, lse, dq, dk, dv)
 
 
+def blas_info() -> str:
+    """The BLAS library numpy calls (vendor and version), as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            return f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+    except Exception:
+        pass
+    return "unknown BLAS"
+
+
 def available_cores() -> int:
     try:
         return len(os.sched_getaffinity(0))
