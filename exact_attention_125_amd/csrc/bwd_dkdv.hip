@@ -150,22 +150,6 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
       dk[kb][db] = f32x16{};
       dv[kb][db] = f32x16{};
     }
-  // into the AGPRs here; the wait states after separate those writes from the first product
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      in_agpr(kreg[kb][ks]);
-      in_agpr(vreg[kb][ks]);
-    }
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      in_agpr(dk[kb][db]);
-      in_agpr(dv[kb][db]);
-    }
-  mfma_operand_wait();
 
   // ---- query steps that can see the workgroup's keys
   int q_lo, q_hi;
@@ -459,6 +443,24 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 
   // ---- prologue: tiles 0..kPD-1, then S_0, dP_0, P_0 and the operands of step 0's phase 1
   for (int t = 0; t < kPD; ++t) issue_copies(t);
+  // K^T, V^T and the accumulators into the AGPRs only now, so that waiting for the K and V rows
+  // does not hold back the copies; the wait states after separate those writes from the first
+  // product
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(kreg[kb][ks]);
+      in_agpr(vreg[kb][ks]);
+    }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      in_agpr(dk[kb][db]);
+      in_agpr(dv[kb][db]);
+    }
+  mfma_operand_wait();
   wait_vmcnt<0>();
   wg_barrier();
   if (NSTEP > 0) {

@@ -118,8 +118,9 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const int q_first = qt * S::QWG;
   const int qw0 = q_first + S::QW * wave;
   i16x8 qreg[QB][KS], greg[QB][KS];
-  float cm[QB];        // c m = -log2(e) LSE
-  f32x16 ndv[QB];      // -delta, the initial accumulator of dP
+  float lse_in[QB], nd_in[QB];   // statistics as loaded (row 0's beyond the sequence)
+  float cm[QB];                  // c m = -log2(e) LSE, set after the prologue copies
+  f32x16 ndv[QB];                // -delta, the initial accumulator of dP, likewise
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + 32 * qb + l32;
@@ -129,30 +130,15 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       qreg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, off));
       greg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, off));
     }
-    const bool ok = q < n;
-    const long r = stat_index(bh, n, ok ? q : 0);
-    cm[qb] = ok ? c_scale * a.stats[r] : 0.f;
-    const float nd = ok ? a.stats[r + kStatRows] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ndv[qb][i] = nd;
+    const long r = stat_index(bh, n, q < n ? q : 0);
+    lse_in[qb] = a.stats[r];
+    nd_in[qb] = a.stats[r + kStatRows];
   }
   f32x16 dqacc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqacc[qb][db] = f32x16{};
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      in_agpr(qreg[qb][ks]);
-      in_agpr(greg[qb][ks]);
-    }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) in_agpr(dqacc[qb][db]);
-  mfma_operand_wait();
 
   // ---- key steps the workgroup's queries can see
   int k_lo, k_hi;
@@ -342,6 +328,28 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // ---- prologue: tiles 0..kPD-1, S_0 and the V_0 rows; dQ_{-1} adds zeros (zero dS and
   // K^T operands)
   for (int t = 0; t < kPD; ++t) issue_copies(t);
+  // Q^T, dO^T, dQ^T and the statistics are used only now: waiting for the Q and dO rows does
+  // not hold back the copies, whose latency overlaps theirs
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(qreg[qb][ks]);
+      in_agpr(greg[qb][ks]);
+    }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) in_agpr(dqacc[qb][db]);
+  mfma_operand_wait();
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool ok = qw0 + 32 * qb + l32 < n;
+    cm[qb] = ok ? c_scale * lse_in[qb] : 0.f;
+    const float nd = ok ? nd_in[qb] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndv[qb][i] = nd;
+  }
   wait_vmcnt<0>();
   wg_barrier();
 #pragma unroll
