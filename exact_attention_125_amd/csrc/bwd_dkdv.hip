@@ -350,9 +350,36 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // no mask: their dO and -delta are zero fills, so they add nothing to dV and their dS is 0;
   // keys past the sequence are not stored.  So only the band dlo <= q - key <= dhi is tested:
   // q - key - dlo = u + 8 (i/4) + i%4 with u per lane, compared unsigned against dhi - dlo.
+  //
+  // Where only a lower band edge on a multiple of 32 crosses the step (the causal diagonal, a
+  // right window of a multiple of 32), every 32x32 block of the step is wholly visible,
+  // wholly hidden or cut along its diagonal: q - key = x - 32 kb + (row - column) with x =
+  // q0 - kw0 a multiple of 32 and row - column in [-31, 31].  Those blocks take constant lane
+  // masks instead of compares.
   auto mask_step = [&](int t) __attribute__((always_inline)) {
     keep_branch();   // not worth running on every step
     const int q0 = (s_begin + t) * kBQ;
+    const int x = q0 - kw0;   // wave-uniform
+    if ((a.dlo & 31) == 0 && a.dhi - x >= 31) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int lo = a.dlo - x + 32 * kb;   // visible iff row - column >= lo
+        if (lo >= 32) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[kb][i] = 0.f;
+#pragma unroll
+          for (int g = 0; g < 8; ++g) pk[kb][g] = 0u;
+        } else if (lo == 0) {
+          static_for<16>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            pv[kb][i] = keep_lanes(pv[kb][i], diag_lanes<false>(i));
+          });
+#pragma unroll
+          for (int g = 0; g < 8; ++g) pk[kb][g] = pack2<BF16>(pv[kb][2 * g], pv[kb][2 * g + 1]);
+        }
+      }
+      return;
+    }
     const unsigned span = (unsigned)(a.dhi - a.dlo);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {

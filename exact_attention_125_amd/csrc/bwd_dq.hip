@@ -254,9 +254,29 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // Hidden pairs of band-edge steps are zeroed after P is formed (a branch around VALU only).
   // Keys past the sequence need no mask (their K rows are zero fills, so they add nothing to
   // dQ); queries past it are not stored.  q - key - dlo = u - (8 (i/4) + i%4), u per lane.
+  //
+  // Where only a lower band edge on a multiple of 32 crosses the step, every 32x32 block is
+  // wholly visible, wholly hidden or cut along its diagonal: q - key = x + (column - row) with
+  // x = qw0 + 32 qb - k0 a multiple of 32.  Those blocks take constant lane masks.
   auto mask_step = [&](int t) __attribute__((always_inline)) {
     keep_branch();   // not worth running on every step
     const int k0 = (s_begin + t) * kBK;
+    if ((a.dlo & 31) == 0 && a.dhi - (qw0 + 32 * (QB - 1) - k0) >= 31) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int lo = a.dlo - (qw0 + 32 * qb - k0);   // visible iff column - row >= lo
+        if (lo >= 32) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[qb][i] = 0.f;
+        } else if (lo == 0) {
+          static_for<16>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            pv[qb][i] = keep_lanes(pv[qb][i], diag_lanes<true>(i));
+          });
+        }
+      }
+      return;
+    }
     const unsigned span = (unsigned)(a.dhi - a.dlo);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {

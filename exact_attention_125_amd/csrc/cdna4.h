@@ -285,6 +285,26 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------- masks
+// The 32x32 MFMA accumulator layout: element i of lane L sits in row 8 (i/4) + 4 (L/32) + i%4
+// and column L % 32.  diag_lanes<KeyRows>(i) is the wave-wide lane mask of the elements i on
+// or below the diagonal of a block whose rows and columns start at the same sequence
+// position: row >= column when rows are queries and columns keys, column >= row when rows are
+// keys and columns queries, i.e. query >= key either way.
+template <bool KeyRows>
+constexpr unsigned long long diag_lanes(int i) {
+  unsigned long long m = 0;
+  for (int lane = 0; lane < 64; ++lane) {
+    const int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), col = lane & 31;
+    if (KeyRows ? col >= row : row >= col) m |= 1ull << lane;
+  }
+  return m;
+}
+// x in the lanes whose bit of the (wave-uniform) mask is set, 0 elsewhere: one v_cndmask with
+// the mask as its scalar condition
+__device__ __forceinline__ float keep_lanes(float x, unsigned long long lanes) {
+  return __builtin_amdgcn_inverse_ballot_w64(lanes) ? x : 0.f;
+}
+
 // Key j is visible to query i iff (!causal || j <= i) && (wl < 0 || j >= i - wl)
 // && (wr < 0 || j <= i + wr), and j < N.
 struct Mask {

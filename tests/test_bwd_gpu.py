@@ -109,8 +109,11 @@ def test_train_workload_backward(fa):
     assert float(sdk.abs().max()) <= 0.02 * float(dk.double().abs().sum(dim=2).max())
 
 
+# (False, (-1, 64)) and (False, (128, 32)) put band edges on multiples of 32, the case the
+# kernels mask with constant lane masks away from the causal diagonal
 MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (0, 0)), (False, (7, 3)),
-         (True, (50, -1)), (False, (0, 40)), (True, (1024, 0))]
+         (True, (50, -1)), (False, (0, 40)), (True, (1024, 0)), (False, (-1, 64)),
+         (False, (128, 32))]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
