@@ -52,38 +52,54 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------- delta
-// One thread per query slot of the padded statistics blocks: delta = sum_c dO[c] * O[c] with
-// both rounded inputs in fp32, stored negated next to m = -LSE / sigma (the exponent offset
-// the recomputation of P needs); slots past the sequence get zeros.
-// Grid: x over a head's padded query slots, y (with a stride loop) over (batch, head).
+// delta = sum_c dO[c] * O[c] per query with both rounded inputs in fp32, stored negated next
+// to m = -LSE / sigma (the exponent offset the recomputation of P needs); slots of the padded
+// statistics blocks past the sequence get zeros.  A row is D / 8 lanes of 16 bytes, so every
+// load instruction of a wave reads 64 / (D / 8) whole consecutive rows (1 KiB, no partial
+// lines); the lanes of a row add their partial sums by butterfly shuffles.
+// Grid: x over a head's padded query slots, 256 per workgroup (64 per wave); y, with a stride
+// loop, over (batch, head).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= stat_blocks(a.n) * kStatRows) return;
+  constexpr int LPR = D / 8;            // lanes per row
+  constexpr int RPI = 64 / LPR;         // rows per load instruction
+  constexpr int IT = 64 / RPI;          // load instructions per wave and tensor
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LPR;
+  const int q_base = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + lane / LPR;
+  const int slots = stat_blocks(a.n) * kStatRows;
   for (long bh = blockIdx.y; bh < a.n_bh; bh += gridDim.y) {
-    float* out = a.stats + stat_index(bh, a.n, q);
-    if (q >= a.n) {
-      out[0] = 0.f;
-      out[kStatRows] = 0.f;
-      continue;
-    }
-    const long r = bh * a.n + q;
-    const u32x4* o = reinterpret_cast<const u32x4*>(a.o + r * D * 2);
-    const u32x4* g = reinterpret_cast<const u32x4*>(a.dout + r * D * 2);
-    float acc = 0.f;
-  #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const u32x4 ov = o[c], gv = g[c];
-  #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc += to_float<BF16>((unsigned short)(ov[w] & 0xffff)) *
-               to_float<BF16>((unsigned short)(gv[w] & 0xffff));
-        acc += to_float<BF16>((unsigned short)(ov[w] >> 16)) *
-               to_float<BF16>((unsigned short)(gv[w] >> 16));
+    u32x4 ov[IT], gv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = q_base + RPI * it;
+      ov[it] = gv[it] = u32x4{};
+      if (q < a.n) {
+        const long off = ((bh * a.n + q) * D + 8 * sub) * 2;
+        ov[it] = *reinterpret_cast<const u32x4*>(a.o + off);
+        gv[it] = *reinterpret_cast<const u32x4*>(a.dout + off);
       }
     }
-    out[0] = -a.lse[r] / a.sigma;
-    out[kStatRows] = -acc;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc += to_float<BF16>((unsigned short)(ov[it][w] & 0xffff)) *
+               to_float<BF16>((unsigned short)(gv[it][w] & 0xffff));
+        acc += to_float<BF16>((unsigned short)(ov[it][w] >> 16)) *
+               to_float<BF16>((unsigned short)(gv[it][w] >> 16));
+      }
+#pragma unroll
+      for (int x = 1; x < LPR; x *= 2) acc += __shfl_xor(acc, x);
+      const int q = q_base + RPI * it;
+      if (sub == 0 && q < slots) {
+        float* out = a.stats + stat_index(bh, a.n, q);
+        const bool in = q < a.n;
+        out[0] = in ? -a.lse[bh * a.n + q] / a.sigma : 0.f;
+        out[kStatRows] = in ? -acc : 0.f;
+      }
+    }
   }
 }
 
