@@ -271,9 +271,41 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
                                      ks == 0 ? f32x16{} : sb[X][mb]);
     };
     // hidden scores -> -inf (edge tiles only): key j is visible iff j - row_lo, as an unsigned
-    // number, is at most row_hi - row_lo
+    // number, is at most row_hi - row_lo.
+    //
+    // Where the band's edges lie on multiples of 32 (causal, windows of multiples of 32) and the
+    // tile holds no key past the sequence, each 32x32 block is wholly visible, wholly hidden or
+    // cut along its diagonal by an edge: q - key = x + (column - row), x = wq0 - (first key of
+    // the block) a multiple of 32, column - row in [-31, 31].  Those blocks take constant lane
+    // masks instead of compares.
+    const bool has_lo = mk.causal || mk.wr >= 0, has_hi = mk.wl >= 0;
+    const int d_lo = mk.causal ? 0 : mk.wr >= 0 ? -mk.wr : 0;   // q - key >= d_lo (has_lo)
+    const bool band32 = (!has_lo || (d_lo & 31) == 0) && (!has_hi || (mk.wl & 31) == 0);
     auto mask = [&](auto xb, int t) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
+      if (band32 && (t_begin + t + 1) * BC <= n) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int x = wq0 - ((t_begin + t) * BC + 32 * mb);   // wave-uniform
+          const int lo = has_lo ? d_lo - x : -32, up = has_hi ? mk.wl - x : 32;
+          if (lo >= 32 || up <= -32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sb[X][mb][r] = NEG_INF;
+            continue;
+          }
+          if (lo == 0)   // column >= row
+            static_for<16>([&](auto rc) __attribute__((always_inline)) {
+              constexpr int r = decltype(rc)::value;
+              sb[X][mb][r] = __builtin_amdgcn_inverse_ballot_w64(diag_lanes<true>(r)) ? sb[X][mb][r] : NEG_INF;
+            });
+          if (up == 0)   // row >= column
+            static_for<16>([&](auto rc) __attribute__((always_inline)) {
+              constexpr int r = decltype(rc)::value;
+              sb[X][mb][r] = __builtin_amdgcn_inverse_ballot_w64(diag_lanes<false>(r)) ? sb[X][mb][r] : NEG_INF;
+            });
+        }
+        return;
+      }
       const unsigned u0 = (unsigned)((t_begin + t) * BC + 4 * hi - row_lo);
       const unsigned width = (unsigned)(row_hi - row_lo);
 #pragma unroll
