@@ -82,12 +82,26 @@ def allowed_pairs(n, causal, window):
     return total
 
 
-def flops(w, pairs):
-    fwd = 4.0 * w.d * w.B * w.H * pairs
-    return {"fwd": fwd, "bwd": 10.0 * w.d * w.B * w.H * pairs,
+def seqlens_of(w):
+    """Per-sample lengths of a padded workload (None for a plain one)."""
+    return [int(x) for x in W.draw_seqlens(w.B, w.N, w.seed)] if w.padded else None
+
+
+def total_pairs(w):
+    """Visible (query, key) pairs of the whole batch: every head of sample b over its own
+    length in a padded batch."""
+    lens = seqlens_of(w)
+    if lens is None:
+        return w.B * w.H * allowed_pairs(w.N, w.causal, w.window)
+    return w.H * sum(allowed_pairs(L, w.causal, w.window) for L in lens)
+
+
+def flops(w, pairs_total):
+    fwd = 4.0 * w.d * pairs_total
+    return {"fwd": fwd, "bwd": 10.0 * w.d * pairs_total,
             # algorithmic share of each backward kernel: dK/dV does 4 of the 5 products,
             # dQ does 1 (its 2 recomputed products are not counted)
-            "dkdv": 8.0 * w.d * w.B * w.H * pairs, "dq": 2.0 * w.d * w.B * w.H * pairs}
+            "dkdv": 8.0 * w.d * pairs_total, "dq": 2.0 * w.d * pairs_total}
 
 
 def source_digest():
@@ -123,13 +137,18 @@ def cpu_baseline(w, sample_heads):
     cores = pool.available_cores()
     n_heads = min(sample_heads or w.B * w.H, w.B * w.H)
     heads = [(i // w.H, i % w.H) for i in range(n_heads)]
+    lens = seqlens_of(w)
+    if lens is not None:   # empty samples have no work: leave them out of the sample
+        heads = [(b, h) for b, h in heads if lens[b] > 0]
     _, secs, used = pool.run_heads(arrays, heads, w.softmax_scale, w.causal, w.window,
-                                   backward=w.backward, workers=cores, keep=False)
-    pairs = allowed_pairs(w.N, w.causal, w.window)
-    per_head = (4.0 + (10.0 if w.backward else 0.0)) * w.d * pairs
-    return {"value": round(per_head * n_heads / secs / 1e12, 6), "unit": "TFLOP/s",
+                                   backward=w.backward, workers=cores, keep=False,
+                                   lengths=lens)
+    per_pair = (4.0 + (10.0 if w.backward else 0.0)) * w.d
+    work = sum(per_pair * allowed_pairs(lens[b] if lens else w.N, w.causal, w.window)
+               for b, _ in heads)
+    return {"value": round(work / secs / 1e12, 6), "unit": "TFLOP/s",
             "cores": used, "kind": "oracle",
-            "sample": f"{n_heads} of {w.B * w.H} (batch, head) slices of {w.name}, "
+            "sample": f"{len(heads)} of {w.B * w.H} (batch, head) slices of {w.name}, "
                       f"{'forward+backward' if w.backward else 'forward'}, float64 numpy "
                       f"materialising S and P, "
                       f"{secs:.2f} s wall, one process and one BLAS thread ({pool.blas_info()}) "
@@ -227,6 +246,8 @@ def main():
     ws = torch.empty(max(fa.bwd_workspace_size(w.B, w.H, w.N, w.d), 16), device="cuda",
                      dtype=torch.uint8)
     scale, causal, window = w.softmax_scale, w.causal, w.window
+    lens = seqlens_of(w)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda") if lens is not None else None
     stages = [("fwd", None)] + ([("delta", fa._lib.BWD_DELTA), ("dkdv", fa._lib.BWD_DKDV),
                                  ("dq", fa._lib.BWD_DQ)] if backward else [])
 
@@ -235,10 +256,10 @@ def main():
             if events is not None:
                 events[idx][0].record()
             if st is None:
-                fa.fwd(q, k, v, scale, causal, window, out=o, lse=lse)
+                fa.fwd(q, k, v, scale, causal, window, out=o, lse=lse, seqlens=sl)
             else:
                 fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv,
-                       workspace=ws, stages=st)
+                       workspace=ws, stages=st, seqlens=sl)
             if events is not None:
                 events[idx][1].record()
 
@@ -283,7 +304,7 @@ def main():
         cold = {name: [cev[s][i][0].elapsed_time(cev[s][i][1]) for s in range(args.steps)]
                 for i, (name, _) in enumerate(stages)}
         del flush
-    pairs = allowed_pairs(w.N, w.causal, w.window)
+    pairs = total_pairs(w)
     fl = flops(w, pairs)
     step_flops = fl["fwd"] + (fl["bwd"] if backward else 0.0)
     ms = wall / args.steps * 1e3
@@ -303,8 +324,9 @@ def main():
             entry["frac"] = round(entry["tflops"] / PEAK_TFLOPS, 4)
             if cold is not None:
                 entry["cold_tflops"] = round(kf / (entry["cold_ms"] * 1e-3) / 1e12, 2)
-        else:   # delta: bandwidth kernel, reads O and dO, writes fp32 delta
-            nbytes = 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+        else:   # delta: bandwidth kernel, reads O and dO (the samples' rows), writes fp32 delta
+            rows = w.H * (sum(lens) if lens is not None else w.B * w.N)
+            nbytes = 2 * rows * w.d * 2 + w.B * w.H * w.N * 4
             entry["gbs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
         kernels[name] = entry
     dominant = max((n for n in kernel_ms if n != "delta"), key=lambda n: kernel_ms[n])
@@ -320,10 +342,13 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q, K, V, dO" +
+                                  (", sample lengths uniform in [N/4, N])" if lens else ")"),
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
                    "head_dim": w.d, "causal": w.causal, "window": list(w.window),
-                   "pass": "fwd+bwd" if backward else "fwd", "visible_pairs_per_head": pairs,
+                   "pass": "fwd+bwd" if backward else "fwd",
+                   "visible_pairs_per_head": pairs // (w.B * w.H),
+                   **({"seqlens": lens, "visible_pairs": pairs} if lens is not None else {}),
                    "flops_per_step": step_flops,
                    "nominal_flops_per_step": nominal * (3.5 if backward else 1.0)},
         "kernels": kernels,

@@ -36,6 +36,9 @@ SIGNATURES = {
                     _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_bwd_stages": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                            _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
+                           _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -112,9 +115,20 @@ def _resolve(q, softmax_scale, window_size):
     return scale, wl, wr
 
 
+def _check_seqlens(seqlens, q):
+    import torch
+    if not seqlens.is_cuda or seqlens.device != q.device:
+        raise ValueError("seqlens must be on the device of q")
+    if seqlens.dtype != torch.int32 or seqlens.dim() != 1 or seqlens.shape[0] != q.shape[0]:
+        raise ValueError("seqlens must be an int32 [B] tensor")
+    if not seqlens.is_contiguous():
+        raise ValueError("seqlens must be contiguous")
+
+
 def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None, lse=None,
-        return_lse=True):
-    """Forward pass.  Returns ``(o, lse)`` (``lse`` None when ``return_lse`` is False)."""
+        return_lse=True, seqlens=None):
+    """Forward pass.  Returns ``(o, lse)`` (``lse`` None when ``return_lse`` is False).
+    ``seqlens`` (int32 [B] on the device) makes it a padded batch (``fa_fwd_varlen``)."""
     import torch
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
@@ -124,16 +138,23 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     if not return_lse:
         lse = None
+    if seqlens is not None:
+        _check_seqlens(seqlens, q)
+        _check(_lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(seqlens),
+                                  B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
+                                  _stream(q.device)))
+        return o, lse
     _check(_lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                        _dtype_code(q), scale, int(bool(causal)), wl, wr, _stream(q.device)))
     return o, lse
 
 
 def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
-        dq=None, dk=None, dv=None, workspace=None, stages=BWD_ALL):
+        dq=None, dk=None, dv=None, workspace=None, stages=BWD_ALL, seqlens=None):
     """Backward pass.  Returns ``(dq, dk, dv)``.  ``stages`` (a mask of BWD_DELTA, BWD_DKDV,
     BWD_DQ) runs a subset of the three kernels; later stages need the earlier ones' results
-    in the same ``workspace`` and outputs."""
+    in the same ``workspace`` and outputs.  ``seqlens`` (int32 [B] on the device) makes it a
+    padded batch (``fa_bwd_varlen``)."""
     import torch
     _check_tensors(q, k, v, o, dout)
     B, H, N, d = q.shape
@@ -144,6 +165,14 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
     need = _lib.fa_bwd_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    if seqlens is not None:
+        _check_seqlens(seqlens, q)
+        _check(_lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(seqlens),
+                                  B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
+                                  int(stages), _stream(q.device)))
+        return dq, dk, dv
     _check(_lib.fa_bwd_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                               workspace.numel() * workspace.element_size(),

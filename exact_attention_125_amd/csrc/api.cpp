@@ -69,22 +69,28 @@ const char* fa_status_string(fa_status s) {
 
 const char* fa_last_error_detail(void) { return g_last_error.c_str(); }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-                 int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
-                 int causal, int window_left, int window_right, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* seqlens, bool varlen, int batch, int heads, int seqlen, int head_dim,
+                   fa_dtype dtype, float softmax_scale, int causal, int window_left,
+                   int window_right, void* stream) {
   g_last_error.clear();
   bool empty = false;
   fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
                               window_right, &empty);
   if (st != FA_OK) return st;
   if (empty) return FA_OK;
-  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+  if (!q || !k || !v || !o || (varlen && !seqlens)) return FA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (lse && !aligned16(lse)))
+      (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
     return FA_ERR_MISALIGNED;
   if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k ||
       (const void*)lse == v || (void*)lse == o)
     return FA_ERR_ALIAS;
+  if (seqlens && ((const void*)seqlens == o || (const void*)seqlens == lse)) return FA_ERR_ALIAS;
 
   fa::FwdParams p;
   p.q = q;
@@ -92,6 +98,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.v = v;
   p.o = o;
   p.lse = lse;
+  p.seqlens = seqlens;
   p.B = batch;
   p.H = heads;
   p.N = seqlen;
@@ -104,6 +111,25 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
+                 int causal, int window_left, int window_right, void* stream) {
+  return fwd_impl(q, k, v, o, lse, nullptr, false, batch, heads, seqlen, head_dim, dtype,
+                  softmax_scale, causal, window_left, window_right, stream);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* seqlens, int batch, int heads, int seqlen, int head_dim,
+                        fa_dtype dtype, float softmax_scale, int causal, int window_left,
+                        int window_right, void* stream) {
+  return fwd_impl(q, k, v, o, lse, seqlens, true, batch, heads, seqlen, head_dim, dtype,
+                  softmax_scale, causal, window_left, window_right, stream);
+}
+
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   bool empty = false;
   if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)
@@ -112,11 +138,16 @@ size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   return (size_t)batch * heads * fa::stat_blocks(seqlen) * 2 * fa::kStatRows * sizeof(float);
 }
 
-fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
-                        int head_dim, fa_dtype dtype, float softmax_scale, int causal,
-                        int window_left, int window_right, unsigned stages, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, const int* seqlens, bool varlen,
+                   int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                   float softmax_scale, int causal, int window_left, int window_right,
+                   unsigned stages, void* stream) {
   g_last_error.clear();
   bool empty = false;
   if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_BAD_STAGES;
@@ -124,7 +155,9 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
                               window_right, &empty);
   if (st != FA_OK) return st;
   if (empty) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (varlen && !seqlens))
+    return FA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0) return FA_ERR_MISALIGNED;
   const size_t need = fa_bwd_workspace_size(batch, heads, seqlen, head_dim);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   const void* ins[] = {q, k, v, o, dout, lse, workspace};
@@ -138,6 +171,9 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
       if (out == in) return FA_ERR_ALIAS;
   }
   if (dq == dk || dq == dv || dk == dv) return FA_ERR_ALIAS;
+  if (seqlens && ((const void*)seqlens == dq || (const void*)seqlens == dk ||
+                  (const void*)seqlens == dv || (const void*)seqlens == workspace))
+    return FA_ERR_ALIAS;
 
   fa::BwdParams p;
   p.q = q;
@@ -150,6 +186,7 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
   p.dk = dk;
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
+  p.seqlens = seqlens;
   p.B = batch;
   p.H = heads;
   p.N = seqlen;
@@ -160,6 +197,31 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
   p.window_left = window_left;
   p.window_right = window_right;
   return hip_status(fa::launch_bwd(p, stages, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen,
+                        int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, unsigned stages, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, nullptr, false,
+                  batch, heads, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
+                  window_right, stages, stream);
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* seqlens, int batch,
+                        int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
+                        int causal, int window_left, int window_right, unsigned stages,
+                        void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, seqlens, true,
+                  batch, heads, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
+                  window_right, stages, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -42,6 +42,8 @@ struct BwdArgs {
   char* dk;
   char* dv;
   float* stats;   // per-query statistics in 32-query blocks (stat_index)
+  const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
+  int heads;
   int n;
   int n_bh;
   int n_tiles;
@@ -59,7 +61,8 @@ struct BwdArgs {
 // lines); the lanes of a row add their partial sums by butterfly shuffles.
 // Grid: x over a head's padded query slots, 256 per workgroup (64 per wave); y, with a stride
 // loop, over (batch, head).
-template <int D, bool BF16>
+// PADDED: a padded batch (per-batch lengths), a separate instance
+template <int D, bool BF16, bool PADDED>
 __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;            // lanes per row
   constexpr int RPI = 64 / LPR;         // rows per load instruction
@@ -69,12 +72,14 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   const int q_base = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + lane / LPR;
   const int slots = stat_blocks(a.n) * kStatRows;
   for (long bh = blockIdx.y; bh < a.n_bh; bh += gridDim.y) {
+    // rows of the sequence; rows len .. n-1 of a padded batch get zeros like the slots past n
+    const int len = PADDED ? min(max(a.seqlens[bh / a.heads], 0), a.n) : a.n;
     u32x4 ov[IT], gv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int q = q_base + RPI * it;
       ov[it] = gv[it] = u32x4{};
-      if (q < a.n) {
+      if (q < len) {
         const long off = ((bh * a.n + q) * D + 8 * sub) * 2;
         ov[it] = *reinterpret_cast<const u32x4*>(a.o + off);
         gv[it] = *reinterpret_cast<const u32x4*>(a.dout + off);
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
       const int q = q_base + RPI * it;
       if (sub == 0 && q < slots) {
         float* out = a.stats + stat_index(bh, a.n, q);
-        const bool in = q < a.n;
+        const bool in = q < len;
         out[0] = in ? -a.lse[bh * a.n + q] / a.sigma : 0.f;
         out[kStatRows] = in ? -acc : 0.f;
       }
@@ -474,6 +479,8 @@ BwdArgs make_args(const BwdParams& p) {
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
+  a.seqlens = p.seqlens;
+  a.heads = p.H;
   a.n = p.N;
   a.n_bh = p.B * p.H;
   a.n_tiles = 0;
@@ -492,10 +499,15 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (stages & kBwdDelta) {
     const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
     const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
-    hipLaunchKernelGGL((delta_kernel<D, BF16>), dim3(gx, gy), dim3(256), 0, stream, a);
+    if (p.seqlens != nullptr)
+      hipLaunchKernelGGL((delta_kernel<D, BF16, true>), dim3(gx, gy), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  if ((stages & kBwdDkDv) && env_bwd_choice() != 2) {
+  // padded batches always take the main kernels
+  const bool main_kernels = env_bwd_choice() != 2 || p.seqlens != nullptr;
+  if ((stages & kBwdDkDv) && main_kernels) {
     if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDkDv) {
     a.n_tiles = (a.n + kKvRows - 1) / kKvRows;
@@ -503,7 +515,7 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  if ((stages & kBwdDq) && env_bwd_choice() != 2) {
+  if ((stages & kBwdDq) && main_kernels) {
     if (hipError_t e = launch_dq_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDq) {
     a.n_tiles = (a.n + kDqRows - 1) / kDqRows;

@@ -64,7 +64,9 @@ struct DkdvArgs {
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dk;
   char* dv;
-  int n;
+  const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
+  int n;                 // rows per (batch, head) in memory
+  int heads;
   int n_bh;
   int n_tiles;           // key tiles of KWG keys per head
   int n_units;           // workgroups per head: n_tiles, or ceil(n_tiles / 2) when paired
@@ -105,7 +107,7 @@ __device__ __forceinline__ void slices(F&& f) {
 }
 
 // dK, dV of key tile kt of head bh (the whole workgroup)
-template <int D, bool BF16>
+template <int D, bool BF16, bool PADDED>
 __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int bh, int kt) {
   using S = DShape<D>;
   constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
@@ -117,15 +119,18 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int n = a.n;
-  const long head = (long)bh * n * RB;
+  // rows of the head in memory (nr) and of its sequence (n): rows n .. nr-1 are padding, read
+  // as zeros through the buffer resources, with zero gradients
+  const int nr = a.n;
+  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  const long head = (long)bh * nr * RB;
   const int head_bytes = n * RB;
   const auto rq = make_rsrc(a.q + head, head_bytes);
   const auto rk = make_rsrc(a.k + head, head_bytes);
   const auto rv = make_rsrc(a.v + head, head_bytes);
   const auto rg = make_rsrc(a.dout + head, head_bytes);
-  const int stat_bytes = stat_blocks(n) * 2 * kStatRows * 4;
-  const auto rs = make_rsrc(a.stats + (long)bh * stat_blocks(n) * 2 * kStatRows, stat_bytes);
+  const int stat_bytes = stat_blocks(nr) * 2 * kStatRows * 4;
+  const auto rs = make_rsrc(a.stats + (long)bh * stat_blocks(nr) * 2 * kStatRows, stat_bytes);
   const Mask mk{n, a.causal, a.wl, a.wr};
   const float c_scale = a.c;
 
@@ -155,7 +160,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   int q_lo, q_hi;
   mk.query_range(k_first, min(k_first + S::KWG, n) - 1, q_lo, q_hi);
   const int s_begin = q_lo / kBQ;
-  const int NSTEP = q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - s_begin : 0;
+  const int NSTEP = (!PADDED || k_first < n) && q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - s_begin : 0;
 
   // ---- per-lane constants
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
@@ -548,7 +553,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw0 + 32 * kb + l32;
-    if (key < n) {
+    if (key < (PADDED ? nr : n)) {
       char* dkrow = a.dk + head + (long)key * RB;
       char* dvrow = a.dv + head + (long)key * RB;
       const float sc = a.scale;
@@ -561,6 +566,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
                       pack2<BF16>(dk[kb][db][4 * g + 2] * sc, dk[kb][db][4 * g + 3] * sc)};
           u32x2 wv = {pack2<BF16>(dv[kb][db][4 * g + 0], dv[kb][db][4 * g + 1]),
                       pack2<BF16>(dv[kb][db][4 * g + 2], dv[kb][db][4 * g + 3])};
+          if (PADDED && key >= n) wk = wv = u32x2{};   // padding keys: zero gradients
           *reinterpret_cast<u32x2*>(dkrow + dim * 2) = wk;
           *reinterpret_cast<u32x2*>(dvrow + dim * 2) = wv;
         }
@@ -571,7 +577,8 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 // Under a causal mask (no left window) the number of query steps falls linearly with the key
 // tile, so tiles t and n_tiles - 1 - t together take the same time for every t: paired, the
 // workgroups are of equal length and fill the chip evenly.
-template <int D, bool BF16>
+// PADDED: a padded batch (per-batch lengths), a separate instance
+template <int D, bool BF16, bool PADDED>
 __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * DShape<D>::STAGE];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dkdv_tile<D, BF16>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dkdv_tile<D, BF16, PADDED>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -595,7 +602,9 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.stats = p.stats;
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
+  a.seqlens = p.seqlens;
   a.n = p.N;
+  a.heads = p.H;
   a.n_bh = p.B * p.H;
   a.n_tiles = (p.N + S::KWG - 1) / S::KWG;
   a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
@@ -614,7 +623,10 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   const long blocks = (long)a.n_bh * a.n_units;
-  hipLaunchKernelGGL((dkdv_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (p.seqlens != nullptr)
+    hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

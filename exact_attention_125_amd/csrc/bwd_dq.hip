@@ -56,7 +56,9 @@ struct DqArgs {
   const char* dout;
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dq;
-  int n;
+  const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
+  int n;                 // rows per (batch, head) in memory
+  int heads;
   int n_bh;
   int n_tiles;           // query tiles of QWG queries per head
   int n_units;           // workgroups per head: n_tiles, or ceil(n_tiles / 2) when paired
@@ -91,7 +93,7 @@ __device__ __forceinline__ void dq_slices(F&& f) {
 }
 
 // dQ of query tile qt of head bh (the whole workgroup)
-template <int D, bool BF16>
+template <int D, bool BF16, bool PADDED>
 __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int bh, int qt) {
   using S = QShape<D>;
   constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
@@ -103,8 +105,11 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int n = a.n;
-  const long head = (long)bh * n * RB;
+  // rows of the head in memory (nr) and of its sequence (n): rows n .. nr-1 are padding, read
+  // as zeros through the buffer resources, with zero gradients
+  const int nr = a.n;
+  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  const long head = (long)bh * nr * RB;
   const int head_bytes = n * RB;
   const auto rq = make_rsrc(a.q + head, head_bytes);
   const auto rk = make_rsrc(a.k + head, head_bytes);
@@ -130,7 +135,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       qreg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, off));
       greg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, off));
     }
-    const long r = stat_index(bh, n, q < n ? q : 0);
+    const long r = stat_index(bh, nr, q < n ? q : 0);
     lse_in[qb] = a.stats[r];
     nd_in[qb] = a.stats[r + kStatRows];
   }
@@ -144,7 +149,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   int k_lo, k_hi;
   mk.key_range(q_first, min(q_first + S::QWG, n) - 1, k_lo, k_hi);
   const int s_begin = k_lo / kBK;
-  const int NSTEP = k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
+  const int NSTEP = (!PADDED || q_first < n) && k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
 
   // ---- per-lane LDS addresses, moved on by one ring stage per step:
   //   row_a[ks]   A operand rows (key l32, chunk 2 ks + hi) in the stage of tile s+1 (K at
@@ -431,7 +436,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + 32 * qb + l32;
-    if (q < n) {
+    if (q < (PADDED ? nr : n)) {
       char* row = a.dq + head + (long)q * RB;
       const float sc = a.scale;
 #pragma unroll
@@ -441,6 +446,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
           const int dim = 32 * db + 8 * g + 4 * hi;
           u32x2 w = {pack2<BF16>(dqacc[qb][db][4 * g + 0] * sc, dqacc[qb][db][4 * g + 1] * sc),
                      pack2<BF16>(dqacc[qb][db][4 * g + 2] * sc, dqacc[qb][db][4 * g + 3] * sc)};
+          if (PADDED && q >= n) w = u32x2{};   // padding rows: zero gradients
           *reinterpret_cast<u32x2*>(row + dim * 2) = w;
         }
     }
@@ -450,7 +456,8 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 // Under a causal mask (no left window) the number of key steps grows linearly with the query
 // tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
 // latest (longest) tiles go first.
-template <int D, bool BF16>
+// PADDED: a padded batch (per-batch lengths), a separate instance
+template <int D, bool BF16, bool PADDED>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
@@ -460,7 +467,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqAr
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dq_tile<D, BF16>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dq_tile<D, BF16, PADDED>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -474,7 +481,9 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.dout = static_cast<const char*>(p.dout);
   a.stats = p.stats;
   a.dq = static_cast<char*>(p.dq);
+  a.seqlens = p.seqlens;
   a.n = p.N;
+  a.heads = p.H;
   a.n_bh = p.B * p.H;
   a.n_tiles = (p.N + S::QWG - 1) / S::QWG;
   a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
@@ -492,7 +501,10 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   const long blocks = (long)a.n_bh * a.n_units;
-  hipLaunchKernelGGL((dq_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (p.seqlens != nullptr)
+    hipLaunchKernelGGL((dq_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dq_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -74,7 +74,9 @@ struct MainArgs {
   const char* v;
   char* o;
   float* lse;
-  int n;          // sequence length
+  const int* seqlens;   // per-batch lengths (device, may be null: every sequence has n rows)
+  int n;          // rows per (batch, head): the sequence length, or the padded one with seqlens
+  int heads;
   int n_bh;       // batch * heads
   int n_qt;       // query tiles per head
   int n_units;    // workgroups per head: n_qt, or ceil(n_qt / 2) query-tile pairs
@@ -100,7 +102,9 @@ struct Shape {
                 (kNS - 1) * TILE + (MB - 1) * 32 * RB < 65536, "operand offsets fit the ds immediate");
 };
 
-template <int D, bool BF16>
+// PADDED: a padded batch (per-batch lengths); a separate instance, so that the plain one
+// carries none of its code
+template <int D, bool BF16, bool PADDED>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
@@ -118,8 +122,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 
   int bh, unit;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, unit);
-  const int n = a.n;
-  const long head = (long)bh * n * RB;
+  // rows of the head in memory (nr) and of its sequence (n); rows n .. nr-1 are padding, read
+  // as zeros through the buffer resources and written as zeros
+  const int nr = a.n;
+  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  const long head = (long)bh * nr * RB;
   const int head_bytes = n * RB;
   const auto rq = make_rsrc(a.q + head, head_bytes);
   const auto rk = make_rsrc(a.k + head, head_bytes);
@@ -163,6 +170,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     const int q0 = qt * kBr;
     const int wq0 = q0 + 32 * stripe;
     const int qi = wq0 + l32;
+    if (PADDED && q0 >= n) {   // padding rows only: O = 0, LSE = -inf
+      if (qi < nr) {
+        char* orow = a.o + head + (long)qi * RB;
+#pragma unroll
+        for (int c16 = 0; c16 < RB / 32; ++c16)
+          *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
+        if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
+      }
+      continue;
+    }
 
     // Q^T operands, read once (B operand of every S^T product)
     i16x8 qreg[KS];
@@ -587,7 +604,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
           *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
         }
       if (a.lse != nullptr && hi == 0)
-        a.lse[(long)bh * n + qi] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+        a.lse[(long)bh * nr + qi] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+    } else if (PADDED && qi < nr) {   // a padding row
+      char* orow = a.o + head + (long)qi * RB;
+#pragma unroll
+      for (int c16 = 0; c16 < RB / 32; ++c16)
+        *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
+      if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
     }
   }
 }
@@ -600,7 +623,9 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   a.v = static_cast<const char*>(p.v);
   a.o = static_cast<char*>(p.o);
   a.lse = p.lse;
+  a.seqlens = p.seqlens;
   a.n = p.N;
+  a.heads = p.H;
   a.n_bh = p.B * p.H;
   a.n_qt = (p.N + kBr - 1) / kBr;
   // pairing balances causal rows whose visible key count grows with the query index
@@ -615,8 +640,12 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
   const long blocks = (long)a.n_bh * a.n_units;
-  hipLaunchKernelGGL((fwd_main_kernel<D, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     a);
+  if (p.seqlens != nullptr)
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;          // may be null
+  const int* seqlens = nullptr;   // device int32[B], or null: sequence b is rows
+                                  // 0 .. seqlens[b]-1 of its N (values clamped to [0, N]);
+                                  // the rest is padding
   int B, H, N, D;
   bool bf16;
   float scale;         // softmax scale
@@ -32,6 +35,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* stats;        // workspace: per-query statistics in 32-query blocks (stat_index)
+  const int* seqlens = nullptr;   // as in FwdParams
   int B, H, N, D;
   bool bf16;
   float scale;
@@ -41,9 +45,9 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
-// The 8-wave forward (256 query rows per workgroup, direct global->LDS copies, two-phase
-// software pipeline), for grids that fill the chip; launch_fwd chooses between it and the
-// four-wave kernel of fwd.hip.
+// The main forward (128 query rows per workgroup, direct global->LDS copies, two-phase
+// software pipeline), for grids that fill the chip and for padded batches; launch_fwd chooses
+// between it and the four-wave kernel of fwd.hip.
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream);
 // Backward stages, run in this order on one stream: the row statistics (log2(e) * LSE and
 // delta = rowsum(dO * O)) into the workspace, then dK/dV, then dQ (both read them).

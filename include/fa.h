@@ -132,6 +132,34 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
                         float softmax_scale, int causal, int window_left, int window_right,
                         unsigned stages, void* stream);
 
+/* Padded batches: sequence b is rows 0 .. L_b - 1 of its N rows (every head of batch b), the
+ * remaining rows are padding.  This is the per-sample actual length the page "告别OOM和训练慢：
+ * 用Flash Attention加速你的PyTorch大模型（含A100环境配置）" passes to its length-grouped batch
+ * attention (§6), on the padded [B, H, N, d] layout whose keys the page "Flash Attention 3.7
+ * 核心原理与实战：加速Transformer模型训练与推理" hides with a key padding mask (§4.2).  Each
+ * sample is attention over its own L_b rows alone:
+ *   - keys j >= L_b are hidden from every query;
+ *   - rows i >= L_b are written as O_i = 0 and LSE_i = -inf (fa_fwd_varlen), and as zero
+ *     dQ_i, dK_i, dV_i (fa_bwd_varlen); their Q, K, V, O and dO rows are never used.
+ *   seqlens  in: device int32[B], the lengths L_b.  Read by the kernels, so it is not
+ *            checked on the host: a value below 0 counts as 0 and one above N as N.  It must
+ *            be 4-byte aligned and must not be an output buffer (FA_ERR_ALIAS).
+ * Every other argument, convention and error is that of fa_fwd / fa_bwd_stages (`stages` as
+ * there: FA_BWD_ALL for the whole backward pass); seqlens NULL gives FA_ERR_NULL_PTR.  A row
+ * i < L_b sees at least its own key, as in fa_fwd.  The backward call needs the forward's o
+ * and lse of the same seqlens, and the workspace size of fa_bwd. */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* seqlens, int batch, int heads, int seqlen, int head_dim,
+                        fa_dtype dtype, float softmax_scale, int causal, int window_left,
+                        int window_right, void* stream);
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* seqlens, int batch,
+                        int heads, int seqlen, int head_dim, fa_dtype dtype, float softmax_scale,
+                        int causal, int window_left, int window_right, unsigned stages,
+                        void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

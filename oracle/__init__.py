@@ -25,6 +25,8 @@ Modules
              closed forms and by ``attention``)
   online     the tiled running-max / running-sum recurrence in the pages'
              order — pinned against ``attention``
+  padded     padded batches (per-sample lengths): the definition over each
+             sample's own rows, zeros past them — pinned
   pool       a process pool over (batch, head) for timing the oracle on a
              bounded sample
 
@@ -36,9 +38,11 @@ from .attention import (allowed_mask, attention_forward, attention_backward,
                         allowed_pairs, score_matrix_nbytes)
 from .online import attention_forward_online
 from .brute import attention_forward_brute
+from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
 
 __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
     "attention_forward_bh", "attention_backward_bh", "allowed_pairs", "score_matrix_nbytes",
     "attention_forward_online", "attention_forward_brute",
+    "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
 ]

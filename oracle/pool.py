@@ -16,13 +16,13 @@ from . import attention
 _SHARED = {}
 
 
-def _init(arrays, scale, causal, window):
+def _init(arrays, scale, causal, window, lengths):
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)
     except Exception:
         pass
-    _SHARED.update(arrays=arrays, scale=scale, causal=causal, window=window)
+    _SHARED.update(arrays=arrays, scale=scale, causal=causal, window=window, lengths=lengths)
 
 
 def _one_head(task):
@@ -38,11 +38,14 @@ def _one_head(task):
 def _eval_head(kind, b, h):
     a = _SHARED["arrays"]
     s, c, w = _SHARED["scale"], _SHARED["causal"], _SHARED["window"]
-    o, lse = attention.attention_forward(a["q"][b, h], a["k"][b, h], a["v"][b, h], s, c, w)
+    # a padded batch: the sample's own rows (oracle.padded), the rest is zeros
+    L = _SHARED["lengths"][b] if _SHARED["lengths"] is not None else a["q"].shape[2]
+    o, lse = attention.attention_forward(a["q"][b, h, :L], a["k"][b, h, :L], a["v"][b, h, :L],
+                                         s, c, w)
     if kind == "fwd":
         return (b, h, o, lse)
-    dq, dk, dv = attention.attention_backward(a["q"][b, h], a["k"][b, h], a["v"][b, h],
-                                              a["do"][b, h], s, c, w)
+    dq, dk, dv = attention.attention_backward(a["q"][b, h, :L], a["k"][b, h, :L],
+                                              a["v"][b, h, :L], a["do"][b, h, :L], s, c, w)
     return (b, h, o, lse, dq, dk, dv)
 
 
@@ -66,17 +69,21 @@ def available_cores() -> int:
         return os.cpu_count() or 1
 
 
-def run_heads(arrays, heads, scale, causal, window, backward=False, workers=None, keep=True):
+def run_heads(arrays, heads, scale, causal, window, backward=False, workers=None, keep=True,
+              lengths=None):
     """Evaluate the listed (b, h) heads; returns (results, seconds, workers_used).
 
-    ``arrays`` maps "q", "k", "v" (and "do" when ``backward``) to float64 [B, H, N, d].
+    ``arrays`` maps "q", "k", "v" (and "do" when ``backward``) to float64 [B, H, N, d];
+    ``lengths`` (per batch, already clamped to [1, N]) makes them a padded batch, each head
+    evaluated on its sample's rows only.  Results then cover those rows only.
     The timed interval covers the pool's work only, not its start-up.  With ``keep`` False
     each result is (b, h, checksum) instead of the output arrays.
     """
     workers = max(1, min(workers or available_cores(), len(heads)))
     kind = "fwdbwd" if backward else "fwd"
     ctx = mp.get_context("fork")
-    with ctx.Pool(workers, initializer=_init, initargs=(arrays, scale, causal, window)) as pool:
+    with ctx.Pool(workers, initializer=_init,
+                  initargs=(arrays, scale, causal, window, lengths)) as pool:
         pool.map(_noop, range(workers))           # start every worker before timing
         t0 = time.perf_counter()
         res = pool.map(_one_head, [(kind, b, h, keep) for b, h in heads], chunksize=1)

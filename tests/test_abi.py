@@ -32,7 +32,8 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
-                            "fa_bwd_stages", "fa_status_string", "fa_last_error_detail"])
+                            "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
+                            "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
     from exact_attention_125_amd import _lib
@@ -48,7 +49,7 @@ def test_status_strings(lib):
 
 
 # Fake, 16-byte aligned "device" addresses: validation never dereferences them.
-Q, K, V, O, L, DO, DQ, DK, DV, WS = (0x10000 * (i + 1) for i in range(10))
+Q, K, V, O, L, DO, DQ, DK, DV, WS, SL = (0x10000 * (i + 1) for i in range(11))
 GOOD = dict(B=2, H=3, N=100, d=64, dtype=1, scale=0.125, causal=0, wl=-1, wr=-1)
 
 
@@ -65,7 +66,21 @@ def bwd(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, ws=WS, ws_by
                       a["d"], a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd])
+def fwd_varlen(lib, q=Q, k=K, v=V, o=O, lse=L, seqlens=SL, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_fwd_varlen(q, k, v, o, lse, seqlens, a["B"], a["H"], a["N"], a["d"],
+                             a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+
+
+def bwd_varlen(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, ws=WS,
+               ws_bytes=1 << 20, seqlens=SL, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, seqlens, a["B"],
+                             a["H"], a["N"], a["d"], a["dtype"], a["scale"], a["causal"],
+                             a["wl"], a["wr"], a.get("stages", 7), None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_varlen, bwd_varlen])
 def test_rejections(lib, call):
     inf = float("inf")
     assert call(lib, dtype=2) == 4
@@ -111,6 +126,21 @@ def test_backward_specific(lib):
     assert bwd(lib, ws=DK) == 10
 
 
+def test_padded_batch_specific(lib):
+    assert fwd_varlen(lib, seqlens=0) == 1
+    assert bwd_varlen(lib, seqlens=0) == 1
+    assert fwd_varlen(lib, seqlens=SL + 2) == 6      # int32 lengths: 4-byte aligned
+    assert bwd_varlen(lib, seqlens=SL + 6) == 6
+    assert fwd_varlen(lib, seqlens=O) == 10          # not an output buffer
+    assert fwd_varlen(lib, seqlens=L) == 10
+    assert bwd_varlen(lib, seqlens=DK) == 10
+    assert bwd_varlen(lib, seqlens=WS) == 10
+    assert bwd_varlen(lib, ws_bytes=lib.fa_bwd_workspace_size(2, 3, 100, 64) - 1) == 8
+    assert fwd_varlen(lib, o=Q) == 10
+    assert bwd_varlen(lib, stages=0) == 11
+    assert bwd_varlen(lib, stages=9) == 11
+
+
 def test_stage_mask_rejections(lib):
     args = [Q, K, V, O, DO, L, DQ, DK, DV, WS, 1 << 20, 2, 3, 100, 64, 1, 0.125, 0, -1, -1]
     assert lib.fa_bwd_stages(*args, 0, None) == 11
@@ -129,7 +159,7 @@ def test_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(-1, 1, 10, 64) == 0
 
 
-@pytest.mark.parametrize("call", [fwd, bwd])
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_varlen, bwd_varlen])
 def test_empty_is_a_noop(lib, call):
     # zero-sized work returns FA_OK before any pointer check or HIP call
     for dims in (dict(B=0), dict(H=0), dict(N=0)):

@@ -1,0 +1,177 @@
+"""Padded batches on the GPU: fa_fwd_varlen / fa_bwd_varlen through the C ABI against the
+float64 padded-batch oracle (oracle/padded.py).  Padding rows are filled with NaN on the
+device, so any read of them would show; their outputs must be exactly 0 (LSE -inf)."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import GRAD_REL_L2, LSE_TOL, O_TOL, rel_l2, say, to64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_125_amd as fa
+    return fa
+
+
+def device_inputs(inp, lens, poison=True):
+    """q, k, v, dO on the device, rows at or past each sample's length set to NaN."""
+    import torch
+    out = []
+    for name in ("q", "k", "v", "do"):
+        t = to_dev(inp[name]).clone()
+        if poison:
+            for b, L in enumerate(lens):
+                t[b, :, max(L, 0):] = float("nan")
+        out.append(t)
+    return out
+
+
+def run(fa, inp, lens, scale, causal, window, backward=True, poison=True):
+    import torch
+    q, k, v, do = device_inputs(inp, lens, poison)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = fa.fwd(q, k, v, scale, causal, window, seqlens=sl)
+    grads = fa.bwd(do, q, k, v, o, lse, scale, causal, window, seqlens=sl) if backward else None
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+def check(fa, inp, lens, scale, causal, window, dtype, label, backward=True, heads=None):
+    """Every head (or the listed (b, h) pairs) against the oracle; padding rows exactly zero."""
+    import oracle
+    q64, k64, v64, do64 = (inp[n + "64"] for n in ("q", "k", "v", "do"))
+    B, H, N, _ = q64.shape
+    o, lse, grads = run(fa, inp, lens, scale, causal, window, backward)
+    o64, lse64 = to64(o), lse.detach().cpu().numpy().astype(np.float64)
+    Ls = oracle.clamp_lengths(lens, N)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b in range(B):   # padding rows of every head
+        L = Ls[b]
+        assert np.all(o64[b, :, L:] == 0.0), f"{label}: padding rows of O not zero (b={b})"
+        assert np.all(np.isneginf(lse64[b, :, L:])), f"{label}: padding LSE not -inf (b={b})"
+    worst_o = worst_l = 0.0
+    for b, h in heads:
+        L = Ls[b]
+        if L == 0:
+            continue
+        ro, rl = oracle.attention_forward(q64[b, h, :L], k64[b, h, :L], v64[b, h, :L], scale,
+                                          causal, window)
+        worst_o = max(worst_o, float(np.abs(o64[b, h, :L] - ro).max()))
+        worst_l = max(worst_l, float(np.abs(lse64[b, h, :L] - rl).max()))
+    say(f"{label}: max|dO|={worst_o:.2e} max|dLSE|={worst_l:.2e}")
+    assert worst_o <= O_TOL[dtype], f"{label}: O {worst_o:.3e} > {O_TOL[dtype]}"
+    assert worst_l <= LSE_TOL, f"{label}: LSE {worst_l:.3e} > {LSE_TOL}"
+    if not backward:
+        return
+    got = [to64(g) for g in grads]
+    for b in range(B):
+        for t in range(3):
+            assert np.all(got[t][b, :, Ls[b]:] == 0.0), f"{label}: padding gradients not zero"
+    mine, ref = [[], [], []], [[], [], []]
+    dnorm = []
+    for b, h in heads:
+        L = Ls[b]
+        if L == 0:
+            continue
+        r = oracle.attention_backward(q64[b, h, :L], k64[b, h, :L], v64[b, h, :L],
+                                      do64[b, h, :L], scale, causal, window)
+        for t in range(3):
+            mine[t].append(got[t][b, h, :L])
+            ref[t].append(r[t])
+        dnorm.append(do64[b, h, :L])
+    if not dnorm:
+        return
+    floor = 1e-3 * float(np.linalg.norm(np.concatenate(dnorm)))
+    errs = [rel_l2(np.concatenate(mine[t]), np.concatenate(ref[t]), floor=floor) for t in range(3)]
+    say(f"{label}: rel L2 dQ={errs[0]:.2e} dK={errs[1]:.2e} dV={errs[2]:.2e}")
+    for name, e in zip(("dQ", "dK", "dV"), errs):
+        assert e <= GRAD_REL_L2, f"{label}: {name} rel L2 {e:.3e} > {GRAD_REL_L2}"
+
+
+MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (37, 5)), (True, (64, -1)),
+         (False, (-1, 64))]
+
+
+@pytest.mark.parametrize("n", [65, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_padded_batch_parity(fa, n, d, dtype):
+    inp = W.random_case((4, 2, n, d), dtype, seed=200 + n + d, with_grad=True)
+    lens = [n, n // 2 + 3, 1, 0]
+    for causal, window in MASKS:
+        check(fa, inp, lens, 1.0 / math.sqrt(d), causal, window, dtype,
+              f"n={n} d={d} {dtype} causal={causal} window={window}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_padded_batch_many_tiles(fa, d):
+    """Lengths spanning many query and key tiles (paired causal tiles included), ragged."""
+    inp = W.random_case((3, 2, 1500, d), "bf16", seed=231 + d, with_grad=True)
+    lens = [1500, 777, 1029]
+    for causal, window in [(True, (-1, -1)), (False, (-1, -1)), (True, (300, -1))]:
+        check(fa, inp, lens, 1.0 / math.sqrt(d), causal, window, "bf16",
+              f"n=1500 d={d} causal={causal} window={window}")
+
+
+def test_lengths_are_clamped(fa):
+    import torch
+    inp = W.random_case((3, 2, 100, 64), "bf16", seed=240, with_grad=True)
+    a = run(fa, inp, [-5, 170, 3], 0.125, True, (-1, -1), poison=False)
+    b = run(fa, inp, [0, 100, 3], 0.125, True, (-1, -1), poison=False)
+    for x, y in zip([a[0], a[1], *a[2]], [b[0], b[1], *b[2]]):
+        assert torch.equal(x, y)
+
+
+def test_full_lengths_equal_the_unpadded_call(fa):
+    """With every length N the padded call is the main kernels' unpadded call, bit for bit."""
+    import torch
+    inp = W.random_case((2, 3, 333, 64), "bf16", seed=241, with_grad=True)
+    q, k, v, do = device_inputs(inp, [333, 333], poison=False)
+    old = os.environ.get("FA_FWD_KERNEL")
+    os.environ["FA_FWD_KERNEL"] = "main"
+    try:
+        o, lse = fa.fwd(q, k, v, 0.125, True)
+        g = fa.bwd(do, q, k, v, o, lse, 0.125, True)
+    finally:
+        if old is None:
+            os.environ.pop("FA_FWD_KERNEL", None)
+        else:
+            os.environ["FA_FWD_KERNEL"] = old
+    p = run(fa, inp, [333, 333], 0.125, True, (-1, -1), poison=False)
+    for x, y in zip([o, lse, *g], [p[0], p[1], *p[2]]):
+        assert torch.equal(x, y)
+
+
+def test_autograd_padded(fa):
+    import torch
+    inp = W.random_case((2, 2, 130, 64), "bf16", seed=242, with_grad=True)
+    q, k, v, do = device_inputs(inp, [130, 61], poison=False)
+    sl = torch.tensor([130, 61], dtype=torch.int32, device="cuda")
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = fa.attention(qa, ka, va, causal=True, seqlens=sl)
+    out.backward(do)
+    o, lse = fa.fwd(q, k, v, None, True, seqlens=sl)
+    g = fa.bwd(do, q, k, v, o, lse, None, True, seqlens=sl)
+    assert torch.equal(out, o)
+    for x, y in zip((qa.grad, ka.grad, va.grad), g):
+        assert torch.equal(x, y)
+
+
+def test_padded_training_workload_sampled(fa):
+    """The padded training workload at full size, in the launch configuration the benchmark
+    times (B=8, H=16, N=4096, d=64, causal, bf16, lengths from draw_seqlens): sampled heads
+    of every length against the oracle, every padding row checked."""
+    w = W.VARLEN
+    inp = W.make_inputs(w)
+    lens = W.draw_seqlens(w.B, w.N, w.seed).tolist()
+    heads = [(b, (5 * b) % w.H) for b in range(w.B)]
+    say(f"[varlen] {w.name} lengths {lens}")
+    check(fa, inp, lens, w.softmax_scale, w.causal, w.window, w.dtype, w.name, heads=heads)

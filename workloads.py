@@ -33,6 +33,7 @@ class Workload:
     seed: int
     backward: bool = False
     scale: float = field(default=float("nan"))
+    padded: bool = False     # a padded batch: per-sample lengths from draw_seqlens
 
     @property
     def softmax_scale(self) -> float:
@@ -53,7 +54,11 @@ TRAIN = Workload("train_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1,
                  backward=True)
 
 ALL = (TINY, BERT, CAUSAL, LONG_4K, LONG_8K, TRAIN)
-BY_NAME = {w.name: w for w in ALL}
+# The training step over a padded batch: sample lengths drawn by draw_seqlens (the pages fix
+# no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
+VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
+                  backward=True, padded=True)
+BY_NAME = {w.name: w for w in ALL + (VARLEN,)}
 
 
 def draw_f32(shape, seed: int, count: int):
@@ -92,6 +97,13 @@ def make_inputs(w: Workload, dtype: str | None = None, shape=None, seed=None, wi
         out[name] = t
         out[name + "64"] = a64
     return out
+
+
+def draw_seqlens(B: int, N: int, seed: int):
+    """B sample lengths, uniform integers in [N/4, N], from their own seeded stream (the
+    seed's Q, K, V, dO stream is untouched): ``int32`` numpy array."""
+    rng = np.random.default_rng([seed, 1])
+    return rng.integers(N // 4, N, size=B, endpoint=True).astype(np.int32)
 
 
 def random_case(shape, dtype: str, seed: int, with_grad: bool = False, scale_inputs: float = 1.0):
