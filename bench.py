@@ -181,7 +181,13 @@ def pmc_summary(fetch_dir, write_dir, workload, calib_mib):
                         continue
                     per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                     per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in per.items()}
+        out = {}
+        for k, v in per.items():
+            vals = list(v.values())
+            if k == "copy":   # the calibration copies only, not small copies of other buffers
+                vals = [x for x in vals if x >= 0.5 * max(vals)]
+            out[k] = sum(vals) / len(vals)
+        return out
 
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     expected_kib = calib_mib * 1024.0

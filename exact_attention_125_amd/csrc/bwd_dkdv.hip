@@ -26,8 +26,9 @@
 // also issues, one per MFMA, the LDS reads of the next phase's operands.  Q and dO tiles and
 // the per-query statistics arrive by direct global->LDS copies into a ring of kNS stages, kPD
 // steps ahead, published by one workgroup barrier per step.  Step s reads tiles s, s+1 and
-// s+2 and writes tile s+kPD into the stage of tile s-1; the copies of tile s+3 must have
-// landed, in every wave, before the barrier that ends step s.
+// s+2 and writes tile s+kPD into the stage of tile s+kPD-kNS (read last in an earlier step);
+// the copies of tile s+3 must have landed, in every wave, before the barrier that ends step
+// s.  kNS is a power of two, so that the stage of a tile is a mask of its index.
 //
 // The MFMAs are issued as inline assembly (cdna4.h), so the register dependencies the
 // compiler would resolve for the builtins are kept apart by the order written here: VALU
@@ -54,7 +55,8 @@ namespace {
 constexpr int kThreads = 256;   // 4 waves, one per SIMD
 constexpr int kBQ = 32;         // queries per step
 constexpr int kPD = 5;          // query tiles copied ahead
-constexpr int kNS = kPD + 1;    // LDS ring stages
+constexpr int kNS = 8;          // LDS ring stages
+static_assert((kNS & (kNS - 1)) == 0 && kNS >= kPD + 1, "a power of two, above kPD");
 
 struct DkdvArgs {
   const char* q;
@@ -185,7 +187,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
       tr_a[h][db] = ring_a + tile_offset<D>(tr_row + 8 * h, 4 * db + 2 * (tg & 1) + (tq >> 1)) + tr_byte;
   // byte distance from the stage of tile t to that of tile t+1
   auto stage_step = [&](int t) __attribute__((always_inline)) {
-    return (t % kNS) == kNS - 1 ? -(kNS - 1) * STAGE : STAGE;
+    return (t & (kNS - 1)) == kNS - 1 ? -(kNS - 1) * STAGE : STAGE;
   };
   auto advance_rows = [&](int t) __attribute__((always_inline)) {   // stage of t -> of t+1
     const int dlt = stage_step(t);
@@ -207,8 +209,10 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     const int r = p / RB;
     cp_src[i] = r * RB + ((((p % RB) / 16) ^ chunk_swizzle<D>(r))) * 16;
   }
-  // statistics of a 32-query tile, one 256-byte block (m, then -delta): lane L < 16 of wave 0
-  // copies 16 bytes to LDS slot L (m for L < 8, -delta for 8 <= L < 16): the values of queries
+  // statistics of a 32-query tile, one 256-byte block (m, then -delta): lane L < 16 of every
+  // wave copies 16 bytes to LDS slot L (m for L < 8, -delta for 8 <= L < 16; the four waves
+  // write the same bytes, which spares a branch and keeps every wave's copy count equal): the
+  // values of queries
   // 4 sig(L % 8) .. +3 with sig(j) = 2j (j < 4) or 2(j-4)+1, so that lanes of half hi find the
   // 16 values of their accumulator rows 8 g + 4 hi + 0..3 (g = 0..3) contiguous at slot 4 hi
   // (of the m or -delta half).  Lanes 16..63 read past the buffer and write zeros to slots
@@ -217,12 +221,12 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   const int st_src = lane < 16 ? 128 * (lane >> 3) + 16 * (jl < 4 ? 2 * jl : 2 * (jl - 4) + 1)
                                : stat_bytes;
 
-  // ---- copies of query tile t (relative step) into stage t % kNS: Q and dO (every wave its
-  // share), and the statistics block (wave 0); past the last step they read beyond the
-  // buffers (zero fills, no traffic) so every step issues the same copies
+  // ---- copies of query tile t (relative step) into stage t mod kNS: Q and dO (every wave its
+  // share), and the statistics block; past the last step they read beyond the buffers (zero
+  // fills, no traffic) so every step issues the same copies
   auto copy_tiles = [&](int t) __attribute__((always_inline)) {
     const int off = t < NSTEP ? (s_begin + t) * kBQ * RB : head_bytes;
-    char FA_LDS* st = ring + (t % kNS) * STAGE;
+    char FA_LDS* st = ring + (t & (kNS - 1)) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       buffer_load16_lds(rq, st + 4096 * i + 1024 * wave, cp_src[i] + off);
@@ -230,23 +234,18 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     }
   };
   auto copy_stats = [&](int t) __attribute__((always_inline)) {
-    if (wave == 0) {
-      const int off = t < NSTEP ? (s_begin + t) * 2 * kStatRows * 4 : stat_bytes;
-      buffer_load16_lds(rs, ring + (t % kNS) * STAGE + 2 * QTILE, st_src + off);
-    }
+    const int off = t < NSTEP ? (s_begin + t) * 2 * kStatRows * 4 : stat_bytes;
+    buffer_load16_lds(rs, ring + (t & (kNS - 1)) * STAGE + 2 * QTILE, st_src + off);
   };
   auto issue_copies = [&](int t) __attribute__((always_inline)) {
     copy_stats(t);
     copy_tiles(t);
   };
   // this wave's copies of tiles up to s+3 have landed (loads complete in order), leaving
-  // those of tiles s+4 .. s+kPD in flight; wave 0 also issues the two statistics copies
+  // those of tiles s+4 .. s+kPD in flight (2 CPT tile chunks and one statistics copy each)
   static_assert(kPD >= 3, "the ring holds the three tiles a step reads");
   auto wait_copies = [&]() __attribute__((always_inline)) {
-    if (wave == 0)
-      wait_vmcnt<(kPD - 3) * (2 * CPT + 1)>();
-    else
-      wait_vmcnt<(kPD - 3) * 2 * CPT>();
+    wait_vmcnt<(kPD - 3) * (2 * CPT + 1)>();
   };
 
   // ---- operand registers.  All LDS reads in the steps are issued as inline assembly the
@@ -401,9 +400,15 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     const int kb = c >> 3, g = c & 7;
     dsk[kb][g] = pack2<BF16>(pv[kb][2 * g] * dpacc[kb][2 * g], pv[kb][2 * g + 1] * dpacc[kb][2 * g + 1]);
   };
-  auto edge_step = [&](int t) __attribute__((always_inline)) {   // some pair outside the band
-    const int q0 = (s_begin + t) * kBQ;
-    return q0 - (kw0 + S::KW - 1) < a.dlo || q0 + kBQ - 1 - kw0 > a.dhi;
+  // Some pair of step t lies outside the band unless t_in_lo <= t <= t_in_hi: the step's
+  // queries q0 .. q0+31 (q0 = 32 (s_begin + t)) against this wave's keys need
+  // q0 - (kw0 + KW - 1) >= dlo and q0 + 31 - kw0 <= dhi, solved for t once (the shifts are
+  // floor divisions, also below zero), so each step tests two scalars.
+  static_assert(kBQ == 32, "steps of 32 queries");
+  const int t_in_lo = ((a.dlo + kw0 + S::KW - 1 + 31) >> 5) - s_begin;
+  const int t_in_hi = ((a.dhi + kw0 - 31) >> 5) - s_begin;
+  auto edge_step = [&](int t) __attribute__((always_inline)) {
+    return t < t_in_lo || t > t_in_hi;
   };
 
   // ---- phases: each MFMA followed by its share of the phase's VALU slices, with a
