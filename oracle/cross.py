@@ -1,0 +1,78 @@
+"""Attention with N_q queries over N_k keys (N_q != N_k allowed) — test infrastructure.
+
+Sources: the definition of ``attention`` (the formula softmax(QK^T/sqrt(d_k))V of [PT29],
+scale, -inf mask and safe softmax as there); the inference use the pages name — LLM inference
+([FA37] §1.3) and the KV cache that PagedAttention pages through memory ([PT29], closing section
+"写在最后") — where a step's new queries attend to every cached key; the ``causal`` / ``window_size`` switches of
+[A100] §4.2.  The (batch, num_heads, seq_len, head_dim) tensors of [FA37] §3.2 may come as
+views of (batch, seq_len, num_heads, head_dim) memory (the ``view(...).transpose(1, 2)`` of
+its §4.2 module, the (batch, seq, heads * head_dim) layout of its §3.3): the layout is a
+matter of addressing only and does not enter this definition.
+
+Reading where the pages are silent (they never define a mask for N_q != N_k):
+  * the queries are the LAST N_q positions of the key sequence: query i sits at position
+      p_i = i + (N_k - N_q)
+    and key j is allowed for it iff
+      (not causal or j <= p_i) and (left < 0 or j >= p_i - left) and (right < 0 or j <= p_i + right)
+    (inclusive bounds, -1 unbounded, causal AND window, as in ``attention``).  A decode step
+    (N_q = 1) then sees every cached key, and a block of new queries sees the cache plus its own
+    causal prefix.  With N_q = N_k this is ``attention`` itself.
+  * a row with no allowed key (N_q > N_k under causal, or a window that misses every key) has
+    O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def cross_allowed_mask(n_q: int, n_k: int, causal: bool, window=(-1, -1)) -> np.ndarray:
+    """Boolean [n_q, n_k]: True where key j is visible to query i (reading above)."""
+    left, right = int(window[0]), int(window[1])
+    p = (np.arange(n_q, dtype=np.int64) + (n_k - n_q))[:, None]
+    j = np.arange(n_k, dtype=np.int64)[None, :]
+    ok = np.ones((n_q, n_k), dtype=bool)
+    if causal:
+        ok &= j <= p
+    if left >= 0:
+        ok &= j >= p - left
+    if right >= 0:
+        ok &= j <= p + right
+    return ok
+
+
+def cross_allowed_pairs(n_q: int, n_k: int, causal: bool, window=(-1, -1)) -> int:
+    """Number of (query, key) pairs the mask allows for one (batch, head)."""
+    return int(cross_allowed_mask(n_q, n_k, causal, window).sum())
+
+
+def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1)):
+    """One (batch, head): q float64 [N_q, d], k, v [N_k, d] -> (O [N_q, d], LSE [N_q]).
+
+    S = scale * Q K^T is materialised in full, masked with -inf, and put through the
+    max-shifted softmax; O = P V, LSE = rowmax + ln(rowsum).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
+    s = np.where(ok, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    live = np.isfinite(m)
+    e = np.exp(s - np.where(live, m, 0.0)[:, None])     # exp(-inf) = 0 at hidden entries
+    l = e.sum(axis=1)
+    p = e / np.where(live, l, 1.0)[:, None]
+    o = np.where(live[:, None], p @ v, 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1)):
+    """q [B, H, N_q, d], k, v [B, H, N_k, d] -> (O [B, H, N_q, d], LSE [B, H, N_q])."""
+    B, H, n_q, _ = q.shape
+    o = np.empty((B, H, n_q, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window)
+    return o, lse

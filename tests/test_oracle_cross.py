@@ -1,0 +1,144 @@
+"""The N_q != N_k oracle against its pins (CPU only).
+
+  * suffix property: the queries are the last N_q positions, so attention of Q's last N_q
+    rows over all N_k keys is the square definition's last N_q rows (every mask mode);
+  * torch CPU float64 scaled_dot_product_attention with a boolean mask that torch itself
+    builds (``tril`` with diagonal N_k - N_q, i.e. aligned at the bottom-right);
+  * scalar brute force (pure-Python floats, unshifted softmax) with the position rule
+    written out per pair;
+  * closed forms: a decode step (N_q = 1, causal) sees every key; Q = 0 gives the mean of V
+    over the visible keys and LSE = ln(count); rows with no visible key give O = 0,
+    LSE = -inf.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (3, 2)), (True, (4, -1)), (False, (-1, 0)),
+         (False, (2, -1))]
+SHAPES = [(1, 9), (3, 9), (9, 9), (5, 12), (12, 5), (1, 1), (7, 3)]
+
+
+def _qkv(n_q, n_k, d, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((n_q, d)), rng.standard_normal((n_k, d)), rng.standard_normal((n_k, d))
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q", [1, 4, 11])
+def test_last_rows_of_square_definition(causal, window, n_q):
+    n_k = 11
+    rng = np.random.default_rng(3)
+    q_all = rng.standard_normal((n_k, 6))
+    k = rng.standard_normal((n_k, 6))
+    v = rng.standard_normal((n_k, 6))
+    o, lse = oracle.cross_forward(q_all[n_k - n_q:], k, v, 0.45, causal, window)
+    ro, rl = oracle.attention_forward(q_all, k, v, 0.45, causal, window)
+    np.testing.assert_allclose(o, ro[n_k - n_q:], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, rl[n_k - n_q:], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(1, 9), (3, 9), (5, 12), (9, 9)])
+def test_torch_sdpa_bottom_right_causal(n_q, n_k):
+    q, k, v = _qkv(n_q, n_k, 5, seed=n_q * 31 + n_k)
+    mask = torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=n_k - n_q)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=mask[None], scale=0.6)[0].numpy()
+    o, _ = oracle.cross_forward(q, k, v, 0.6, causal=True)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def _brute(q, k, v, scale, causal, window):
+    n_q, n_k = len(q), len(k)
+    left, right = window
+    out, lse = [], []
+    for i in range(n_q):
+        pos = i + n_k - n_q
+        js = [j for j in range(n_k)
+              if not (causal and j > pos) and not (left >= 0 and j < pos - left)
+              and not (right >= 0 and j > pos + right)]
+        if not js:
+            out.append([0.0] * len(v[0]))
+            lse.append(-math.inf)
+            continue
+        e = {j: math.exp(scale * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j])))
+             for j in js}
+        z = math.fsum(e.values())
+        out.append([math.fsum(e[j] / z * float(v[j][c]) for j in js) for c in range(len(v[0]))])
+        lse.append(math.log(z))
+    return np.array(out), np.array(lse)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q,n_k", SHAPES)
+def test_brute_force(causal, window, n_q, n_k):
+    q, k, v = _qkv(n_q, n_k, 4, seed=7 * n_q + n_k)
+    o, lse = oracle.cross_forward(q, k, v, 0.5, causal, window)
+    bo, bl = _brute(q, k, v, 0.5, causal, window)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_decode_step_sees_every_key():
+    q, k, v = _qkv(1, 37, 8, seed=5)
+    o, lse = oracle.cross_forward(q, k, v, 0.3, causal=True)
+    s = [0.3 * float(np.dot(q[0], k[j])) for j in range(37)]
+    z = math.fsum(math.exp(x) for x in s)
+    ref = [math.fsum(math.exp(s[j]) / z * v[j, c] for j in range(37)) for c in range(8)]
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-12)
+    assert abs(lse[0] - math.log(z)) < 1e-12
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_zero_query_is_mean_over_visible_keys(causal, window):
+    _, k, v = _qkv(1, 10, 3, seed=9)
+    q = np.zeros((4, 3))
+    o, lse = oracle.cross_forward(q, k, v, 1.0, causal, window)
+    for i in range(4):
+        pos = i + 6
+        js = [j for j in range(10) if not (causal and j > pos)
+              and not (window[0] >= 0 and j < pos - window[0])
+              and not (window[1] >= 0 and j > pos + window[1])]
+        np.testing.assert_allclose(o[i], v[js].mean(axis=0), rtol=1e-13, atol=1e-13)
+        assert abs(lse[i] - math.log(len(js))) < 1e-13
+
+
+def test_rows_without_keys():
+    q, k, v = _qkv(7, 3, 4, seed=11)
+    o, lse = oracle.cross_forward(q, k, v, 0.5, causal=True)
+    # positions -4 .. 2: the first four rows see no key
+    assert np.all(o[:4] == 0.0) and np.all(np.isneginf(lse[:4]))
+    assert np.all(np.isfinite(lse[4:]))
+    o2, lse2 = oracle.cross_forward(q, k, v, 0.5, causal=False, window=(-1, 0))
+    # a right bound of 0 is the same mask as causal
+    np.testing.assert_array_equal(o2, o)
+    o3, lse3 = oracle.cross_forward(q, k, v, 0.5, causal=False, window=(-1, 1))
+    # positions -4 .. -2 with right bound 1 see no key
+    assert np.all(o3[:3] == 0.0) and np.all(np.isneginf(lse3[:3])) and np.isfinite(lse3[3])
+
+
+def test_pair_count():
+    assert oracle.cross_allowed_pairs(1, 4096, True) == 4096
+    assert oracle.cross_allowed_pairs(4096, 4096, True) == 4096 * 4097 // 2
+    assert oracle.cross_allowed_pairs(16, 100, True) == sum(85 + i for i in range(16))
+    assert oracle.cross_allowed_pairs(1, 100, True, (9, 0)) == 10
+
+
+def test_mutant_top_left_alignment_fails_the_suffix_pin():
+    """A top-left causal alignment (query i sees keys j <= i) is a plausible mistake; the
+    suffix property rejects it."""
+    rng = np.random.default_rng(4)
+    q_all, k, v = (rng.standard_normal((8, 4)) for _ in range(3))
+    ok = np.tril(np.ones((3, 8), dtype=bool))
+    s = np.where(ok, 0.5 * q_all[5:] @ k.T, -np.inf)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    wrong = (e / e.sum(axis=1, keepdims=True)) @ v
+    ro, _ = oracle.attention_forward(q_all, k, v, 0.5, causal=True)
+    assert not np.allclose(wrong, ro[5:], atol=1e-6)
