@@ -4,12 +4,15 @@
     o, lse = fa.fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1))
     dq, dk, dv = fa.bwd(do, q, k, v, o, lse, ...)
     o = fa.attention(q, k, v, causal=True)           # autograd-aware
+    o, lse = fa.fwd_kv(q, k, v, causal=True)         # N_q != N_k, any strides
 
 q, k, v: contiguous [batch, heads, seqlen, head_dim] float16 / bfloat16 GPU tensors,
 head_dim 64 or 128.  The work runs in the HIP kernels of ``libfa.so`` (C ABI in
 include/fa.h); importing this package fails if that library has not been built.
 """
-from ._lib import FaError, bwd, bwd_workspace_size, fwd, lib  # noqa: F401
+from ._lib import (FaError, bwd, bwd_workspace_size, fwd, fwd_kv,  # noqa: F401
+                   fwd_kv_workspace_size, lib)
 from .autograd import attention  # noqa: F401
 
-__all__ = ["fwd", "bwd", "attention", "bwd_workspace_size", "FaError", "lib"]
+__all__ = ["fwd", "bwd", "attention", "bwd_workspace_size", "fwd_kv", "fwd_kv_workspace_size",
+           "FaError", "lib"]

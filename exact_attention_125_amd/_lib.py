@@ -39,9 +39,17 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
                            _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
+    "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S,
+                       _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
+
+
+class FaStrides(ctypes.Structure):
+    """``fa_strides``: element strides of one [B, H, rows, d] operand."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
 
 
 class FaError(RuntimeError):
@@ -183,3 +191,43 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
 
 def bwd_workspace_size(B, H, N, d) -> int:
     return int(_lib.fa_bwd_workspace_size(B, H, N, d))
+
+
+def fwd_kv_workspace_size(B, H, n_q, n_k, d) -> int:
+    return int(_lib.fa_fwd_kv_workspace_size(B, H, n_q, n_k, d))
+
+
+def _check_kv_tensors(q, k, v):
+    for t in (q, k, v):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("q, k, v must be on one GPU device")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share one dtype")
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("expected [B, H, N, d] tensors with a contiguous last dimension")
+    B, H, n_q, d = q.shape
+    if tuple(k.shape) != (B, H, k.shape[2], d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v must be [B, H, N_k, d] to match q {tuple(q.shape)}")
+
+
+def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None,
+           return_lse=True, workspace=None):
+    """``fa_fwd_kv``: q [B, H, N_q, d] over k, v [B, H, N_k, d], the queries being the last N_q
+    key positions.  Any strides with a contiguous last dimension (for example transposed
+    views of [B, N, H, d] memory).  Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
+    import torch
+    _check_kv_tensors(q, k, v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n_q), device=q.device, dtype=torch.float32) if return_lse else None
+    st = (FaStrides * 4)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o)))
+    need = fwd_kv_workspace_size(B, H, n_q, n_k, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k, d,
+                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(workspace),
+                          ws_bytes, _stream(q.device)))
+    return o, lse

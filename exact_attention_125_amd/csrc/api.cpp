@@ -235,3 +235,98 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// Dense [B, H, rows, d] strides in elements.
+fa::Strides dense_strides(int H, int rows, int d) {
+  return fa::Strides{(long long)H * rows * d, (long long)rows * d, (long long)d};
+}
+
+bool strides_ok(const fa::Strides& s, int rows) {
+  if (s.b < 0 || s.h < 0 || s.r < 0) return false;
+  if (s.b % 8 != 0 || s.h % 8 != 0 || s.r % 8 != 0) return false;
+  // 32-bit byte offsets of rows (the kernels read up to 256 rows past the end as zeros)
+  return ((long long)rows + 256) * s.r * 2 < (1LL << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_kv_workspace_size(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim) {
+  bool e1 = false, e2 = false;
+  if (check_common(batch, heads, seqlen_q, head_dim, FA_BF16, 1.f, -1, -1, &e1) != FA_OK ||
+      check_common(batch, heads, seqlen_k, head_dim, FA_BF16, 1.f, -1, -1, &e2) != FA_OK)
+    return 0;
+  if (batch == 0 || heads == 0 || seqlen_q == 0) return 0;
+  return fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim).ws_bytes;
+}
+
+fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
+                    int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                    int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  bool empty_q = false, empty_k = false;
+  fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
+                              window_left, window_right, &empty_q);
+  if (st != FA_OK) return st;
+  st = check_common(batch, heads, seqlen_k, head_dim, dtype, softmax_scale, window_left,
+                    window_right, &empty_k);
+  if (st != FA_OK) return st;
+  if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;
+  const bool has_keys = seqlen_k > 0;
+  if (!q || !o || (has_keys && (!k || !v))) return FA_ERR_NULL_PTR;
+
+  fa::KvParams p;
+  if (strides) {
+    p.sq = fa::Strides{strides[0].batch, strides[0].head, strides[0].row};
+    p.sk = fa::Strides{strides[1].batch, strides[1].head, strides[1].row};
+    p.sv = fa::Strides{strides[2].batch, strides[2].head, strides[2].row};
+    p.so = fa::Strides{strides[3].batch, strides[3].head, strides[3].row};
+  } else {
+    p.sq = p.so = dense_strides(heads, seqlen_q, head_dim);
+    p.sk = p.sv = dense_strides(heads, seqlen_k, head_dim);
+  }
+  if (!strides_ok(p.sq, seqlen_q) || !strides_ok(p.so, seqlen_q) || !strides_ok(p.sk, seqlen_k) ||
+      !strides_ok(p.sv, seqlen_k))
+    return FA_ERR_BAD_SHAPE;
+
+  const fa::KvPlan plan = fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(o) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+      (lse && !aligned16(lse)) || (plan.ws_bytes > 0 && !aligned16(workspace)))
+    return FA_ERR_MISALIGNED;
+  const void* ins[] = {q, k, v};
+  const void* outs[] = {o, lse, plan.ws_bytes > 0 ? workspace : nullptr};
+  for (const void* out : outs) {
+    if (!out) continue;
+    for (const void* in : ins)
+      if (out == in) return FA_ERR_ALIAS;
+  }
+  if ((lse && (const void*)lse == o) ||
+      (outs[2] && ((const void*)outs[2] == o || (const void*)outs[2] == lse)))
+    return FA_ERR_ALIAS;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  p.D = head_dim;
+  p.bf16 = dtype == FA_BF16;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  return hip_status(fa::launch_fwd_kv(p, plan, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

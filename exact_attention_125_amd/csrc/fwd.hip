@@ -59,13 +59,28 @@ struct FwdArgs {
   const char* v;
   char* o;
   float* lse;
-  int n;          // sequence length
+  long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs;   // batch / head strides, bytes
+  int q_rs, k_rs, v_rs, o_rs;                                 // row strides, bytes
+  int nq, nk;     // query rows, key rows
+  int off;        // key position of query 0 (nk - nq)
+  int n_h;        // heads
   int n_bh;       // batch * heads
   int n_qt;       // query tiles per head
+  int n_split;    // key splits: each workgroup sees only its split's key tiles
+  int split_tiles;  // key tiles per split
+  float* po;      // n_split > 1: normalised partial O, fp32 [n_split, B*H, nq, D]
+  float* plse;    //              and its natural-log LSE [n_split, B*H, nq]
   float c;        // |softmax_scale| * log2(e)
   unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
   int causal, wl, wr;
 };
+
+// Buffer resource over the rows [0, rows) of one operand with a row stride of rs bytes: the
+// last row ends after its D elements, so every row at or past `rows` reads as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int rows, int rs,
+                                                            int row_bytes) {
+  return make_rsrc(base, rows > 0 ? (rows - 1) * rs + row_bytes : 0);
+}
 
 template <int D, bool BF16, int WAVES, int QB>
 __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
@@ -88,18 +103,20 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, qt;
-  xcd_tile_order(blockIdx.x, a.n_bh, a.n_qt, bh, qt);
+  int bh, slot;
+  xcd_tile_order(blockIdx.x, a.n_bh, a.n_qt * a.n_split, bh, slot);
+  int qt = slot / a.n_split;
+  const int split = slot - qt * a.n_split;
   if (a.causal) qt = a.n_qt - 1 - qt;               // longest rows first
-  const int n = a.n;
+  const int nq = a.nq, nk = a.nk, off = a.off;
   const int q0 = qt * kBr;
-  const long head = (long)bh * n * kRowBytes;
-  const int head_bytes = n * kRowBytes;
-  const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
+  const int b = bh / a.n_h, h = bh - b * a.n_h;
+  const auto rq = rows_rsrc(a.q + b * a.q_bs + h * a.q_hs, nq, a.q_rs, kRowBytes);
+  const auto rk = rows_rsrc(a.k + b * a.k_bs + h * a.k_hs, nk, a.k_rs, kRowBytes);
+  const auto rv = rows_rsrc(a.v + b * a.v_bs + h * a.v_hs, nk, a.v_rs, kRowBytes);
 
-  // This wave's queries: block qb holds query wq0 + 32 qb + l32 in lane l.
+  // This wave's queries: block qb holds query wq0 + 32 qb + l32 in lane l.  Query i sits at
+  // key position i + off; the mask works on positions.
   const int wq0 = q0 + 32 * QB * wave;
   const int wq1 = wq0 + 32 * QB - 1;
 
@@ -109,29 +126,30 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      u32x4 x = buffer_load16(rq, (wq0 + 32 * qb + l32) * kRowBytes + (2 * ks + hi) * 16);
+      u32x4 x = buffer_load16(rq, (wq0 + 32 * qb + l32) * a.q_rs + (2 * ks + hi) * 16);
       x ^= a.q_sign;
       qreg[qb][ks] = __builtin_bit_cast(i16x8, x);
     }
 
-  const Mask mk{n, a.causal, a.wl, a.wr};
+  const Mask mk{nk, a.causal, a.wl, a.wr};
   int key_lo, key_hi;
-  mk.key_range(q0, min(q0 + kBr - 1, n - 1), key_lo, key_hi);
-  const int t_begin = key_lo / kBc;
-  const int t_end = (key_hi + kBc - 1) / kBc;
+  mk.key_range(q0 + off, min(q0 + kBr - 1, nq - 1) + off, key_lo, key_hi);
+  // this split's share of the key tiles
+  const int t_begin = max(max(key_lo, 0) / kBc, split * a.split_tiles);
+  const int t_end = min((max(key_hi, 0) + kBc - 1) / kBc, (split + 1) * a.split_tiles);
   // The keys this wave's own queries can see (tiles outside are skipped by this wave).
   int wkey_lo, wkey_hi;
-  mk.key_range(wq0, min(wq1, n - 1), wkey_lo, wkey_hi);
-  const bool wave_has_rows = wq0 < n;
+  mk.key_range(wq0 + off, min(wq1, nq - 1) + off, wkey_lo, wkey_hi);
+  const bool wave_has_rows = wq0 < nq;
 
   u32x4 kbuf[kLoads], vbuf[kLoads];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int c = tid + kThreads * i;
-      const int off = (t * kBc + c / kChunks) * kRowBytes + (c % kChunks) * 16;
-      kbuf[i] = buffer_load16(rk, off);
-      vbuf[i] = buffer_load16(rv, off);
+      const int row = t * kBc + c / kChunks, col = (c % kChunks) * 16;
+      kbuf[i] = buffer_load16(rk, row * a.k_rs + col);
+      vbuf[i] = buffer_load16(rv, row * a.v_rs + col);
     }
   };
   auto store_tile = [&](int stage) {
@@ -194,13 +212,13 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     if constexpr (MASKED) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qi = wq0 + 32 * qb + l32;
+        const int qpos = wq0 + 32 * qb + l32 + off;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            s[mb][qb][i] = mk.visible(qi, j) ? s[mb][qb][i] : NEG_INF;
+            s[mb][qb][i] = mk.visible(qpos, j) ? s[mb][qb][i] : NEG_INF;
           }
       }
     }
@@ -291,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     if (t + 1 < t_end) load_tile(t + 1);
     const int j0 = t * kBc;
     if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo) {
-      if (mk.all_visible(wq0, wq1, j0, j0 + kBc))
+      if (mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
         tile(std::false_type{}, kt, vt, j0);
       else
         tile(std::true_type{}, kt, vt, j0);
@@ -300,50 +318,85 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
+  // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); a row that saw no key (possible
+  // only with nq != nk or a key split) gets O = 0 and LSE = -inf
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = wq0 + 32 * qb + l32;
     const float l_tot = sum_with_partner(l_run[qb]);
-    if (qi < n) {
-      const float inv = 1.f / l_tot;
-      char* orow = a.o + head + (long)qi * kRowBytes;
+    if (qi < nq) {
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_tot : 0.f;
+      const float lse = live ? (m_ref[qb] + __builtin_log2f(l_tot)) * kLn2 : NEG_INF;
+      if (a.n_split == 1) {
+        char* orow = a.o + b * a.o_bs + h * a.o_hs + (long)qi * a.o_rs;
 #pragma unroll
-      for (int db = 0; db < kDb; ++db)
+        for (int db = 0; db < kDb; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dim = 32 * db + 8 * g + 4 * hi;
-          u32x2 w = {pack2<BF16>(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv),
-                     pack2<BF16>(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
-        }
-      if (a.lse != nullptr && hi == 0)
-        a.lse[(long)bh * n + qi] = (m_ref[qb] + __builtin_log2f(l_tot)) * kLn2;
+          for (int g = 0; g < 4; ++g) {
+            const int dim = 32 * db + 8 * g + 4 * hi;
+            u32x2 w = {pack2<BF16>(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv),
+                       pack2<BF16>(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
+          }
+        if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nq + qi] = lse;
+      } else {
+        const long prow = ((long)split * a.n_bh + bh) * nq + qi;
+        float* po = a.po + prow * D;
+#pragma unroll
+        for (int db = 0; db < kDb; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dim = 32 * db + 8 * g + 4 * hi;
+            const f32x4 w = {oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv,
+                             oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(po + dim) = w;
+          }
+        if (hi == 0) a.plse[prow] = lse;
+      }
     }
   }
 }
 
 template <int D, bool BF16, int WAVES, int QB>
-hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_args(FwdArgs& a, hipStream_t stream) {
   constexpr int kBr = 32 * QB * WAVES;
+  a.n_qt = (a.nq + kBr - 1) / kBr;
+  const long blocks = (long)a.n_bh * a.n_qt * a.n_split;
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+void set_mask_and_scale(FwdArgs& a, float scale, int causal, int wl, int wr) {
+  a.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+  a.q_sign = scale < 0.f ? 0x80008000u : 0u;
+  a.causal = causal;
+  a.wl = wl;
+  a.wr = causal ? 0 : wr;   // causal is a right bound of 0
+}
+
+template <int D, bool BF16, int WAVES, int QB>
+hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
+  constexpr long kRow = (long)D * 2;
   FwdArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
   a.v = static_cast<const char*>(p.v);
   a.o = static_cast<char*>(p.o);
   a.lse = p.lse;
-  a.n = p.N;
+  a.q_hs = a.k_hs = a.v_hs = a.o_hs = (long long)p.N * kRow;
+  a.q_bs = a.k_bs = a.v_bs = a.o_bs = (long long)p.H * p.N * kRow;
+  a.q_rs = a.k_rs = a.v_rs = a.o_rs = (int)kRow;
+  a.nq = a.nk = p.N;
+  a.off = 0;
+  a.n_h = p.H;
   a.n_bh = p.B * p.H;
-  a.n_qt = (p.N + kBr - 1) / kBr;
-  a.c = (float)(std::fabs((double)p.scale) * 1.4426950408889634);
-  a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
-  a.causal = p.causal;
-  a.wl = p.window_left;
-  a.wr = p.causal ? 0 : p.window_right;   // causal is a right bound of 0
-  const long blocks = (long)a.n_bh * a.n_qt;
-  hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
-                     stream, a);
-  return hipGetLastError();
+  a.n_split = 1;
+  a.split_tiles = (p.N + kBc - 1) / kBc;
+  a.po = a.plse = nullptr;
+  set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
+  return launch_args<D, BF16, WAVES, QB>(a, stream);
 }
 
 // Four waves of 32 query rows per workgroup: 128-row workgroups, twice as many as the
@@ -352,6 +405,8 @@ template <int D, bool BF16>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   return launch_cfg<D, BF16, 4, 1>(p, stream);
 }
+
+static_assert(kBc == kKvMfmaKeyStep, "key splits of the MFMA kernel are whole key tiles");
 
 // Kernel requested through the environment (FA_FWD_KERNEL = "main" or "basic"), 0 if unset.
 // A tuning and testing knob, read at every call and ignored unless set.
@@ -376,6 +431,35 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (choice == 1) return launch_fwd_main(p, stream);
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
   return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+}
+
+// N_q queries over N_k keys on the four-wave kernel, with any strides and plan.n_split key
+// splits (partial results into p.ws, merged afterwards by the caller's combine launch).
+hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream) {
+  const long long e = 2;   // bytes per element
+  FwdArgs a;
+  a.q = static_cast<const char*>(p.q);
+  a.k = static_cast<const char*>(p.k);
+  a.v = static_cast<const char*>(p.v);
+  a.o = static_cast<char*>(p.o);
+  a.lse = p.lse;
+  a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
+  a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);
+  a.v_bs = p.sv.b * e, a.v_hs = p.sv.h * e, a.v_rs = (int)(p.sv.r * e);
+  a.o_bs = p.so.b * e, a.o_hs = p.so.h * e, a.o_rs = (int)(p.so.r * e);
+  a.nq = p.Nq;
+  a.nk = p.Nk;
+  a.off = p.Nk - p.Nq;
+  a.n_h = p.H;
+  a.n_bh = p.B * p.H;
+  a.n_split = plan.n_split;
+  a.split_tiles = plan.split_keys / kBc;
+  a.po = p.ws;
+  a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * p.D : nullptr;
+  set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
+  if (p.D == 64)
+    return p.bf16 ? launch_args<64, true, 4, 1>(a, stream) : launch_args<64, false, 4, 1>(a, stream);
+  return p.bf16 ? launch_args<128, true, 4, 1>(a, stream) : launch_args<128, false, 4, 1>(a, stream);
 }
 
 }  // namespace fa

@@ -45,6 +45,45 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+
+// Strides of one [B, H, rows, d] operand, in elements (the last dimension is contiguous).
+struct Strides {
+  long long b, h, r;
+};
+
+// N_q queries over N_k keys: query i sits at key position i + (N_k - N_q).
+struct KvParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // [B, H, N_q] dense, may be null
+  float* ws;           // partial results of key splits (KvPlan::ws_bytes), null if none
+  Strides sq, sk, sv, so;
+  int B, H, Nq, Nk, D;
+  bool bf16;
+  float scale;
+  int causal;
+  int window_left;
+  int window_right;
+};
+
+// How a call is run: which kernel, how many key splits of how many keys, and the workspace
+// their partial results take (0 with one split).  A function of the shape alone, so a
+// call's rounding does not depend on the device.
+struct KvPlan {
+  bool decode;         // the few-query kernel (N_q <= kDecodeMaxQ) rather than the MFMA one
+  int n_split;
+  int split_keys;      // keys per split (a multiple of the kernel's key step)
+  size_t ws_bytes;
+};
+constexpr int kDecodeMaxQ = 4;
+constexpr int kKvMfmaKeyStep = 64;   // key tile of the four-wave MFMA kernel
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int D);
+// Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
+hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
+// The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
+hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward (128 query rows per workgroup, direct global->LDS copies, two-phase
 // software pipeline), for grids that fill the chip and for padded batches; launch_fwd chooses
 // between it and the four-wave kernel of fwd.hip.

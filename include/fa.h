@@ -160,6 +160,49 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         int causal, int window_left, int window_right, unsigned stages,
                         void* stream);
 
+/* Queries and keys of different lengths, and operands of any layout.
+ *
+ * N_q queries attend to N_k keys, and the queries are the LAST N_q positions of the key
+ * sequence: query i sits at key position p_i = i + (N_k - N_q), and every mask is applied to
+ * positions (causal hides keys j > p_i; the window hides j < p_i - window_left and
+ * j > p_i + window_right).  A decode step of a language model (N_q = 1) over its KV cache
+ * thus sees every cached key, and a block of new queries sees the cache and its own causal
+ * prefix — the inference use the page "Flash Attention 3.7 核心原理与实战：加速Transformer模型训练
+ * 与推理" names (§1.3) over the KV cache that the page "PyTorch-CUDA-v2.9镜像中使用
+ * FlashAttention提升训练速度" mentions in its closing section.  With N_q = N_k this is fa_fwd.
+ * A query that sees no key (possible when N_q > N_k under causal, or with a window) gets
+ * O_i = 0 and LSE_i = -inf.
+ *
+ *   q, o     [B, H, N_q, head_dim], k, v [B, H, N_k, head_dim], dtype, each with its own
+ *            strides (below); lse out: dense [B, H, N_q] float32, or NULL.
+ *   strides  NULL for dense [B, H, N, d] arrays, else an array of four fa_strides, for q, k,
+ *            v and o in that order.  Element (b, h, r, c) of an operand is at
+ *            base + b * batch + h * head + r * row + c (in elements).  Every stride must be
+ *            >= 0 and a multiple of 8 elements (16 bytes); (rows + 256) * row * 2 must be
+ *            below 2^31 for each operand.  A stride of 0 shares rows: k and v with head
+ *            stride 0 serve every head from one key/value head.  The (batch, seq, heads,
+ *            head_dim) layout behind the transposed views of that page's §4.2 module has
+ *            strides {N H d, d, H d}.  The elements of o must not overlap one another (not
+ *            checked).
+ *   workspace  device scratch of at least fa_fwd_kv_workspace_size() bytes (16-byte aligned;
+ *            NULL allowed when that size is 0).  Long key sequences are split into parts that
+ *            run in parallel; each part's normalised output and LSE go here and are merged by
+ *            the log-sum-exp rule.  Its contents on entry do not matter.
+ * N_q = 0 (or B = 0, H = 0) is a no-op; N_k = 0 writes O = 0 and LSE = -inf (k and v may be
+ * NULL then).  Other conventions and errors as in fa_fwd; FA_ERR_BAD_SHAPE also reports a
+ * stride outside the rules above.  Results depend on the shape only (not on the device). */
+typedef struct fa_strides {
+  long long batch, head, row;
+} fa_strides;
+
+size_t fa_fwd_kv_workspace_size(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim);
+
+fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
+                    int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                    int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
+                            "fa_fwd_kv_workspace_size", "fa_fwd_kv",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -165,3 +166,58 @@ def test_empty_is_a_noop(lib, call):
     for dims in (dict(B=0), dict(H=0), dict(N=0)):
         assert call(lib, q=0, k=0, v=0, o=0, lse=0, **dims) == 0
     assert lib.fa_last_error_detail() == b""
+
+
+def fwd_kv(lib, q=Q, k=K, v=V, o=O, lse=L, strides=None, nq=5, nk=300, ws=WS, ws_bytes=1 << 24,
+           **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_fwd_kv(q, k, v, o, lse, strides, a["B"], a["H"], nq, nk, a["d"], a["dtype"],
+                         a["scale"], a["causal"], a["wl"], a["wr"], ws, ws_bytes, None)
+
+
+def test_kv_rejections(lib):
+    from exact_attention_125_amd import _lib
+    assert fwd_kv(lib, dtype=2) == 4
+    assert fwd_kv(lib, d=96) == 3
+    assert fwd_kv(lib, nq=-1) == 2
+    assert fwd_kv(lib, nk=-1) == 2
+    assert fwd_kv(lib, nk=1 << 24) == 2
+    assert fwd_kv(lib, wl=-2) == 5
+    assert fwd_kv(lib, scale=float("nan")) == 7
+    assert fwd_kv(lib, q=0) == 1
+    assert fwd_kv(lib, o=0) == 1
+    assert fwd_kv(lib, k=0) == 1
+    assert fwd_kv(lib, q=Q + 8) == 6
+    assert fwd_kv(lib, lse=L + 4) == 6
+    assert fwd_kv(lib, o=K) == 10
+    assert fwd_kv(lib, lse=Q) == 10
+    assert fwd_kv(lib, lse=O) == 10
+    # a plan with key splits needs its workspace
+    need = lib.fa_fwd_kv_workspace_size(1, 1, 1, 20000, 64)
+    assert need > 0
+    assert fwd_kv(lib, B=1, H=1, nq=1, nk=20000, ws=0) == 8
+    assert fwd_kv(lib, B=1, H=1, nq=1, nk=20000, ws_bytes=need - 1) == 8
+    assert fwd_kv(lib, B=1, H=1, nq=1, nk=20000, ws=WS + 4, ws_bytes=need) == 6
+    assert fwd_kv(lib, B=1, H=1, nq=1, nk=20000, ws=O, ws_bytes=need) == 10
+    # strides: >= 0, multiples of 8 elements, 32-bit row offsets
+    def st(*rows):
+        return (_lib.FaStrides * 4)(*(_lib.FaStrides(*r) for r in rows))
+    dense = (3 * 300 * 64, 300 * 64, 64)
+    qd = (3 * 5 * 64, 5 * 64, 64)
+    assert fwd_kv(lib, strides=st(qd, dense, dense, qd), ws=0, ws_bytes=0) != 2
+    assert fwd_kv(lib, strides=st(qd, (1, 300 * 64, 64), dense, qd)) == 2
+    assert fwd_kv(lib, strides=st(qd, dense, (dense[0], -64, 64), qd)) == 2
+    assert fwd_kv(lib, strides=st(qd, dense, dense, (qd[0], qd[1], 60))) == 2
+    assert fwd_kv(lib, strides=st(qd, (0, 0, 1 << 22), dense, qd)) == 2
+
+
+def test_kv_empty_and_workspace_size(lib):
+    assert fwd_kv(lib, q=0, k=0, v=0, o=0, lse=0, nq=0) == 0
+    assert fwd_kv(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+    assert lib.fa_fwd_kv_workspace_size(2, 3, 0, 100, 64) == 0
+    assert lib.fa_fwd_kv_workspace_size(2, 3, 5, 100, 96) == 0
+    # short key sequences run in one piece; splits keep (d + 1) floats per query and split
+    assert lib.fa_fwd_kv_workspace_size(8, 16, 1, 256, 64) == 0
+    ws = lib.fa_fwd_kv_workspace_size(1, 1, 1, 20000, 128)
+    assert ws > 0 and ws % (129 * 4) == 0
+    assert lib.fa_fwd_kv_workspace_size(64, 64, 4096, 4096, 64) == 0

@@ -1,0 +1,177 @@
+"""N_q queries over N_k keys on the GPU: fa_fwd_kv through the C ABI against the float64 oracle
+(oracle/cross.py), with the fixed tolerances (max |dO| 2e-3 fp16 / 1e-2 bf16, |dLSE| 1e-3).
+
+Covers the few-query kernel (N_q <= 4) and the MFMA kernel, with and without key splits,
+every mask mode, rows that see no key, strided operands ([B, N, H, d] memory, a key/value
+head shared by every head), and sampled rows of the decode workloads at full size."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import LSE_TOL, O_TOL, say, to64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_125_amd as fa
+    return fa
+
+
+def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None):
+    import oracle
+    q64, k64, v64 = inp["q64"], inp["k64"], inp["v64"]
+    B, H = q64.shape[:2]
+    o64 = to64(o)
+    l64 = lse.detach().cpu().numpy().astype(np.float64)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    worst_o = worst_l = 0.0
+    for b, h in heads:
+        ro, rl = oracle.cross_forward(q64[b, h], k64[b, h], v64[b, h], scale, causal, window)
+        empty = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(l64[b, h]), empty), f"{label}: rows without keys differ"
+        assert np.all(o64[b, h][empty] == 0.0), f"{label}: O of a row without keys is not 0"
+        d_o = float(np.abs(o64[b, h] - ro).max()) if ro.size else 0.0
+        d_l = float(np.abs(l64[b, h][~empty] - rl[~empty]).max()) if (~empty).any() else 0.0
+        worst_o, worst_l = max(worst_o, d_o), max(worst_l, d_l)
+    say(f"{label}: max|dO|={worst_o:.2e} max|dLSE|={worst_l:.2e}")
+    assert worst_o <= O_TOL[dtype], f"{label}: max|dO| {worst_o:.3e} > {O_TOL[dtype]}"
+    assert worst_l <= LSE_TOL, f"{label}: max|dLSE| {worst_l:.3e} > {LSE_TOL}"
+
+
+def run_case(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, scale=None, layout="bhnd"):
+    import torch
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if layout == "bhnd":
+        q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    else:   # [B, N, H, d] memory seen as [B, H, N, d] views
+        q, k, v = (to_dev(inp[n].transpose(1, 2).contiguous()).transpose(1, 2)
+                   for n in ("q", "k", "v"))
+        assert k.stride(1) == d and k.stride(2) == H * d   # rows H heads apart
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window)
+    torch.cuda.synchronize()
+    if layout != "bhnd" and n_q > 1:   # a length-1 dimension makes any view contiguous
+        assert not q.is_contiguous() and o.stride() == q.stride()
+    return o, lse, inp, scale
+
+
+MASKS = [(False, (-1, -1)), (True, (-1, -1)), (True, (300, 0)), (False, (100, 40)),
+         (False, (-1, 0))]
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q", [1, 2, 3, 4])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_few_queries(fa, causal, window, n_q, d, dtype):
+    for n_k, seed in ((1, 1), (77, 2), (1000, 3), (4099, 4)):
+        o, lse, inp, scale = run_case(fa, 2, 3, n_q, n_k, d, dtype, causal, window, seed)
+        compare(o, lse, inp, scale, causal, window, dtype,
+                f"decode nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}")
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(5, 50), (100, 700), (300, 129), (130, 3000)])
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
+def test_many_queries(fa, causal, window, n_q, n_k, d, dtype):
+    o, lse, inp, scale = run_case(fa, 2, 2, n_q, n_k, d, dtype, causal, window, seed=n_q + n_k)
+    compare(o, lse, inp, scale, causal, window, dtype,
+            f"mfma nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}")
+
+
+@pytest.mark.parametrize("n_q,n_k", [(1, 20000), (3, 9000), (128, 8192), (200, 5000)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_splits(fa, n_q, n_k, d):
+    """One (batch, head): the plan splits the keys, and the merge must reproduce the whole."""
+    from exact_attention_125_amd import _lib
+    assert _lib.fwd_kv_workspace_size(1, 1, n_q, n_k, d) > 0
+    for causal, window in ((True, (-1, -1)), (False, (-1, -1)), (True, (2500, 0))):
+        o, lse, inp, scale = run_case(fa, 1, 1, n_q, n_k, d, "bf16", causal, window, seed=n_k)
+        compare(o, lse, inp, scale, causal, window, "bf16",
+                f"split nq={n_q} nk={n_k} d={d} causal={causal} w={window}")
+
+
+@pytest.mark.parametrize("n_q,n_k", [(4, 2), (7, 3), (300, 100)])
+def test_rows_without_keys(fa, n_q, n_k):
+    o, lse, inp, scale = run_case(fa, 1, 2, n_q, n_k, 64, "bf16", True, (-1, -1), seed=9)
+    compare(o, lse, inp, scale, True, (-1, -1), "bf16", f"empty rows nq={n_q} nk={n_k}")
+    l64 = lse.cpu().numpy()
+    assert np.all(np.isneginf(l64[:, :, :n_q - n_k])) and np.all(np.isfinite(l64[:, :, n_q - n_k:]))
+
+
+def test_no_keys(fa):
+    import torch
+    q = torch.randn(2, 3, 5, 64, device="cuda").to(torch.bfloat16)
+    k = torch.empty(2, 3, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = fa.fwd_kv(q, k, k, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("n_q,n_k", [(1, 3000), (4, 500), (64, 1000), (257, 257)])
+def test_strided_bnhd_layout(fa, n_q, n_k):
+    for causal in (False, True):
+        o, lse, inp, scale = run_case(fa, 2, 4, n_q, n_k, 128, "bf16", causal, (-1, -1),
+                                      seed=11 + n_q, layout="bnhd")
+        compare(o, lse, inp, scale, causal, (-1, -1), "bf16", f"bnhd nq={n_q} nk={n_k} c={causal}")
+
+
+@pytest.mark.parametrize("n_q", [1, 3, 96])
+def test_shared_key_value_head(fa, n_q):
+    """k, v with head stride 0: every query head attends to one key/value head."""
+    import torch
+    B, H, n_k, d = 2, 4, 1500, 64
+    inp = W.cross_case(B, 1, n_q, n_k, d, "f16", seed=21)
+    qin = W.cross_case(B, H, n_q, 1, d, "f16", seed=22)
+    q = to_dev(qin["q"])
+    k = to_dev(inp["k"]).expand(B, H, n_k, d)
+    v = to_dev(inp["v"]).expand(B, H, n_k, d)
+    assert k.stride(1) == 0
+    o, lse = fa.fwd_kv(q, k, v, 0.125, True)
+    torch.cuda.synchronize()
+    full = {"q64": qin["q64"], "k64": np.repeat(inp["k64"], H, axis=1),
+            "v64": np.repeat(inp["v64"], H, axis=1)}
+    compare(o, lse, full, 0.125, True, (-1, -1), "f16", f"shared kv head nq={n_q}")
+
+
+def test_square_case_matches_the_oracle(fa):
+    """N_q = N_k through fa_fwd_kv is plain self-attention."""
+    for causal, window in ((True, (-1, -1)), (False, (64, 64))):
+        o, lse, inp, scale = run_case(fa, 1, 4, 700, 700, 64, "bf16", causal, window, seed=31)
+        compare(o, lse, inp, scale, causal, window, "bf16", f"square causal={causal} w={window}")
+
+
+def test_negative_and_zero_scale(fa):
+    for scale in (-0.2, 0.0):
+        for n_q in (2, 40):
+            o, lse, inp, _ = run_case(fa, 1, 2, n_q, 900, 64, "f16", True, (-1, -1), seed=41,
+                                      scale=scale)
+            compare(o, lse, inp, scale, True, (-1, -1), "f16", f"scale={scale} nq={n_q}")
+
+
+def test_deterministic(fa):
+    import torch
+    inp = W.cross_case(2, 2, 1, 9000, 128, "bf16", seed=51)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    o1, l1 = fa.fwd_kv(q, k, v, None, True)
+    o2, l2 = fa.fwd_kv(q, k, v, None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("w", W.DECODES, ids=lambda w: w.name)
+def test_decode_workload_sampled(fa, w):
+    """The bench's decode workloads at full size, in the launch configuration the bench times;
+    every row of a sample of heads is checked against the oracle."""
+    import torch
+    inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    o, lse = fa.fwd_kv(q, k, v, w.softmax_scale, True)
+    torch.cuda.synchronize()
+    heads = [(b, (5 * b + 3) % w.H) for b in range(w.B)] + [(w.B - 1, w.H - 1)]
+    compare(o, lse, inp, w.softmax_scale, True, (-1, -1), w.dtype, w.name, heads=heads)

@@ -54,11 +54,36 @@ TRAIN = Workload("train_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1,
                  backward=True)
 
 ALL = (TINY, BERT, CAUSAL, LONG_4K, LONG_8K, TRAIN)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A decode step: n_q new queries per (batch, head) over a KV cache of n_k keys (the
+    queries are the last n_q positions), causal."""
+    name: str
+    B: int
+    H: int
+    n_q: int
+    n_k: int
+    d: int
+    dtype: str
+    seed: int
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The training workload's head shape (B=8, H=16, d=64) and the long-sequence head dim
+# (d=128), one new query over a 16384-key cache.
+DECODE_64 = DecodeWorkload("decode_b8h16q1k16384d64_bf16", 8, 16, 1, 16384, 64, "bf16", seed=7)
+DECODE_128 = DecodeWorkload("decode_b8h16q1k16384d128_bf16", 8, 16, 1, 16384, 128, "bf16", seed=8)
+DECODES = (DECODE_64, DECODE_128)
 # The training step over a padded batch: sample lengths drawn by draw_seqlens (the pages fix
 # no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
 VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
                   backward=True, padded=True)
-BY_NAME = {w.name: w for w in ALL + (VARLEN,)}
+BY_NAME = {w.name: w for w in ALL + (VARLEN,) + DECODES}
 
 
 def draw_f32(shape, seed: int, count: int):
@@ -104,6 +129,18 @@ def draw_seqlens(B: int, N: int, seed: int):
     seed's Q, K, V, dO stream is untouched): ``int32`` numpy array."""
     rng = np.random.default_rng([seed, 1])
     return rng.integers(N // 4, N, size=B, endpoint=True).astype(np.int32)
+
+
+def cross_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int):
+    """Seeded N(0, 1) inputs with N_q query rows and N_k key rows: q [B, H, n_q, d], then k and
+    v [B, H, n_k, d], drawn in that order from one stream and rounded like ``make_inputs``."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, rows in (("q", n_q), ("k", n_k), ("v", n_k)):
+        t, a64 = round_to(rng.standard_normal((B, H, rows, d), dtype=np.float32), dtype)
+        out[name] = t
+        out[name + "64"] = a64
+    return out
 
 
 def random_case(shape, dtype: str, seed: int, with_grad: bool = False, scale_inputs: float = 1.0):
