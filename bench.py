@@ -41,10 +41,13 @@ PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip",
                   "api.cpp", "launch.h")
+# sources a workload's counters depend on, by workload kind (decode: the few-query kernels)
+DECODE_SOURCES = ("cdna4.h", "fwd_kv.hip", "api.cpp", "launch.h")
 # rocprofv3 kernel names -> the bench's kernel keys
 KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_kernel", "fwd"), ("delta_kernel", "delta"),
                ("dkdv_main_kernel", "dkdv"), ("dq_main_kernel", "dq"),
-               ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"))
+               ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"), ("decode_kernel", "decode"),
+               ("combine_kernel", "combine"))
 
 
 def parse():
@@ -104,9 +107,9 @@ def flops(w, pairs_total):
             "dkdv": 8.0 * w.d * pairs_total, "dq": 2.0 * w.d * pairs_total}
 
 
-def source_digest():
+def source_digest(names=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "exact_attention_125_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -121,7 +124,8 @@ def measured_traffic(kernel, workload):
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
     ent = rec.get(f"{workload}/{kernel}")
-    if not ent or ent.get("source_digest") != source_digest():
+    names = DECODE_SOURCES if workload.startswith("decode_") else KERNEL_SOURCES
+    if not ent or ent.get("source_digest") != source_digest(names):
         return None
     return ent.get("bytes_per_launch")
 
@@ -200,7 +204,9 @@ def pmc_summary(fetch_dir, write_dir, workload, calib_mib):
         fk, wk = fetch.get(key), write.get(key)
         ent = {"fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_scale": f_fac, "write_scale": w_fac,
                "copy_fetch_kib_raw": fetch.get("copy"), "copy_write_kib_raw": write.get("copy"),
-               "copy_mib": calib_mib, "source_digest": source_digest()}
+               "copy_mib": calib_mib,
+               "source_digest": source_digest(DECODE_SOURCES if workload.startswith("decode_")
+                                              else KERNEL_SOURCES)}
         if fk is not None and wk is not None and f_fac and w_fac:
             ent["bytes_per_launch"] = round((fk * f_fac + wk * w_fac) * 1024.0)
         out[f"{workload}/{key}"] = ent
@@ -229,6 +235,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     w = W.BY_NAME[args.workload]
+    if isinstance(w, W.DecodeWorkload):
+        return bench_decode(args, w)
     backward = w.backward and not args.forward_only
 
     # CPU baseline first: the oracle's process pool forks before this process touches the GPU.
@@ -360,6 +368,114 @@ def main():
         "kernels": kernels,
         "fwd_tflops": kernels["fwd"]["tflops"], "fwd_frac_of_peak": kernels["fwd"]["frac"],
         "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode call: Q, K, V read once, O and LSE written once."""
+    e = 2
+    return w.B * w.H * (2 * w.n_k * w.d * e + 2 * w.n_q * w.d * e + w.n_q * 4)
+
+
+def decode_cpu_baseline(w, inp):
+    """The oracle over every (batch, head) of the decode workload, one process."""
+    import oracle
+    from oracle import pool
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.cross_forward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                 w.softmax_scale, True)
+    secs = time.perf_counter() - t0
+    return {"value": round(decode_bytes(w) / secs / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"all {w.B * w.H} (batch, head) slices of {w.name}, float64 numpy "
+                      f"materialising S and P, {secs:.2f} s wall, one process "
+                      f"({pool.blas_info()})"}
+
+
+def bench_decode(args, w):
+    """One decode step per timed step: fa_fwd_kv with n_q new queries over the n_k-key cache,
+    HBM-bound; `value` is algorithmic bytes over wall time."""
+    inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
+    cpu = None if args.no_cpu_baseline else decode_cpu_baseline(w, inp)
+    import torch
+    import exact_attention_125_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q, k, v = (inp[n].to("cuda") for n in "qkv")
+    o = torch.empty_like(q)
+    need = fa.fwd_kv_workspace_size(w.B, w.H, w.n_q, w.n_k, w.d)
+    ws = torch.empty(max(need, 16), device="cuda", dtype=torch.uint8)
+
+    def call():
+        fa._lib.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws)
+
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [a.elapsed_time(b) for a, b in ev]
+    cold = None
+    if args.flush_mib > 0:
+        flush = torch.empty(args.flush_mib << 20, device="cuda", dtype=torch.uint8)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (a, b) in enumerate(cev):
+            flush.fill_(i & 0xFF)
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        cold = [a.elapsed_time(b) for a, b in cev]
+        del flush
+    nbytes = decode_bytes(w)
+    ms = wall / args.steps * 1e3
+    t_mean = sum(times) / len(times)
+    gbs = nbytes / (t_mean * 1e-3) / 1e9
+    pairs = w.B * w.H * w.n_q * w.n_k
+    entry = {"ms": round(t_mean, 4), "median_ms": round(statistics.median(times), 4),
+             "min_ms": round(min(times), 4), "gbs": round(gbs, 1),
+             "tflops": round(4.0 * w.d * pairs / (t_mean * 1e-3) / 1e12, 3)}
+    if cold is not None:
+        entry["cold_ms"] = round(sum(cold) / len(cold), 4)
+        entry["cold_median_ms"] = round(statistics.median(cold), 4)
+        entry["cold_gbs"] = round(nbytes / (entry["cold_ms"] * 1e-3) / 1e9, 1)
+    plan_splits = need // (w.B * w.H * w.n_q * (w.d + 1) * 4) if need else 1
+    out = {
+        "metric": "attention decode forward HBM GB/s on 1 MI355X (algorithmic bytes: Q, K, V "
+                  "read once, O and LSE written once)",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
+                   "head_dim": w.d, "causal": True, "pass": "fwd",
+                   "bytes_per_step": nbytes, "key_splits": int(plan_splits)},
+        "kernels": {"decode+combine": entry},
+        # the call is the decode kernel and the split merge; timing both together
+        # understates the decode kernel's own rate slightly
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (+ combine_kernel)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("decode", w.name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

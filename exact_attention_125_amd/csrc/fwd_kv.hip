@@ -268,29 +268,59 @@ struct CombineArgs {
   int nq, n_h, n_bh, n_split;
 };
 
-// One wave per (batch, head, query): merges the splits' partial results.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per (batch, head, query): merges the splits' partial results, 16 splits at a time.
+// The LSEs of a group (one per lane) and its partial rows are loaded together, so a group
+// costs one memory round trip; the groups are merged with a running maximum.
 template <int D, bool BF16>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   constexpr int E = D / 64;   // elements per lane
+  constexpr int kGroup = 16;
   const int lane = threadIdx.x;
   const int row = blockIdx.x;                 // bh * nq + qi
   const int bh = row / a.nq, qi = row - bh * a.nq;
   const int b = bh / a.n_h, h = bh - b * a.n_h;
   const long stride = (long)a.n_bh * a.nq;    // between splits, in rows
   const float NEG_INF = -__builtin_inff();
-  float mx = NEG_INF;
-  for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, a.plse[s * stride + row]);
-  const float mu = mx == NEG_INF ? 0.f : mx;
-  float L = 0.f, O[E];
+  float mx = NEG_INF, L = 0.f, O[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) O[i] = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float w = exp2_fast((a.plse[s * stride + row] - mu) * kLog2e);
-    L += w;
-    const float* po = a.po + (s * stride + row) * D;
+  for (int s0 = 0; s0 < a.n_split; s0 += kGroup) {
+    const int n = min(kGroup, a.n_split - s0);
+    const float ls = lane < n ? a.plse[(s0 + lane) * stride + row] : NEG_INF;
+    const float* po = a.po + ((long)s0 * stride + row) * D + lane;
+    float pv[kGroup][E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) O[i] = __builtin_fmaf(w, po[lane + 64 * i], O[i]);
+    for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+      for (int i = 0; i < E; ++i) pv[j][i] = j < n ? po[j * stride * D + 64 * i] : 0.f;
+    const float m_new = fmaxf(mx, wave_max(ls));
+    const float mu = m_new == NEG_INF ? 0.f : m_new;
+    const float alpha = exp2_fast((mx - mu) * kLog2e);   // 0 before the first live split
+    const float w = exp2_fast((ls - mu) * kLog2e);        // 0 for lanes without a split
+    L = __builtin_fmaf(L, alpha, w);                       // per lane; summed at the end
+#pragma unroll
+    for (int i = 0; i < E; ++i) O[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float wj = __shfl(w, j);
+#pragma unroll
+      for (int i = 0; i < E; ++i) O[i] = __builtin_fmaf(wj, pv[j][i], O[i]);
+    }
+    mx = m_new;
   }
+  L = wave_sum(L);
   const bool live = L > 0.f;
   const float inv = live ? 1.f / L : 0.f;
   char* orow = a.o + b * a.o_bs + h * a.o_hs + (long)qi * a.o_rs;
