@@ -190,7 +190,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  *            the log-sum-exp rule.  Its contents on entry do not matter.
  * N_q = 0 (or B = 0, H = 0) is a no-op; N_k = 0 writes O = 0 and LSE = -inf (k and v may be
  * NULL then).  Other conventions and errors as in fa_fwd; FA_ERR_BAD_SHAPE also reports a
- * stride outside the rules above.  Results depend on the shape only (not on the device). */
+ * stride outside the rules above.  Results depend on the shape only (not on the device).
+ * Precision: with N_q <= 4 the probabilities stay in float32 for the P V sum (no rounding to
+ * the input type); otherwise as in fa_fwd. */
 typedef struct fa_strides {
   long long batch, head, row;
 } fa_strides;
