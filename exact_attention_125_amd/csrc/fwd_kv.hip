@@ -207,14 +207,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       step(std::true_type{}, kb, vb, r0);
   };
 
-  // two register sets: the loads of step t+1 are issued before step t is computed
+  // Register sets in a ring: the loads of the next one (N_q = 4: register room for one) or two
+  // steps are in flight while a step is computed.
   u32x4 ka[kDecU], va[kDecU], kb2[kDecU], vb2[kDecU];
-  if (n_steps > 0) load(ka, va, lo);
-  for (int t = 0; t < n_steps; t += 2) {
-    if (t + 1 < n_steps) load(kb2, vb2, lo + (t + 1) * STEP);
-    run(ka, va, lo + t * STEP);
-    if (t + 2 < n_steps) load(ka, va, lo + (t + 2) * STEP);
-    if (t + 1 < n_steps) run(kb2, vb2, lo + (t + 1) * STEP);
+  if constexpr (NQ <= 2) {
+    u32x4 kc[kDecU], vc[kDecU];
+    if (n_steps > 0) load(ka, va, lo);
+    if (n_steps > 1) load(kb2, vb2, lo + STEP);
+    for (int t = 0; t < n_steps; t += 3) {
+      if (t + 2 < n_steps) load(kc, vc, lo + (t + 2) * STEP);
+      run(ka, va, lo + t * STEP);
+      if (t + 3 < n_steps) load(ka, va, lo + (t + 3) * STEP);
+      if (t + 1 < n_steps) run(kb2, vb2, lo + (t + 1) * STEP);
+      if (t + 4 < n_steps) load(kb2, vb2, lo + (t + 4) * STEP);
+      if (t + 2 < n_steps) run(kc, vc, lo + (t + 2) * STEP);
+    }
+  } else {
+    if (n_steps > 0) load(ka, va, lo);
+    for (int t = 0; t < n_steps; t += 2) {
+      if (t + 1 < n_steps) load(kb2, vb2, lo + (t + 1) * STEP);
+      run(ka, va, lo + t * STEP);
+      if (t + 2 < n_steps) load(ka, va, lo + (t + 2) * STEP);
+      if (t + 1 < n_steps) run(kb2, vb2, lo + (t + 1) * STEP);
+    }
   }
 
   // ---- merge the row groups
@@ -393,10 +408,12 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D) {
   const long bh = (long)B * H;
   long split_keys;
   if (Nq <= kDecodeMaxQ) {
-    // about 2048 workgroups (8 per CU), each at least four steps of keys
+    // about 512 workgroups: one round at two per CU, so each workgroup's start (query load,
+    // first key rows) and end (merge, stores) latency is paid once per CU pair; at least four
+    // steps of keys each
     p.decode = true;
     const long step = dec_step_rows(D);
-    const long want = ceil_div(2048, bh > 0 ? bh : 1);
+    const long want = ceil_div(512, bh > 0 ? bh : 1);
     split_keys = ceil_div(ceil_div(Nk, want), step) * step;
     if (split_keys < 4 * step) split_keys = 4 * step;
   } else {
