@@ -41,7 +41,8 @@ from .attention import (allowed_mask, attention_forward, attention_backward,
 from .online import attention_forward_online
 from .brute import attention_forward_brute
 from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
-from .cross import cross_allowed_mask, cross_allowed_pairs, cross_forward, cross_forward_bh
+from .cross import (cross_allowed_mask, cross_allowed_pairs, cross_backward, cross_backward_bh,
+                    cross_forward, cross_forward_bh)
 
 __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
@@ -49,4 +50,5 @@ __all__ = [
     "attention_forward_online", "attention_forward_brute",
     "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
+    "cross_backward", "cross_backward_bh",
 ]

@@ -76,3 +76,40 @@ def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1)):
         for h in range(H):
             o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window)
     return o, lse
+
+
+def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, -1)):
+    """One (batch, head): gradients (dQ [N_q, d], dK, dV [N_k, d]) of <dO, O> for
+    ``cross_forward``, the ordinary derivative of that definition:
+
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(P * dP)),
+        dQ = scale * dS K,   dK = scale * dS^T Q
+
+    with P recomputed from Q and K; rows without a visible key have P = 0 and contribute
+    nothing.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
+    s = np.where(ok, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    live = np.isfinite(m)
+    e = np.exp(s - np.where(live, m, 0.0)[:, None])
+    p = e / np.where(live, e.sum(axis=1), 1.0)[:, None]
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1)):
+    """[B, H, N_q, d] q and dO, [B, H, N_k, d] k and v -> (dQ, dK, dV), one head at a time."""
+    B, H = q.shape[:2]
+    dq, dk, dv = (np.empty(t.shape, dtype=np.float64) for t in (q, k, v))
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = cross_backward(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                          scale, causal, window)
+    return dq, dk, dv

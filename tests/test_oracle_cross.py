@@ -9,6 +9,10 @@
   * closed forms: a decode step (N_q = 1, causal) sees every key; Q = 0 gives the mean of V
     over the visible keys and LSE = ln(count); rows with no visible key give O = 0,
     LSE = -inf.
+The backward: central differences of the forward, the square backward for N_q = N_k and
+(for the last N_q rows, dO zero elsewhere) for N_q < N_k, torch CPU float64 autograd through
+SDPA with the bottom-right mask, and the invariants sum_j dV_j = sum_i dO_i over rows that see
+a key and sum_j dK_j = 0.
 """
 import math
 
@@ -142,3 +146,77 @@ def test_mutant_top_left_alignment_fails_the_suffix_pin():
     wrong = (e / e.sum(axis=1, keepdims=True)) @ v
     ro, _ = oracle.attention_forward(q_all, k, v, 0.5, causal=True)
     assert not np.allclose(wrong, ro[5:], atol=1e-6)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(1, 6), (3, 7), (6, 6), (7, 3), (5, 9)])
+def test_backward_central_differences(causal, window, n_q, n_k):
+    rng = np.random.default_rng(n_q * 13 + n_k)
+    q, k, v, do = (rng.standard_normal((r, 3)) for r in (n_q, n_k, n_k, n_q))
+    dq, dk, dv = oracle.cross_backward(q, k, v, do, 0.7, causal, window)
+    h = 1e-6
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.cross_forward(q_, k_, v_, 0.7, causal, window)
+        return float((o * do).sum())
+
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = plus, minus
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_backward_reduces_to_square_and_suffix(causal, window):
+    rng = np.random.default_rng(17)
+    n = 10
+    q, k, v, do = (rng.standard_normal((n, 4)) for _ in range(4))
+    ref = oracle.attention_backward(q, k, v, do, 0.5, causal, window)
+    got = oracle.cross_backward(q, k, v, do, 0.5, causal, window)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+    n_q = 4   # the last rows only: dO zero on the first n - n_q rows of the square problem
+    do_sq = do.copy()
+    do_sq[: n - n_q] = 0.0
+    rq, rk, rv = oracle.attention_backward(q, k, v, do_sq, 0.5, causal, window)
+    gq, gk, gv = oracle.cross_backward(q[n - n_q:], k, v, do[n - n_q:], 0.5, causal, window)
+    np.testing.assert_allclose(gq, rq[n - n_q:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gk, rk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gv, rv, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(3, 8), (8, 5), (1, 6)])
+def test_backward_torch_autograd(n_q, n_k):
+    rng = np.random.default_rng(n_q + 5 * n_k)
+    q, k, v, do = (rng.standard_normal((r, 4)) for r in (n_q, n_k, n_k, n_q))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    mask = torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=n_k - n_q)
+    live = mask.any(dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[None], tk[None], tv[None], attn_mask=mask[None], scale=0.6)[0]
+    # rows without a key come out NaN from SDPA; they take no part in the loss
+    (torch.where(live[:, None], o, 0.0) * torch.tensor(do)).sum().backward()
+    gq, gk, gv = oracle.cross_backward(q, k, v, do, 0.6, causal=True)
+    np.testing.assert_allclose(gq[live.numpy()], tq.grad.numpy()[live.numpy()], rtol=1e-10,
+                               atol=1e-12)
+    np.testing.assert_allclose(gk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(gv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.all(gq[~live.numpy()] == 0.0)
+
+
+def test_backward_invariants():
+    rng = np.random.default_rng(23)
+    q, do = rng.standard_normal((9, 5)), rng.standard_normal((9, 5))
+    k, v = rng.standard_normal((4, 5)), rng.standard_normal((4, 5))
+    dq, dk, dv = oracle.cross_backward(q, k, v, do, 0.8, causal=True)
+    live = np.isfinite(oracle.cross_forward(q, k, v, 0.8, causal=True)[1])
+    np.testing.assert_allclose(dv.sum(axis=0), do[live].sum(axis=0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    assert np.all(dq[~live] == 0.0)
