@@ -42,6 +42,8 @@ SIGNATURES = {
     "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S,
                        _P]),
+    "fa_bwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F,
+                       _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -231,3 +233,32 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(workspace),
                           ws_bytes, _stream(q.device)))
     return o, lse
+
+
+def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
+           dq=None, dk=None, dv=None, workspace=None):
+    """``fa_bwd_kv``: gradients ``(dq, dk, dv)`` of ``fwd_kv``.  Any strides with a contiguous
+    last dimension; new gradients take the strides of q, k, v."""
+    import torch
+    _check_kv_tensors(q, k, v)
+    for t in (o, dout):
+        if t.dtype != q.dtype or tuple(t.shape) != tuple(q.shape) or t.stride(-1) != 1:
+            raise ValueError("o and dout must match q")
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g, t in ((dk, k), (dv, v)):
+        if any(st == 0 for st in g.stride()[:3]) and g.numel() > 0:
+            raise ValueError("gradient outputs must not share rows (stride 0): pass dense ones")
+    need = _lib.fa_bwd_workspace_size(B, H, n_q, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    st = (FaStrides * 8)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o, dout, dq, dk, dv)))
+    _check(_lib.fa_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                          _ptr(dk), _ptr(dv), st, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), B, H, n_q, n_k, d,
+                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _stream(q.device)))
+    return dq, dk, dv

@@ -330,3 +330,78 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
 }
 
 }  // extern "C"
+
+extern "C" {
+
+fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
+                    void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
+                    int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                    int window_left, int window_right, void* stream) {
+  g_last_error.clear();
+  bool empty_q = false, empty_k = false;
+  fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
+                              window_left, window_right, &empty_q);
+  if (st != FA_OK) return st;
+  st = check_common(batch, heads, seqlen_k, head_dim, dtype, softmax_scale, window_left,
+                    window_right, &empty_k);
+  if (st != FA_OK) return st;
+  if (batch == 0 || heads == 0 || (seqlen_q == 0 && seqlen_k == 0)) return FA_OK;
+  const bool has_q = seqlen_q > 0, has_k = seqlen_k > 0;
+  if ((has_q && (!q || !o || !dout || !lse || !dq)) || (has_k && (!k || !v || !dk || !dv)))
+    return FA_ERR_NULL_PTR;
+
+  fa::BwdKvParams p;
+  if (strides) {
+    fa::Strides* dst[] = {&p.sq, &p.sk, &p.sv, &p.so, &p.sg, &p.sdq, &p.sdk, &p.sdv};
+    for (int i = 0; i < 8; ++i) *dst[i] = fa::Strides{strides[i].batch, strides[i].head, strides[i].row};
+  } else {
+    p.sq = p.so = p.sg = p.sdq = dense_strides(heads, seqlen_q, head_dim);
+    p.sk = p.sv = p.sdk = p.sdv = dense_strides(heads, seqlen_k, head_dim);
+  }
+  const fa::Strides* qs[] = {&p.sq, &p.so, &p.sg, &p.sdq};
+  const fa::Strides* ks[] = {&p.sk, &p.sv, &p.sdk, &p.sdv};
+  for (const fa::Strides* x : qs)
+    if (!strides_ok(*x, seqlen_q)) return FA_ERR_BAD_SHAPE;
+  for (const fa::Strides* x : ks)
+    if (!strides_ok(*x, seqlen_k)) return FA_ERR_BAD_SHAPE;
+
+  const size_t need = has_q ? fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  const void* ins[] = {q, k, v, o, dout, lse, need > 0 ? workspace : nullptr};
+  void* outs[] = {dq, dk, dv};
+  for (const void* x : ins)
+    if (x && !aligned16(x)) return FA_ERR_MISALIGNED;
+  for (const void* x : outs)
+    if (x && !aligned16(x)) return FA_ERR_MISALIGNED;
+  for (void* out : outs) {
+    if (!out) continue;
+    for (const void* in : ins)
+      if (in && out == in) return FA_ERR_ALIAS;
+  }
+  if ((dq && (dq == dk || dq == dv)) || (dk && dk == dv)) return FA_ERR_ALIAS;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.stats = static_cast<float*>(workspace);
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  p.D = head_dim;
+  p.bf16 = dtype == FA_BF16;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  return hip_status(fa::launch_bwd_kv(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

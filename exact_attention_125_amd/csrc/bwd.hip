@@ -43,8 +43,14 @@ struct BwdArgs {
   char* dv;
   float* stats;   // per-query statistics in 32-query blocks (stat_index)
   const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
+  // batch / head strides (bytes) and row strides (bytes) of q, k, v, o, dout, dq, dk, dv
+  long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs, g_bs, g_hs;
+  long long dq_bs, dq_hs, dk_bs, dk_hs, dv_bs, dv_hs;
+  int q_rs, k_rs, v_rs, o_rs, g_rs, dq_rs, dk_rs, dv_rs;
   int heads;
-  int n;
+  int n;          // query rows (statistics, LSE)
+  int nk;         // key rows
+  int off;        // key position of query 0 (nk - n)
   int n_bh;
   int n_tiles;
   float c;        // sigma * log2(e)
@@ -52,6 +58,13 @@ struct BwdArgs {
   float scale;    // softmax_scale
   int causal, wl, wr;
 };
+
+// Buffer resource over rows [0, rows) with a row stride of rs bytes (rows at or past the end
+// read as zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int rows, int rs,
+                                                            int row_bytes) {
+  return make_rsrc(base, rows > 0 ? (rows - 1) * rs + row_bytes : 0);
+}
 
 // ---------------------------------------------------------------------------- delta
 // delta = sum_c dO[c] * O[c] per query with both rounded inputs in fp32, stored negated next
@@ -73,16 +86,18 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   const int slots = stat_blocks(a.n) * kStatRows;
   for (long bh = blockIdx.y; bh < a.n_bh; bh += gridDim.y) {
     // rows of the sequence; rows len .. n-1 of a padded batch get zeros like the slots past n
-    const int len = PADDED ? min(max(a.seqlens[bh / a.heads], 0), a.n) : a.n;
+    const int b = (int)(bh / a.heads), h = (int)(bh - (long)b * a.heads);
+    const int len = PADDED ? min(max(a.seqlens[b], 0), a.n) : a.n;
+    const char* orows = a.o + b * a.o_bs + h * a.o_hs + 16 * sub;
+    const char* grows = a.dout + b * a.g_bs + h * a.g_hs + 16 * sub;
     u32x4 ov[IT], gv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int q = q_base + RPI * it;
       ov[it] = gv[it] = u32x4{};
       if (q < len) {
-        const long off = ((bh * a.n + q) * D + 8 * sub) * 2;
-        ov[it] = *reinterpret_cast<const u32x4*>(a.o + off);
-        gv[it] = *reinterpret_cast<const u32x4*>(a.dout + off);
+        ov[it] = *reinterpret_cast<const u32x4*>(orows + (long)q * a.o_rs);
+        gv[it] = *reinterpret_cast<const u32x4*>(grows + (long)q * a.g_rs);
       }
     }
 #pragma unroll
@@ -101,8 +116,12 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
       if (sub == 0 && q < slots) {
         float* out = a.stats + stat_index(bh, a.n, q);
         const bool in = q < len;
-        out[0] = in ? -a.lse[bh * a.n + q] / a.sigma : 0.f;
-        out[kStatRows] = in ? -acc : 0.f;
+        // a row that sees no key (LSE = -inf; only with fewer keys than queries or a window)
+        // gets zeros too: every one of its scores is masked
+        const float lse = in ? a.lse[bh * a.n + q] : 0.f;
+        const bool live = in && lse != -__builtin_inff();
+        out[0] = live ? -lse / a.sigma : 0.f;
+        out[kStatRows] = live ? -acc : 0.f;
       }
     }
   }
@@ -130,13 +149,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
   int bh, kt;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, kt);
-  const int n = a.n;
-  const long head = (long)bh * n * kRowBytes;
-  const int head_bytes = n * kRowBytes;
-  const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
-  const auto rg = make_rsrc(a.dout + head, head_bytes);
+  const int n = a.n, nk = a.nk, off = a.off;   // queries, keys, key position of query 0
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const auto rq = rows_rsrc(a.q + b * a.q_bs + h * a.q_hs, n, a.q_rs, kRowBytes);
+  const auto rk = rows_rsrc(a.k + b * a.k_bs + h * a.k_hs, nk, a.k_rs, kRowBytes);
+  const auto rv = rows_rsrc(a.v + b * a.v_bs + h * a.v_hs, nk, a.v_rs, kRowBytes);
+  const auto rg = rows_rsrc(a.dout + b * a.g_bs + h * a.g_hs, n, a.g_rs, kRowBytes);
 
   // K^T and V^T as B operands: lane holds key (k0 + l32), head-dim chunk 2 ks + hi.
   const int k_first = kt * kKvRows;
@@ -144,14 +162,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   i16x8 kreg[kKs], vreg[kKs];
 #pragma unroll
   for (int ks = 0; ks < kKs; ++ks) {
-    kreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rk, key * kRowBytes + (2 * ks + hi) * 16));
-    vreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rv, key * kRowBytes + (2 * ks + hi) * 16));
+    kreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rk, key * a.k_rs + (2 * ks + hi) * 16));
+    vreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rv, key * a.v_rs + (2 * ks + hi) * 16));
   }
 
-  const Mask mk{n, a.causal, a.wl, a.wr};
-  const int k_last = min(k_first + kKvRows, n) - 1;
-  int q_lo, q_hi;
-  mk.query_range(k_first, k_last, q_lo, q_hi);
+  // queries that see any of the keys: the mask works on positions (index + off), which
+  // start at off (negative when there are more queries than keys)
+  const Mask mk{nk, a.causal, a.wl, a.wr};
+  const int k_last = min(k_first + kKvRows, nk) - 1;
+  int p_lo = off, p_hi = off + n;                        // positions [p_lo, p_hi)
+  if (a.causal) p_lo = max(p_lo, k_first);
+  if (a.wr >= 0) p_lo = max(p_lo, k_first - a.wr);
+  if (a.wl >= 0) p_hi = min(p_hi, k_last + a.wl + 1);
+  const int q_lo = max(p_lo - off, 0), q_hi = min(p_hi - off, n);
   const int s_begin = q_lo / kQStep;
   const int s_end = q_hi > q_lo ? (q_hi + kQStep - 1) / kQStep : s_begin;
 
@@ -161,9 +184,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int c = tid + 256 * i;
-      const int off = (s * kQStep + c / kChunks) * kRowBytes + (c % kChunks) * 16;
-      qbuf[i] = buffer_load16(rq, off);
-      gbuf[i] = buffer_load16(rg, off);
+      const int row = s * kQStep + c / kChunks, col = (c % kChunks) * 16;
+      qbuf[i] = buffer_load16(rq, row * a.q_rs + col);
+      gbuf[i] = buffer_load16(rg, row * a.g_rs + col);
     }
     const int q = s * kQStep + tid;
     if (tid < kQStep && q < n) {
@@ -226,7 +249,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
 
     const int q0 = s * kQStep;
-    const bool full = mk.all_visible(q0, q0 + kQStep - 1, k_first, k_first + kKvRows) &&
+    const bool full = mk.all_visible(q0 + off, q0 + kQStep - 1 + off, k_first, k_first + kKvRows) &&
                       q0 + kQStep <= n;
     unsigned pk[8], dk_pk[8];
 #pragma unroll
@@ -241,7 +264,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         float pe = exp2_fast(__builtin_fmaf(sc[i], c, c * l2[e]));
         if (!full) {
           const int qq = q0 + 8 * g + 4 * hi + e;
-          pe = (qq < n && mk.visible(qq, key)) ? pe : 0.f;
+          pe = (qq < n && mk.visible(qq + off, key)) ? pe : 0.f;
         }
         p[e] = pe;
         d[e] = pe * (dp[i] + de[e]);
@@ -277,9 +300,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   }
 
   // epilogue: lane holds key (k_first + 32 wave + l32), dims 32 db + 8 g + 4 hi + 0..3
-  if (key < n) {
-    char* dkrow = a.dk + head + (long)key * kRowBytes;
-    char* dvrow = a.dv + head + (long)key * kRowBytes;
+  if (key < nk) {
+    char* dkrow = a.dk + b * a.dk_bs + h * a.dk_hs + (long)key * a.dk_rs;
+    char* dvrow = a.dv + b * a.dv_bs + h * a.dv_hs + (long)key * a.dv_rs;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < kDb; ++db)
@@ -318,41 +341,40 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   int bh, qt;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_tiles, bh, qt);
   if (a.causal) qt = a.n_tiles - 1 - qt;
-  const int n = a.n;
+  const int n = a.n, nk = a.nk, off = a.off;   // queries, keys, key position of query 0
   const int q0 = qt * kDqRows;
-  const long head = (long)bh * n * kRowBytes;
-  const int head_bytes = n * kRowBytes;
-  const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
-  const auto rg = make_rsrc(a.dout + head, head_bytes);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const auto rq = rows_rsrc(a.q + b * a.q_bs + h * a.q_hs, n, a.q_rs, kRowBytes);
+  const auto rk = rows_rsrc(a.k + b * a.k_bs + h * a.k_hs, nk, a.k_rs, kRowBytes);
+  const auto rv = rows_rsrc(a.v + b * a.v_bs + h * a.v_hs, nk, a.v_rs, kRowBytes);
+  const auto rg = rows_rsrc(a.dout + b * a.g_bs + h * a.g_hs, n, a.g_rs, kRowBytes);
 
   const int qi = q0 + 32 * wave + l32;
   i16x8 qreg[kKs], greg[kKs];
 #pragma unroll
   for (int ks = 0; ks < kKs; ++ks) {
-    qreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, qi * kRowBytes + (2 * ks + hi) * 16));
-    greg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, qi * kRowBytes + (2 * ks + hi) * 16));
+    qreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, qi * a.q_rs + (2 * ks + hi) * 16));
+    greg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, qi * a.g_rs + (2 * ks + hi) * 16));
   }
   const bool row_ok = qi < n;
   const float mrow = row_ok ? a.stats[stat_index(bh, n, qi)] : 0.f;               // -LSE / sigma
   const float ndlt = row_ok ? a.stats[stat_index(bh, n, qi) + kStatRows] : 0.f;   // -delta
 
-  const Mask mk{n, a.causal, a.wl, a.wr};
+  const Mask mk{nk, a.causal, a.wl, a.wr};
   const int q_last = q0 + kDqRows - 1;
   int key_lo, key_hi;
-  mk.key_range(q0, min(q_last, n - 1), key_lo, key_hi);
-  const int t_begin = key_lo / kKStep;
-  const int t_end = (key_hi + kKStep - 1) / kKStep;
+  mk.key_range(q0 + off, min(q_last, n - 1) + off, key_lo, key_hi);
+  const int t_begin = max(key_lo, 0) / kKStep;
+  const int t_end = (max(key_hi, 0) + kKStep - 1) / kKStep;
 
   u32x4 kbuf[kLoads], vbuf[kLoads];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int cc = tid + 256 * i;
-      const int off = (t * kKStep + cc / kChunks) * kRowBytes + (cc % kChunks) * 16;
-      kbuf[i] = buffer_load16(rk, off);
-      vbuf[i] = buffer_load16(rv, off);
+      const int row = t * kKStep + cc / kChunks, col = (cc % kChunks) * 16;
+      kbuf[i] = buffer_load16(rk, row * a.k_rs + col);
+      vbuf[i] = buffer_load16(rv, row * a.v_rs + col);
     }
   };
   auto store_tile = [&](int stage) {
@@ -403,7 +425,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     }
 
     const int j0 = t * kKStep;
-    const bool full = mk.all_visible(q0, q_last, j0, j0 + kKStep);
+    const bool full = mk.all_visible(q0 + off, q_last + off, j0, j0 + kKStep);
     unsigned dsk[2][8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
           float p = exp2_fast(__builtin_fmaf(sc[mb][i + e], c, cm));
           if (!full) {
             const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
-            p = (row_ok && mk.visible(qi, j)) ? p : 0.f;
+            p = (row_ok && mk.visible(qi + off, j)) ? p : 0.f;
           }
           d2[e] = p * (dp[mb][i + e] + ndlt);
         }
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   }
 
   if (row_ok) {
-    char* row = a.dq + head + (long)qi * kRowBytes;
+    char* row = a.dq + b * a.dq_bs + h * a.dq_hs + (long)qi * a.dq_rs;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < kDb; ++db)
@@ -480,8 +502,14 @@ BwdArgs make_args(const BwdParams& p) {
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
   a.seqlens = p.seqlens;
+  const long long row = (long long)p.D * 2, head = (long long)p.N * row, batch = p.H * head;
+  a.q_bs = a.k_bs = a.v_bs = a.o_bs = a.g_bs = a.dq_bs = a.dk_bs = a.dv_bs = batch;
+  a.q_hs = a.k_hs = a.v_hs = a.o_hs = a.g_hs = a.dq_hs = a.dk_hs = a.dv_hs = head;
+  a.q_rs = a.k_rs = a.v_rs = a.o_rs = a.g_rs = a.dq_rs = a.dk_rs = a.dv_rs = (int)row;
   a.heads = p.H;
   a.n = p.N;
+  a.nk = p.N;
+  a.off = 0;
   a.n_bh = p.B * p.H;
   a.n_tiles = 0;
   a.sigma = softmax_sigma(p.scale);
@@ -526,7 +554,67 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <int D, bool BF16>
+hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
+  const long long e = 2;
+  BwdArgs a;
+  a.q = static_cast<const char*>(p.q);
+  a.k = static_cast<const char*>(p.k);
+  a.v = static_cast<const char*>(p.v);
+  a.o = static_cast<const char*>(p.o);
+  a.dout = static_cast<const char*>(p.dout);
+  a.lse = p.lse;
+  a.dq = static_cast<char*>(p.dq);
+  a.dk = static_cast<char*>(p.dk);
+  a.dv = static_cast<char*>(p.dv);
+  a.stats = p.stats;
+  a.seqlens = nullptr;
+  a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
+  a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);
+  a.v_bs = p.sv.b * e, a.v_hs = p.sv.h * e, a.v_rs = (int)(p.sv.r * e);
+  a.o_bs = p.so.b * e, a.o_hs = p.so.h * e, a.o_rs = (int)(p.so.r * e);
+  a.g_bs = p.sg.b * e, a.g_hs = p.sg.h * e, a.g_rs = (int)(p.sg.r * e);
+  a.dq_bs = p.sdq.b * e, a.dq_hs = p.sdq.h * e, a.dq_rs = (int)(p.sdq.r * e);
+  a.dk_bs = p.sdk.b * e, a.dk_hs = p.sdk.h * e, a.dk_rs = (int)(p.sdk.r * e);
+  a.dv_bs = p.sdv.b * e, a.dv_hs = p.sdv.h * e, a.dv_rs = (int)(p.sdv.r * e);
+  a.heads = p.H;
+  a.n = p.Nq;
+  a.nk = p.Nk;
+  a.off = p.Nk - p.Nq;
+  a.n_bh = p.B * p.H;
+  a.sigma = softmax_sigma(p.scale);
+  a.c = (float)((double)a.sigma * 1.4426950408889634);
+  a.scale = p.scale;
+  a.causal = p.causal;
+  a.wl = p.window_left;
+  a.wr = p.causal ? 0 : p.window_right;
+  // with no query, only dK = dV = 0 is left to write (the dK/dV kernel sees no query step);
+  // with no key, dQ = 0
+  if (p.Nq > 0) {
+    const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
+    const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
+    hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
+    if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+  }
+  if (p.Nk > 0) {
+    a.n_tiles = (p.Nk + kKvRows - 1) / kKvRows;
+    hipLaunchKernelGGL((dkdv_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256),
+                       0, stream, a);
+    if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+  }
+  if (p.Nq == 0) return hipSuccess;
+  a.n_tiles = (p.Nq + kDqRows - 1) / kDqRows;
+  hipLaunchKernelGGL((dq_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_kv(const BwdKvParams& p, hipStream_t stream) {
+  if (p.D == 64) return p.bf16 ? launch_kv<64, true>(p, stream) : launch_kv<64, false>(p, stream);
+  return p.bf16 ? launch_kv<128, true>(p, stream) : launch_kv<128, false>(p, stream);
+}
 
 hipError_t launch_bwd(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, stages, stream) : launch<64, false>(p, stages, stream);

@@ -93,6 +93,28 @@ hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream);
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u;
 hipError_t launch_bwd(const BwdParams& p, unsigned stages, hipStream_t stream);
 
+// Backward of fa_fwd_kv: N_q queries over N_k keys, any strides (the four-wave kernels).
+struct BwdKvParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // [B, H, N_q] dense
+  void* dq;
+  void* dk;
+  void* dv;
+  float* stats;        // workspace, as for BwdParams with N = N_q
+  Strides sq, sk, sv, so, sg, sdq, sdk, sdv;
+  int B, H, Nq, Nk, D;
+  bool bf16;
+  float scale;
+  int causal;
+  int window_left;
+  int window_right;
+};
+hipError_t launch_bwd_kv(const BwdKvParams& p, hipStream_t stream);
+
 // The backward passes evaluate P = exp(scale s - LSE) as 2^(c (s + m)) with c = sigma log2(e)
 // and the per-row m = -LSE / sigma, where sigma is the scale moved away from zero (a zero
 // scale leaves every score weight equal, which sigma = 1e-30 reproduces to fp32 rounding).

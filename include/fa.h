@@ -205,6 +205,26 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     int window_left, int window_right, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Backward pass of fa_fwd_kv (by recomputation, as fa_bwd): gradients of sum(dout * o) for
+ * N_q queries over N_k keys with the queries at the end of the key sequence.
+ *   q, o, dout, dq   [B, H, N_q, head_dim]; k, v, dk, dv [B, H, N_k, head_dim]; dtype
+ *   lse              in: dense [B, H, N_q] float32 from fa_fwd_kv (-inf for rows without keys)
+ *   strides          NULL for dense arrays, else eight fa_strides for q, k, v, o, dout, dq, dk,
+ *                    dv in that order, under the rules of fa_fwd_kv.  Inputs may share rows
+ *                    (e.g. head stride 0 for k, v); the elements of each output must not
+ *                    overlap, so with shared key/value heads dk and dv hold one gradient per
+ *                    query head, which the caller sums.
+ *   workspace        at least fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim) bytes,
+ *                    16-byte aligned; contents on entry do not matter.
+ * A row without keys has dQ = 0; with N_q = 0, dK = dV = 0 (and q, o, dout, lse, dq may be
+ * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks and scale must be those of
+ * the forward call.  Errors as in fa_bwd and fa_fwd_kv. */
+fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
+                    void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
+                    int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                    int window_left, int window_right, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

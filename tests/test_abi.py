@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
-                            "fa_fwd_kv_workspace_size", "fa_fwd_kv",
+                            "fa_fwd_kv_workspace_size", "fa_fwd_kv", "fa_bwd_kv",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -221,3 +221,31 @@ def test_kv_empty_and_workspace_size(lib):
     ws = lib.fa_fwd_kv_workspace_size(1, 1, 1, 20000, 128)
     assert ws > 0 and ws % (129 * 4) == 0
     assert lib.fa_fwd_kv_workspace_size(64, 64, 4096, 4096, 64) == 0
+
+
+def bwd_kv(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, strides=None, ws=WS,
+           ws_bytes=1 << 24, nq=5, nk=300, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, strides, ws, ws_bytes, a["B"], a["H"],
+                         nq, nk, a["d"], a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"],
+                         None)
+
+
+def test_bwd_kv_rejections(lib):
+    assert bwd_kv(lib, d=96) == 3
+    assert bwd_kv(lib, nq=-1) == 2
+    assert bwd_kv(lib, wl=-3) == 5
+    assert bwd_kv(lib, lse=0) == 1
+    assert bwd_kv(lib, dk=0) == 1
+    assert bwd_kv(lib, ws=0) == 8
+    assert bwd_kv(lib, ws_bytes=lib.fa_bwd_workspace_size(2, 3, 5, 64) - 1) == 8
+    assert bwd_kv(lib, dq=Q + 4) == 6
+    assert bwd_kv(lib, dq=K) == 10
+    assert bwd_kv(lib, dv=WS) == 10
+    assert bwd_kv(lib, dk=DV) == 10
+    from exact_attention_125_amd import _lib
+    bad = (_lib.FaStrides * 8)(*([_lib.FaStrides(0, 0, 64)] * 7 + [_lib.FaStrides(0, 0, 4)]))
+    assert bwd_kv(lib, strides=bad) == 2
+    # nothing to do
+    assert bwd_kv(lib, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, nq=0, nk=0) == 0
+    assert bwd_kv(lib, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, B=0) == 0

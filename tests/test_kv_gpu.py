@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import LSE_TOL, O_TOL, say, to64, to_dev
+from gpu_util import GRAD_REL_L2, LSE_TOL, O_TOL, rel_l2, say, to64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +175,79 @@ def test_decode_workload_sampled(fa, w):
     torch.cuda.synchronize()
     heads = [(b, (5 * b + 3) % w.H) for b in range(w.B)] + [(w.B - 1, w.H - 1)]
     compare(o, lse, inp, w.softmax_scale, True, (-1, -1), w.dtype, w.name, heads=heads)
+
+
+# ---------------------------------------------------------------------------- backward
+def run_backward(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, layout="bhnd"):
+    """fa_fwd_kv then fa_bwd_kv on seeded inputs (dO drawn after q, k, v from its own seed);
+    gradients against the oracle's by relative L2 per tensor over all heads."""
+    import oracle
+    import torch
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed)
+    dout_in = W.cross_case(B, H, n_q, 1, d, dtype, seed + 1000)
+    scale = 1.0 / math.sqrt(d)
+    if layout == "bhnd":
+        q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], dout_in["q"]))
+    else:
+        q, k, v, do = (to_dev(t.transpose(1, 2).contiguous()).transpose(1, 2)
+                       for t in (inp["q"], inp["k"], inp["v"], dout_in["q"]))
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window)
+    torch.cuda.synchronize()
+    if layout != "bhnd":
+        assert dk.stride() == k.stride() and dq.stride() == q.stride()
+    rq, rk, rv = oracle.cross_backward_bh(inp["q64"], inp["k64"], inp["v64"], dout_in["q64"],
+                                          scale, causal, window)
+    floor = 1e-3 * float(np.linalg.norm(dout_in["q64"]))
+    errs = [rel_l2(to64(g), r, floor) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
+    say(f"bwd nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window} {layout}: "
+        f"rel L2 dq={errs[0]:.2e} dk={errs[1]:.2e} dv={errs[2]:.2e}")
+    for name, e in zip(("dq", "dk", "dv"), errs):
+        assert e <= GRAD_REL_L2, f"{name} rel L2 {e:.3e} > {GRAD_REL_L2}"
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(1, 300), (4, 1000), (100, 700), (300, 129), (130, 3000),
+                                     (257, 257)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_backward(fa, causal, window, n_q, n_k, d, dtype):
+    run_backward(fa, 2, 2, n_q, n_k, d, dtype, causal, window, seed=n_q * 7 + n_k)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(64, 1000), (3, 500)])
+def test_backward_strided(fa, n_q, n_k):
+    for causal in (False, True):
+        run_backward(fa, 2, 4, n_q, n_k, 128, "bf16", causal, (-1, -1), seed=77, layout="bnhd")
+
+
+def test_backward_rows_without_keys(fa):
+    import torch
+    dq, dk, dv = run_backward(fa, 1, 2, 300, 100, 64, "bf16", True, (-1, -1), seed=88)
+    assert torch.all(dq[:, :, :200] == 0)
+
+
+def test_backward_empty_sides(fa):
+    import torch
+    q = torch.randn(1, 2, 5, 64, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 2, 0, 64, device="cuda").to(torch.bfloat16)
+    o, lse = fa.fwd_kv(q, k, k, 0.125)
+    dq, _, _ = fa.bwd_kv(torch.ones_like(q), q, k, k, o, lse, 0.125)
+    q0 = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    k1 = torch.randn(1, 2, 40, 64, device="cuda").to(torch.bfloat16)
+    o0, lse0 = fa.fwd_kv(q0, k1, k1, 0.125)
+    _, dk, dv = fa.bwd_kv(q0, q0, k1, k1, o0, lse0, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_backward_deterministic(fa):
+    import torch
+    inp = W.cross_case(2, 2, 200, 900, 64, "bf16", seed=99)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    do = torch.ones_like(q)
+    o, lse = fa.fwd_kv(q, k, v, None, True)
+    g1 = fa.bwd_kv(do, q, k, v, o, lse, None, True)
+    g2 = fa.bwd_kv(do, q, k, v, o, lse, None, True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
