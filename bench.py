@@ -237,6 +237,8 @@ def main():
     w = W.BY_NAME[args.workload]
     if isinstance(w, W.DecodeWorkload):
         return bench_decode(args, w)
+    if isinstance(w, W.BlockWorkload):
+        return bench_block(args, w)
     backward = w.backward and not args.forward_only
 
     # CPU baseline first: the oracle's process pool forks before this process touches the GPU.
@@ -476,6 +478,92 @@ def bench_decode(args, w):
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("decode", w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_block(args, w):
+    """One training step of a query block over a longer key sequence: fa_fwd_kv then fa_bwd_kv
+    (the four-wave kernels), MFMA-bound; `value` is algorithmic TFLOP/s over wall time."""
+    import oracle
+    inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
+    g = W.cross_case(w.B, w.H, w.n_q, 1, w.d, w.dtype, w.seed + 1000)["q"]
+    pairs = w.B * w.H * oracle.cross_allowed_pairs(w.n_q, w.n_k, True)
+    fwd_flops, bwd_flops = 4.0 * w.d * pairs, 10.0 * w.d * pairs
+    cpu = None
+    if not args.no_cpu_baseline:   # the oracle on a bounded sample: the first heads' slices
+        n = args.cpu_sample_heads or 4
+        t0 = time.perf_counter()
+        for i in range(n):
+            b, h = divmod(i, w.H)
+            args_ = (inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h])
+            oracle.cross_forward(*args_, w.softmax_scale, True)
+            oracle.cross_backward(*args_, g.double().numpy()[b, h], w.softmax_scale, True)
+        secs = time.perf_counter() - t0
+        from oracle import pool
+        cpu = {"value": round(n * (fwd_flops + bwd_flops) / (w.B * w.H) / secs / 1e12, 6),
+               "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} of {w.B * w.H} (batch, head) slices of {w.name}, forward+backward, "
+                         f"float64 numpy materialising S and P, {secs:.2f} s wall, one process "
+                         f"({pool.blas_info()})"}
+    import torch
+    import exact_attention_125_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q, k, v, do = (t.to("cuda") for t in (inp["q"], inp["k"], inp["v"], g))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_f = torch.empty(max(fa.fwd_kv_workspace_size(w.B, w.H, w.n_q, w.n_k, w.d), 16),
+                       device="cuda", dtype=torch.uint8)
+    ws_b = torch.empty(max(fa.bwd_workspace_size(w.B, w.H, w.n_q, w.d), 16), device="cuda",
+                       dtype=torch.uint8)
+    state = {}
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f)
+        if ev:
+            ev[1].record()
+        fa.bwd_kv(do, q, k, v, o, state["lse"], w.softmax_scale, True, dq=dq, dk=dk, dv=dv,
+                  workspace=ws_b)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    b_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms = wall / args.steps * 1e3
+    fm, bm = sum(f_ms) / len(f_ms), sum(b_ms) / len(b_ms)
+    kernels = {"fwd_kv": {"ms": round(fm, 4), "median_ms": round(statistics.median(f_ms), 4),
+                          "tflops": round(fwd_flops / (fm * 1e-3) / 1e12, 2)},
+               "bwd_kv": {"ms": round(bm, 4), "median_ms": round(statistics.median(b_ms), 4),
+                          "tflops": round(bwd_flops / (bm * 1e-3) / 1e12, 2)}}
+    dom = "bwd_kv" if bm >= fm else "fwd_kv"
+    ach = kernels[dom]["tflops"]
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s on 1 MI355X, query block over a longer key "
+                  "sequence (fa_fwd_kv + fa_bwd_kv)",
+        "value": round((fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
+                   "head_dim": w.d, "causal": True, "pass": "fwd+bwd",
+                   "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
+        "kernels": kernels,
+        # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -79,11 +79,34 @@ class DecodeWorkload:
 DECODE_64 = DecodeWorkload("decode_b8h16q1k16384d64_bf16", 8, 16, 1, 16384, 64, "bf16", seed=7)
 DECODE_128 = DecodeWorkload("decode_b8h16q1k16384d128_bf16", 8, 16, 1, 16384, 128, "bf16", seed=8)
 DECODES = (DECODE_64, DECODE_128)
+
+
+@dataclass(frozen=True)
+class BlockWorkload:
+    """A training step of a block of n_q new queries over n_k keys (the block being the last
+    n_q positions: a cache of n_k - n_q keys plus the block itself), causal, forward and
+    backward through fa_fwd_kv / fa_bwd_kv."""
+    name: str
+    B: int
+    H: int
+    n_q: int
+    n_k: int
+    d: int
+    dtype: str
+    seed: int
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# the training workload's heads, a 1024-query block over 4096 keys
+BLOCK = BlockWorkload("block_b8h16q1024k4096d64_bf16", 8, 16, 1024, 4096, 64, "bf16", seed=9)
 # The training step over a padded batch: sample lengths drawn by draw_seqlens (the pages fix
 # no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
 VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
                   backward=True, padded=True)
-BY_NAME = {w.name: w for w in ALL + (VARLEN,) + DECODES}
+BY_NAME = {w.name: w for w in ALL + (VARLEN,) + DECODES + (BLOCK,)}
 
 
 def draw_f32(shape, seed: int, count: int):
