@@ -28,7 +28,8 @@ Modules
   padded     padded batches (per-sample lengths): the definition over each
              sample's own rows, zeros past them — pinned
   cross      N_q queries over N_k keys, the queries being the last N_q positions
-             (decode steps, a new block over a cache) — pinned
+             (decode steps, a new block over a cache), optional ALiBi distance
+             penalty, forward and backward — pinned
   pool       a process pool over (batch, head) for timing the oracle on a
              bounded sample
 
@@ -41,8 +42,8 @@ from .attention import (allowed_mask, attention_forward, attention_backward,
 from .online import attention_forward_online
 from .brute import attention_forward_brute
 from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
-from .cross import (cross_allowed_mask, cross_allowed_pairs, cross_backward, cross_backward_bh,
-                    cross_forward, cross_forward_bh)
+from .cross import (alibi_bias, cross_allowed_mask, cross_allowed_pairs, cross_backward,
+                    cross_backward_bh, cross_forward, cross_forward_bh)
 
 __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
@@ -50,5 +51,5 @@ __all__ = [
     "attention_forward_online", "attention_forward_brute",
     "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
-    "cross_backward", "cross_backward_bh",
+    "cross_backward", "cross_backward_bh", "alibi_bias",
 ]

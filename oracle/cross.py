@@ -19,6 +19,14 @@ Reading where the pages are silent (they never define a mask for N_q != N_k):
     causal prefix.  With N_q = N_k this is ``attention`` itself.
   * a row with no allowed key (N_q > N_k under causal, or a window that misses every key) has
     O = 0 and LSE = -inf.
+
+ALiBi: [A100] §4.2 lists ``alibi_slopes`` ("linear bias coefficients") among the switches of
+its attention call and [FA37] §6 names ALiBi as the relative position encoding for very long
+sequences; neither page writes the bias out.  Reading: head h adds -slope_h * |p_i - j| to
+the scaled score of query i and key j (a penalty linear in the distance between their
+positions), before the mask and the softmax:
+      S_ij = scale * <q_i, k_j> - slope * |p_i - j|
+With slope = 0 this is the definition above.
 """
 from __future__ import annotations
 
@@ -45,17 +53,33 @@ def cross_allowed_pairs(n_q: int, n_k: int, causal: bool, window=(-1, -1)) -> in
     return int(cross_allowed_mask(n_q, n_k, causal, window).sum())
 
 
-def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1)):
+def alibi_bias(n_q: int, n_k: int, slope: float) -> np.ndarray:
+    """[n_q, n_k] float64: -slope * |p_i - j| with p_i = i + (n_k - n_q)."""
+    p = (np.arange(n_q, dtype=np.float64) + (n_k - n_q))[:, None]
+    j = np.arange(n_k, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(p - j)
+
+
+def _scores(q, k, scale, causal, window, slope):
+    ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
+    s = scale * (q @ k.T)
+    if slope:
+        s = s + alibi_bias(q.shape[0], k.shape[0], slope)
+    return np.where(ok, s, -np.inf)
+
+
+def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1),
+                  slope: float = 0.0):
     """One (batch, head): q float64 [N_q, d], k, v [N_k, d] -> (O [N_q, d], LSE [N_q]).
 
-    S = scale * Q K^T is materialised in full, masked with -inf, and put through the
-    max-shifted softmax; O = P V, LSE = rowmax + ln(rowsum).
+    S = scale * Q K^T (minus the ALiBi distance penalty when slope != 0) is materialised in
+    full, masked with -inf, and put through the max-shifted softmax; O = P V,
+    LSE = rowmax + ln(rowsum).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
-    s = np.where(ok, scale * (q @ k.T), -np.inf)
+    s = _scores(q, k, scale, causal, window, slope)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])     # exp(-inf) = 0 at hidden entries
@@ -67,18 +91,21 @@ def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1)):
     return o, lse
 
 
-def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1)):
-    """q [B, H, N_q, d], k, v [B, H, N_k, d] -> (O [B, H, N_q, d], LSE [B, H, N_q])."""
+def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1), slopes=None):
+    """q [B, H, N_q, d], k, v [B, H, N_k, d] -> (O [B, H, N_q, d], LSE [B, H, N_q]);
+    ``slopes``: the H ALiBi slopes, or None."""
     B, H, n_q, _ = q.shape
     o = np.empty((B, H, n_q, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, n_q), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window)
+            o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window,
+                                               0.0 if slopes is None else float(slopes[h]))
     return o, lse
 
 
-def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, -1)):
+def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, -1),
+                   slope: float = 0.0):
     """One (batch, head): gradients (dQ [N_q, d], dK, dV [N_k, d]) of <dO, O> for
     ``cross_forward``, the ordinary derivative of that definition:
 
@@ -86,14 +113,13 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
         dQ = scale * dS K,   dK = scale * dS^T Q
 
     with P recomputed from Q and K; rows without a visible key have P = 0 and contribute
-    nothing.
+    nothing.  The ALiBi penalty does not depend on Q or K, so it enters only through P.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
-    s = np.where(ok, scale * (q @ k.T), -np.inf)
+    s = _scores(q, k, scale, causal, window, slope)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])
@@ -104,12 +130,13 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
     return scale * (ds @ k), scale * (ds.T @ q), dv
 
 
-def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1)):
+def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=None):
     """[B, H, N_q, d] q and dO, [B, H, N_k, d] k and v -> (dQ, dK, dV), one head at a time."""
     B, H = q.shape[:2]
     dq, dk, dv = (np.empty(t.shape, dtype=np.float64) for t in (q, k, v))
     for b in range(B):
         for h in range(H):
-            dq[b, h], dk[b, h], dv[b, h] = cross_backward(q[b, h], k[b, h], v[b, h], do[b, h],
-                                                          scale, causal, window)
+            dq[b, h], dk[b, h], dv[b, h] = cross_backward(
+                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, window,
+                0.0 if slopes is None else float(slopes[h]))
     return dq, dk, dv

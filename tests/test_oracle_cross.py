@@ -220,3 +220,109 @@ def test_backward_invariants():
     np.testing.assert_allclose(dv.sum(axis=0), do[live].sum(axis=0), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
     assert np.all(dq[~live] == 0.0)
+
+
+# ---------------------------------------------------------------------------- ALiBi
+def _brute_alibi(q, k, v, scale, slope, causal, window):
+    n_q, n_k = len(q), len(k)
+    left, right = window
+    out, lse = [], []
+    for i in range(n_q):
+        pos = i + n_k - n_q
+        js = [j for j in range(n_k)
+              if not (causal and j > pos) and not (left >= 0 and j < pos - left)
+              and not (right >= 0 and j > pos + right)]
+        if not js:
+            out.append([0.0] * len(v[0]))
+            lse.append(-math.inf)
+            continue
+        e = {j: math.exp(scale * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j]))
+                         - slope * abs(pos - j)) for j in js}
+        z = math.fsum(e.values())
+        out.append([math.fsum(e[j] / z * float(v[j][c]) for j in js) for c in range(len(v[0]))])
+        lse.append(math.log(z))
+    return np.array(out), np.array(lse)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(1, 9), (5, 12), (9, 9), (12, 5)])
+def test_alibi_brute_force(causal, window, n_q, n_k):
+    q, k, v = _qkv(n_q, n_k, 4, seed=3 * n_q + n_k)
+    o, lse = oracle.cross_forward(q, k, v, 0.5, causal, window, slope=0.37)
+    bo, bl = _brute_alibi(q, k, v, 0.5, 0.37, causal, window)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(3, 8), (8, 8), (8, 5)])
+def test_alibi_torch_float_mask(n_q, n_k):
+    """torch CPU float64 SDPA with an additive float mask: -slope |p - j| on visible pairs,
+    -inf elsewhere (torch adds a float attn_mask to the scaled scores)."""
+    q, k, v = _qkv(n_q, n_k, 5, seed=n_q * 11 + n_k)
+    pos = torch.arange(n_q, dtype=torch.float64)[:, None] + (n_k - n_q)
+    j = torch.arange(n_k, dtype=torch.float64)[None, :]
+    bias = -0.25 * (pos - j).abs()
+    bias = bias.masked_fill(j > pos, float("-inf"))
+    live = torch.isfinite(bias).any(dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=bias[None], scale=0.6)[0].numpy()
+    o, _ = oracle.cross_forward(q, k, v, 0.6, causal=True, slope=0.25)
+    np.testing.assert_allclose(o[live.numpy()], ref[live.numpy()], rtol=1e-12, atol=1e-12)
+
+
+def test_alibi_closed_form_geometric():
+    """Q = 0, one query at the end of n keys, causal: the weights are e^{-slope d} over the
+    distances d = 0 .. n-1, so LSE = ln((1 - e^{-slope n}) / (1 - e^{-slope})) and O is the
+    e^{-slope d}-weighted mean of V."""
+    n, slope = 50, 0.3
+    _, k, v = _qkv(1, n, 3, seed=4)
+    o, lse = oracle.cross_forward(np.zeros((1, 3)), k, v, 1.0, causal=True, slope=slope)
+    z = (1 - math.exp(-slope * n)) / (1 - math.exp(-slope))
+    assert abs(lse[0] - math.log(z)) < 1e-13
+    w = np.exp(-slope * (n - 1 - np.arange(n)))
+    np.testing.assert_allclose(o[0], (w[:, None] * v).sum(axis=0) / w.sum(), rtol=1e-12)
+
+
+def test_alibi_zero_slope_is_plain():
+    q, k, v = _qkv(4, 9, 3, seed=6)
+    a = oracle.cross_forward(q, k, v, 0.5, True, slope=0.0)
+    b = oracle.cross_forward(q, k, v, 0.5, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (False, (-1, -1)), (False, (2, 3))])
+def test_alibi_backward_central_differences(causal, window):
+    rng = np.random.default_rng(31)
+    q, k, v, do = (rng.standard_normal((r, 3)) for r in (4, 6, 6, 4))
+    dq, dk, dv = oracle.cross_backward(q, k, v, do, 0.7, causal, window, slope=0.45)
+    h = 1e-6
+
+    def loss(q_, k_, v_):
+        return float((oracle.cross_forward(q_, k_, v_, 0.7, causal, window, slope=0.45)[0]
+                      * do).sum())
+
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[which], args_m[which] = plus, minus
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+def test_mutant_alibi_sign_fails_closed_form():
+    """A bias of the wrong sign (+slope |p - j|) is a plausible mistake; the geometric closed
+    form rejects it."""
+    n, slope = 20, 0.3
+    ok = np.ones((1, n), dtype=bool)
+    s = np.where(ok, +slope * np.abs((n - 1) - np.arange(n))[None, :], -np.inf)
+    lse_wrong = float(np.log(np.exp(s).sum()))
+    z = (1 - math.exp(-slope * n)) / (1 - math.exp(-slope))
+    assert abs(lse_wrong - math.log(z)) > 1.0
