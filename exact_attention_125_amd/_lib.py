@@ -40,10 +40,10 @@ SIGNATURES = {
     "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
                            _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
-    "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S,
-                       _P]),
+    "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P,
+                       _S, _P]),
     "fa_bwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F,
-                       _I, _I, _I, _P]),
+                       _I, _I, _I, _P, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -212,13 +212,25 @@ def _check_kv_tensors(q, k, v):
         raise ValueError(f"k, v must be [B, H, N_k, d] to match q {tuple(q.shape)}")
 
 
+def _check_slopes(slopes, q):
+    import torch
+    if slopes is None:
+        return
+    if not slopes.is_cuda or slopes.device != q.device or slopes.dtype != torch.float32:
+        raise ValueError("alibi_slopes must be a float32 tensor on the device of q")
+    if slopes.dim() != 1 or slopes.shape[0] != q.shape[1] or not slopes.is_contiguous():
+        raise ValueError("alibi_slopes must be a contiguous [heads] tensor")
+
+
 def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None,
-           return_lse=True, workspace=None):
+           return_lse=True, workspace=None, alibi_slopes=None):
     """``fa_fwd_kv``: q [B, H, N_q, d] over k, v [B, H, N_k, d], the queries being the last N_q
     key positions.  Any strides with a contiguous last dimension (for example transposed
-    views of [B, N, H, d] memory).  Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
+    views of [B, N, H, d] memory).  ``alibi_slopes``: float32 [H] on the device, or None.
+    Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
     import torch
     _check_kv_tensors(q, k, v)
+    _check_slopes(alibi_slopes, q)
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
@@ -230,17 +242,18 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k, d,
-                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(workspace),
-                          ws_bytes, _stream(q.device)))
+                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
+                          _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, lse
 
 
 def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
-           dq=None, dk=None, dv=None, workspace=None):
+           dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
     """``fa_bwd_kv``: gradients ``(dq, dk, dv)`` of ``fwd_kv``.  Any strides with a contiguous
     last dimension; new gradients take the strides of q, k, v."""
     import torch
     _check_kv_tensors(q, k, v)
+    _check_slopes(alibi_slopes, q)
     for t in (o, dout):
         if t.dtype != q.dtype or tuple(t.shape) != tuple(q.shape) or t.stride(-1) != 1:
             raise ValueError("o and dout must match q")
@@ -260,5 +273,6 @@ def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=
     _check(_lib.fa_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), st, _ptr(workspace),
                           workspace.numel() * workspace.element_size(), B, H, n_q, n_k, d,
-                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _stream(q.device)))
+                          _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
+                          _stream(q.device)))
     return dq, dk, dv

@@ -266,8 +266,8 @@ size_t fa_fwd_kv_workspace_size(int batch, int heads, int seqlen_q, int seqlen_k
 fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
-                    int window_left, int window_right, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    int window_left, int window_right, const float* alibi_slopes,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -309,6 +309,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   if ((lse && (const void*)lse == o) ||
       (outs[2] && ((const void*)outs[2] == o || (const void*)outs[2] == lse)))
     return FA_ERR_ALIAS;
+  if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
+  for (const void* out : outs)
+    if (alibi_slopes && out == (const void*)alibi_slopes) return FA_ERR_ALIAS;
 
   p.q = q;
   p.k = k;
@@ -316,6 +319,7 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   p.o = o;
   p.lse = lse;
   p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.slopes = alibi_slopes;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;
@@ -337,7 +341,8 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
-                    int window_left, int window_right, void* stream) {
+                    int window_left, int window_right, const float* alibi_slopes,
+                    void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -380,6 +385,9 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
       if (in && out == in) return FA_ERR_ALIAS;
   }
   if ((dq && (dq == dk || dq == dv)) || (dk && dk == dv)) return FA_ERR_ALIAS;
+  if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
+  for (void* out : outs)
+    if (alibi_slopes && out == (const void*)alibi_slopes) return FA_ERR_ALIAS;
 
   p.q = q;
   p.k = k;
@@ -391,6 +399,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   p.dk = dk;
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
+  p.slopes = alibi_slopes;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;

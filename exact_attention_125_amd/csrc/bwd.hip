@@ -43,6 +43,7 @@ struct BwdArgs {
   char* dv;
   float* stats;   // per-query statistics in 32-query blocks (stat_index)
   const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
+  const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
   // batch / head strides (bytes) and row strides (bytes) of q, k, v, o, dout, dq, dk, dv
   long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs, g_bs, g_hs;
   long long dq_bs, dq_hs, dk_bs, dk_hs, dv_bs, dv_hs;
@@ -131,7 +132,8 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
 constexpr int kKvRows = 128;   // keys per workgroup (32 per wave)
 constexpr int kQStep = 32;     // queries per step
 
-template <int D, bool BF16>
+// ALIBI: P carries the forward's ALiBi penalty, 2^(... - slope log2(e) |p - j|)
+template <int D, bool BF16, bool ALIBI>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kQStep * kRowBytes;    // one Q or dO tile
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const auto rk = rows_rsrc(a.k + b * a.k_bs + h * a.k_hs, nk, a.k_rs, kRowBytes);
   const auto rv = rows_rsrc(a.v + b * a.v_bs + h * a.v_hs, nk, a.v_rs, kRowBytes);
   const auto rg = rows_rsrc(a.dout + b * a.g_bs + h * a.g_hs, n, a.g_rs, kRowBytes);
+  const float b2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
 
   // K^T and V^T as B operands: lane holds key (k0 + l32), head-dim chunk 2 ks + hi.
   const int k_first = kt * kKvRows;
@@ -261,7 +264,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e;
-        float pe = exp2_fast(__builtin_fmaf(sc[i], c, c * l2[e]));
+        float x = __builtin_fmaf(sc[i], c, c * l2[e]);
+        if constexpr (ALIBI)
+          x = __builtin_fmaf(-b2, __builtin_fabsf((float)(q0 + 8 * g + 4 * hi + e + off - key)), x);
+        float pe = exp2_fast(x);
         if (!full) {
           const int qq = q0 + 8 * g + 4 * hi + e;
           pe = (qq < n && mk.visible(qq + off, key)) ? pe : 0.f;
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;   // queries per workgroup (32 per wave)
 constexpr int kKStep = 64;     // keys per K/V tile
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool ALIBI>
 __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kKStep * kRowBytes;
@@ -348,6 +354,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const auto rk = rows_rsrc(a.k + b * a.k_bs + h * a.k_hs, nk, a.k_rs, kRowBytes);
   const auto rv = rows_rsrc(a.v + b * a.v_bs + h * a.v_hs, nk, a.v_rs, kRowBytes);
   const auto rg = rows_rsrc(a.dout + b * a.g_bs + h * a.g_hs, n, a.g_rs, kRowBytes);
+  const float b2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
 
   const int qi = q0 + 32 * wave + l32;
   i16x8 qreg[kKs], greg[kKs];
@@ -434,7 +441,12 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
         float d2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float p = exp2_fast(__builtin_fmaf(sc[mb][i + e], c, cm));
+          float x = __builtin_fmaf(sc[mb][i + e], c, cm);
+          if constexpr (ALIBI) {
+            const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
+            x = __builtin_fmaf(-b2, __builtin_fabsf((float)(qi + off - j)), x);
+          }
+          float p = exp2_fast(x);
           if (!full) {
             const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
             p = (row_ok && mk.visible(qi + off, j)) ? p : 0.f;
@@ -502,6 +514,7 @@ BwdArgs make_args(const BwdParams& p) {
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
   a.seqlens = p.seqlens;
+  a.slopes = nullptr;
   const long long row = (long long)p.D * 2, head = (long long)p.N * row, batch = p.H * head;
   a.q_bs = a.k_bs = a.v_bs = a.o_bs = a.g_bs = a.dq_bs = a.dk_bs = a.dv_bs = batch;
   a.q_hs = a.k_hs = a.v_hs = a.o_hs = a.g_hs = a.dq_hs = a.dk_hs = a.dv_hs = head;
@@ -539,16 +552,16 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
     if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDkDv) {
     a.n_tiles = (a.n + kKvRows - 1) / kKvRows;
-    hipLaunchKernelGGL((dkdv_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256),
-                       0, stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, BF16, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
+                       dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   if ((stages & kBwdDq) && main_kernels) {
     if (hipError_t e = launch_dq_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDq) {
     a.n_tiles = (a.n + kDqRows - 1) / kDqRows;
-    hipLaunchKernelGGL((dq_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BF16, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
+                       dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -569,6 +582,7 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
   a.seqlens = nullptr;
+  a.slopes = p.slopes;
   a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
   a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);
   a.v_bs = p.sv.b * e, a.v_hs = p.sv.h * e, a.v_rs = (int)(p.sv.r * e);
@@ -598,14 +612,20 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   }
   if (p.Nk > 0) {
     a.n_tiles = (p.Nk + kKvRows - 1) / kKvRows;
-    hipLaunchKernelGGL((dkdv_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256),
-                       0, stream, a);
+    const dim3 grid((unsigned)((long)a.n_bh * a.n_tiles));
+    if (p.slopes != nullptr)
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
     if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   }
   if (p.Nq == 0) return hipSuccess;
   a.n_tiles = (p.Nq + kDqRows - 1) / kDqRows;
-  hipLaunchKernelGGL((dq_kernel<D, BF16>), dim3((unsigned)((long)a.n_bh * a.n_tiles)), dim3(256), 0,
-                     stream, a);
+  const dim3 grid((unsigned)((long)a.n_bh * a.n_tiles));
+  if (p.slopes != nullptr)
+    hipLaunchKernelGGL((dq_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

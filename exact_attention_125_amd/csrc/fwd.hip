@@ -70,6 +70,7 @@ struct FwdArgs {
   int split_tiles;  // key tiles per split
   float* po;      // n_split > 1: normalised partial O, fp32 [n_split, B*H, nq, D]
   float* plse;    //              and its natural-log LSE [n_split, B*H, nq]
+  const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
   float c;        // |softmax_scale| * log2(e)
   unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
   int causal, wl, wr;
@@ -82,7 +83,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
   return make_rsrc(base, rows > 0 ? (rows - 1) * rs + row_bytes : 0);
 }
 
-template <int D, bool BF16, int WAVES, int QB>
+// ALIBI: every score gets the ALiBi penalty -slope_h |p - j| (p the query's key position), in
+// the exponent domain: s <- s c - slope log2(e) |p - j| right after the product, after which
+// the tile works with a unit factor in place of c.
+template <int D, bool BF16, int WAVES, int QB, bool ALIBI>
 __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kBr = 32 * QB * WAVES;
@@ -164,7 +168,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     }
   };
 
-  const float c = a.c;
+  const float c = ALIBI ? 1.f : a.c;   // the ALIBI instances scale the scores in place
+  const float b2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
   const float NEG_INF = -__builtin_inff();
   float m_ref[QB];      // reference of the exponent per query, base-2 units
   float l_run[QB];      // sum of 2^(s*c - m_ref) over this lane's keys
@@ -208,6 +213,20 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[mb][qb] = mfma32x32x16<BF16>(kop, qreg[qb][ks], s[mb][qb]);
       }
+
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qpos = wq0 + 32 * qb + l32 + off;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            s[mb][qb][i] = __builtin_fmaf(s[mb][qb][i], a.c, -b2 * __builtin_fabsf((float)(qpos - j)));
+          }
+      }
+    }
 
     if constexpr (MASKED) {
 #pragma unroll
@@ -363,8 +382,12 @@ hipError_t launch_args(FwdArgs& a, hipStream_t stream) {
   constexpr int kBr = 32 * QB * WAVES;
   a.n_qt = (a.nq + kBr - 1) / kBr;
   const long blocks = (long)a.n_bh * a.n_qt * a.n_split;
-  hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
-                     stream, a);
+  if (a.slopes != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, true>), dim3((unsigned)blocks),
+                       dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, false>), dim3((unsigned)blocks),
+                       dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -395,6 +418,7 @@ hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
   a.n_split = 1;
   a.split_tiles = (p.N + kBc - 1) / kBc;
   a.po = a.plse = nullptr;
+  a.slopes = nullptr;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   return launch_args<D, BF16, WAVES, QB>(a, stream);
 }
@@ -456,6 +480,7 @@ hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t
   a.split_tiles = plan.split_keys / kBc;
   a.po = p.ws;
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * p.D : nullptr;
+  a.slopes = p.slopes;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   if (p.D == 64)
     return p.bf16 ? launch_args<64, true, 4, 1>(a, stream) : launch_args<64, false, 4, 1>(a, stream);

@@ -47,6 +47,7 @@ struct DecArgs {
   int nq, nk, off, n_h, n_bh, n_split, split_keys;
   float* po;      // n_split > 1: partial O [n_split, B*H, nq, D] and LSE [n_split, B*H, nq]
   float* plse;
+  const float* slopes;   // ALiBi slopes [heads] (device), or null
   float c;        // softmax_scale * log2(e), signed
   int causal, wl, wr;
 };
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   const int b = bh / a.n_h, h = bh - b * a.n_h;
   const int nq = a.nq, nk = a.nk, off = a.off;
   const float NEG_INF = -__builtin_inff();
+  const float b2 = a.slopes != nullptr ? a.slopes[h] * kLog2e : 0.f;   // ALiBi, base 2
 
   // keys of this split that some query can see
   const Mask mk{nk, a.causal, a.wl, a.wr};
@@ -163,8 +165,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         for (int e = 1; e < 8; ++e) part = __builtin_fmaf(qf[qi][e], kf[e], part);
         s[qi][u] = group_sum<G>(part);
       }
+      // ALiBi penalty -slope |p - j| (zero without slopes)
+      const int r = r0 + u * GROUPS + grp;
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi)
+        s[qi][u] = __builtin_fmaf(-b2, __builtin_fabsf((float)(qi + off - r)), s[qi][u]);
       if constexpr (MASKED) {
-        const int r = r0 + u * GROUPS + grp;
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi)
           s[qi][u] = (r < hi && mk.visible(qi + off, r)) ? s[qi][u] : NEG_INF;
@@ -368,6 +374,7 @@ hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stre
   a.split_keys = plan.split_keys;
   a.po = p.ws;
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * D : nullptr;
+  a.slopes = p.slopes;
   a.c = (float)((double)p.scale * 1.4426950408889634);
   a.causal = p.causal;
   a.wl = p.window_left;

@@ -59,6 +59,7 @@ struct KvParams {
   void* o;
   float* lse;          // [B, H, N_q] dense, may be null
   float* ws;           // partial results of key splits (KvPlan::ws_bytes), null if none
+  const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk, D;
   bool bf16;
@@ -105,6 +106,7 @@ struct BwdKvParams {
   void* dk;
   void* dv;
   float* stats;        // workspace, as for BwdParams with N = N_q
+  const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Strides sq, sk, sv, so, sg, sdq, sdk, sdv;
   int B, H, Nq, Nk, D;
   bool bf16;

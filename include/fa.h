@@ -192,7 +192,16 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * NULL then).  Other conventions and errors as in fa_fwd; FA_ERR_BAD_SHAPE also reports a
  * stride outside the rules above.  Results depend on the shape only (not on the device).
  * Precision: with N_q <= 4 the probabilities stay in float32 for the P V sum (no rounding to
- * the input type); otherwise as in fa_fwd. */
+ * the input type); otherwise as in fa_fwd.
+ *
+ * ALiBi: alibi_slopes is a device float32 array [heads] (4-byte aligned, not an output), or
+ * NULL for none.  Head h then subtracts slope_h * |p_i - j| from every scaled score before
+ * the mask and the softmax: S_ij = softmax_scale * <Q_i, K_j> - slope_h * |p_i - j|, a penalty
+ * linear in the distance between the query's and the key's positions.  These are the "linear
+ * bias coefficients" the page "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型（含A100环境配置）"
+ * lists as alibi_slopes in §4.2 (and the ALiBi relative position encoding "Flash Attention
+ * 3.7 核心原理与实战" names for very long sequences in §6).  The values are read by the kernels
+ * and not checked: they must be finite.  fa_bwd_kv takes the same slopes. */
 typedef struct fa_strides {
   long long batch, head, row;
 } fa_strides;
@@ -202,8 +211,8 @@ size_t fa_fwd_kv_workspace_size(int batch, int heads, int seqlen_q, int seqlen_k
 fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
-                    int window_left, int window_right, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    int window_left, int window_right, const float* alibi_slopes,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass of fa_fwd_kv (by recomputation, as fa_bwd): gradients of sum(dout * o) for
  * N_q queries over N_k keys with the queries at the end of the key sequence.
@@ -217,13 +226,14 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
  *   workspace        at least fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim) bytes,
  *                    16-byte aligned; contents on entry do not matter.
  * A row without keys has dQ = 0; with N_q = 0, dK = dV = 0 (and q, o, dout, lse, dq may be
- * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks and scale must be those of
- * the forward call.  Errors as in fa_bwd and fa_fwd_kv. */
+ * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale and alibi_slopes
+ * must be those of the forward call.  Errors as in fa_bwd and fa_fwd_kv. */
 fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
-                    int window_left, int window_right, void* stream);
+                    int window_left, int window_right, const float* alibi_slopes,
+                    void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

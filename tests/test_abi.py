@@ -172,7 +172,8 @@ def fwd_kv(lib, q=Q, k=K, v=V, o=O, lse=L, strides=None, nq=5, nk=300, ws=WS, ws
            **kw):
     a = dict(GOOD, **kw)
     return lib.fa_fwd_kv(q, k, v, o, lse, strides, a["B"], a["H"], nq, nk, a["d"], a["dtype"],
-                         a["scale"], a["causal"], a["wl"], a["wr"], ws, ws_bytes, None)
+                         a["scale"], a["causal"], a["wl"], a["wr"], a.get("slopes"), ws,
+                         ws_bytes, None)
 
 
 def test_kv_rejections(lib):
@@ -192,6 +193,9 @@ def test_kv_rejections(lib):
     assert fwd_kv(lib, o=K) == 10
     assert fwd_kv(lib, lse=Q) == 10
     assert fwd_kv(lib, lse=O) == 10
+    assert fwd_kv(lib, slopes=SL + 2) == 6          # float32 slopes: 4-byte aligned
+    assert fwd_kv(lib, slopes=O) == 10              # not an output
+    assert fwd_kv(lib, slopes=L) == 10
     # a plan with key splits needs its workspace
     need = lib.fa_fwd_kv_workspace_size(1, 1, 1, 20000, 64)
     assert need > 0
@@ -228,7 +232,7 @@ def bwd_kv(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, strides=N
     a = dict(GOOD, **kw)
     return lib.fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, strides, ws, ws_bytes, a["B"], a["H"],
                          nq, nk, a["d"], a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"],
-                         None)
+                         a.get("slopes"), None)
 
 
 def test_bwd_kv_rejections(lib):
@@ -243,6 +247,8 @@ def test_bwd_kv_rejections(lib):
     assert bwd_kv(lib, dq=K) == 10
     assert bwd_kv(lib, dv=WS) == 10
     assert bwd_kv(lib, dk=DV) == 10
+    assert bwd_kv(lib, slopes=SL + 1) == 6
+    assert bwd_kv(lib, slopes=DQ) == 10
     from exact_attention_125_amd import _lib
     bad = (_lib.FaStrides * 8)(*([_lib.FaStrides(0, 0, 64)] * 7 + [_lib.FaStrides(0, 0, 4)]))
     assert bwd_kv(lib, strides=bad) == 2

@@ -23,7 +23,7 @@ def fa():
     return fa
 
 
-def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None):
+def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None, slopes=None):
     import oracle
     q64, k64, v64 = inp["q64"], inp["k64"], inp["v64"]
     B, H = q64.shape[:2]
@@ -32,7 +32,9 @@ def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None):
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     worst_o = worst_l = 0.0
     for b, h in heads:
-        ro, rl = oracle.cross_forward(q64[b, h], k64[b, h], v64[b, h], scale, causal, window)
+        slope = 0.0 if slopes is None else float(slopes[h])
+        ro, rl = oracle.cross_forward(q64[b, h], k64[b, h], v64[b, h], scale, causal, window,
+                                      slope)
         empty = np.isneginf(rl)
         assert np.array_equal(np.isneginf(l64[b, h]), empty), f"{label}: rows without keys differ"
         assert np.all(o64[b, h][empty] == 0.0), f"{label}: O of a row without keys is not 0"
@@ -44,7 +46,8 @@ def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None):
     assert worst_l <= LSE_TOL, f"{label}: max|dLSE| {worst_l:.3e} > {LSE_TOL}"
 
 
-def run_case(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, scale=None, layout="bhnd"):
+def run_case(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, scale=None, layout="bhnd",
+             slopes=None):
     import torch
     inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -54,7 +57,8 @@ def run_case(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, scale=None, lay
         q, k, v = (to_dev(inp[n].transpose(1, 2).contiguous()).transpose(1, 2)
                    for n in ("q", "k", "v"))
         assert k.stride(1) == d and k.stride(2) == H * d   # rows H heads apart
-    o, lse = fa.fwd_kv(q, k, v, scale, causal, window)
+    sl = None if slopes is None else torch.tensor(slopes, dtype=torch.float32, device="cuda")
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window, alibi_slopes=sl)
     torch.cuda.synchronize()
     if layout != "bhnd" and n_q > 1:   # a length-1 dimension makes any view contiguous
         assert not q.is_contiguous() and o.stride() == q.stride()
@@ -178,7 +182,7 @@ def test_decode_workload_sampled(fa, w):
 
 
 # ---------------------------------------------------------------------------- backward
-def run_backward(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, layout="bhnd"):
+def run_backward(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, layout="bhnd", slopes=None):
     """fa_fwd_kv then fa_bwd_kv on seeded inputs (dO drawn after q, k, v from its own seed);
     gradients against the oracle's by relative L2 per tensor over all heads."""
     import oracle
@@ -191,13 +195,14 @@ def run_backward(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, layout="bhn
     else:
         q, k, v, do = (to_dev(t.transpose(1, 2).contiguous()).transpose(1, 2)
                        for t in (inp["q"], inp["k"], inp["v"], dout_in["q"]))
-    o, lse = fa.fwd_kv(q, k, v, scale, causal, window)
-    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window)
+    sl = None if slopes is None else torch.tensor(slopes, dtype=torch.float32, device="cuda")
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window, alibi_slopes=sl)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window, alibi_slopes=sl)
     torch.cuda.synchronize()
     if layout != "bhnd":
         assert dk.stride() == k.stride() and dq.stride() == q.stride()
     rq, rk, rv = oracle.cross_backward_bh(inp["q64"], inp["k64"], inp["v64"], dout_in["q64"],
-                                          scale, causal, window)
+                                          scale, causal, window, slopes)
     floor = 1e-3 * float(np.linalg.norm(dout_in["q64"]))
     errs = [rel_l2(to64(g), r, floor) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
     say(f"bwd nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window} {layout}: "
@@ -251,3 +256,47 @@ def test_backward_deterministic(fa):
     g2 = fa.bwd_kv(do, q, k, v, o, lse, None, True)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+# ---------------------------------------------------------------------------- ALiBi
+def alibi_slopes(H):
+    """The geometric slopes 2^(-8 h / H), h = 1 .. H, and one steep slope first."""
+    return [0.5] + [2.0 ** (-8.0 * h / H) for h in range(2, H + 1)]
+
+
+ALIBI_MASKS = [(False, (-1, -1)), (True, (-1, -1)), (True, (300, 0)), (False, (100, 40))]
+
+
+@pytest.mark.parametrize("causal,window", ALIBI_MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(1, 77), (3, 4099), (1, 20000), (100, 700), (300, 129),
+                                     (128, 8192), (257, 257)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_alibi_forward(fa, causal, window, n_q, n_k, d, dtype):
+    sl = alibi_slopes(4)
+    o, lse, inp, scale = run_case(fa, 1, 4, n_q, n_k, d, dtype, causal, window, seed=n_q + 3 * n_k,
+                                  slopes=sl)
+    compare(o, lse, inp, scale, causal, window, dtype,
+            f"alibi nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}", slopes=sl)
+
+
+@pytest.mark.parametrize("causal,window", ALIBI_MASKS)
+@pytest.mark.parametrize("n_q,n_k", [(1, 300), (100, 700), (300, 129), (257, 257)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_alibi_backward(fa, causal, window, n_q, n_k, d, dtype):
+    run_backward(fa, 1, 4, n_q, n_k, d, dtype, causal, window, seed=5 * n_q + n_k,
+                 slopes=alibi_slopes(4))
+
+
+def test_alibi_zero_slopes_match_no_alibi(fa):
+    """All-zero slopes go through the ALiBi instances and must give the plain results, up to
+    rounding: those instances scale the scores before taking the row maximum, so the
+    reference of the exponent (and with it the rounding of P) may differ."""
+    import torch
+    inp = W.cross_case(1, 2, 200, 900, 64, "bf16", seed=61)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    zero = torch.zeros(2, dtype=torch.float32, device="cuda")
+    a = fa.fwd_kv(q, k, v, None, True, alibi_slopes=zero)
+    b = fa.fwd_kv(q, k, v, None, True)
+    torch.cuda.synchronize()
+    assert float((a[0].float() - b[0].float()).abs().max()) <= O_TOL["bf16"]
+    assert float((a[1] - b[1]).abs().max()) <= 1e-5
