@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward kernel alone (default: forward + backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--alibi", action="store_true",
+                    help="decode and block workloads: ALiBi slopes 2^(-8 h / H), h = 1 .. H")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="(batch, head) slices the oracle times (default: all of them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -375,6 +377,13 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def alibi_slopes(H):
+    """The geometric ALiBi slopes 2^(-8 h / H), h = 1 .. H, as a float32 device tensor."""
+    import torch
+    return torch.tensor([2.0 ** (-8.0 * h / H) for h in range(1, H + 1)], dtype=torch.float32,
+                        device="cuda")
+
+
 def decode_bytes(w):
     """Algorithmic HBM bytes of one decode call: Q, K, V read once, O and LSE written once."""
     e = 2
@@ -411,9 +420,10 @@ def bench_decode(args, w):
     o = torch.empty_like(q)
     need = fa.fwd_kv_workspace_size(w.B, w.H, w.n_q, w.n_k, w.d)
     ws = torch.empty(max(need, 16), device="cuda", dtype=torch.uint8)
+    slopes = alibi_slopes(w.H) if args.alibi else None
 
     def call():
-        fa._lib.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws)
+        fa._lib.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws, alibi_slopes=slopes)
 
     if args.copy_calibration_mib:
         src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
@@ -469,7 +479,7 @@ def bench_decode(args, w):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q, K, V)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
-                   "head_dim": w.d, "causal": True, "pass": "fwd",
+                   "head_dim": w.d, "causal": True, "pass": "fwd", "alibi": bool(args.alibi),
                    "bytes_per_step": nbytes, "key_splits": int(plan_splits)},
         "kernels": {"decode+combine": entry},
         # the call is the decode kernel and the split merge; timing both together
@@ -518,16 +528,18 @@ def bench_block(args, w):
                        device="cuda", dtype=torch.uint8)
     ws_b = torch.empty(max(fa.bwd_workspace_size(w.B, w.H, w.n_q, w.d), 16), device="cuda",
                        dtype=torch.uint8)
+    slopes = alibi_slopes(w.H) if args.alibi else None
     state = {}
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f)
+        _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f,
+                                    alibi_slopes=slopes)
         if ev:
             ev[1].record()
         fa.bwd_kv(do, q, k, v, o, state["lse"], w.softmax_scale, True, dq=dq, dk=dk, dv=dv,
-                  workspace=ws_b)
+                  workspace=ws_b, alibi_slopes=slopes)
         if ev:
             ev[2].record()
 
@@ -558,7 +570,7 @@ def bench_block(args, w):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
-                   "head_dim": w.d, "causal": True, "pass": "fwd+bwd",
+                   "head_dim": w.d, "causal": True, "pass": "fwd+bwd", "alibi": bool(args.alibi),
                    "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
         "kernels": kernels,
         # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together
