@@ -30,6 +30,8 @@ Modules
   cross      N_q queries over N_k keys, the queries being the last N_q positions
              (decode steps, a new block over a cache), optional ALiBi distance
              penalty, forward and backward — pinned
+  dropout    attention dropout with masks from Philox4x32-10 (a published
+             counter-based generator), forward and backward — pinned
   pool       a process pool over (batch, head) for timing the oracle on a
              bounded sample
 
@@ -45,6 +47,9 @@ from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
 from .cross import (alibi_bias, cross_allowed_mask, cross_allowed_pairs, cross_backward,
                     cross_backward_bh, cross_forward, cross_forward_bh)
 
+from .dropout import (dropout_backward, dropout_backward_bh, dropout_forward, dropout_forward_bh,
+                      dropout_keep, keep_threshold, philox4x32_10)
+
 __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
     "attention_forward_bh", "attention_backward_bh", "allowed_pairs", "score_matrix_nbytes",
@@ -52,4 +57,6 @@ __all__ = [
     "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
     "cross_backward", "cross_backward_bh", "alibi_bias",
+    "philox4x32_10", "keep_threshold", "dropout_keep", "dropout_forward", "dropout_backward",
+    "dropout_forward_bh", "dropout_backward_bh",
 ]
