@@ -16,12 +16,13 @@ M. A. Moraes, R. O. Dror and D. E. Shaw, "Parallel Random Numbers: As Easy as 1,
       (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
     with M0 = 0xD2511F53, M1 = 0xCD9E8D57 and 32x32 -> 64-bit products;
   * between rounds the key is bumped by (0x9E3779B9, 0xBB67AE85); 10 rounds.
-Counter layout (this library's choice): one call covers a 2 x 2 block of (query, key) pairs
-of one (batch, head):
-    counter = (j >> 1, i >> 1, b * H + h, offset),  key = (seed mod 2^32, seed >> 32),
-    word    = 2 (i & 1) + (j & 1)
-for query index i and key index j.  Pair (i, j) is kept iff word >= floor(p 2^32), which
-happens with probability 1 - floor(p 2^32) / 2^32.
+Counter layout (this library's choice): one call covers 2 queries x 4 keys of one
+(batch, head), 16 random bits per (query, key) pair:
+    counter = (j >> 2, i >> 1, b * H + h, offset),  key = (seed mod 2^32, seed >> 32),
+    half-word index t = 4 (i & 1) + (j & 3),  u = bits 16 (t & 1) .. 16 (t & 1) + 15 of word t >> 1
+for query index i and key index j.  Pair (i, j) is kept iff u >= floor(p 2^16), which happens
+with probability 1 - floor(p 2^16) / 2^16 (p quantised to 2^-16); kept weights are scaled by
+exactly 1 / (1 - p).
 """
 from __future__ import annotations
 
@@ -52,22 +53,23 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    """floor(p 2^32) for 0 <= p < 1: a 32-bit word at or above it keeps its pair."""
+    """floor(p 2^16) for 0 <= p < 1: a 16-bit draw at or above it keeps its pair."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(math.floor(p * 4294967296.0))
+    return int(math.floor(p * 65536.0))
 
 
 def dropout_keep(n_q: int, n_k: int, bh: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
     """Boolean [n_q, n_k] keep mask of (batch, head) number bh = b * H + h."""
     i = np.arange(n_q, dtype=np.uint64)[:, None]
     j = np.arange(n_k, dtype=np.uint64)[None, :]
-    one = np.uint64(1)
-    words = philox4x32_10(j >> one, i >> one, np.uint64(bh), np.uint64(offset),
+    one, two, three = np.uint64(1), np.uint64(2), np.uint64(3)
+    words = philox4x32_10(j >> two, i >> one, np.uint64(bh), np.uint64(offset),
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    sel = (np.uint64(2) * (i & one) + (j & one)).astype(np.int64)
-    w = np.choose(np.broadcast_to(sel, (n_q, n_k)), [np.broadcast_to(x, (n_q, n_k)) for x in words])
-    return w >= np.uint64(keep_threshold(p))
+    t = np.broadcast_to(np.uint64(4) * (i & one) + (j & three), (n_q, n_k))
+    w = np.choose((t >> one).astype(np.int64), [np.broadcast_to(x, (n_q, n_k)) for x in words])
+    u = (w >> (np.uint64(16) * (t & one))) & np.uint64(0xFFFF)
+    return u >= np.uint64(keep_threshold(p))
 
 
 def _probs(q, k, scale, causal, window, slope):

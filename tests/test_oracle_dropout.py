@@ -48,11 +48,13 @@ def _philox_scalar(c, k):
 def test_mask_layout_per_pair(bh, seed, offset, p):
     n_q, n_k = 7, 9
     keep = oracle.dropout_keep(n_q, n_k, bh, p, seed, offset)
-    t = math.floor(p * 2 ** 32)
+    thr = math.floor(p * 2 ** 16)
     for i in range(n_q):
         for j in range(n_k):
-            w = _philox_scalar([j >> 1, i >> 1, bh, offset], [seed & 0xFFFFFFFF, seed >> 32])
-            assert keep[i, j] == (w[2 * (i & 1) + (j & 1)] >= t)
+            w = _philox_scalar([j >> 2, i >> 1, bh, offset], [seed & 0xFFFFFFFF, seed >> 32])
+            t = 4 * (i & 1) + (j & 3)
+            u = (w[t >> 1] >> (16 * (t & 1))) & 0xFFFF
+            assert keep[i, j] == (u >= thr)
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.83])
@@ -60,13 +62,13 @@ def test_keep_fraction_and_word_independence(p):
     n = 512
     keeps = [oracle.dropout_keep(n, n, bh, p, seed=2024) for bh in range(4)]
     frac = np.mean([k.mean() for k in keeps])
-    expect = 1.0 - math.floor(p * 2 ** 32) / 2 ** 32
+    expect = 1.0 - math.floor(p * 2 ** 16) / 2 ** 16
     sigma = math.sqrt(expect * (1 - expect) / (4 * n * n))
     assert abs(frac - expect) < 6 * sigma
     k = keeps[0]
-    # the four words of a call (2 x 2 blocks) are independent: pairwise agreement of the
-    # (0,0) and (1,1) members matches independent draws
-    a, b = k[0::2, 0::2].ravel(), k[1::2, 1::2].ravel()
+    # the draws of one call (2 queries x 4 keys) are independent: agreement of two members
+    # of each block from different words matches independent draws
+    a, b = k[0::2, 0::4].ravel(), k[1::2, 3::4].ravel()
     agree = np.mean(a == b)
     e2 = expect * expect + (1 - expect) ** 2
     assert abs(agree - e2) < 6 * math.sqrt(e2 * (1 - e2) / a.size)
