@@ -23,11 +23,13 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA_ERR_BAD_DTYPE", 5: "FA_ERR_BAD_WINDOW", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_BAD_SCALE",
     8: "FA_ERR_WORKSPACE", 9: "FA_ERR_HIP", 10: "FA_ERR_ALIAS", 11: "FA_ERR_BAD_STAGES",
+    12: "FA_ERR_BAD_DROPOUT",
 }
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 # Every function include/fa.h declares, with its ctypes signature.
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_U64, _U32 = ctypes.c_ulonglong, ctypes.c_uint
 SIGNATURES = {
     "fa_version": (_I, []),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -40,10 +42,10 @@ SIGNATURES = {
     "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
                            _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
-    "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P,
-                       _S, _P]),
+    "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P,
+                       _F, _U64, _U32, _P, _S, _P]),
     "fa_bwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F,
-                       _I, _I, _I, _P, _P]),
+                       _I, _I, _I, _P, _F, _U64, _U32, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -223,10 +225,13 @@ def _check_slopes(slopes, q):
 
 
 def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None,
-           return_lse=True, workspace=None, alibi_slopes=None):
+           return_lse=True, workspace=None, alibi_slopes=None, dropout_p=0.0, dropout_seed=0,
+           dropout_offset=0):
     """``fa_fwd_kv``: q [B, H, N_q, d] over k, v [B, H, N_k, d], the queries being the last N_q
     key positions.  Any strides with a contiguous last dimension (for example transposed
     views of [B, N, H, d] memory).  ``alibi_slopes``: float32 [H] on the device, or None.
+    ``dropout_p`` / ``dropout_seed`` / ``dropout_offset``: attention dropout with masks from
+    the library's Philox stream (the same three values go to ``bwd_kv``).
     Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
     import torch
     _check_kv_tensors(q, k, v)
@@ -243,12 +248,14 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k, d,
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
+                          float(dropout_p), int(dropout_seed), int(dropout_offset),
                           _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, lse
 
 
 def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
-           dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
+           dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None, dropout_p=0.0,
+           dropout_seed=0, dropout_offset=0):
     """``fa_bwd_kv``: gradients ``(dq, dk, dv)`` of ``fwd_kv``.  Any strides with a contiguous
     last dimension; new gradients take the strides of q, k, v."""
     import torch
@@ -274,5 +281,6 @@ def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=
                           _ptr(dk), _ptr(dv), st, _ptr(workspace),
                           workspace.numel() * workspace.element_size(), B, H, n_q, n_k, d,
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
+                          float(dropout_p), int(dropout_seed), int(dropout_offset),
                           _stream(q.device)))
     return dq, dk, dv

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -63,6 +64,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output buffer is also an input buffer";
     case FA_ERR_BAD_STAGES: return "FA_ERR_BAD_STAGES: stage mask empty or unknown bits set";
+    case FA_ERR_BAD_DROPOUT: return "FA_ERR_BAD_DROPOUT: dropout_p must be in [0, 1)";
   }
   return "unknown fa_status";
 }
@@ -243,6 +245,18 @@ fa::Strides dense_strides(int H, int rows, int d) {
   return fa::Strides{(long long)H * rows * d, (long long)rows * d, (long long)d};
 }
 
+// Dropout parameters as the kernels take them: the keep threshold floor(p 2^16) on 16-bit
+// draws and the factor 1 / (1 - p) of kept weights (exactly 1 without dropout).
+bool dropout_from(float p, unsigned long long seed, unsigned offset, fa::Dropout* d) {
+  if (!(p >= 0.f && p < 1.f)) return false;   // also rejects NaN
+  d->seed_lo = (unsigned)(seed & 0xffffffffull);
+  d->seed_hi = (unsigned)(seed >> 32);
+  d->offset = offset;
+  d->threshold = (unsigned)std::floor((double)p * 65536.0);
+  d->scale = p > 0.f ? (float)(1.0 / (1.0 - (double)p)) : 1.f;
+  return true;
+}
+
 bool strides_ok(const fa::Strides& s, int rows) {
   if (s.b < 0 || s.h < 0 || s.r < 0) return false;
   if (s.b % 8 != 0 || s.h % 8 != 0 || s.r % 8 != 0) return false;
@@ -260,13 +274,16 @@ size_t fa_fwd_kv_workspace_size(int batch, int heads, int seqlen_q, int seqlen_k
       check_common(batch, heads, seqlen_k, head_dim, FA_BF16, 1.f, -1, -1, &e2) != FA_OK)
     return 0;
   if (batch == 0 || heads == 0 || seqlen_q == 0) return 0;
-  return fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim).ws_bytes;
+  // enough for either plan (with and without dropout)
+  return std::max(fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim, false).ws_bytes,
+                  fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim, true).ws_bytes);
 }
 
 fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
                     void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
@@ -294,7 +311,10 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
       !strides_ok(p.sv, seqlen_k))
     return FA_ERR_BAD_SHAPE;
 
-  const fa::KvPlan plan = fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim);
+  fa::Dropout drop;
+  if (!dropout_from(dropout_p, dropout_seed, dropout_offset, &drop)) return FA_ERR_BAD_DROPOUT;
+  const fa::KvPlan plan = fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim,
+                                      drop.scale != 1.f);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(o) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
       (lse && !aligned16(lse)) || (plan.ws_bytes > 0 && !aligned16(workspace)))
@@ -320,6 +340,7 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   p.lse = lse;
   p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
   p.slopes = alibi_slopes;
+  p.drop = drop;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;
@@ -342,6 +363,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
                     void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
@@ -400,6 +422,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
   p.slopes = alibi_slopes;
+  if (!dropout_from(dropout_p, dropout_seed, dropout_offset, &p.drop)) return FA_ERR_BAD_DROPOUT;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;

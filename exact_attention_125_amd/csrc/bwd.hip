@@ -44,6 +44,7 @@ struct BwdArgs {
   float* stats;   // per-query statistics in 32-query blocks (stat_index)
   const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
+  Dropout drop;         // used by the DROPOUT instances only
   // batch / head strides (bytes) and row strides (bytes) of q, k, v, o, dout, dq, dk, dv
   long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs, g_bs, g_hs;
   long long dq_bs, dq_hs, dk_bs, dk_hs, dv_bs, dv_hs;
@@ -132,8 +133,10 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
 constexpr int kKvRows = 128;   // keys per workgroup (32 per wave)
 constexpr int kQStep = 32;     // queries per step
 
-// ALIBI: P carries the forward's ALiBi penalty, 2^(... - slope log2(e) |p - j|)
-template <int D, bool BF16, bool ALIBI>
+// ALIBI: P carries the forward's ALiBi penalty, 2^(... - slope log2(e) |p - j|).
+// DROPOUT: the forward's weights were P * keep / (1 - p), so dV uses them and dP is
+// (dO V^T) * keep / (1 - p), with keep drawn again from a.drop.
+template <int D, bool BF16, bool ALIBI, bool DROPOUT>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kQStep * kRowBytes;    // one Q or dO tile
@@ -261,6 +264,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st_lse + 8 * g + 4 * hi);
       const f32x4 de = *reinterpret_cast<const f32x4 FA_LDS*>(st_delta + 8 * g + 4 * hi);
       float p[4], d[4];
+      unsigned rnd[2][4];   // DROPOUT: draws of the query pairs 8 g + 4 hi + {0, 1} and {2, 3}
+      if constexpr (DROPOUT) {
+        a.drop.call(bh, q0 + 8 * g + 4 * hi, key, rnd[0]);
+        a.drop.call(bh, q0 + 8 * g + 4 * hi + 2, key, rnd[1]);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e;
@@ -272,8 +280,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
           const int qq = q0 + 8 * g + 4 * hi + e;
           pe = (qq < n && mk.visible(qq + off, key)) ? pe : 0.f;
         }
-        p[e] = pe;
-        d[e] = pe * (dp[i] + de[e]);
+        if constexpr (DROPOUT) {
+          const bool kept = a.drop.keep(rnd[e >> 1], q0 + 8 * g + 4 * hi + e, key);
+          p[e] = kept ? pe * a.drop.scale : 0.f;
+          d[e] = pe * ((kept ? dp[i] * a.drop.scale : 0.f) + de[e]);
+        } else {
+          p[e] = pe;
+          d[e] = pe * (dp[i] + de[e]);
+        }
       }
       pk[2 * g] = pack2<BF16>(p[0], p[1]);
       pk[2 * g + 1] = pack2<BF16>(p[2], p[3]);
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;   // queries per workgroup (32 per wave)
 constexpr int kKStep = 64;     // keys per K/V tile
 
-template <int D, bool BF16, bool ALIBI>
+template <int D, bool BF16, bool ALIBI, bool DROPOUT>
 __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kKStep * kRowBytes;
@@ -439,6 +453,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float d2[2];
+        unsigned rnd[4];   // DROPOUT: this query's draws for the run of 4 keys holding i
+        if constexpr (DROPOUT)
+          a.drop.call(bh, qi, j0 + 32 * mb + 8 * (i >> 2) + 4 * hi, rnd);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           float x = __builtin_fmaf(sc[mb][i + e], c, cm);
@@ -451,7 +468,12 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
             const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
             p = (row_ok && mk.visible(qi + off, j)) ? p : 0.f;
           }
-          d2[e] = p * (dp[mb][i + e] + ndlt);
+          if constexpr (DROPOUT) {
+            const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
+            d2[e] = p * ((a.drop.keep(rnd, qi, j) ? dp[mb][i + e] * a.drop.scale : 0.f) + ndlt);
+          } else {
+            d2[e] = p * (dp[mb][i + e] + ndlt);
+          }
         }
         dsk[mb][i >> 1] = pack2<BF16>(d2[0], d2[1]);
       }
@@ -515,6 +537,7 @@ BwdArgs make_args(const BwdParams& p) {
   a.stats = p.stats;
   a.seqlens = p.seqlens;
   a.slopes = nullptr;
+  a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
   const long long row = (long long)p.D * 2, head = (long long)p.N * row, batch = p.H * head;
   a.q_bs = a.k_bs = a.v_bs = a.o_bs = a.g_bs = a.dq_bs = a.dk_bs = a.dv_bs = batch;
   a.q_hs = a.k_hs = a.v_hs = a.o_hs = a.g_hs = a.dq_hs = a.dk_hs = a.dv_hs = head;
@@ -552,7 +575,7 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
     if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDkDv) {
     a.n_tiles = (a.n + kKvRows - 1) / kKvRows;
-    hipLaunchKernelGGL((dkdv_kernel<D, BF16, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
+    hipLaunchKernelGGL((dkdv_kernel<D, BF16, false, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
                        dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
@@ -560,7 +583,7 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
     if (hipError_t e = launch_dq_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDq) {
     a.n_tiles = (a.n + kDqRows - 1) / kDqRows;
-    hipLaunchKernelGGL((dq_kernel<D, BF16, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
+    hipLaunchKernelGGL((dq_kernel<D, BF16, false, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
                        dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
@@ -583,6 +606,8 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.stats = p.stats;
   a.seqlens = nullptr;
   a.slopes = p.slopes;
+  a.drop = p.drop;
+  const bool alibi = p.slopes != nullptr, drop = p.drop.scale != 1.f;
   a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
   a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);
   a.v_bs = p.sv.b * e, a.v_hs = p.sv.h * e, a.v_rs = (int)(p.sv.r * e);
@@ -613,19 +638,27 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   if (p.Nk > 0) {
     a.n_tiles = (p.Nk + kKvRows - 1) / kKvRows;
     const dim3 grid((unsigned)((long)a.n_bh * a.n_tiles));
-    if (p.slopes != nullptr)
-      hipLaunchKernelGGL((dkdv_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
+    if (alibi && drop)
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, true, true>), grid, dim3(256), 0, stream, a);
+    else if (alibi)
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, true, false>), grid, dim3(256), 0, stream, a);
+    else if (drop)
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, false, true>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((dkdv_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, BF16, false, false>), grid, dim3(256), 0, stream, a);
     if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   }
   if (p.Nq == 0) return hipSuccess;
   a.n_tiles = (p.Nq + kDqRows - 1) / kDqRows;
   const dim3 grid((unsigned)((long)a.n_bh * a.n_tiles));
-  if (p.slopes != nullptr)
-    hipLaunchKernelGGL((dq_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
+  if (alibi && drop)
+    hipLaunchKernelGGL((dq_kernel<D, BF16, true, true>), grid, dim3(256), 0, stream, a);
+  else if (alibi)
+    hipLaunchKernelGGL((dq_kernel<D, BF16, true, false>), grid, dim3(256), 0, stream, a);
+  else if (drop)
+    hipLaunchKernelGGL((dq_kernel<D, BF16, false, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((dq_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BF16, false, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -284,6 +284,52 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------- dropout
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products
+// (multipliers 0xD2511F53, 0xCD9E8D57) mixed with the other counter words and the key, the key
+// bumped by (0x9E3779B9, 0xBB67AE85) between rounds.  The key schedule is wave-uniform.
+__device__ __forceinline__ void philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3,
+                                              unsigned k0, unsigned k1, unsigned (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long p0 = (unsigned long long)0xD2511F53u * c0;
+    const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c2;
+    const unsigned n0 = (unsigned)(p1 >> 32) ^ c1 ^ k0;
+    const unsigned n2 = (unsigned)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (unsigned)p1;
+    c3 = (unsigned)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;   // the bump after the last round is never used
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// Dropout of attention weights: one generator call draws 16 bits for each of 2 queries x 4
+// keys of one (batch, head): counter (j >> 2, i >> 1, batch * heads + head, offset), key = the
+// 64-bit seed; pair (i, j) takes half-word 4 (i & 1) + (j & 3) (word t >> 1, high half when t
+// is odd) and is kept when that half-word is at least floor(p 2^16).
+struct Dropout {
+  unsigned seed_lo, seed_hi, offset;
+  unsigned threshold;   // floor(p 2^16); 0 keeps everything
+  float scale;          // 1 / (1 - p)
+  // the call that holds the draws of queries i & ~1, i | 1 for keys j & ~3 .. j | 3
+  __device__ __forceinline__ void call(int bh, int i, int j, unsigned (&o)[4]) const {
+    philox4x32_10((unsigned)j >> 2, (unsigned)i >> 1, (unsigned)bh, offset, seed_lo, seed_hi, o);
+  }
+  // whether (i, j) is kept, from its call's words
+  __device__ __forceinline__ bool keep(const unsigned (&o)[4], int i, int j) const {
+    const int t = 4 * (i & 1) + (j & 3);
+    const unsigned w = (t >> 1) == 0 ? o[0] : (t >> 1) == 1 ? o[1] : (t >> 1) == 2 ? o[2] : o[3];
+    return ((t & 1) ? (w >> 16) : (w & 0xffffu)) >= threshold;
+  }
+};
+
 // ---------------------------------------------------------------------------- masks
 // The 32x32 MFMA accumulator layout: element i of lane L sits in row 8 (i/4) + 4 (L/32) + i%4
 // and column L % 32.  diag_lanes<KeyRows>(i) is the wave-wide lane mask of the elements i on

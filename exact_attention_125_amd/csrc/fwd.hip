@@ -71,6 +71,7 @@ struct FwdArgs {
   float* po;      // n_split > 1: normalised partial O, fp32 [n_split, B*H, nq, D]
   float* plse;    //              and its natural-log LSE [n_split, B*H, nq]
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
+  Dropout drop;          // used by the DROPOUT instances only
   float c;        // |softmax_scale| * log2(e)
   unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
   int causal, wl, wr;
@@ -86,7 +87,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
 // ALIBI: every score gets the ALiBi penalty -slope_h |p - j| (p the query's key position), in
 // the exponent domain: s <- s c - slope log2(e) |p - j| right after the product, after which
 // the tile works with a unit factor in place of c.
-template <int D, bool BF16, int WAVES, int QB, bool ALIBI>
+// DROPOUT: the weights that multiply V are P * keep / (1 - p) (the row sums stay those of P),
+// with keep drawn by a.drop.
+template <int D, bool BF16, int WAVES, int QB, bool ALIBI, bool DROPOUT>
 __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kBr = 32 * QB * WAVES;
@@ -286,7 +289,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
       const float neg_m = m_ref[qb] == NEG_INF ? 0.f : -m_ref[qb];
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        unsigned rnd[4];   // DROPOUT: the draws of this lane's current run of 4 keys
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           float p0 = exp2_fast(__builtin_fmaf(s[mb][qb][i], c, neg_m));
@@ -296,8 +300,16 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
             p1 = s[mb][qb][i + 1] == NEG_INF ? 0.f : p1;
           }
           part[(i >> 1) & 3] += p0 + p1;
+          if constexpr (DROPOUT) {
+            const int qi = wq0 + 32 * qb + l32;
+            const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if ((i & 3) == 0) a.drop.call(bh, qi, j, rnd);
+            p0 = a.drop.keep(rnd, qi, j) ? p0 * a.drop.scale : 0.f;
+            p1 = a.drop.keep(rnd, qi, j + 1) ? p1 * a.drop.scale : 0.f;
+          }
           pk[qb][mb][i >> 1] = pack2<BF16>(p0, p1);
         }
+      }
       l_run[qb] += (part[0] + part[1]) + (part[2] + part[3]);
     }
 
@@ -382,12 +394,16 @@ hipError_t launch_args(FwdArgs& a, hipStream_t stream) {
   constexpr int kBr = 32 * QB * WAVES;
   a.n_qt = (a.nq + kBr - 1) / kBr;
   const long blocks = (long)a.n_bh * a.n_qt * a.n_split;
-  if (a.slopes != nullptr)
-    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, true>), dim3((unsigned)blocks),
-                       dim3(64 * WAVES), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(64 * WAVES);
+  const bool alibi = a.slopes != nullptr, drop = a.drop.scale != 1.f;
+  if (alibi && drop)
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, true, true>), grid, block, 0, stream, a);
+  else if (alibi)
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, true, false>), grid, block, 0, stream, a);
+  else if (drop)
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, false>), dim3((unsigned)blocks),
-                       dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, BF16, WAVES, QB, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -419,6 +435,7 @@ hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
   a.split_tiles = (p.N + kBc - 1) / kBc;
   a.po = a.plse = nullptr;
   a.slopes = nullptr;
+  a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   return launch_args<D, BF16, WAVES, QB>(a, stream);
 }
@@ -481,6 +498,7 @@ hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t
   a.po = p.ws;
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * p.D : nullptr;
   a.slopes = p.slopes;
+  a.drop = p.drop;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   if (p.D == 64)
     return p.bf16 ? launch_args<64, true, 4, 1>(a, stream) : launch_args<64, false, 4, 1>(a, stream);

@@ -410,11 +410,11 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-KvPlan kv_plan(int B, int H, int Nq, int Nk, int D) {
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout) {
   KvPlan p{};
   const long bh = (long)B * H;
   long split_keys;
-  if (Nq <= kDecodeMaxQ) {
+  if (Nq <= kDecodeMaxQ && !dropout) {
     // about 512 workgroups: one round at two per CU, so each workgroup's start (query load,
     // first key rows) and end (merge, stores) latency is paid once per CU pair; at least four
     // steps of keys each

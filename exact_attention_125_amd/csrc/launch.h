@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "cdna4.h"
+
 namespace fa {
 
 struct FwdParams {
@@ -60,6 +62,7 @@ struct KvParams {
   float* lse;          // [B, H, N_q] dense, may be null
   float* ws;           // partial results of key splits (KvPlan::ws_bytes), null if none
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
+  Dropout drop{0u, 0u, 0u, 0u, 1.f};   // scale 1: no dropout
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk, D;
   bool bf16;
@@ -80,7 +83,8 @@ struct KvPlan {
 };
 constexpr int kDecodeMaxQ = 4;
 constexpr int kKvMfmaKeyStep = 64;   // key tile of the four-wave MFMA kernel
-KvPlan kv_plan(int B, int H, int Nq, int Nk, int D);
+// dropout: the few-query kernel has no dropout, so such calls take the MFMA kernel
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout);
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
@@ -107,6 +111,7 @@ struct BwdKvParams {
   void* dv;
   float* stats;        // workspace, as for BwdParams with N = N_q
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
+  Dropout drop{0u, 0u, 0u, 0u, 1.f};   // as in the forward call
   Strides sq, sk, sv, so, sg, sdq, sdk, sdv;
   int B, H, Nq, Nk, D;
   bool bf16;

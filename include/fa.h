@@ -66,7 +66,8 @@ typedef enum fa_status {
   FA_ERR_WORKSPACE = 8,           /* backward workspace NULL or smaller than required   */
   FA_ERR_HIP = 9,                 /* the HIP runtime reported an error                  */
   FA_ERR_ALIAS = 10,              /* an output buffer is also an input buffer           */
-  FA_ERR_BAD_STAGES = 11          /* fa_bwd_stages: empty mask or unknown stage bits     */
+  FA_ERR_BAD_STAGES = 11,         /* fa_bwd_stages: empty mask or unknown stage bits     */
+  FA_ERR_BAD_DROPOUT = 12         /* dropout_p outside [0, 1)                           */
 } fa_status;
 
 typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -201,7 +202,21 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * bias coefficients" the page "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型（含A100环境配置）"
  * lists as alibi_slopes in §4.2 (and the ALiBi relative position encoding "Flash Attention
  * 3.7 核心原理与实战" names for very long sequences in §6).  The values are read by the kernels
- * and not checked: they must be finite.  fa_bwd_kv takes the same slopes. */
+ * and not checked: they must be finite.  fa_bwd_kv takes the same slopes.
+ *
+ * Dropout: with dropout_p in (0, 1) the weights that multiply V are P_ij * M_ij / (1 - p),
+ * M_ij in {0, 1}, as the dropout_p argument of the attention calls of the A100 page (§4.2)
+ * and of the SDPA call of the FA3.7 page (§3.2) and the F.dropout of that page's §4.2 module
+ * (applied to the softmax weights before V) describe; LSE is that of the softmax before
+ * dropout.  M comes from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011), so a call is reproducible: one generator call with
+ * counter (j >> 2, i >> 1, batch * heads + head, dropout_offset) and key dropout_seed (low
+ * word first) draws 16 bits for each of queries 2 (i >> 1) + {0, 1} and keys
+ * 4 (j >> 2) + {0 .. 3}; pair (i, j) takes half-word t = 4 (i & 1) + (j & 3) (word t >> 1,
+ * its high half when t is odd) and is kept when that value is at least floor(p 2^16).  The
+ * keep probability is thus p quantised to 2^-16.  dropout_p = 0 is no dropout; values
+ * outside [0, 1) give FA_ERR_BAD_DROPOUT.  fa_bwd_kv must get the forward's p, seed and
+ * offset.  With dropout, calls with N_q <= 4 take the MFMA kernel. */
 typedef struct fa_strides {
   long long batch, head, row;
 } fa_strides;
@@ -212,6 +227,7 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass of fa_fwd_kv (by recomputation, as fa_bwd): gradients of sum(dout * o) for
@@ -226,13 +242,15 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
  *   workspace        at least fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim) bytes,
  *                    16-byte aligned; contents on entry do not matter.
  * A row without keys has dQ = 0; with N_q = 0, dK = dV = 0 (and q, o, dout, lse, dq may be
- * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale and alibi_slopes
- * must be those of the forward call.  Errors as in fa_bwd and fa_fwd_kv. */
+ * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale, alibi_slopes and
+ * the dropout arguments must be those of the forward call.  Errors as in fa_bwd and
+ * fa_fwd_kv. */
 fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
                     void* stream);
 
 /* Static, human-readable name of a status code. */

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import GRAD_REL_L2, LSE_TOL, O_TOL, rel_l2, say, to64, to_dev
+from gpu_util import GRAD_REL_L2, LSE_TOL, O_TOL, UNIT_ROUNDOFF, rel_l2, say, to64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -300,3 +300,87 @@ def test_alibi_zero_slopes_match_no_alibi(fa):
     torch.cuda.synchronize()
     assert float((a[0].float() - b[0].float()).abs().max()) <= O_TOL["bf16"]
     assert float((a[1] - b[1]).abs().max()) <= 1e-5
+
+
+# ---------------------------------------------------------------------------- dropout
+def run_dropout(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, p, rng_seed, offset,
+                slopes=None, backward=False):
+    """fa_fwd_kv (and fa_bwd_kv) with dropout against the oracle with the same Philox masks."""
+    import oracle
+    import torch
+    p = float(np.float32(p))   # the value the C ABI receives
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed)
+    g = W.cross_case(B, H, n_q, 1, d, dtype, seed + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
+    scale = 1.0 / math.sqrt(d)
+    sl = None if slopes is None else torch.tensor(slopes, dtype=torch.float32, device="cuda")
+    kw = dict(alibi_slopes=sl, dropout_p=p, dropout_seed=rng_seed, dropout_offset=offset)
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window, **kw)
+    grads = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window, **kw) if backward else None
+    torch.cuda.synchronize()
+    ro, rl = oracle.dropout_forward_bh(inp["q64"], inp["k64"], inp["v64"], scale, causal, window,
+                                       p, rng_seed, offset, slopes)
+    label = f"dropout p={p:.3f} nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}"
+    o64, l64 = to64(o), lse.cpu().numpy().astype(np.float64)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(l64), empty)
+    d_o = float(np.abs(o64 - ro).max())
+    d_l = float(np.abs(l64[~empty] - rl[~empty]).max()) if (~empty).any() else 0.0
+    say(f"{label}: max|dO|={d_o:.2e} max|dLSE|={d_l:.2e}")
+    assert d_l <= LSE_TOL, label
+    diff = np.abs(o64 - ro)
+    over = diff > O_TOL[dtype]
+    if over.any():
+        # Rows that see few keys have |O| up to about 4 / (1 - p), where one bf16 step exceeds
+        # the fixed tolerance.  The kernel rounds each kept weight P / (1 - p) once to the input
+        # type and O once at the end, so |dO| <= u (sum_j P_ij M_ij / (1 - p) |V_jc| + |O_ic|)
+        # (u the unit roundoff); elements over the fixed tolerance must be within that bound.
+        wabs, _ = oracle.dropout_forward_bh(inp["q64"], inp["k64"], np.abs(inp["v64"]), scale,
+                                            causal, window, p, rng_seed, offset, slopes)
+        derived = UNIT_ROUNDOFF[dtype] * (wabs + np.abs(ro)) + 1e-5
+        ratio = float((diff[over] / derived[over]).max())
+        say(f"{label}: {int(over.sum())} element(s) over {O_TOL[dtype]} (max |O| "
+            f"{float(np.abs(ro[over]).max()):.2f}), worst |dO| / rounding bound {ratio:.2f}")
+        assert ratio <= 1.0, f"{label}: max|dO| {d_o:.3e} beyond the rounding bound"
+    if backward:
+        rq, rk, rv = oracle.dropout_backward_bh(inp["q64"], inp["k64"], inp["v64"], g["q64"],
+                                                scale, causal, window, p, rng_seed, offset, slopes)
+        floor = 1e-3 * float(np.linalg.norm(g["q64"]))
+        for name, got, ref in zip(("dq", "dk", "dv"), grads, (rq, rk, rv)):
+            e = rel_l2(to64(got), ref, floor)
+            assert e <= GRAD_REL_L2, f"{label} {name} rel L2 {e:.3e}"
+    return o
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (300, 0))])
+@pytest.mark.parametrize("n_q,n_k", [(1, 300), (3, 129), (100, 700), (300, 129), (128, 8192),
+                                     (257, 257)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_dropout_forward(fa, causal, window, n_q, n_k, d, dtype):
+    run_dropout(fa, 1, 3, n_q, n_k, d, dtype, causal, window, seed=n_q + 7 * n_k, p=0.17,
+                rng_seed=0x1234_5678_9ABC, offset=3)
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (100, 40))])
+@pytest.mark.parametrize("n_q,n_k", [(1, 300), (100, 700), (300, 129), (257, 257)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_dropout_backward(fa, causal, window, n_q, n_k, d, dtype):
+    run_dropout(fa, 1, 2, n_q, n_k, d, dtype, causal, window, seed=3 * n_q + n_k, p=0.3,
+                rng_seed=987654321, offset=0, backward=True)
+
+
+@pytest.mark.parametrize("p", [0.05, 0.5, 0.9])
+def test_dropout_with_alibi(fa, p):
+    run_dropout(fa, 2, 4, 200, 900, 64, "bf16", True, (-1, -1), seed=12, p=p, rng_seed=42,
+                offset=11, slopes=alibi_slopes(4), backward=True)
+
+
+def test_dropout_reproducible_and_offset_changes_mask(fa):
+    import torch
+    a = run_dropout(fa, 1, 2, 64, 512, 64, "bf16", False, (-1, -1), seed=5, p=0.25, rng_seed=7,
+                    offset=0)
+    b = run_dropout(fa, 1, 2, 64, 512, 64, "bf16", False, (-1, -1), seed=5, p=0.25, rng_seed=7,
+                    offset=0)
+    c = run_dropout(fa, 1, 2, 64, 512, 64, "bf16", False, (-1, -1), seed=5, p=0.25, rng_seed=7,
+                    offset=1)
+    assert torch.equal(a, b) and not torch.equal(a, c)
