@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--alibi", action="store_true",
                     help="decode and block workloads: ALiBi slopes 2^(-8 h / H), h = 1 .. H")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="block workload: attention dropout probability (seed 1234)")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="(batch, head) slices the oracle times (default: all of them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -534,12 +536,13 @@ def bench_block(args, w):
     def step(ev=None):
         if ev:
             ev[0].record()
+        drop = dict(dropout_p=args.dropout, dropout_seed=1234)
         _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f,
-                                    alibi_slopes=slopes)
+                                    alibi_slopes=slopes, **drop)
         if ev:
             ev[1].record()
         fa.bwd_kv(do, q, k, v, o, state["lse"], w.softmax_scale, True, dq=dq, dk=dk, dv=dv,
-                  workspace=ws_b, alibi_slopes=slopes)
+                  workspace=ws_b, alibi_slopes=slopes, **drop)
         if ev:
             ev[2].record()
 
@@ -571,6 +574,7 @@ def bench_block(args, w):
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
                    "head_dim": w.d, "causal": True, "pass": "fwd+bwd", "alibi": bool(args.alibi),
+                   "dropout_p": args.dropout,
                    "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
         "kernels": kernels,
         # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together
