@@ -29,7 +29,7 @@ Modules
              sample's own rows, zeros past them — pinned
   cross      N_q queries over N_k keys, the queries being the last N_q positions
              (decode steps, a new block over a cache), optional ALiBi distance
-             penalty, forward and backward — pinned
+             penalty and block-sparse mask, forward and backward — pinned
   dropout    attention dropout with masks from Philox4x32-10 (a published
              counter-based generator), forward and backward — pinned
   pool       a process pool over (batch, head) for timing the oracle on a
@@ -44,7 +44,7 @@ from .attention import (allowed_mask, attention_forward, attention_backward,
 from .online import attention_forward_online
 from .brute import attention_forward_brute
 from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
-from .cross import (alibi_bias, cross_allowed_mask, cross_allowed_pairs, cross_backward,
+from .cross import (BLOCK, alibi_bias, block_allowed, cross_allowed_mask, cross_allowed_pairs, cross_backward,
                     cross_backward_bh, cross_forward, cross_forward_bh)
 
 from .dropout import (dropout_backward, dropout_backward_bh, dropout_forward, dropout_forward_bh,
@@ -56,7 +56,7 @@ __all__ = [
     "attention_forward_online", "attention_forward_brute",
     "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
-    "cross_backward", "cross_backward_bh", "alibi_bias",
+    "cross_backward", "cross_backward_bh", "alibi_bias", "BLOCK", "block_allowed",
     "philox4x32_10", "keep_threshold", "dropout_keep", "dropout_forward", "dropout_backward",
     "dropout_forward_bh", "dropout_backward_bh",
 ]

@@ -27,6 +27,13 @@ the scaled score of query i and key j (a penalty linear in the distance between 
 positions), before the mask and the softmax:
       S_ij = scale * <q_i, k_j> - slope * |p_i - j|
 With slope = 0 this is the definition above.
+
+Block-sparse attention: [A100] §6 lists block-sparse FlashAttention (90% sparsity on 64k-token
+texts) among the next steps and [FA37] §6 names sparse attention for very long sequences;
+neither fixes the pattern.  Reading: a boolean mask over blocks of BLOCK = 64 queries x 64
+keys (query index i // 64, key index j // 64) selects the blocks that are computed; a pair
+outside the selected blocks is hidden like any masked pair (its score is -inf), so it takes
+no part in the softmax.
 """
 from __future__ import annotations
 
@@ -60,8 +67,19 @@ def alibi_bias(n_q: int, n_k: int, slope: float) -> np.ndarray:
     return -float(slope) * np.abs(p - j)
 
 
-def _scores(q, k, scale, causal, window, slope):
+BLOCK = 64   # queries and keys per block of a block-sparse mask
+
+
+def block_allowed(n_q: int, n_k: int, block_mask) -> np.ndarray:
+    """[n_q, n_k] bool: True where the pair's (query block, key block) is selected."""
+    bm = np.asarray(block_mask, dtype=bool)
+    return bm[np.arange(n_q)[:, None] // BLOCK, np.arange(n_k)[None, :] // BLOCK]
+
+
+def _scores(q, k, scale, causal, window, slope, block_mask=None):
     ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
+    if block_mask is not None:
+        ok &= block_allowed(q.shape[0], k.shape[0], block_mask)
     s = scale * (q @ k.T)
     if slope:
         s = s + alibi_bias(q.shape[0], k.shape[0], slope)
@@ -69,17 +87,18 @@ def _scores(q, k, scale, causal, window, slope):
 
 
 def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1),
-                  slope: float = 0.0):
+                  slope: float = 0.0, block_mask=None):
     """One (batch, head): q float64 [N_q, d], k, v [N_k, d] -> (O [N_q, d], LSE [N_q]).
 
     S = scale * Q K^T (minus the ALiBi distance penalty when slope != 0) is materialised in
-    full, masked with -inf, and put through the max-shifted softmax; O = P V,
-    LSE = rowmax + ln(rowsum).
+    full, masked with -inf (also outside the selected blocks of ``block_mask``
+    [ceil(N_q / 64), ceil(N_k / 64)], if given), and put through the max-shifted softmax;
+    O = P V, LSE = rowmax + ln(rowsum).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    s = _scores(q, k, scale, causal, window, slope)
+    s = _scores(q, k, scale, causal, window, slope, block_mask)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])     # exp(-inf) = 0 at hidden entries
@@ -91,21 +110,23 @@ def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1),
     return o, lse
 
 
-def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1), slopes=None):
+def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1), slopes=None,
+                     block_mask=None):
     """q [B, H, N_q, d], k, v [B, H, N_k, d] -> (O [B, H, N_q, d], LSE [B, H, N_q]);
-    ``slopes``: the H ALiBi slopes, or None."""
+    ``slopes``: the H ALiBi slopes, or None; ``block_mask``: [H, n_qb, n_kb] or None."""
     B, H, n_q, _ = q.shape
     o = np.empty((B, H, n_q, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, n_q), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window,
-                                               0.0 if slopes is None else float(slopes[h]))
+                                               0.0 if slopes is None else float(slopes[h]),
+                                               None if block_mask is None else block_mask[h])
     return o, lse
 
 
 def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, -1),
-                   slope: float = 0.0):
+                   slope: float = 0.0, block_mask=None):
     """One (batch, head): gradients (dQ [N_q, d], dK, dV [N_k, d]) of <dO, O> for
     ``cross_forward``, the ordinary derivative of that definition:
 
@@ -119,7 +140,7 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    s = _scores(q, k, scale, causal, window, slope)
+    s = _scores(q, k, scale, causal, window, slope, block_mask)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])
@@ -130,7 +151,8 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
     return scale * (ds @ k), scale * (ds.T @ q), dv
 
 
-def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=None):
+def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=None,
+                      block_mask=None):
     """[B, H, N_q, d] q and dO, [B, H, N_k, d] k and v -> (dQ, dK, dV), one head at a time."""
     B, H = q.shape[:2]
     dq, dk, dv = (np.empty(t.shape, dtype=np.float64) for t in (q, k, v))
@@ -138,5 +160,6 @@ def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = cross_backward(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, window,
-                0.0 if slopes is None else float(slopes[h]))
+                0.0 if slopes is None else float(slopes[h]),
+                None if block_mask is None else block_mask[h])
     return dq, dk, dv

@@ -326,3 +326,80 @@ def test_mutant_alibi_sign_fails_closed_form():
     lse_wrong = float(np.log(np.exp(s).sum()))
     z = (1 - math.exp(-slope * n)) / (1 - math.exp(-slope))
     assert abs(lse_wrong - math.log(z)) > 1.0
+
+
+# ---------------------------------------------------------------------------- block-sparse
+def _random_blocks(n_qb, n_kb, seed, density=0.5):
+    return np.random.default_rng(seed).random((n_qb, n_kb)) < density
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (70, 30))])
+@pytest.mark.parametrize("n_q,n_k", [(130, 200), (64, 64), (200, 70)])
+def test_block_sparse_torch_bool_mask(causal, window, n_q, n_k):
+    """torch CPU float64 SDPA with a boolean mask expanded from the blocks by torch's own
+    repeat_interleave, ANDed with the position mask written out with tril / triu."""
+    q, k, v = _qkv(n_q, n_k, 4, seed=n_q + n_k)
+    bm = _random_blocks(-(-n_q // 64), -(-n_k // 64), seed=n_q * n_k)
+    tb = torch.from_numpy(bm).repeat_interleave(64, 0).repeat_interleave(64, 1)[:n_q, :n_k]
+    off = n_k - n_q
+    pos = torch.ones(n_q, n_k, dtype=torch.bool)
+    if causal:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=off)
+    if window[0] >= 0:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).triu(diagonal=off - window[0])
+    if window[1] >= 0:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=off + window[1])
+    mask = tb & pos
+    live = mask.any(dim=1).numpy()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=mask[None], scale=0.4)[0].numpy()
+    o, lse = oracle.cross_forward(q, k, v, 0.4, causal, window, block_mask=bm)
+    np.testing.assert_allclose(o[live], ref[live], rtol=1e-12, atol=1e-12)
+    assert np.all(o[~live] == 0.0) and np.all(np.isneginf(lse[~live]))
+
+
+def test_block_diagonal_is_attention_within_blocks():
+    """A block-diagonal mask over equal-length queries and keys is self-attention of each
+    64-row block on its own."""
+    n = 200
+    q, k, v = _qkv(n, n, 5, seed=8)
+    nb = -(-n // 64)
+    o, lse = oracle.cross_forward(q, k, v, 0.5, False, block_mask=np.eye(nb, dtype=bool))
+    for b in range(nb):
+        sl = slice(64 * b, min(64 * (b + 1), n))
+        ro, rl = oracle.attention_forward(q[sl], k[sl], v[sl], 0.5)
+        np.testing.assert_allclose(o[sl], ro, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse[sl], rl, rtol=1e-13, atol=1e-13)
+
+
+def test_block_sparse_all_blocks_is_plain():
+    q, k, v = _qkv(100, 150, 4, seed=9)
+    a = oracle.cross_forward(q, k, v, 0.5, True, block_mask=np.ones((2, 3), bool))
+    b = oracle.cross_forward(q, k, v, 0.5, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_block_sparse_backward_central_differences():
+    rng = np.random.default_rng(10)
+    n_q, n_k = 70, 130   # two query blocks, three key blocks; d = 2 keeps it quick
+    q, k, v, do = (rng.standard_normal((r, 2)) for r in (n_q, n_k, n_k, n_q))
+    bm = np.array([[1, 0, 1], [0, 1, 1]], dtype=bool)
+    dq, dk, dv = oracle.cross_backward(q, k, v, do, 0.6, True, block_mask=bm)
+    h = 1e-6
+
+    def loss(q_, k_, v_):
+        return float((oracle.cross_forward(q_, k_, v_, 0.6, True, block_mask=bm)[0] * do).sum())
+
+    rows = [(0, 0, (3, 1)), (0, 1, (66, 0)), (1, 2, (5, 1)), (1, 0, (100, 1)), (2, 0, (129, 0))]
+    args = [q, k, v]
+    for which, grad_i, idx in [(w, w, i) for w, _, i in rows]:
+        grad = (dq, dk, dv)[grad_i]
+        plus, minus = args[which].copy(), args[which].copy()
+        plus[idx] += h
+        minus[idx] -= h
+        ap, am = list(args), list(args)
+        ap[which], am[which] = plus, minus
+        num = (loss(*ap) - loss(*am)) / (2 * h)
+        assert abs(grad[idx] - num) <= 1e-6 * max(1.0, abs(num))
