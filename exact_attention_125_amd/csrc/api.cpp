@@ -283,8 +283,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    const unsigned char* block_mask, float dropout_p,
+                    unsigned long long dropout_seed, unsigned dropout_offset, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -331,7 +332,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
     return FA_ERR_ALIAS;
   if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
   for (const void* out : outs)
-    if (alibi_slopes && out == (const void*)alibi_slopes) return FA_ERR_ALIAS;
+    if ((alibi_slopes && out == (const void*)alibi_slopes) ||
+        (block_mask && out == (const void*)block_mask))
+      return FA_ERR_ALIAS;
 
   p.q = q;
   p.k = k;
@@ -341,6 +344,7 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
   p.slopes = alibi_slopes;
   p.drop = drop;
+  p.blocks = block_mask;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;
@@ -363,8 +367,8 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
-                    void* stream) {
+                    const unsigned char* block_mask, float dropout_p,
+                    unsigned long long dropout_seed, unsigned dropout_offset, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -409,7 +413,9 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   if ((dq && (dq == dk || dq == dv)) || (dk && dk == dv)) return FA_ERR_ALIAS;
   if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
   for (void* out : outs)
-    if (alibi_slopes && out == (const void*)alibi_slopes) return FA_ERR_ALIAS;
+    if ((alibi_slopes && out == (const void*)alibi_slopes) ||
+        (block_mask && out == (const void*)block_mask))
+      return FA_ERR_ALIAS;
 
   p.q = q;
   p.k = k;
@@ -422,6 +428,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
   p.slopes = alibi_slopes;
+  p.blocks = block_mask;
   if (!dropout_from(dropout_p, dropout_seed, dropout_offset, &p.drop)) return FA_ERR_BAD_DROPOUT;
   p.B = batch;
   p.H = heads;

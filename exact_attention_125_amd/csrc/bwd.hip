@@ -45,6 +45,8 @@ struct BwdArgs {
   const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
   Dropout drop;         // used by the DROPOUT instances only
+  const unsigned char* blocks;   // block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks, or null
+  int n_qb, n_kb;
   // batch / head strides (bytes) and row strides (bytes) of q, k, v, o, dout, dq, dk, dv
   long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs, g_bs, g_hs;
   long long dq_bs, dq_hs, dk_bs, dk_hs, dv_bs, dv_hs;
@@ -245,6 +247,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const float FA_LDS* st_delta = st_lse + kQStep;
     if (s + 1 < s_end) load_tile(s + 1);
 
+    // block-sparse: this wave's 32 keys and the step's 32 queries lie in one 64 x 64 block;
+    // an unselected block contributes nothing (the wave still takes part in the copies)
+    // (a wave past the last key has no output: it skips, and reads no mask entry)
+    if (a.blocks == nullptr ||
+        (k_first + 32 * wave < nk &&
+         a.blocks[((long)h * a.n_qb + (s * kQStep) / 64) * a.n_kb + (k_first + 32 * wave) / 64])) {
     // S = Q K^T and dP = dO V^T: C[m = query][n = key], 32 queries x this wave's 32 keys
     f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -314,6 +322,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         dk[db] = mfma32x32x16<BF16>(qo, __builtin_bit_cast(i16x8, sb), dk[db]);
       }
     }
+    }   // selected block
 
     if (s + 1 < s_end) store_tile(stage ^ 1);
     __syncthreads();
@@ -431,6 +440,10 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const char FA_LDS* vt = kt + kTileBytes;
     if (t + 1 < t_end) load_tile(t + 1);
 
+    // block-sparse: this wave's 32 queries and the 64-key tile lie in one 64 x 64 block
+    // (a wave past the last query has no output: it skips, and reads no mask entry)
+    if (a.blocks == nullptr ||
+        (q0 + 32 * wave < n && a.blocks[((long)h * a.n_qb + (q0 + 32 * wave) / 64) * a.n_kb + t])) {
     // S^T = K Q^T and dP^T = V dO^T: C[m = key][n = query]
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -493,6 +506,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
         dqacc[db] = mfma32x32x16<BF16>(ko, __builtin_bit_cast(i16x8, sb), dqacc[db]);
       }
     }
+    }   // selected block
 
     if (t + 1 < t_end) store_tile(stage ^ 1);
     __syncthreads();
@@ -538,6 +552,8 @@ BwdArgs make_args(const BwdParams& p) {
   a.seqlens = p.seqlens;
   a.slopes = nullptr;
   a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
+  a.blocks = nullptr;
+  a.n_qb = a.n_kb = 0;
   const long long row = (long long)p.D * 2, head = (long long)p.N * row, batch = p.H * head;
   a.q_bs = a.k_bs = a.v_bs = a.o_bs = a.g_bs = a.dq_bs = a.dk_bs = a.dv_bs = batch;
   a.q_hs = a.k_hs = a.v_hs = a.o_hs = a.g_hs = a.dq_hs = a.dk_hs = a.dv_hs = head;
@@ -607,6 +623,9 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.seqlens = nullptr;
   a.slopes = p.slopes;
   a.drop = p.drop;
+  a.blocks = p.blocks;
+  a.n_qb = (p.Nq + 63) / 64;
+  a.n_kb = (p.Nk + 63) / 64;
   const bool alibi = p.slopes != nullptr, drop = p.drop.scale != 1.f;
   a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
   a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);

@@ -72,6 +72,8 @@ struct FwdArgs {
   float* plse;    //              and its natural-log LSE [n_split, B*H, nq]
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
   Dropout drop;          // used by the DROPOUT instances only
+  const unsigned char* blocks;   // block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks, or null
+  int n_qb, n_kb;
   float c;        // |softmax_scale| * log2(e)
   unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
   int causal, wl, wr;
@@ -126,6 +128,11 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   // key position i + off; the mask works on positions.
   const int wq0 = q0 + 32 * QB * wave;
   const int wq1 = wq0 + 32 * QB - 1;
+  // block-sparse: this wave's row of the block mask (its queries lie in one 64-query block;
+  // a key tile is one 64-key block)
+  static_assert(32 * QB <= 64 && kBc == 64, "a wave's tile lies in one 64 x 64 block");
+  const unsigned char* brow =
+      a.blocks ? a.blocks + ((long)h * a.n_qb + wq0 / 64) * a.n_kb : nullptr;
 
   // Q^T as the B operand: lane holds query (wq0 + 32 qb + l32), head-dim chunk 2 ks + hi.
   i16x8 qreg[QB][kKs];
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     const char FA_LDS* vt = kt + kTileBytes;
     if (t + 1 < t_end) load_tile(t + 1);
     const int j0 = t * kBc;
-    if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo) {
+    if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo && (brow == nullptr || brow[t])) {
       if (mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
         tile(std::false_type{}, kt, vt, j0);
       else
@@ -436,6 +443,8 @@ hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
   a.po = a.plse = nullptr;
   a.slopes = nullptr;
   a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
+  a.blocks = nullptr;
+  a.n_qb = a.n_kb = 0;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   return launch_args<D, BF16, WAVES, QB>(a, stream);
 }
@@ -499,6 +508,9 @@ hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * p.D : nullptr;
   a.slopes = p.slopes;
   a.drop = p.drop;
+  a.blocks = p.blocks;
+  a.n_qb = (p.Nq + 63) / 64;
+  a.n_kb = (p.Nk + 63) / 64;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   if (p.D == 64)
     return p.bf16 ? launch_args<64, true, 4, 1>(a, stream) : launch_args<64, false, 4, 1>(a, stream);

@@ -48,6 +48,8 @@ struct DecArgs {
   float* po;      // n_split > 1: partial O [n_split, B*H, nq, D] and LSE [n_split, B*H, nq]
   float* plse;
   const float* slopes;   // ALiBi slopes [heads] (device), or null
+  const unsigned char* brow0;   // block-sparse mask [heads][n_qb][n_kb] (queries < 64: row 0)
+  int n_qb, n_kb;
   float c;        // softmax_scale * log2(e), signed
   int causal, wl, wr;
 };
@@ -110,7 +112,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   mk.key_range(off, nq - 1 + off, lo, hi);
   lo = max(lo, split * a.split_keys);
   hi = min(hi, (split + 1) * a.split_keys);
-  const bool all_vis = lo < hi && mk.all_visible(off, nq - 1 + off, lo, hi);
+  const bool all_vis = lo < hi && mk.all_visible(off, nq - 1 + off, lo, hi) && a.brow0 == nullptr;
+  // block-sparse: the (single, nq <= 4 < 64) query block's row of the mask
+  const unsigned char* brow = a.brow0 ? a.brow0 + (long)h * a.n_qb * a.n_kb : nullptr;
   const int n_steps = lo < hi ? (hi - lo + STEP - 1) / STEP : 0;
 
   // the queries' 8 elements of this lane, times c (so scores come out in base-2 units)
@@ -171,9 +175,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       for (int qi = 0; qi < NQ; ++qi)
         s[qi][u] = __builtin_fmaf(-b2, __builtin_fabsf((float)(qi + off - r)), s[qi][u]);
       if constexpr (MASKED) {
+        const bool in_block = brow == nullptr || (r < hi && brow[r >> 6]);
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi)
-          s[qi][u] = (r < hi && mk.visible(qi + off, r)) ? s[qi][u] : NEG_INF;
+          s[qi][u] = (r < hi && in_block && mk.visible(qi + off, r)) ? s[qi][u] : NEG_INF;
       }
     }
     float p[NQ][kDecU];
@@ -375,6 +380,9 @@ hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stre
   a.po = p.ws;
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * D : nullptr;
   a.slopes = p.slopes;
+  a.brow0 = p.blocks;
+  a.n_qb = (p.Nq + 63) / 64;
+  a.n_kb = (p.Nk + 63) / 64;
   a.c = (float)((double)p.scale * 1.4426950408889634);
   a.causal = p.causal;
   a.wl = p.window_left;

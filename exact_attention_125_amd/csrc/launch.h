@@ -63,6 +63,7 @@ struct KvParams {
   float* ws;           // partial results of key splits (KvPlan::ws_bytes), null if none
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Dropout drop{0u, 0u, 0u, 0u, 1.f};   // scale 1: no dropout
+  const unsigned char* blocks = nullptr;   // block-sparse mask [H][ceil(Nq/64)][ceil(Nk/64)]
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk, D;
   bool bf16;
@@ -112,6 +113,7 @@ struct BwdKvParams {
   float* stats;        // workspace, as for BwdParams with N = N_q
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Dropout drop{0u, 0u, 0u, 0u, 1.f};   // as in the forward call
+  const unsigned char* blocks = nullptr;   // as in the forward call
   Strides sq, sk, sv, so, sg, sdq, sdk, sdv;
   int B, H, Nq, Nk, D;
   bool bf16;

@@ -216,7 +216,17 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * its high half when t is odd) and is kept when that value is at least floor(p 2^16).  The
  * keep probability is thus p quantised to 2^-16.  dropout_p = 0 is no dropout; values
  * outside [0, 1) give FA_ERR_BAD_DROPOUT.  fa_bwd_kv must get the forward's p, seed and
- * offset.  With dropout, calls with N_q <= 4 take the MFMA kernel. */
+ * offset.  With dropout, calls with N_q <= 4 take the MFMA kernel.
+ *
+ * Block-sparse attention: block_mask is a device uint8 array [heads][ceil(N_q / 64)]
+ * [ceil(N_k / 64)] (dense, C order), or NULL for none.  Entry (h, a, c) nonzero selects the
+ * block of queries 64 a .. 64 a + 63 and keys 64 c .. 64 c + 63 of head h (every batch); a pair
+ * in an unselected block is hidden like a masked pair (its score is -inf), and unselected
+ * blocks are skipped, not computed.  This is the block-sparse FlashAttention the A100 page
+ * lists among its next steps (§6) and the sparse attention the FA3.7 page names for very long
+ * sequences (§6); neither fixes a pattern.  It combines with causal, window, ALiBi and dropout;
+ * a query whose row selects no visible key gets O = 0, LSE = -inf.  It must not be an output
+ * buffer; fa_bwd_kv must get the forward's mask. */
 typedef struct fa_strides {
   long long batch, head, row;
 } fa_strides;
@@ -227,8 +237,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    const unsigned char* block_mask, float dropout_p,
+                    unsigned long long dropout_seed, unsigned dropout_offset, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Backward pass of fa_fwd_kv (by recomputation, as fa_bwd): gradients of sum(dout * o) for
  * N_q queries over N_k keys with the queries at the end of the key sequence.
@@ -242,16 +253,16 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
  *   workspace        at least fa_bwd_workspace_size(batch, heads, seqlen_q, head_dim) bytes,
  *                    16-byte aligned; contents on entry do not matter.
  * A row without keys has dQ = 0; with N_q = 0, dK = dV = 0 (and q, o, dout, lse, dq may be
- * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale, alibi_slopes and
- * the dropout arguments must be those of the forward call.  Errors as in fa_bwd and
+ * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale, alibi_slopes,
+ * block_mask and the dropout arguments must be those of the forward call.  Errors as in fa_bwd and
  * fa_fwd_kv. */
 fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
-                    void* stream);
+                    const unsigned char* block_mask, float dropout_p,
+                    unsigned long long dropout_seed, unsigned dropout_offset, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

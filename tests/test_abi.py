@@ -173,7 +173,7 @@ def fwd_kv(lib, q=Q, k=K, v=V, o=O, lse=L, strides=None, nq=5, nk=300, ws=WS, ws
     a = dict(GOOD, **kw)
     return lib.fa_fwd_kv(q, k, v, o, lse, strides, a["B"], a["H"], nq, nk, a["d"], a["dtype"],
                          a["scale"], a["causal"], a["wl"], a["wr"], a.get("slopes"),
-                         a.get("p", 0.0), 0, 0, ws, ws_bytes, None)
+                         a.get("blocks"), a.get("p", 0.0), 0, 0, ws, ws_bytes, None)
 
 
 def test_kv_rejections(lib):
@@ -196,6 +196,8 @@ def test_kv_rejections(lib):
     assert fwd_kv(lib, slopes=SL + 2) == 6          # float32 slopes: 4-byte aligned
     assert fwd_kv(lib, slopes=O) == 10              # not an output
     assert fwd_kv(lib, slopes=L) == 10
+    assert fwd_kv(lib, blocks=O) == 10               # block mask: not an output
+    assert bwd_kv(lib, blocks=DK) == 10
     for p in (-0.1, 1.0, 2.0, float("nan"), float("inf")):
         assert fwd_kv(lib, p=p) == 12
         assert bwd_kv(lib, p=p) == 12
@@ -235,7 +237,7 @@ def bwd_kv(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, strides=N
     a = dict(GOOD, **kw)
     return lib.fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, strides, ws, ws_bytes, a["B"], a["H"],
                          nq, nk, a["d"], a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"],
-                         a.get("slopes"), a.get("p", 0.0), 0, 0, None)
+                         a.get("slopes"), a.get("blocks"), a.get("p", 0.0), 0, 0, None)
 
 
 def test_bwd_kv_rejections(lib):

@@ -23,7 +23,8 @@ def fa():
     return fa
 
 
-def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None, slopes=None):
+def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None, slopes=None,
+            block_mask=None):
     import oracle
     q64, k64, v64 = inp["q64"], inp["k64"], inp["v64"]
     B, H = q64.shape[:2]
@@ -34,7 +35,7 @@ def compare(o, lse, inp, scale, causal, window, dtype, label, heads=None, slopes
     for b, h in heads:
         slope = 0.0 if slopes is None else float(slopes[h])
         ro, rl = oracle.cross_forward(q64[b, h], k64[b, h], v64[b, h], scale, causal, window,
-                                      slope)
+                                      slope, None if block_mask is None else block_mask[h])
         empty = np.isneginf(rl)
         assert np.array_equal(np.isneginf(l64[b, h]), empty), f"{label}: rows without keys differ"
         assert np.all(o64[b, h][empty] == 0.0), f"{label}: O of a row without keys is not 0"
@@ -384,3 +385,61 @@ def test_dropout_reproducible_and_offset_changes_mask(fa):
     c = run_dropout(fa, 1, 2, 64, 512, 64, "bf16", False, (-1, -1), seed=5, p=0.25, rng_seed=7,
                     offset=1)
     assert torch.equal(a, b) and not torch.equal(a, c)
+
+
+# ---------------------------------------------------------------------------- block-sparse
+def random_blocks(H, n_q, n_k, seed, density=0.5):
+    rng = np.random.default_rng(seed)
+    return rng.random((H, -(-n_q // 64), -(-n_k // 64))) < density
+
+
+def run_blocks(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, blocks, backward=False,
+               slopes=None, p=0.0):
+    import oracle
+    import torch
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed)
+    g = W.cross_case(B, H, n_q, 1, d, dtype, seed + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
+    scale = 1.0 / math.sqrt(d)
+    bm = torch.tensor(blocks.astype(np.uint8), device="cuda")
+    sl = None if slopes is None else torch.tensor(slopes, dtype=torch.float32, device="cuda")
+    kw = dict(block_mask=bm, alibi_slopes=sl)
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window, **kw)
+    grads = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window, **kw) if backward else None
+    torch.cuda.synchronize()
+    compare(o, lse, inp, scale, causal, window, dtype,
+            f"blocks nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}", slopes=slopes,
+            block_mask=blocks)
+    if backward:
+        rq, rk, rv = oracle.cross_backward_bh(inp["q64"], inp["k64"], inp["v64"], g["q64"], scale,
+                                              causal, window, slopes, blocks)
+        floor = 1e-3 * float(np.linalg.norm(g["q64"]))
+        for name, got, ref in zip(("dq", "dk", "dv"), grads, (rq, rk, rv)):
+            e = rel_l2(to64(got), ref, floor)
+            assert e <= GRAD_REL_L2, f"blocks {name} rel L2 {e:.3e}"
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (100, 40))])
+@pytest.mark.parametrize("n_q,n_k", [(1, 3000), (4, 20000), (64, 64), (100, 700), (300, 129),
+                                     (128, 8192), (257, 1000)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_block_sparse_forward(fa, causal, window, n_q, n_k, d, dtype):
+    run_blocks(fa, 1, 3, n_q, n_k, d, dtype, causal, window, seed=n_q + n_k,
+               blocks=random_blocks(3, n_q, n_k, seed=7 * n_q + n_k))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_q,n_k", [(64, 64), (100, 700), (300, 129), (257, 1000), (1, 500)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_block_sparse_backward(fa, causal, n_q, n_k, d, dtype):
+    run_blocks(fa, 1, 2, n_q, n_k, d, dtype, causal, (-1, -1), seed=n_q * 3 + n_k,
+               blocks=random_blocks(2, n_q, n_k, seed=n_q + 5 * n_k), backward=True)
+
+
+def test_block_sparse_with_alibi_and_structure(fa):
+    """Block-diagonal, empty and full masks, with ALiBi slopes."""
+    H, n = 3, 320
+    nb = -(-n // 64)
+    blocks = np.stack([np.eye(nb, dtype=bool), np.zeros((nb, nb), bool), np.ones((nb, nb), bool)])
+    run_blocks(fa, 2, H, n, n, 64, "bf16", False, (-1, -1), seed=3, blocks=blocks, backward=True,
+               slopes=alibi_slopes(H))
