@@ -65,6 +65,9 @@ def parse():
                     help="decode and block workloads: ALiBi slopes 2^(-8 h / H), h = 1 .. H")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="block workload: attention dropout probability (seed 1234)")
+    ap.add_argument("--block-density", type=float, default=0.0,
+                    help="block workload: a seeded block-sparse mask selecting about this "
+                         "fraction of the 64 x 64 blocks (0: no mask)")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="(batch, head) slices the oracle times (default: all of them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -499,9 +502,17 @@ def bench_block(args, w):
     """One training step of a query block over a longer key sequence: fa_fwd_kv then fa_bwd_kv
     (the four-wave kernels), MFMA-bound; `value` is algorithmic TFLOP/s over wall time."""
     import oracle
+    import numpy as np
     inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
     g = W.cross_case(w.B, w.H, w.n_q, 1, w.d, w.dtype, w.seed + 1000)["q"]
-    pairs = w.B * w.H * oracle.cross_allowed_pairs(w.n_q, w.n_k, True)
+    blocks = None
+    if args.block_density > 0:
+        blocks = W.draw_blocks(w.H, w.n_q, w.n_k, args.block_density, w.seed)
+        allowed = oracle.cross_allowed_mask(w.n_q, w.n_k, True)
+        pairs = w.B * sum(int((allowed & oracle.block_allowed(w.n_q, w.n_k, blocks[h])).sum())
+                          for h in range(w.H))
+    else:
+        pairs = w.B * w.H * oracle.cross_allowed_pairs(w.n_q, w.n_k, True)
     fwd_flops, bwd_flops = 4.0 * w.d * pairs, 10.0 * w.d * pairs
     cpu = None
     if not args.no_cpu_baseline:   # the oracle on a bounded sample: the first heads' slices
@@ -510,8 +521,10 @@ def bench_block(args, w):
         for i in range(n):
             b, h = divmod(i, w.H)
             args_ = (inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h])
-            oracle.cross_forward(*args_, w.softmax_scale, True)
-            oracle.cross_backward(*args_, g.double().numpy()[b, h], w.softmax_scale, True)
+            bm = None if blocks is None else blocks[h]
+            oracle.cross_forward(*args_, w.softmax_scale, True, block_mask=bm)
+            oracle.cross_backward(*args_, g.double().numpy()[b, h], w.softmax_scale, True,
+                                  block_mask=bm)
         secs = time.perf_counter() - t0
         from oracle import pool
         cpu = {"value": round(n * (fwd_flops + bwd_flops) / (w.B * w.H) / secs / 1e12, 6),
@@ -531,12 +544,13 @@ def bench_block(args, w):
     ws_b = torch.empty(max(fa.bwd_workspace_size(w.B, w.H, w.n_q, w.d), 16), device="cuda",
                        dtype=torch.uint8)
     slopes = alibi_slopes(w.H) if args.alibi else None
+    bmask = None if blocks is None else torch.tensor(blocks.astype(np.uint8), device="cuda")
     state = {}
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        drop = dict(dropout_p=args.dropout, dropout_seed=1234)
+        drop = dict(dropout_p=args.dropout, dropout_seed=1234, block_mask=bmask)
         _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f,
                                     alibi_slopes=slopes, **drop)
         if ev:
@@ -574,7 +588,7 @@ def bench_block(args, w):
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
                    "head_dim": w.d, "causal": True, "pass": "fwd+bwd", "alibi": bool(args.alibi),
-                   "dropout_p": args.dropout,
+                   "dropout_p": args.dropout, "block_density": args.block_density,
                    "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
         "kernels": kernels,
         # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together

@@ -229,8 +229,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   }
   const float c = a.c;
 
-  if (s_begin < s_end) {
-    load_tile(s_begin);
+  // Block-sparse: the workgroup visits only the query steps that one of its two 64-key block
+  // columns selects (the others are neither loaded nor waited for).
+  const int kb0 = k_first / 64, kb1 = min(kb0 + 1, a.n_kb - 1);
+  auto next_step = [&](int s) {   // first visited step at or after s (32 queries = half a block)
+    if (a.blocks != nullptr) {
+      const unsigned char* hm = a.blocks + (long)h * a.n_qb * a.n_kb;
+      while (s < s_end && !(hm[(s >> 1) * a.n_kb + kb0] | hm[(s >> 1) * a.n_kb + kb1])) ++s;
+    }
+    return s;
+  };
+  const int s_first = next_step(s_begin);
+  if (s_first < s_end) {
+    load_tile(s_first);
     store_tile(0);
   }
   __syncthreads();
@@ -239,13 +250,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const int tr_row = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
 
-  for (int s = s_begin; s < s_end; ++s) {
-    const int stage = (s - s_begin) & 1;
+  int stage = 0;
+  for (int s = s_first; s < s_end;) {
     const char FA_LDS* qt = lds + stage * kStage;
     const char FA_LDS* gt = qt + kTileBytes;
     const float FA_LDS* st_lse = (const float FA_LDS*)(qt + 2 * kTileBytes);
     const float FA_LDS* st_delta = st_lse + kQStep;
-    if (s + 1 < s_end) load_tile(s + 1);
+    const int s_next = next_step(s + 1);
+    if (s_next < s_end) load_tile(s_next);
 
     // block-sparse: this wave's 32 keys and the step's 32 queries lie in one 64 x 64 block;
     // an unselected block contributes nothing (the wave still takes part in the copies)
@@ -324,8 +336,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
     }   // selected block
 
-    if (s + 1 < s_end) store_tile(stage ^ 1);
+    if (s_next < s_end) store_tile(stage ^ 1);
     __syncthreads();
+    stage ^= 1;
+    s = s_next;
   }
 
   // epilogue: lane holds key (k_first + 32 wave + l32), dims 32 db + 8 g + 4 hi + 0..3
@@ -424,8 +438,20 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const float c = a.c;
   const float cm = c * mrow;   // -log2(e) LSE
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
+  // Block-sparse: the workgroup visits only the key tiles that one of its two 64-query block
+  // rows selects.
+  const unsigned char* wg_row0 =
+      a.blocks ? a.blocks + ((long)h * a.n_qb + q0 / 64) * a.n_kb : nullptr;
+  const unsigned char* wg_row1 =
+      (a.blocks && q0 / 64 + 1 < a.n_qb) ? wg_row0 + a.n_kb : wg_row0;
+  auto next_tile = [&](int t) {
+    if (wg_row0 != nullptr)
+      while (t < t_end && !(wg_row0[t] | wg_row1[t])) ++t;
+    return t;
+  };
+  const int t_first = next_tile(t_begin);
+  if (t_first < t_end) {
+    load_tile(t_first);
     store_tile(0);
   }
   __syncthreads();
@@ -434,11 +460,12 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const int tr_key = (tg >> 1) * 4 + tr;
   const int tr_byte = (tq & 1) * 8;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int stage = (t - t_begin) & 1;
+  int stage = 0;
+  for (int t = t_first; t < t_end;) {
     const char FA_LDS* kt = lds + stage * 2 * kTileBytes;
     const char FA_LDS* vt = kt + kTileBytes;
-    if (t + 1 < t_end) load_tile(t + 1);
+    const int t_next = next_tile(t + 1);
+    if (t_next < t_end) load_tile(t_next);
 
     // block-sparse: this wave's 32 queries and the 64-key tile lie in one 64 x 64 block
     // (a wave past the last query has no output: it skips, and reads no mask entry)
@@ -508,8 +535,10 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     }
     }   // selected block
 
-    if (t + 1 < t_end) store_tile(stage ^ 1);
+    if (t_next < t_end) store_tile(stage ^ 1);
     __syncthreads();
+    stage ^= 1;
+    t = t_next;
   }
 
   if (row_ok) {

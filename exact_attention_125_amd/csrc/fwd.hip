@@ -192,8 +192,20 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     for (int db = 0; db < kDb; ++db) oacc[db][qb] = f32x16{};
   }
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
+  // Block-sparse: the workgroup visits only the key tiles that one of its two 64-query
+  // block rows selects (the others are neither loaded nor waited for).
+  const unsigned char* wg_row0 =
+      a.blocks ? a.blocks + ((long)h * a.n_qb + q0 / 64) * a.n_kb : nullptr;
+  const unsigned char* wg_row1 =
+      (a.blocks && q0 / 64 + 1 < a.n_qb) ? wg_row0 + a.n_kb : wg_row0;
+  auto next_tile = [&](int t) {   // first visited tile at or after t
+    if (wg_row0 != nullptr)
+      while (t < t_end && !(wg_row0[t] | wg_row1[t])) ++t;
+    return t;
+  };
+  const int t_first = next_tile(t_begin);
+  if (t_first < t_end) {
+    load_tile(t_first);
     store_tile(0);
   }
   __syncthreads();
@@ -340,11 +352,12 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     }
   };
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int stage = (t - t_begin) & 1;
+  int stage = 0;
+  for (int t = t_first; t < t_end;) {
     const char FA_LDS* kt = lds + stage * 2 * kTileBytes;
     const char FA_LDS* vt = kt + kTileBytes;
-    if (t + 1 < t_end) load_tile(t + 1);
+    const int t_next = next_tile(t + 1);
+    if (t_next < t_end) load_tile(t_next);
     const int j0 = t * kBc;
     if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo && (brow == nullptr || brow[t])) {
       if (mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
@@ -352,8 +365,10 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
       else
         tile(std::true_type{}, kt, vt, j0);
     }
-    if (t + 1 < t_end) store_tile(stage ^ 1);
+    if (t_next < t_end) store_tile(stage ^ 1);
     __syncthreads();
+    stage ^= 1;
+    t = t_next;
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); a row that saw no key (possible

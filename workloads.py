@@ -166,6 +166,13 @@ def cross_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int
     return out
 
 
+def draw_blocks(H: int, n_q: int, n_k: int, density: float, seed: int):
+    """A seeded block-sparse mask [H, ceil(n_q / 64), ceil(n_k / 64)] (bool) selecting each
+    64 x 64 block with probability ``density``, from its own stream."""
+    rng = np.random.default_rng([seed, 2])
+    return rng.random((H, -(-n_q // 64), -(-n_k // 64))) < density
+
+
 def random_case(shape, dtype: str, seed: int, with_grad: bool = False, scale_inputs: float = 1.0):
     """Seeded N(0, scale_inputs^2) inputs of an arbitrary shape (edge-case tests)."""
     names = ["q", "k", "v"] + (["do"] if with_grad else [])
