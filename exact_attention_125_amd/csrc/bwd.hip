@@ -278,17 +278,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const bool full = mk.all_visible(q0 + off, q0 + kQStep - 1 + off, k_first, k_first + kKvRows) &&
                       q0 + kQStep <= n;
     unsigned pk[8], dk_pk[8];
+    // DROPOUT: this key's draws for the step's query pairs 8 g + 4 hi + 2 c' + {0, 1}
+    unsigned rw[8][2];
+    if constexpr (DROPOUT) a.drop.pairs8(bh, q0 + 4 * hi, key, rw);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // queries 8 g + 4 hi + 0..3 of this step
       const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st_lse + 8 * g + 4 * hi);
       const f32x4 de = *reinterpret_cast<const f32x4 FA_LDS*>(st_delta + 8 * g + 4 * hi);
       float p[4], d[4];
-      unsigned rnd[2][4];   // DROPOUT: draws of the query pairs 8 g + 4 hi + {0, 1} and {2, 3}
-      if constexpr (DROPOUT) {
-        a.drop.call(bh, q0 + 8 * g + 4 * hi, key, rnd[0]);
-        a.drop.call(bh, q0 + 8 * g + 4 * hi + 2, key, rnd[1]);
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e;
@@ -301,7 +299,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
           pe = (qq < n && mk.visible(qq + off, key)) ? pe : 0.f;
         }
         if constexpr (DROPOUT) {
-          const bool kept = a.drop.keep(rnd[e >> 1], q0 + 8 * g + 4 * hi + e, key);
+          const bool kept = a.drop.keep_half(rw[2 * g + (e >> 1)][e & 1], key & 1);
           p[e] = kept ? pe * a.drop.scale : 0.f;
           d[e] = pe * ((kept ? dp[i] * a.drop.scale : 0.f) + de[e]);
         } else {
@@ -488,14 +486,16 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const int j0 = t * kKStep;
     const bool full = mk.all_visible(q0 + off, q_last + off, j0, j0 + kKStep);
     unsigned dsk[2][8];
+    unsigned rw[2][4][2];   // DROPOUT: this query's draws for each block's four runs of keys
+    if constexpr (DROPOUT) {
+      a.drop.runs4(bh, qi, j0 + 4 * hi, rw[0]);
+      a.drop.runs4(bh, qi, j0 + 32 + 4 * hi, rw[1]);
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float d2[2];
-        unsigned rnd[4];   // DROPOUT: this query's draws for the run of 4 keys holding i
-        if constexpr (DROPOUT)
-          a.drop.call(bh, qi, j0 + 32 * mb + 8 * (i >> 2) + 4 * hi, rnd);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           float x = __builtin_fmaf(sc[mb][i + e], c, cm);
@@ -508,9 +508,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
             const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
             p = (row_ok && mk.visible(qi + off, j)) ? p : 0.f;
           }
-          if constexpr (DROPOUT) {
-            const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
-            d2[e] = p * ((a.drop.keep(rnd, qi, j) ? dp[mb][i + e] * a.drop.scale : 0.f) + ndlt);
+          if constexpr (DROPOUT) {   // key j: half e of word rw[i >> 2][(i & 3) >> 1]
+            const bool kept = a.drop.keep_half(rw[mb][i >> 2][(i & 3) >> 1], e);
+            d2[e] = p * ((kept ? dp[mb][i + e] * a.drop.scale : 0.f) + ndlt);
           } else {
             d2[e] = p * (dp[mb][i + e] + ndlt);
           }

@@ -328,6 +328,57 @@ struct Dropout {
     const unsigned w = (t >> 1) == 0 ? o[0] : (t >> 1) == 1 ? o[1] : (t >> 1) == 2 ? o[2] : o[3];
     return ((t & 1) ? (w >> 16) : (w & 0xffffu)) >= threshold;
   }
+  __device__ __forceinline__ bool keep_half(unsigned w, int high) const {
+    return (high ? (w >> 16) : (w & 0xffffu)) >= threshold;
+  }
+  // Query-per-lane layouts (forward, dQ): lane l holds query i with i & 1 == l & 1, and keys in
+  // four runs jr0 + 8 r + 0..3 (r = 0..3).  The queries 2a, 2a + 1 of lanes l, l ^ 1 share
+  // every call, so each lane makes the calls of two runs and swaps words with its neighbour
+  // (DPP quad_perm [1, 0, 3, 2]; every lane of the wave must be active).  out[r] = the words
+  // of query i for keys jr, jr + 1 (out[r][0], low / high half) and jr + 2, jr + 3 (out[r][1]).
+  __device__ __forceinline__ void runs4(int bh, int i, int jr0, unsigned (&out)[4][2]) const {
+    const int par = i & 1;
+    unsigned own[2][4];
+    call(bh, i, jr0 + 8 * (2 * par + 0), own[0]);
+    call(bh, i, jr0 + 8 * (2 * par + 1), own[1]);
+    unsigned recv[2][2];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        // the neighbour's query has the other parity: send it the words of that parity
+        const unsigned send = par ? own[rr][w] : own[rr][2 + w];
+        recv[rr][w] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool mine = (r >> 1) == par;
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+        out[r][w] = mine ? (par ? own[r & 1][2 + w] : own[r & 1][w]) : recv[r & 1][w];
+    }
+  }
+  // Key-per-lane layout (dK/dV): lane l holds key j with j & 3 == l & 3 and, per step, queries
+  // q0 + 8 g + 2 c' + 0..1 for the call index c = 2 g + c' (c = 0..7).  The four lanes of a quad
+  // (keys 4a .. 4a + 3) share every call, so lane (l & 3) makes calls 2 (l & 3) and
+  // 2 (l & 3) + 1 and the quad broadcasts them.  out[c] = the words of the even and the odd query
+  // of call c for this lane's key (low half for even keys, high half for odd ones).
+  __device__ __forceinline__ void pairs8(int bh, int q0, int j, unsigned (&out)[8][2]) const {
+    const int kq = j & 3;
+    unsigned own[2][4];
+    call(bh, q0 + 8 * kq + 0, j, own[0]);
+    call(bh, q0 + 8 * kq + 2, j, own[1]);
+    static_for<8>([&](auto cc) {
+      constexpr int c = decltype(cc)::value, owner = c >> 1, r = c & 1;
+      constexpr int kBcast = owner | (owner << 2) | (owner << 4) | (owner << 6);   // quad_perm
+      unsigned x[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        x[w] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)own[r][w], kBcast, 0xF, 0xF, false);
+      out[c][0] = (kq >> 1) ? x[1] : x[0];
+      out[c][1] = (kq >> 1) ? x[3] : x[2];
+    });
+  }
 };
 
 // ---------------------------------------------------------------------------- masks

@@ -309,7 +309,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        unsigned rnd[4];   // DROPOUT: the draws of this lane's current run of 4 keys
+        unsigned rw[4][2];   // DROPOUT: this query's draws for the block's four runs of keys
+        if constexpr (DROPOUT) a.drop.runs4(bh, wq0 + 32 * qb + l32, j0 + 32 * mb + 4 * hi, rw);
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           float p0 = exp2_fast(__builtin_fmaf(s[mb][qb][i], c, neg_m));
@@ -319,12 +320,10 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
             p1 = s[mb][qb][i + 1] == NEG_INF ? 0.f : p1;
           }
           part[(i >> 1) & 3] += p0 + p1;
-          if constexpr (DROPOUT) {
-            const int qi = wq0 + 32 * qb + l32;
-            const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if ((i & 3) == 0) a.drop.call(bh, qi, j, rnd);
-            p0 = a.drop.keep(rnd, qi, j) ? p0 * a.drop.scale : 0.f;
-            p1 = a.drop.keep(rnd, qi, j + 1) ? p1 * a.drop.scale : 0.f;
+          if constexpr (DROPOUT) {   // keys j, j + 1: the low and high half of one word
+            const unsigned w = rw[i >> 2][(i & 3) >> 1];
+            p0 = a.drop.keep_half(w, 0) ? p0 * a.drop.scale : 0.f;
+            p1 = a.drop.keep_half(w, 1) ? p1 * a.drop.scale : 0.f;
           }
           pk[qb][mb][i >> 1] = pack2<BF16>(p0, p1);
         }
