@@ -257,6 +257,10 @@ bool dropout_from(float p, unsigned long long seed, unsigned offset, fa::Dropout
   return true;
 }
 
+bool same_strides(const fa::Strides& a, const fa::Strides& b) {
+  return a.b == b.b && a.h == b.h && a.r == b.r;
+}
+
 bool strides_ok(const fa::Strides& s, int rows) {
   if (s.b < 0 || s.h < 0 || s.r < 0) return false;
   if (s.b % 8 != 0 || s.h % 8 != 0 || s.r % 8 != 0) return false;
@@ -336,6 +340,29 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
         (block_mask && out == (const void*)block_mask))
       return FA_ERR_ALIAS;
 
+  // Plain self-attention (equal lengths, dense operands, nothing extra) takes the kernels of
+  // fa_fwd, which compute the same function.
+  const fa::Strides dq_ = dense_strides(heads, seqlen_q, head_dim);
+  if (seqlen_q == seqlen_k && seqlen_q > fa::kDecodeMaxQ && !alibi_slopes && !block_mask &&
+      drop.scale == 1.f && same_strides(p.sq, dq_) && same_strides(p.sk, dq_) &&
+      same_strides(p.sv, dq_) && same_strides(p.so, dq_)) {
+    fa::FwdParams f;
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.o = o;
+    f.lse = lse;
+    f.B = batch;
+    f.H = heads;
+    f.N = seqlen_q;
+    f.D = head_dim;
+    f.bf16 = dtype == FA_BF16;
+    f.scale = softmax_scale;
+    f.causal = causal != 0;
+    f.window_left = window_left;
+    f.window_right = window_right;
+    return hip_status(fa::launch_fwd(f, static_cast<hipStream_t>(stream)));
+  }
   p.q = q;
   p.k = k;
   p.v = v;
@@ -417,6 +444,36 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
         (block_mask && out == (const void*)block_mask))
       return FA_ERR_ALIAS;
 
+  // Plain self-attention takes the kernels of fa_bwd (the forward took those of fa_fwd).
+  {
+    const fa::Strides d_ = dense_strides(heads, seqlen_q, head_dim);
+    bool dense = seqlen_q == seqlen_k && seqlen_q > fa::kDecodeMaxQ;
+    const fa::Strides* all[] = {&p.sq, &p.sk, &p.sv, &p.so, &p.sg, &p.sdq, &p.sdk, &p.sdv};
+    for (const fa::Strides* x : all) dense = dense && same_strides(*x, d_);
+    if (dense && !alibi_slopes && !block_mask && dropout_p == 0.f) {
+      fa::BwdParams b;
+      b.q = q;
+      b.k = k;
+      b.v = v;
+      b.o = o;
+      b.dout = dout;
+      b.lse = lse;
+      b.dq = dq;
+      b.dk = dk;
+      b.dv = dv;
+      b.stats = static_cast<float*>(workspace);
+      b.B = batch;
+      b.H = heads;
+      b.N = seqlen_q;
+      b.D = head_dim;
+      b.bf16 = dtype == FA_BF16;
+      b.scale = softmax_scale;
+      b.causal = causal != 0;
+      b.window_left = window_left;
+      b.window_right = window_right;
+      return hip_status(fa::launch_bwd(b, fa::kBwdAll, static_cast<hipStream_t>(stream)));
+    }
+  }
   p.q = q;
   p.k = k;
   p.v = v;

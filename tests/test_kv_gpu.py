@@ -443,3 +443,19 @@ def test_block_sparse_with_alibi_and_structure(fa):
     blocks = np.stack([np.eye(nb, dtype=bool), np.zeros((nb, nb), bool), np.ones((nb, nb), bool)])
     run_blocks(fa, 2, H, n, n, 64, "bf16", False, (-1, -1), seed=3, blocks=blocks, backward=True,
                slopes=alibi_slopes(H))
+
+
+def test_plain_self_attention_takes_the_fa_fwd_kernels(fa):
+    """Equal lengths, dense operands and nothing extra: fa_fwd_kv / fa_bwd_kv give bit for bit
+    what fa_fwd / fa_bwd give (they run the same kernels)."""
+    import torch
+    inp = W.cross_case(2, 8, 1024, 1024, 64, "bf16", seed=71)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    do = torch.ones_like(q)
+    o1, l1 = fa.fwd_kv(q, k, v, None, True)
+    o2, l2 = fa.fwd(q, k, v, None, True)
+    g1 = fa.bwd_kv(do, q, k, v, o1, l1, None, True)
+    g2 = fa.bwd(do, q, k, v, o2, l2, None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
