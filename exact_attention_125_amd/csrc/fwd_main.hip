@@ -75,7 +75,9 @@ struct MainArgs {
   char* o;
   float* lse;
   const int* seqlens;   // per-batch lengths (device, may be null: every sequence has n rows)
-  int n;          // rows per (batch, head): the sequence length, or the padded one with seqlens
+  int n;          // query rows per (batch, head): the sequence length, or the padded one with seqlens
+  int nk;         // key rows per (batch, head) (n for self-attention and padded batches)
+  int off;        // key position of query 0 (nk - n; 0 for padded batches)
   int heads;
   int n_bh;       // batch * heads
   int n_qt;       // query tiles per head
@@ -126,12 +128,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
   // as zeros through the buffer resources and written as zeros
   const int nr = a.n;
   const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  // keys: a padded batch has as many as queries; otherwise nk rows, query i at position i + off
+  const int nkr = PADDED ? n : a.nk;
+  const int off = PADDED ? 0 : a.off;
   const long head = (long)bh * nr * RB;
-  const int head_bytes = n * RB;
-  const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
-  const Mask mk{n, a.causal, a.wl, a.wr};
+  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;
+  const int head_bytes = nkr * RB;   // K and V bytes of the head's keys
+  const auto rq = make_rsrc(a.q + head, n * RB);
+  const auto rk = make_rsrc(a.k + khead, head_bytes);
+  const auto rv = make_rsrc(a.v + khead, head_bytes);
+  const Mask mk{nkr, a.causal, a.wl, a.wr};
   const float c = a.c;
   const float NEG_INF = -__builtin_inff();
 
@@ -191,12 +197,25 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     }
 
     int key_lo, key_hi;
-    mk.key_range(q0, min(q0 + kBr - 1, n - 1), key_lo, key_hi);
+    mk.key_range(q0 + off, min(q0 + kBr - 1, n - 1) + off, key_lo, key_hi);
+    if (key_hi <= key_lo) {   // no query of the tile sees a key (only with fewer keys): O = 0
+      if (qi < n) {
+        char* orow = a.o + head + (long)qi * RB;
+#pragma unroll
+        for (int c16 = 0; c16 < RB / 32; ++c16)
+          *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
+        if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
+      }
+      continue;
+    }
     const int t_begin = key_lo / BC;
     const int T = (key_hi + BC - 1) / BC - t_begin;   // key tiles the workgroup visits (>= 1)
-    // visible key interval of this lane's query (edge tiles)
-    const int row_lo = mk.wl >= 0 ? max(0, qi - mk.wl) : 0;
-    const int row_hi = min(n - 1, mk.causal ? qi : (mk.wr >= 0 ? qi + mk.wr : n - 1));
+    // visible key interval of this lane's query (edge tiles), from its key position; a query
+    // that sees no key gets an interval past every key
+    const int qpos = qi + off;
+    int row_lo = mk.wl >= 0 ? max(0, qpos - mk.wl) : 0;
+    int row_hi = min(nkr - 1, mk.causal ? qpos : (mk.wr >= 0 ? qpos + mk.wr : nkr - 1));
+    if (row_hi < row_lo) row_lo = row_hi = nkr + 2 * BC;
 
     // ring stage of a tile is its index mod kNS; ST is that stage where the caller knows it
     auto issue_copies = [&](int tk, int tv, int st_k, int st_v) __attribute__((always_inline)) {
@@ -228,10 +247,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // test is two scalar compares).  Shifts by log2(BC) are floor divisions, also below 0.
     constexpr int SH = BC == 64 ? 6 : 5;
     static_assert((1 << SH) == BC, "tile width is a power of two");
-    int t_in_hi = (n >> SH) - 1;                                          // j1 <= n
-    if (mk.causal) t_in_hi = min(t_in_hi, (wq0 - BC + 1) >> SH);        // j1 - 1 <= q_first
-    if (mk.wr >= 0) t_in_hi = min(t_in_hi, (wq0 + mk.wr - BC + 1) >> SH);
-    const int t_in_lo = (mk.wl >= 0 ? -((mk.wl - wq0 - 31) >> SH) : 0) - t_begin;  // j0 >= q_last - wl
+    const int wp0 = wq0 + off;                                          // key position of wq0
+    int t_in_hi = (nkr >> SH) - 1;                                        // j1 <= n
+    if (mk.causal) t_in_hi = min(t_in_hi, (wp0 - BC + 1) >> SH);        // j1 - 1 <= q_first
+    if (mk.wr >= 0) t_in_hi = min(t_in_hi, (wp0 + mk.wr - BC + 1) >> SH);
+    const int t_in_lo = (mk.wl >= 0 ? -((mk.wl - wp0 - 31) >> SH) : 0) - t_begin;  // j0 >= q_last - wl
     t_in_hi -= t_begin;
     auto edge = [&](int t) __attribute__((always_inline)) {
       return t < t_in_lo || t > t_in_hi;
@@ -297,13 +317,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // masks instead of compares.
     const bool has_lo = mk.causal || mk.wr >= 0, has_hi = mk.wl >= 0;
     const int d_lo = mk.causal ? 0 : mk.wr >= 0 ? -mk.wr : 0;   // q - key >= d_lo (has_lo)
-    const bool band32 = (!has_lo || (d_lo & 31) == 0) && (!has_hi || (mk.wl & 31) == 0);
+    const bool band32 = (!has_lo || (d_lo & 31) == 0) && (!has_hi || (mk.wl & 31) == 0) &&
+                        (off & 31) == 0;
     auto mask = [&](auto xb, int t) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
-      if (band32 && (t_begin + t + 1) * BC <= n) {
+      if (band32 && (t_begin + t + 1) * BC <= nkr) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int x = wq0 - ((t_begin + t) * BC + 32 * mb);   // wave-uniform
+          const int x = wp0 - ((t_begin + t) * BC + 32 * mb);   // wave-uniform
           const int lo = has_lo ? d_lo - x : -32, up = has_hi ? mk.wl - x : 32;
           if (lo >= 32 || up <= -32) {
 #pragma unroll
@@ -592,7 +613,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
     const float l_tot = sum_with_partner(l_run);
     if (qi < n) {
-      const float inv = 1.f / l_tot;
+      // a row that saw no key (fewer keys than queries, or a window past every key): O = 0
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_tot : 0.f;
       char* orow = a.o + head + (long)qi * RB;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -604,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
           *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
         }
       if (a.lse != nullptr && hi == 0)
-        a.lse[(long)bh * nr + qi] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+        a.lse[(long)bh * nr + qi] = live ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : NEG_INF;
     } else if (PADDED && qi < nr) {   // a padding row
       char* orow = a.o + head + (long)qi * RB;
 #pragma unroll
@@ -615,8 +638,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
   }
 }
 
+// nq query rows over nk key rows (dense [B, H, rows, D] operands), query i at key position
+// i + nk - nq; nq == nk for self-attention and padded batches
 template <int D, bool BF16>
-hipError_t launch(const FwdParams& p, hipStream_t stream) {
+hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
   MainArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -624,10 +649,12 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   a.o = static_cast<char*>(p.o);
   a.lse = p.lse;
   a.seqlens = p.seqlens;
-  a.n = p.N;
+  a.n = nq;
+  a.nk = nk;
+  a.off = nk - nq;
   a.heads = p.H;
   a.n_bh = p.B * p.H;
-  a.n_qt = (p.N + kBr - 1) / kBr;
+  a.n_qt = (nq + kBr - 1) / kBr;
   // pairing balances causal rows whose visible key count grows with the query index
   const bool growing = p.causal && p.window_left < 0;
   a.paired = growing && (long)a.n_bh * ((a.n_qt + 1) / 2) >= 256;
@@ -652,8 +679,30 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream) {
-  if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  if (p.D == 64) return p.bf16 ? launch<64, true>(p, p.N, p.N, stream) : launch<64, false>(p, p.N, p.N, stream);
+  return p.bf16 ? launch<128, true>(p, p.N, p.N, stream) : launch<128, false>(p, p.N, p.N, stream);
+}
+
+hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
+  FwdParams f;
+  f.q = p.q;
+  f.k = p.k;
+  f.v = p.v;
+  f.o = p.o;
+  f.lse = p.lse;
+  f.seqlens = nullptr;
+  f.B = p.B;
+  f.H = p.H;
+  f.N = p.Nq;
+  f.D = p.D;
+  f.bf16 = p.bf16;
+  f.scale = p.scale;
+  f.causal = p.causal;
+  f.window_left = p.window_left;
+  f.window_right = p.window_right;
+  if (p.D == 64)
+    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream) : launch<64, false>(f, p.Nq, p.Nk, stream);
+  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream) : launch<128, false>(f, p.Nq, p.Nk, stream);
 }
 
 }  // namespace fa

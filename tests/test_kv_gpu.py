@@ -459,3 +459,25 @@ def test_plain_self_attention_takes_the_fa_fwd_kernels(fa):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+# ---------------------------------------------------------------------------- main kernel, N_q != N_k
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (300, 0)),
+                                           (False, (100, 40)), (True, (256, 0))])
+@pytest.mark.parametrize("n_q,n_k", [(256, 320), (256, 1000), (256, 2065), (512, 300), (130, 4096)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_main_kernel_queries_over_more_keys(fa, causal, window, n_q, n_k, d, dtype):
+    """128 heads: enough query tiles for the main forward kernel (key offsets that are and are
+    not multiples of 32; rows without keys when N_q > N_k)."""
+    B, H = 8, 16
+    o, lse, inp, scale = run_case(fa, B, H, n_q, n_k, d, dtype, causal, window, seed=n_q + n_k)
+    heads = [(b, (3 * b + 5) % H) for b in range(B)] + [(B - 1, H - 1), (0, 0)]
+    compare(o, lse, inp, scale, causal, window, dtype,
+            f"main nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}", heads=heads)
+    if n_q > n_k and causal:
+        assert bool(torch_isneginf_rows(lse, n_q - n_k))
+
+
+def torch_isneginf_rows(lse, rows):
+    import torch
+    return torch.all(torch.isneginf(lse[:, :, :rows])) and torch.all(torch.isfinite(lse[:, :, rows:]))
