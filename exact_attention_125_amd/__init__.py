@@ -6,6 +6,7 @@
     o = fa.attention(q, k, v, causal=True)           # autograd-aware
     o, lse = fa.fwd_kv(q, k, v, causal=True)         # N_q != N_k, any strides
     dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, causal=True)
+    o = fa.attention_kv(q, k, v, causal=True, alibi_slopes=s, dropout_p=0.1, block_mask=m)
 
 q, k, v: contiguous [batch, heads, seqlen, head_dim] float16 / bfloat16 GPU tensors,
 head_dim 64 or 128.  The work runs in the HIP kernels of ``libfa.so`` (C ABI in
@@ -13,8 +14,9 @@ include/fa.h); importing this package fails if that library has not been built.
 """
 from ._lib import (FaError, bwd, bwd_kv, bwd_workspace_size, fwd, fwd_kv,  # noqa: F401
                    fwd_kv_workspace_size, lib)
-from .autograd import attention  # noqa: F401
+from .autograd import attention, attention_kv  # noqa: F401
 
-__all__ = ["fwd", "bwd", "attention", "bwd_workspace_size", "fwd_kv", "fwd_kv_workspace_size",
+__all__ = ["fwd", "bwd", "attention", "attention_kv", "bwd_workspace_size", "fwd_kv",
+           "fwd_kv_workspace_size",
            "bwd_kv",
            "FaError", "lib"]

@@ -481,3 +481,26 @@ def test_main_kernel_queries_over_more_keys(fa, causal, window, n_q, n_k, d, dty
 def torch_isneginf_rows(lse, rows):
     import torch
     return torch.all(torch.isneginf(lse[:, :, :rows])) and torch.all(torch.isfinite(lse[:, :, rows:]))
+
+
+
+def test_autograd_kv_wrapper(fa):
+    """fa.attention_kv through torch.autograd gives bit for bit what fa_fwd_kv / fa_bwd_kv give
+    with the same arguments (ALiBi, dropout and a block mask together); those calls are checked
+    against the oracle above."""
+    import torch
+    B, H, n_q, n_k, d = 1, 2, 150, 400, 64
+    inp = W.cross_case(B, H, n_q, n_k, d, "bf16", seed=81)
+    g = to_dev(W.cross_case(B, H, n_q, 1, d, "bf16", seed=82)["q"])
+    q, k, v = (to_dev(inp[n]).requires_grad_() for n in ("q", "k", "v"))
+    extra = dict(alibi_slopes=torch.tensor([0.25, 0.0625], device="cuda"), dropout_p=0.2,
+                 dropout_seed=5, dropout_offset=1,
+                 block_mask=torch.tensor(random_blocks(H, n_q, n_k, seed=83, density=0.7)
+                                         .astype(np.uint8), device="cuda"))
+    o = fa.attention_kv(q, k, v, 0.125, True, **extra)
+    o.backward(g)
+    o_ref, lse = fa.fwd_kv(q.detach(), k.detach(), v.detach(), 0.125, True, **extra)
+    grads = fa.bwd_kv(g, q.detach(), k.detach(), v.detach(), o_ref, lse, 0.125, True, **extra)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    assert all(torch.equal(a, b) for a, b in zip((q.grad, k.grad, v.grad), grads))
