@@ -683,6 +683,38 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   }
+  // dense operands, nothing extra, and query tiles enough to fill the chip: the dK/dV and dQ
+  // kernels of fa_bwd (their band of visible query - key differences shifted by N_k - N_q)
+  if (!alibi && !drop && p.blocks == nullptr && p.Nq > 0 && p.Nk > 0 &&
+      (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 && is_dense(p.sq, p.H, p.Nq, p.D) &&
+      is_dense(p.so, p.H, p.Nq, p.D) && is_dense(p.sg, p.H, p.Nq, p.D) &&
+      is_dense(p.sdq, p.H, p.Nq, p.D) && is_dense(p.sk, p.H, p.Nk, p.D) &&
+      is_dense(p.sv, p.H, p.Nk, p.D) && is_dense(p.sdk, p.H, p.Nk, p.D) &&
+      is_dense(p.sdv, p.H, p.Nk, p.D)) {
+    BwdParams m;
+    m.q = p.q;
+    m.k = p.k;
+    m.v = p.v;
+    m.o = p.o;
+    m.dout = p.dout;
+    m.lse = p.lse;
+    m.dq = p.dq;
+    m.dk = p.dk;
+    m.dv = p.dv;
+    m.stats = p.stats;
+    m.seqlens = nullptr;
+    m.B = p.B;
+    m.H = p.H;
+    m.N = p.Nq;
+    m.D = p.D;
+    m.bf16 = p.bf16;
+    m.scale = p.scale;
+    m.causal = p.causal;
+    m.window_left = p.window_left;
+    m.window_right = p.window_right;
+    if (hipError_t err = launch_dkdv_main_kv(m, p.Nq, p.Nk, stream); err != hipSuccess) return err;
+    return launch_dq_main_kv(m, p.Nq, p.Nk, stream);
+  }
   if (p.Nk > 0) {
     a.n_tiles = (p.Nk + kKvRows - 1) / kKvRows;
     const dim3 grid((unsigned)((long)a.n_bh * a.n_tiles));

@@ -67,7 +67,8 @@ struct DkdvArgs {
   char* dk;
   char* dv;
   const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
-  int n;                 // rows per (batch, head) in memory
+  int n;                 // query rows per (batch, head) in memory
+  int nk;                // key rows per (batch, head) (n for self-attention, padded batches)
   int heads;
   int n_bh;
   int n_tiles;           // key tiles of KWG keys per head
@@ -125,15 +126,18 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // as zeros through the buffer resources, with zero gradients
   const int nr = a.n;
   const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
-  const long head = (long)bh * nr * RB;
-  const int head_bytes = n * RB;
+  // keys: as many as queries in a padded batch, else nk rows (query i at key position
+  // i + nk - n, which the band dlo .. dhi already accounts for)
+  const int nkr = PADDED ? n : a.nk;
+  const long head = (long)bh * nr * RB;                        // Q, dO
+  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;     // K, V, dK, dV
+  const int head_bytes = n * RB;                               // Q, dO bytes
   const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
+  const auto rk = make_rsrc(a.k + khead, nkr * RB);
+  const auto rv = make_rsrc(a.v + khead, nkr * RB);
   const auto rg = make_rsrc(a.dout + head, head_bytes);
   const int stat_bytes = stat_blocks(nr) * 2 * kStatRows * 4;
   const auto rs = make_rsrc(a.stats + (long)bh * stat_blocks(nr) * 2 * kStatRows, stat_bytes);
-  const Mask mk{n, a.causal, a.wl, a.wr};
   const float c_scale = a.c;
 
   // ---- this wave's keys: K^T and V^T as B operands (lane: key kw0 + 32 kb + l32, dims of
@@ -159,8 +163,10 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     }
 
   // ---- query steps that can see the workgroup's keys
-  int q_lo, q_hi;
-  mk.query_range(k_first, min(k_first + S::KWG, n) - 1, q_lo, q_hi);
+  // (queries i with dlo <= i - j <= dhi for some key j of the workgroup, within [0, n))
+  const int k_last = min(k_first + S::KWG, nkr) - 1;
+  const int q_lo = max(0, k_first + a.dlo);
+  const int q_hi = min(n, k_last + a.dhi + 1);
   const int s_begin = q_lo / kBQ;
   const int NSTEP = (!PADDED || k_first < n) && q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - s_begin : 0;
 
@@ -558,9 +564,9 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw0 + 32 * kb + l32;
-    if (key < (PADDED ? nr : n)) {
-      char* dkrow = a.dk + head + (long)key * RB;
-      char* dvrow = a.dv + head + (long)key * RB;
+    if (key < (PADDED ? nr : nkr)) {
+      char* dkrow = a.dk + khead + (long)key * RB;
+      char* dvrow = a.dv + khead + (long)key * RB;
       const float sc = a.scale;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -596,8 +602,9 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   }
 }
 
+// nq query rows over nk key rows (dense operands); query i at key position i + nk - nq
 template <int D, bool BF16>
-hipError_t launch(const BwdParams& p, hipStream_t stream) {
+hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   using S = DShape<D>;
   DkdvArgs a;
   a.q = static_cast<const char*>(p.q);
@@ -608,10 +615,11 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
   a.seqlens = p.seqlens;
-  a.n = p.N;
+  a.n = nq;
+  a.nk = nk;
   a.heads = p.H;
   a.n_bh = p.B * p.H;
-  a.n_tiles = (p.N + S::KWG - 1) / S::KWG;
+  a.n_tiles = (nk + S::KWG - 1) / S::KWG;
   a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
   a.scale = p.scale;
   a.causal = p.causal;
@@ -622,8 +630,9 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   constexpr int kUnbounded = 1 << 30;
   const int wr = p.window_right < 0 ? kUnbounded : std::min(p.window_right, kUnbounded);
   const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
-  a.dlo = p.causal ? 0 : -wr;
-  a.dhi = wl;
+  // the band in query-index space: positions are indices + nk - nq
+  a.dlo = (p.causal ? 0 : -wr) - (nk - nq);
+  a.dhi = wl - (nk - nq);
   const int half = (a.n_tiles + 1) / 2;
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
@@ -638,8 +647,12 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream) {
-  if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  return launch_dkdv_main_kv(p, p.N, p.N, stream);
+}
+
+hipError_t launch_dkdv_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream) {
+  if (p.D == 64) return p.bf16 ? launch<64, true>(p, nq, nk, stream) : launch<64, false>(p, nq, nk, stream);
+  return p.bf16 ? launch<128, true>(p, nq, nk, stream) : launch<128, false>(p, nq, nk, stream);
 }
 
 }  // namespace fa

@@ -57,7 +57,9 @@ struct DqArgs {
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dq;
   const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
-  int n;                 // rows per (batch, head) in memory
+  int n;                 // query rows per (batch, head) in memory
+  int nk;                // key rows per (batch, head) (n for self-attention, padded batches)
+  int off;               // key position of query 0 (nk - n)
   int heads;
   int n_bh;
   int n_tiles;           // query tiles of QWG queries per head
@@ -109,13 +111,17 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // as zeros through the buffer resources, with zero gradients
   const int nr = a.n;
   const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
-  const long head = (long)bh * nr * RB;
-  const int head_bytes = n * RB;
-  const auto rq = make_rsrc(a.q + head, head_bytes);
-  const auto rk = make_rsrc(a.k + head, head_bytes);
-  const auto rv = make_rsrc(a.v + head, head_bytes);
-  const auto rg = make_rsrc(a.dout + head, head_bytes);
-  const Mask mk{n, a.causal, a.wl, a.wr};
+  // keys: as many as queries in a padded batch, else nk rows, query i at key position i + off
+  const int nkr = PADDED ? n : a.nk;
+  const int off = PADDED ? 0 : a.off;
+  const long head = (long)bh * nr * RB;                        // Q, dO, dQ
+  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;     // K, V
+  const int head_bytes = nkr * RB;                             // K, V bytes
+  const auto rq = make_rsrc(a.q + head, n * RB);
+  const auto rk = make_rsrc(a.k + khead, head_bytes);
+  const auto rv = make_rsrc(a.v + khead, head_bytes);
+  const auto rg = make_rsrc(a.dout + head, n * RB);
+  const Mask mk{nkr, a.causal, a.wl, a.wr};
   const float c_scale = a.c;
 
   // ---- this wave's queries: Q^T and dO^T as B operands (lane: query qw0 + 32 qb + l32, dims
@@ -147,7 +153,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 
   // ---- key steps the workgroup's queries can see
   int k_lo, k_hi;
-  mk.key_range(q_first, min(q_first + S::QWG, n) - 1, k_lo, k_hi);
+  mk.key_range(q_first + off, min(q_first + S::QWG, n) - 1 + off, k_lo, k_hi);
   const int s_begin = k_lo / kBK;
   const int NSTEP = (!PADDED || q_first < n) && k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
 
@@ -471,8 +477,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqAr
   }
 }
 
+// nq query rows over nk key rows (dense operands); query i at key position i + nk - nq
 template <int D, bool BF16>
-hipError_t launch(const BwdParams& p, hipStream_t stream) {
+hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   using S = QShape<D>;
   DqArgs a;
   a.q = static_cast<const char*>(p.q);
@@ -482,10 +489,12 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   a.stats = p.stats;
   a.dq = static_cast<char*>(p.dq);
   a.seqlens = p.seqlens;
-  a.n = p.N;
+  a.n = nq;
+  a.nk = nk;
+  a.off = nk - nq;
   a.heads = p.H;
   a.n_bh = p.B * p.H;
-  a.n_tiles = (p.N + S::QWG - 1) / S::QWG;
+  a.n_tiles = (nq + S::QWG - 1) / S::QWG;
   a.c = (float)((double)softmax_sigma(p.scale) * 1.4426950408889634);
   a.scale = p.scale;
   a.causal = p.causal;
@@ -495,8 +504,9 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   constexpr int kUnbounded = 1 << 30;
   const int wr = p.window_right < 0 ? kUnbounded : std::min(p.window_right, kUnbounded);
   const int wl = p.window_left < 0 ? kUnbounded : std::min(p.window_left, kUnbounded);
-  a.dlo = p.causal ? 0 : -wr;
-  a.dhi = wl;
+  // the band in query-index space: positions are indices + nk - nq
+  a.dlo = (p.causal ? 0 : -wr) - (nk - nq);
+  a.dhi = wl - (nk - nq);
   const int half = (a.n_tiles + 1) / 2;
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
@@ -511,8 +521,12 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream) {
-  if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  return launch_dq_main_kv(p, p.N, p.N, stream);
+}
+
+hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream) {
+  if (p.D == 64) return p.bf16 ? launch<64, true>(p, nq, nk, stream) : launch<64, false>(p, nq, nk, stream);
+  return p.bf16 ? launch<128, true>(p, nq, nk, stream) : launch<128, false>(p, nq, nk, stream);
 }
 
 }  // namespace fa

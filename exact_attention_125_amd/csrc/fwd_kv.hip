@@ -445,17 +445,13 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout) {
   return p;
 }
 
-bool dense(const Strides& s, int H, int rows, int D) {
-  return s.r == D && s.h == (long long)rows * D && s.b == (long long)H * rows * D;
-}
-
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream) {
   // dense operands, nothing extra, one key split, and query tiles enough to fill the chip:
   // the main forward kernel
   if (!plan.decode && plan.n_split == 1 && p.slopes == nullptr && p.blocks == nullptr &&
       p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
-      dense(p.sq, p.H, p.Nq, p.D) && dense(p.so, p.H, p.Nq, p.D) && dense(p.sk, p.H, p.Nk, p.D) &&
-      dense(p.sv, p.H, p.Nk, p.D))
+      is_dense(p.sq, p.H, p.Nq, p.D) && is_dense(p.so, p.H, p.Nq, p.D) &&
+      is_dense(p.sk, p.H, p.Nk, p.D) && is_dense(p.sv, p.H, p.Nk, p.D))
     return launch_fwd_main_kv(p, stream);
   hipError_t e;
   if (plan.decode) {

@@ -53,6 +53,11 @@ struct Strides {
   long long b, h, r;
 };
 
+// Whether s is the dense layout of [B, H, rows, D] (rows of D elements, heads of rows rows).
+inline bool is_dense(const Strides& s, int H, int rows, int D) {
+  return s.r == D && s.h == (long long)rows * D && s.b == (long long)H * rows * D;
+}
+
 // N_q queries over N_k keys: query i sits at key position i + (N_k - N_q).
 struct KvParams {
   const void* q;
@@ -150,5 +155,9 @@ inline float softmax_sigma(float scale) {
 hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream);
 // dQ with query-owned workgroups of one wave per SIMD (bwd_dq.hip).
 hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream);
+// The same two kernels for nq query rows over nk key rows of dense [B, H, rows, D] operands
+// (query i at key position i + nk - nq; p.N is ignored, no padded batch).
+hipError_t launch_dkdv_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream);
+hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream);
 
 }  // namespace fa

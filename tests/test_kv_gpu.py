@@ -504,3 +504,33 @@ def test_autograd_kv_wrapper(fa):
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), o_ref)
     assert all(torch.equal(a, b) for a, b in zip((q.grad, k.grad, v.grad), grads))
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (300, 0)),
+                                           (False, (100, 40))])
+@pytest.mark.parametrize("n_q,n_k", [(256, 320), (256, 1000), (512, 300), (130, 2065)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_main_kernels_backward_queries_over_more_keys(fa, causal, window, n_q, n_k, d, dtype):
+    """128 heads: fa_bwd_kv takes the dK/dV and dQ kernels of fa_bwd (band shifted by the key
+    offset); gradients of sampled heads against the oracle by relative L2."""
+    import oracle
+    import torch
+    B, H = 8, 16
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed=n_q * 3 + n_k)
+    g = W.cross_case(B, H, n_q, 1, d, dtype, seed=n_q * 3 + n_k + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window)
+    torch.cuda.synchronize()
+    heads = [(b, (5 * b + 2) % H) for b in range(B)] + [(0, 0), (B - 1, H - 1)]
+    got = [to64(t) for t in (dq, dk, dv)]
+    for b, h in heads:
+        ref = oracle.cross_backward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                    g["q64"][b, h], scale, causal, window)
+        floor = 1e-3 * float(np.linalg.norm(g["q64"][b, h]))
+        for name, gt, rf in zip(("dq", "dk", "dv"), got, ref):
+            e = rel_l2(gt[b, h], rf, floor)
+            assert e <= GRAD_REL_L2, f"{name} b={b} h={h} nq={n_q} nk={n_k}: rel L2 {e:.3e}"
+    if causal and n_q > n_k:   # rows without keys: zero dQ
+        assert torch.all(dq[:, :, : n_q - n_k] == 0)
