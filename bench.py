@@ -498,6 +498,14 @@ def bench_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+def block_traffic(workload, call):
+    """HBM bytes of the kernels of one fa_fwd_kv ("fwd_kv") or fa_bwd_kv ("bwd_kv") call of the
+    block workload, from the committed counter summary, or None."""
+    keys = ("fwd",) if call == "fwd_kv" else ("delta", "dkdv", "dq")
+    vals = [measured_traffic(k, workload) for k in keys]
+    return None if any(v is None for v in vals) else sum(vals)
+
+
 def bench_block(args, w):
     """One training step of a query block over a longer key sequence: fa_fwd_kv then fa_bwd_kv
     (the four-wave kernels), MFMA-bound; `value` is algorithmic TFLOP/s over wall time."""
@@ -560,6 +568,13 @@ def bench_block(args, w):
         if ev:
             ev[2].record()
 
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -591,9 +606,11 @@ def bench_block(args, w):
                    "dropout_p": args.dropout, "block_density": args.block_density,
                    "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
         "kernels": kernels,
-        # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together
+        # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together;
+        # traffic: the HBM bytes of all kernels of that call
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4),
+                     "traffic": block_traffic(w.name, dom)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
