@@ -534,3 +534,27 @@ def test_main_kernels_backward_queries_over_more_keys(fa, causal, window, n_q, n
             assert e <= GRAD_REL_L2, f"{name} b={b} h={h} nq={n_q} nk={n_k}: rel L2 {e:.3e}"
     if causal and n_q > n_k:   # rows without keys: zero dQ
         assert torch.all(dq[:, :, : n_q - n_k] == 0)
+
+
+def test_block_workload_sampled(fa):
+    """The bench's block training workload at full size, in the configuration the bench times
+    (fa_fwd_kv, then fa_bwd_kv on the tuned kernels); sampled heads against the oracle."""
+    import oracle
+    import torch
+    w = W.BLOCK
+    inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
+    g = W.cross_case(w.B, w.H, w.n_q, 1, w.d, w.dtype, w.seed + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
+    o, lse = fa.fwd_kv(q, k, v, w.softmax_scale, True)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, w.softmax_scale, True)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (3, 7), (w.B - 1, w.H - 1)]
+    compare(o, lse, inp, w.softmax_scale, True, (-1, -1), w.dtype, w.name, heads=heads)
+    got = [to64(t) for t in (dq, dk, dv)]
+    for b, h in heads:
+        ref = oracle.cross_backward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                    g["q64"][b, h], w.softmax_scale, True)
+        floor = 1e-3 * float(np.linalg.norm(g["q64"][b, h]))
+        for name, gt, rf in zip(("dq", "dk", "dv"), got, ref):
+            e = rel_l2(gt[b, h], rf, floor)
+            assert e <= GRAD_REL_L2, f"{w.name} {name} b={b} h={h}: rel L2 {e:.3e}"
