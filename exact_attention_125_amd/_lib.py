@@ -46,6 +46,8 @@ SIGNATURES = {
                        _F, _U64, _U32, _P, _S, _P]),
     "fa_bwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F,
                        _I, _I, _I, _P, _P, _F, _U64, _U32, _P]),
+    "fa_fwd_kv_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _I, _I,
+                           _I, _P, _S, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -265,6 +267,39 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
                           _ptr(block_mask), float(dropout_p), int(dropout_seed),
                           int(dropout_offset), _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, lse
+
+
+def fwd_kv_fp8(q, k, v, k_descale, v_descale, softmax_scale=None, causal=False,
+               window_size=(-1, -1), out=None, return_lse=True, workspace=None):
+    """``fa_fwd_kv_fp8``: a decode step (N_q <= 4) of q [B, H, N_q, d] (fp16 / bf16) over an
+    FP8 E4M3 cache k, v [B, H, N_k, d] (``torch.float8_e4m3fn`` or its ``uint8`` codes), key
+    element ``k_descale * value``, value element ``v_descale * value``.  Any strides with a
+    contiguous last dimension.  Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
+    import torch
+    for t in (k, v):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("k, v must be float8_e4m3fn or uint8 (E4M3 codes)")
+        if not t.is_cuda or t.device != q.device or t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("k, v must be [B, H, N_k, d] on q's device, last dimension contiguous")
+    if q.dtype not in (torch.float16, torch.bfloat16) or q.dim() != 4 or q.stride(-1) != 1:
+        raise ValueError("q must be an fp16 / bf16 [B, H, N_q, d] tensor, last dimension contiguous")
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    if tuple(k.shape) != (B, H, n_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v must be [B, H, N_k, d] to match q {tuple(q.shape)}")
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n_q), device=q.device, dtype=torch.float32) if return_lse else None
+    st = (FaStrides * 4)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o)))
+    need = fwd_kv_workspace_size(B, H, n_q, n_k, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.fa_fwd_kv_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k,
+                              d, _dtype_code(q), scale, float(k_descale), float(v_descale),
+                              int(bool(causal)), wl, wr, _ptr(workspace), ws_bytes,
+                              _stream(q.device)))
     return o, lse
 
 

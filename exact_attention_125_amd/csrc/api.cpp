@@ -385,6 +385,78 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   return hip_status(fa::launch_fwd_kv(p, plan, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_strides* strides, int batch, int heads, int seqlen_q,
+                        int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale,
+                        float k_descale, float v_descale, int causal, int window_left,
+                        int window_right, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  bool empty_q = false, empty_k = false;
+  fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
+                              window_left, window_right, &empty_q);
+  if (st != FA_OK) return st;
+  st = check_common(batch, heads, seqlen_k, head_dim, dtype, softmax_scale, window_left,
+                    window_right, &empty_k);
+  if (st != FA_OK) return st;
+  if (seqlen_q > fa::kDecodeMaxQ) return FA_ERR_BAD_SHAPE;
+  if (!(std::isfinite(k_descale) && k_descale > 0.f && std::isfinite(v_descale) && v_descale > 0.f))
+    return FA_ERR_BAD_SCALE;
+  if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;
+  const bool has_keys = seqlen_k > 0;
+  if (!q || !o || (has_keys && (!k || !v))) return FA_ERR_NULL_PTR;
+
+  fa::KvParams p;
+  if (strides) {
+    p.sq = fa::Strides{strides[0].batch, strides[0].head, strides[0].row};
+    p.sk = fa::Strides{strides[1].batch, strides[1].head, strides[1].row};
+    p.sv = fa::Strides{strides[2].batch, strides[2].head, strides[2].row};
+    p.so = fa::Strides{strides[3].batch, strides[3].head, strides[3].row};
+  } else {
+    p.sq = p.so = dense_strides(heads, seqlen_q, head_dim);
+    p.sk = p.sv = dense_strides(heads, seqlen_k, head_dim);
+  }
+  // the 16-bit bound also covers the one-byte keys and values
+  if (!strides_ok(p.sq, seqlen_q) || !strides_ok(p.so, seqlen_q) || !strides_ok(p.sk, seqlen_k) ||
+      !strides_ok(p.sv, seqlen_k))
+    return FA_ERR_BAD_SHAPE;
+  const fa::KvPlan plan = fa::kv_plan(batch, heads, seqlen_q, seqlen_k, head_dim, false, true);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(o) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+      (lse && !aligned16(lse)) || (plan.ws_bytes > 0 && !aligned16(workspace)))
+    return FA_ERR_MISALIGNED;
+  const void* ins[] = {q, k, v};
+  const void* outs[] = {o, lse, plan.ws_bytes > 0 ? workspace : nullptr};
+  for (const void* out : outs) {
+    if (!out) continue;
+    for (const void* in : ins)
+      if (out == in) return FA_ERR_ALIAS;
+  }
+  if ((lse && (const void*)lse == o) ||
+      (outs[2] && ((const void*)outs[2] == o || (const void*)outs[2] == lse)))
+    return FA_ERR_ALIAS;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  p.D = head_dim;
+  p.bf16 = dtype == FA_BF16;
+  p.fp8 = true;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.scale = softmax_scale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  return hip_status(fa::launch_fwd_kv(p, plan, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 extern "C" {

@@ -32,9 +32,16 @@ namespace fa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecU = 4;   // key rows per row group and step
+constexpr int kDecU = 4;   // key rows per row group and step (16-bit keys)
 
-__host__ __device__ constexpr int dec_step_rows(int d) { return kDecThreads / (d / 8) * kDecU; }
+// Key rows per step: D / 8 lanes per row; an FP8 cache (8-byte lane loads) takes twice the rows
+// per step, so a step keeps as many bytes in flight.
+__host__ __device__ constexpr int dec_step_rows(int d, bool fp8 = false) {
+  return kDecThreads / (d / 8) * kDecU * (fp8 ? 2 : 1);
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct DecArgs {
   const char* q;
@@ -50,7 +57,8 @@ struct DecArgs {
   const float* slopes;   // ALiBi slopes [heads] (device), or null
   const unsigned char* brow0;   // block-sparse mask [heads][n_qb][n_kb] (queries < 64: row 0)
   int n_qb, n_kb;
-  float c;        // softmax_scale * log2(e), signed
+  float c;        // softmax_scale * log2(e) (* the key descale of an FP8 cache), signed
+  float vs;       // the value descale of an FP8 cache (1 otherwise)
   int causal, wl, wr;
 };
 
@@ -66,6 +74,20 @@ __device__ __forceinline__ void unpack8(u32x4 x, float (&f)[8]) {
     const unsigned word = x[w];
     f[2 * w] = to_float<BF16>((unsigned short)(word & 0xffffu));
     f[2 * w + 1] = to_float<BF16>((unsigned short)(word >> 16));
+  }
+}
+
+// Eight FP8 E4M3 codes (the OCP 8-bit format: 4 exponent bits, bias 7, 3 mantissa bits) of
+// one key or value row, lowest address first, widened exactly to float by the hardware.
+__device__ __forceinline__ void unpack8_fp8(u32x2 x, float (&f)[8]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], true);
+    f[4 * w] = lo[0];
+    f[4 * w + 1] = lo[1];
+    f[4 * w + 2] = hi[0];
+    f[4 * w + 3] = hi[1];
   }
 }
 
@@ -86,13 +108,20 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int D, bool BF16, int NQ>
+// FP8: keys and values are FP8 E4M3 codes (one byte per element, 8 bytes per lane); the key
+// descale is folded into a.c and the value descale a.vs scales the normalised output.
+template <int D, bool BF16, int NQ, bool FP8>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
-  constexpr int G = D / 8;                      // lanes per key row, 16 bytes each
+  constexpr int G = D / 8;                      // lanes per key row, 8 elements each
   constexpr int GROUPS = kDecThreads / G;       // rows per load instruction of the workgroup
-  constexpr int STEP = GROUPS * kDecU;          // rows per step
-  constexpr int kRowBytes = D * 2;
-  static_assert(STEP == dec_step_rows(D), "step size");
+  // rows per group and step: an FP8 cache takes twice as many (the same bytes), except at
+  // N_q > 2, where the scores of a step would not fit the registers
+  constexpr int U = FP8 && NQ <= 2 ? 2 * kDecU : kDecU;
+  constexpr int STEP = GROUPS * U;              // rows per step
+  constexpr int kElt = FP8 ? 1 : 2;             // bytes per key / value element
+  constexpr int kRowBytes = D * kElt;
+  using KV = std::conditional_t<FP8, u32x2, u32x4>;   // one lane's 8 elements of a row
+  static_assert(STEP * (FP8 && NQ > 2 ? 2 : 1) == dec_step_rows(D, FP8), "step size");
 
   __shared__ float sm_m[GROUPS][NQ];
   __shared__ float sm_l[GROUPS][NQ];
@@ -145,23 +174,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     for (int e = 0; e < 8; ++e) o[qi][e] = 0.f;
   }
 
-  auto load = [&](u32x4 (&kb)[kDecU], u32x4 (&vb)[kDecU], int r0) {
+  auto load = [&](KV (&kb)[U], KV (&vb)[U], int r0) {
 #pragma unroll
-    for (int u = 0; u < kDecU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int r = r0 + u * GROUPS + grp;
-      kb[u] = buffer_load16(rk, r * a.k_rs + cl * 16);
-      vb[u] = buffer_load16(rv, r * a.v_rs + cl * 16);
+      if constexpr (FP8) {
+        kb[u] = __builtin_amdgcn_raw_buffer_load_b64(rk, r * a.k_rs + cl * 8, 0, 0);
+        vb[u] = __builtin_amdgcn_raw_buffer_load_b64(rv, r * a.v_rs + cl * 8, 0, 0);
+      } else {
+        kb[u] = buffer_load16(rk, r * a.k_rs + cl * 16);
+        vb[u] = buffer_load16(rv, r * a.v_rs + cl * 16);
+      }
     }
   };
+  auto unpack_kv = [](const KV& x, float (&f)[8]) {
+    if constexpr (FP8)
+      unpack8_fp8(x, f);
+    else
+      unpack8<BF16>(x, f);
+  };
 
-  // One step: kDecU rows of this group.  MASKED hides rows past hi and rows a query cannot see.
-  auto step = [&](auto masked_tag, const u32x4 (&kb)[kDecU], const u32x4 (&vb)[kDecU], int r0) {
+  // One step: U rows of this group.  MASKED hides rows past hi and rows a query cannot see.
+  auto step = [&](auto masked_tag, const KV (&kb)[U], const KV (&vb)[U], int r0) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    float s[NQ][kDecU];
+    float s[NQ][U];
 #pragma unroll
-    for (int u = 0; u < kDecU; ++u) {
+    for (int u = 0; u < U; ++u) {
       float kf[8];
-      unpack8<BF16>(kb[u], kf);
+      unpack_kv(kb[u], kf);
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
         float part = qf[qi][0] * kf[0];
@@ -181,17 +221,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
           s[qi][u] = (r < hi && in_block && mk.visible(qi + off, r)) ? s[qi][u] : NEG_INF;
       }
     }
-    float p[NQ][kDecU];
+    float p[NQ][U];
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
       float mx = m[qi];
 #pragma unroll
-      for (int u = 0; u < kDecU; ++u) mx = fmaxf(mx, s[qi][u]);
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[qi][u]);
       const float mu = mx == NEG_INF ? 0.f : mx;
       const float alpha = exp2_fast(m[qi] - mu);   // 0 while nothing was seen
       float sum = 0.f;
 #pragma unroll
-      for (int u = 0; u < kDecU; ++u) {
+      for (int u = 0; u < U; ++u) {
         p[qi][u] = exp2_fast(s[qi][u] - mu);
         sum += p[qi][u];
       }
@@ -201,9 +241,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       m[qi] = mx;
     }
 #pragma unroll
-    for (int u = 0; u < kDecU; ++u) {
+    for (int u = 0; u < U; ++u) {
       float vf[8];
-      unpack8<BF16>(vb[u], vf);
+      unpack_kv(vb[u], vf);
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
@@ -211,7 +251,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     }
   };
 
-  auto run = [&](const u32x4 (&kb)[kDecU], const u32x4 (&vb)[kDecU], int r0) {
+  auto run = [&](const KV (&kb)[U], const KV (&vb)[U], int r0) {
     if (all_vis && r0 + STEP <= hi)
       step(std::false_type{}, kb, vb, r0);
     else
@@ -220,9 +260,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
 
   // Register sets in a ring: the loads of the next one (N_q = 4: register room for one) or two
   // steps are in flight while a step is computed.
-  u32x4 ka[kDecU], va[kDecU], kb2[kDecU], vb2[kDecU];
+  KV ka[U], va[U], kb2[U], vb2[U];
   if constexpr (NQ <= 2) {
-    u32x4 kc[kDecU], vc[kDecU];
+    KV kc[U], vc[U];
     if (n_steps > 0) load(ka, va, lo);
     if (n_steps > 1) load(kb2, vb2, lo + STEP);
     for (int t = 0; t < n_steps; t += 3) {
@@ -270,7 +310,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       O = __builtin_fmaf(w, sm_o[g][qi][e], O);
     }
     const bool live = L > 0.f;
-    const float val = live ? O / L : 0.f;
+    const float val = live ? (FP8 ? O / L * a.vs : O / L) : 0.f;
     const float lse = live ? (mx + __builtin_log2f(L)) * kLn2 : NEG_INF;
     if (a.n_split == 1) {
       char* orow = a.o + b * a.o_bs + h * a.o_hs + (long)qi * a.o_rs;
@@ -357,9 +397,9 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   if (lane == 0 && a.lse != nullptr) a.lse[row] = live ? mx + __builtin_logf(L) : NEG_INF;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool FP8>
 hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stream) {
-  const long long e = 2;
+  const long long e = 2, ekv = FP8 ? 1 : 2;   // bytes per element: queries / outputs, keys / values
   DecArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -367,8 +407,8 @@ hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stre
   a.o = static_cast<char*>(p.o);
   a.lse = p.lse;
   a.q_bs = p.sq.b * e, a.q_hs = p.sq.h * e, a.q_rs = (int)(p.sq.r * e);
-  a.k_bs = p.sk.b * e, a.k_hs = p.sk.h * e, a.k_rs = (int)(p.sk.r * e);
-  a.v_bs = p.sv.b * e, a.v_hs = p.sv.h * e, a.v_rs = (int)(p.sv.r * e);
+  a.k_bs = p.sk.b * ekv, a.k_hs = p.sk.h * ekv, a.k_rs = (int)(p.sk.r * ekv);
+  a.v_bs = p.sv.b * ekv, a.v_hs = p.sv.h * ekv, a.v_rs = (int)(p.sv.r * ekv);
   a.o_bs = p.so.b * e, a.o_hs = p.so.h * e, a.o_rs = (int)(p.so.r * e);
   a.nq = p.Nq;
   a.nk = p.Nk;
@@ -383,17 +423,18 @@ hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stre
   a.brow0 = p.blocks;
   a.n_qb = (p.Nq + 63) / 64;
   a.n_kb = (p.Nk + 63) / 64;
-  a.c = (float)((double)p.scale * 1.4426950408889634);
+  a.c = (float)((double)p.scale * 1.4426950408889634 * (FP8 ? (double)p.k_descale : 1.0));
+  a.vs = FP8 ? p.v_descale : 1.f;
   a.causal = p.causal;
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
   const dim3 grid((unsigned)((long)a.n_bh * a.n_split));
   if (p.Nq == 1)
-    hipLaunchKernelGGL((decode_kernel<D, BF16, 1>), grid, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BF16, 1, FP8>), grid, dim3(kDecThreads), 0, stream, a);
   else if (p.Nq == 2)
-    hipLaunchKernelGGL((decode_kernel<D, BF16, 2>), grid, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BF16, 2, FP8>), grid, dim3(kDecThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, BF16, kDecodeMaxQ>), grid, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BF16, kDecodeMaxQ, FP8>), grid, dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -418,7 +459,7 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout) {
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8) {
   KvPlan p{};
   const long bh = (long)B * H;
   long split_keys;
@@ -427,7 +468,7 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout) {
     // first key rows) and end (merge, stores) latency is paid once per CU pair; at least four
     // steps of keys each
     p.decode = true;
-    const long step = dec_step_rows(D);
+    const long step = dec_step_rows(D, fp8);
     const long want = ceil_div(512, bh > 0 ? bh : 1);
     split_keys = ceil_div(ceil_div(Nk, want), step) * step;
     if (split_keys < 4 * step) split_keys = 4 * step;
@@ -448,17 +489,28 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout) {
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream) {
   // dense operands, nothing extra, one key split, and query tiles enough to fill the chip:
   // the main forward kernel
-  if (!plan.decode && plan.n_split == 1 && p.slopes == nullptr && p.blocks == nullptr &&
+  if (!plan.decode && !p.fp8 && plan.n_split == 1 && p.slopes == nullptr && p.blocks == nullptr &&
       p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
       is_dense(p.sq, p.H, p.Nq, p.D) && is_dense(p.so, p.H, p.Nq, p.D) &&
       is_dense(p.sk, p.H, p.Nk, p.D) && is_dense(p.sv, p.H, p.Nk, p.D))
     return launch_fwd_main_kv(p, stream);
   hipError_t e;
-  if (plan.decode) {
+  if (plan.decode && p.fp8) {
     if (p.D == 64)
-      e = p.bf16 ? launch_decode<64, true>(p, plan, stream) : launch_decode<64, false>(p, plan, stream);
+      e = p.bf16 ? launch_decode<64, true, true>(p, plan, stream)
+                 : launch_decode<64, false, true>(p, plan, stream);
     else
-      e = p.bf16 ? launch_decode<128, true>(p, plan, stream) : launch_decode<128, false>(p, plan, stream);
+      e = p.bf16 ? launch_decode<128, true, true>(p, plan, stream)
+                 : launch_decode<128, false, true>(p, plan, stream);
+  } else if (p.fp8) {
+    return hipErrorInvalidValue;   // an FP8 cache is read by the few-query kernel only
+  } else if (plan.decode) {
+    if (p.D == 64)
+      e = p.bf16 ? launch_decode<64, true, false>(p, plan, stream)
+                 : launch_decode<64, false, false>(p, plan, stream);
+    else
+      e = p.bf16 ? launch_decode<128, true, false>(p, plan, stream)
+                 : launch_decode<128, false, false>(p, plan, stream);
   } else {
     e = launch_fwd_kv_mfma(p, plan, stream);
   }

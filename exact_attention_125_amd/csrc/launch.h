@@ -72,6 +72,9 @@ struct KvParams {
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk, D;
   bool bf16;
+  bool fp8 = false;          // keys and values are FP8 E4M3 codes (the few-query kernel only)
+  float k_descale = 1.f;     // FP8: key element = k_descale * code value
+  float v_descale = 1.f;     // FP8: value element = v_descale * code value
   float scale;
   int causal;
   int window_left;
@@ -90,7 +93,8 @@ struct KvPlan {
 constexpr int kDecodeMaxQ = 4;
 constexpr int kKvMfmaKeyStep = 64;   // key tile of the four-wave MFMA kernel
 // dropout: the few-query kernel has no dropout, so such calls take the MFMA kernel
-KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout);
+// fp8: keys and values are FP8 codes (the few-query kernel then takes twice the rows per step).
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8 = false);
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward kernel (fwd_main.hip) for N_q != N_k over dense operands with no ALiBi,

@@ -264,6 +264,34 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                     const unsigned char* block_mask, float dropout_p,
                     unsigned long long dropout_seed, unsigned dropout_offset, void* stream);
 
+/* ---- Decode steps over an FP8 key/value cache ------------------------------------------
+ * fa_fwd_kv (no ALiBi, dropout or block mask) with K and V held as FP8 E4M3 codes: the OCP
+ * 8-bit floating-point format of sign, 4 exponent bits (bias 7) and 3 mantissa bits, largest
+ * finite magnitude 448, smallest subnormal 2^-9, no infinities, codes 0x7F and 0xFF NaN.
+ * Key element (b, h, r, c) is k_descale * value(code), value element v_descale * value(code).
+ * The A100 page lists FP8 support among its next steps (§6); the cache a decode step reads is
+ * the KV cache of the LLM inference the FA3.7 page names (§1.3) and that PagedAttention pages
+ * through memory (closing section of the PyTorch-CUDA-v2.9 page).  A decode step is bound by
+ * the bytes it reads, and one-byte keys and values halve them.  The scores and the output are
+ * computed in fp32 from the exact decoded values, as in fa_fwd_kv.
+ *
+ *   q, o       [B, H, N_q, head_dim] of dtype (fp16 or bf16); lse out: dense [B, H, N_q]
+ *              float32 or NULL.
+ *   k, v       [B, H, N_k, head_dim] FP8 E4M3 codes, one byte per element.
+ *   strides    NULL (dense) or four fa_strides for q, k, v, o, in elements (one byte for k and
+ *              v), each >= 0 and a multiple of 8; the bounds of fa_fwd_kv apply.
+ *   seqlen_q   0 .. 4; a larger N_q gives FA_ERR_BAD_SHAPE.
+ *   k_descale, v_descale  finite and > 0, else FA_ERR_BAD_SCALE.
+ *   workspace  at least fa_fwd_kv_workspace_size() bytes for the same sizes (16-byte aligned);
+ *              it holds the partial results of key splits.
+ * NaN codes in k or v are outside the domain (not checked).  The reading of positions, masks,
+ * rows without keys and the other errors are those of fa_fwd_kv. */
+fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_strides* strides, int batch, int heads, int seqlen_q,
+                        int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale,
+                        float k_descale, float v_descale, int causal, int window_left,
+                        int window_right, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -34,6 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
                             "fa_fwd_kv_workspace_size", "fa_fwd_kv", "fa_bwd_kv",
+                            "fa_fwd_kv_fp8",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -260,3 +261,23 @@ def test_bwd_kv_rejections(lib):
     # nothing to do
     assert bwd_kv(lib, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, nq=0, nk=0) == 0
     assert bwd_kv(lib, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, B=0) == 0
+
+
+def test_fwd_kv_fp8_argument_errors(lib):
+    """Errors fa_fwd_kv_fp8 reports before it touches a device (no GPU needed)."""
+    import ctypes
+    P = ctypes.c_void_p
+    fake = P(1 << 20)   # never dereferenced: each call fails validation first
+
+    def call(nq=1, nk=64, d=64, kd=1.0, vd=1.0, dtype=1):
+        return lib.fa_fwd_kv_fp8(fake, fake, fake, fake, None, None, 1, 1, nq, nk, d, dtype,
+                                 0.125, kd, vd, 1, -1, -1, None, 0, None)
+
+    assert call(nq=5) == 2                      # FA_ERR_BAD_SHAPE: more than 4 queries
+    assert call(kd=0.0) == 7                    # FA_ERR_BAD_SCALE
+    assert call(vd=float("inf")) == 7
+    assert call(kd=-1.0) == 7
+    assert call(d=96) == 3                      # FA_ERR_UNSUPPORTED_HEAD_DIM
+    assert call(dtype=7) == 4                   # FA_ERR_BAD_DTYPE
+    assert lib.fa_fwd_kv_fp8(None, None, None, None, None, None, 0, 1, 1, 1, 64, 1, 0.125, 1.0,
+                             1.0, 0, -1, -1, None, 0, None) == 0   # empty batch: no-op

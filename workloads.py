@@ -166,6 +166,23 @@ def cross_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int
     return out
 
 
+def fp8_cache_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int,
+                   amax: float = 16.0):
+    """Seeded decode inputs over an FP8 cache: q [B, H, n_q, d] N(0, 1) rounded like
+    ``make_inputs``; k and v [B, H, n_k, d] as E4M3 codes (uint8) of N(0, 1) * amax, rounded to
+    nearest by torch's float8_e4m3fn conversion, with descale 1 / amax (so the decoded keys and
+    values are about N(0, 1)).  Any codes but the NaN ones are valid input; the rounding only
+    picks them."""
+    import torch
+    rng = np.random.default_rng(seed)
+    q, q64 = round_to(rng.standard_normal((B, H, n_q, d), dtype=np.float32), dtype)
+    out = {"q": q, "q64": q64, "k_descale": 1.0 / amax, "v_descale": 1.0 / amax}
+    for name in ("k", "v"):
+        x = torch.from_numpy(rng.standard_normal((B, H, n_k, d), dtype=np.float32) * amax)
+        out[name + "8"] = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out
+
+
 def draw_blocks(H: int, n_q: int, n_k: int, density: float, seed: int):
     """A seeded block-sparse mask [H, ceil(n_q / 64), ceil(n_k / 64)] (bool) selecting each
     64 x 64 block with probability ``density``, from its own stream."""
