@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--alibi", action="store_true",
                     help="decode and block workloads: ALiBi slopes 2^(-8 h / H), h = 1 .. H")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="decode workloads: keys and values as FP8 E4M3 codes (fa_fwd_kv_fp8)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="block workload: attention dropout probability (seed 1234)")
     ap.add_argument("--block-density", type=float, default=0.0,
@@ -229,11 +231,12 @@ def main():
         if os.path.exists(path):
             with open(path, encoding="utf-8") as f:
                 rec = json.load(f)
-        rec.update(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], w.name,
+        name = w.name + ("_kvfp8" if args.kv_fp8 else "")
+        rec.update(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], name,
                                args.copy_calibration_mib or 256))
         with open(path, "w", encoding="utf-8") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
-        print(json.dumps({k: v for k, v in rec.items() if k.startswith(w.name + "/")}, indent=1))
+        print(json.dumps({k: v for k, v in rec.items() if k.startswith(name + "/")}, indent=1))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -389,23 +392,31 @@ def alibi_slopes(H):
                         device="cuda")
 
 
-def decode_bytes(w):
-    """Algorithmic HBM bytes of one decode call: Q, K, V read once, O and LSE written once."""
+def decode_bytes(w, kv_bytes=2):
+    """Algorithmic HBM bytes of one decode call: Q, K, V read once, O and LSE written once
+    (kv_bytes per key / value element: 2, or 1 for an FP8 cache)."""
     e = 2
-    return w.B * w.H * (2 * w.n_k * w.d * e + 2 * w.n_q * w.d * e + w.n_q * 4)
+    return w.B * w.H * (2 * w.n_k * w.d * kv_bytes + 2 * w.n_q * w.d * e + w.n_q * 4)
 
 
 def decode_cpu_baseline(w, inp):
     """The oracle over every (batch, head) of the decode workload, one process."""
     import oracle
     from oracle import pool
+    fp8 = "k8" in inp
     t0 = time.perf_counter()
     for b in range(w.B):
         for h in range(w.H):
-            oracle.cross_forward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
-                                 w.softmax_scale, True)
+            if fp8:
+                oracle.fp8_cache_forward(inp["q64"][b, h], inp["k8"][b, h], inp["v8"][b, h],
+                                         w.softmax_scale, inp["k_descale"], inp["v_descale"],
+                                         True)
+            else:
+                oracle.cross_forward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                     w.softmax_scale, True)
     secs = time.perf_counter() - t0
-    return {"value": round(decode_bytes(w) / secs / 1e9, 3), "unit": "GB/s", "cores": 1,
+    return {"value": round(decode_bytes(w, 1 if fp8 else 2) / secs / 1e9, 3), "unit": "GB/s",
+            "cores": 1,
             "kind": "oracle",
             "sample": f"all {w.B * w.H} (batch, head) slices of {w.name}, float64 numpy "
                       f"materialising S and P, {secs:.2f} s wall, one process "
@@ -415,20 +426,33 @@ def decode_cpu_baseline(w, inp):
 def bench_decode(args, w):
     """One decode step per timed step: fa_fwd_kv with n_q new queries over the n_k-key cache,
     HBM-bound; `value` is algorithmic bytes over wall time."""
-    inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
+    fp8 = bool(args.kv_fp8)
+    if fp8 and args.alibi:
+        raise SystemExit("--kv-fp8 takes no --alibi (the FP8 cache entry point has no ALiBi)")
+    inp = (W.fp8_cache_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed) if fp8
+           else W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed))
     cpu = None if args.no_cpu_baseline else decode_cpu_baseline(w, inp)
     import torch
     import exact_attention_125_amd as fa
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    q, k, v = (inp[n].to("cuda") for n in "qkv")
+    if fp8:
+        q = inp["q"].to("cuda")
+        k, v = (torch.from_numpy(inp[n]).to("cuda") for n in ("k8", "v8"))
+    else:
+        q, k, v = (inp[n].to("cuda") for n in "qkv")
     o = torch.empty_like(q)
     need = fa.fwd_kv_workspace_size(w.B, w.H, w.n_q, w.n_k, w.d)
     ws = torch.empty(max(need, 16), device="cuda", dtype=torch.uint8)
     slopes = alibi_slopes(w.H) if args.alibi else None
 
     def call():
-        fa._lib.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws, alibi_slopes=slopes)
+        if fp8:
+            fa._lib.fwd_kv_fp8(q, k, v, inp["k_descale"], inp["v_descale"], w.softmax_scale,
+                               True, out=o, workspace=ws)
+        else:
+            fa._lib.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws,
+                           alibi_slopes=slopes)
 
     if args.copy_calibration_mib:
         src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
@@ -463,7 +487,7 @@ def bench_decode(args, w):
         torch.cuda.synchronize()
         cold = [a.elapsed_time(b) for a, b in cev]
         del flush
-    nbytes = decode_bytes(w)
+    nbytes = decode_bytes(w, 1 if fp8 else 2)
     ms = wall / args.steps * 1e3
     t_mean = sum(times) / len(times)
     gbs = nbytes / (t_mean * 1e-3) / 1e9
@@ -481,9 +505,11 @@ def bench_decode(args, w):
                   "read once, O and LSE written once)",
         "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) Q, K, V)",
-        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"fp8_e4m3 k/v, {w.dtype} q/o" if fp8 else w.dtype,
+        "data": ("synthetic (seeded N(0,1) Q; K, V as E4M3 codes of N(0,1) * 16, descale 1/16)"
+                 if fp8 else "synthetic (seeded N(0,1) Q, K, V)"),
+        "config": {"workload": w.name + ("_kvfp8" if fp8 else ""), "kv_fp8": fp8, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
                    "head_dim": w.d, "causal": True, "pass": "fwd", "alibi": bool(args.alibi),
                    "bytes_per_step": nbytes, "key_splits": int(plan_splits)},
         "kernels": {"decode+combine": entry},
@@ -492,7 +518,7 @@ def bench_decode(args, w):
         "roofline": {"bound": "hbm", "kernel": "decode_kernel (+ combine_kernel)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("decode", w.name)},
+                     "traffic": measured_traffic("decode", w.name + ("_kvfp8" if fp8 else ""))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
