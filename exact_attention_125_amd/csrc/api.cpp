@@ -246,14 +246,16 @@ fa::Strides dense_strides(int H, int rows, int d) {
 }
 
 // Dropout parameters as the kernels take them: the keep threshold floor(p 2^16) on 16-bit
-// draws and the factor 1 / (1 - p) of kept weights (exactly 1 without dropout).
+// draws and the factor of kept weights, the inverse of the keep probability
+// (2^16 - threshold) / 2^16, so that the expected weight is the undropped one (exactly 1
+// without dropout).
 bool dropout_from(float p, unsigned long long seed, unsigned offset, fa::Dropout* d) {
   if (!(p >= 0.f && p < 1.f)) return false;   // also rejects NaN
   d->seed_lo = (unsigned)(seed & 0xffffffffull);
   d->seed_hi = (unsigned)(seed >> 32);
   d->offset = offset;
   d->threshold = (unsigned)std::floor((double)p * 65536.0);
-  d->scale = p > 0.f ? (float)(1.0 / (1.0 - (double)p)) : 1.f;
+  d->scale = (float)(65536.0 / (double)(65536u - d->threshold));
   return true;
 }
 

@@ -136,8 +136,9 @@ constexpr int kKvRows = 128;   // keys per workgroup (32 per wave)
 constexpr int kQStep = 32;     // queries per step
 
 // ALIBI: P carries the forward's ALiBi penalty, 2^(... - slope log2(e) |p - j|).
-// DROPOUT: the forward's weights were P * keep / (1 - p), so dV uses them and dP is
-// (dO V^T) * keep / (1 - p), with keep drawn again from a.drop.
+// DROPOUT: the forward's weights were P * keep * s (s = a.drop.scale, the inverse of the keep
+// probability), so dV uses them and dP is (dO V^T) * keep * s, with keep drawn again from
+// a.drop.
 template <int D, bool BF16, bool ALIBI, bool DROPOUT>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   constexpr int kRowBytes = D * 2;

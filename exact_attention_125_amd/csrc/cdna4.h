@@ -317,7 +317,7 @@ __device__ __forceinline__ void philox4x32_10(unsigned c0, unsigned c1, unsigned
 struct Dropout {
   unsigned seed_lo, seed_hi, offset;
   unsigned threshold;   // floor(p 2^16); 0 keeps everything
-  float scale;          // 1 / (1 - p)
+  float scale;          // 2^16 / (2^16 - threshold): inverse of the keep probability
   // the call that holds the draws of queries i & ~1, i | 1 for keys j & ~3 .. j | 3
   __device__ __forceinline__ void call(int bh, int i, int j, unsigned (&o)[4]) const {
     philox4x32_10((unsigned)j >> 2, (unsigned)i >> 1, (unsigned)bh, offset, seed_lo, seed_hi, o);

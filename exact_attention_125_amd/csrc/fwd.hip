@@ -89,7 +89,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
 // ALIBI: every score gets the ALiBi penalty -slope_h |p - j| (p the query's key position), in
 // the exponent domain: s <- s c - slope log2(e) |p - j| right after the product, after which
 // the tile works with a unit factor in place of c.
-// DROPOUT: the weights that multiply V are P * keep / (1 - p) (the row sums stay those of P),
+// DROPOUT: the weights that multiply V are P * keep * drop.scale, drop.scale the inverse of the
+// keep probability (the row sums stay those of P),
 // with keep drawn by a.drop.
 template <int D, bool BF16, int WAVES, int QB, bool ALIBI, bool DROPOUT>
 __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdArgs a) {

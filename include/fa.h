@@ -204,8 +204,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * 3.7 核心原理与实战" names for very long sequences in §6).  The values are read by the kernels
  * and not checked: they must be finite.  fa_bwd_kv takes the same slopes.
  *
- * Dropout: with dropout_p in (0, 1) the weights that multiply V are P_ij * M_ij / (1 - p),
- * M_ij in {0, 1}, as the dropout_p argument of the attention calls of the A100 page (§4.2)
+ * Dropout: with dropout_p in (0, 1) the weights that multiply V are P_ij * M_ij / r, M_ij in
+ * {0, 1} kept with probability r (about 1 - p), so that their expectation is P_ij, as the
+ * dropout_p argument of the attention calls of the A100 page (§4.2)
  * and of the SDPA call of the FA3.7 page (§3.2) and the F.dropout of that page's §4.2 module
  * (applied to the softmax weights before V) describe; LSE is that of the softmax before
  * dropout.  M comes from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
@@ -214,8 +215,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * word first) draws 16 bits for each of queries 2 (i >> 1) + {0, 1} and keys
  * 4 (j >> 2) + {0 .. 3}; pair (i, j) takes half-word t = 4 (i & 1) + (j & 3) (word t >> 1,
  * its high half when t is odd) and is kept when that value is at least floor(p 2^16).  The
- * keep probability is thus p quantised to 2^-16.  dropout_p = 0 is no dropout; values
- * outside [0, 1) give FA_ERR_BAD_DROPOUT.  fa_bwd_kv must get the forward's p, seed and
+ * keep probability is thus r = (2^16 - floor(p 2^16)) / 2^16, and kept weights are scaled by
+ * 1 / r = 2^16 / (2^16 - floor(p 2^16)) (rounded to float32).  dropout_p = 0 is no dropout;
+ * values outside [0, 1) give FA_ERR_BAD_DROPOUT.  fa_bwd_kv must get the forward's p, seed and
  * offset.  With dropout, calls with N_q <= 4 take the MFMA kernel.
  *
  * Block-sparse attention: block_mask is a device uint8 array [heads][ceil(N_q / 64)]

@@ -50,7 +50,7 @@ from .cross import (BLOCK, alibi_bias, block_allowed, cross_allowed_mask, cross_
                     cross_backward_bh, cross_forward, cross_forward_bh)
 
 from .dropout import (dropout_backward, dropout_backward_bh, dropout_forward, dropout_forward_bh,
-                      dropout_keep, keep_threshold, philox4x32_10)
+                      dropout_keep, keep_scale, keep_threshold, philox4x32_10)
 from .fp8 import e4m3_value, fp8_cache_forward, fp8_cache_forward_bh
 
 __all__ = [
@@ -60,7 +60,7 @@ __all__ = [
     "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
     "cross_backward", "cross_backward_bh", "alibi_bias", "BLOCK", "block_allowed",
-    "philox4x32_10", "keep_threshold", "dropout_keep", "dropout_forward", "dropout_backward",
+    "philox4x32_10", "keep_threshold", "keep_scale", "dropout_keep", "dropout_forward", "dropout_backward",
     "dropout_forward_bh", "dropout_backward_bh",
     "e4m3_value", "fp8_cache_forward", "fp8_cache_forward_bh",
 ]

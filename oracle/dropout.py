@@ -3,9 +3,10 @@
 Sources: the ``dropout_p`` argument of the attention call in [A100] §4.2 and of the SDPA call
 in [FA37] §3.2, and the ``StandardMultiHeadAttention`` module of [FA37] §4.2, which applies
 ``F.dropout`` to the softmax weights before multiplying by V.  Reading: each weight P_ij is
-kept with probability 1 - p and scaled by 1 / (1 - p), or zeroed:
+kept with probability r (about 1 - p) and scaled by 1 / r, or zeroed, so that the expected
+weight is P_ij itself (the unbiased drop that ``F.dropout`` performs):
 
-    O = (P * M / (1 - p)) V,     M_ij in {0, 1}
+    O = (P * M / r) V,     M_ij in {0, 1},  P(M_ij = 1) = r
 
 The LSE is that of the softmax before dropout (dropout acts on the weights, after the
 normalisation).  The pages fix no generator; M must be reproducible by the GPU and by this
@@ -21,8 +22,9 @@ Counter layout (this library's choice): one call covers 2 queries x 4 keys of on
     counter = (j >> 2, i >> 1, b * H + h, offset),  key = (seed mod 2^32, seed >> 32),
     half-word index t = 4 (i & 1) + (j & 3),  u = bits 16 (t & 1) .. 16 (t & 1) + 15 of word t >> 1
 for query index i and key index j.  Pair (i, j) is kept iff u >= floor(p 2^16), which happens
-with probability 1 - floor(p 2^16) / 2^16 (p quantised to 2^-16); kept weights are scaled by
-exactly 1 / (1 - p).
+with probability r = (2^16 - floor(p 2^16)) / 2^16 (1 - p quantised to 2^-16); kept weights are
+scaled by 1 / r = 2^16 / (2^16 - floor(p 2^16)), the inverse of that probability, so the mean
+of M / r is exactly 1.
 """
 from __future__ import annotations
 
@@ -59,6 +61,12 @@ def keep_threshold(p: float) -> int:
     return int(math.floor(p * 65536.0))
 
 
+def keep_scale(p: float) -> float:
+    """Factor of kept weights: 1 / r with r = (2^16 - floor(p 2^16)) / 2^16 the probability that
+    a pair is kept (1 for p = 0)."""
+    return 65536.0 / (65536 - keep_threshold(p))
+
+
 def dropout_keep(n_q: int, n_k: int, bh: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
     """Boolean [n_q, n_k] keep mask of (batch, head) number bh = b * H + h."""
     i = np.arange(n_q, dtype=np.uint64)[:, None]
@@ -86,19 +94,20 @@ def _probs(q, k, scale, causal, window, slope):
 
 def dropout_forward(q, k, v, scale, causal, window, slope, p_drop, keep):
     """One (batch, head) with the keep mask ``keep`` [N_q, N_k]: (O, LSE) with
-    O = (P * keep / (1 - p)) V and LSE of the softmax before dropout."""
+    O = (P * keep / r) V (1 / r = ``keep_scale(p_drop)``) and LSE of the softmax before
+    dropout."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     p, lse = _probs(q, k, scale, causal, window, slope)
-    return (p * keep / (1.0 - p_drop)) @ v, lse
+    return (p * keep * keep_scale(p_drop)) @ v, lse
 
 
 def dropout_backward(q, k, v, do, scale, causal, window, slope, p_drop, keep):
     """Gradients (dQ, dK, dV) of <dO, O> for ``dropout_forward`` with a fixed mask:
-        dV = (P * keep / (1 - p))^T dO,   dP = (dO V^T) * keep / (1 - p),
+        dV = (P * keep / r)^T dO,   dP = (dO V^T) * keep / r,
         dS = P * (dP - rowsum(P * dP)),   dQ = scale dS K,   dK = scale dS^T Q."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     p, _ = _probs(q, k, scale, causal, window, slope)
-    f = keep / (1.0 - p_drop)
+    f = keep * keep_scale(p_drop)
     dv = (p * f).T @ do
     dp = (do @ v.T) * f
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))

@@ -332,9 +332,10 @@ def run_dropout(fa, B, H, n_q, n_k, d, dtype, causal, window, seed, p, rng_seed,
     diff = np.abs(o64 - ro)
     over = diff > O_TOL[dtype]
     if over.any():
-        # Rows that see few keys have |O| up to about 4 / (1 - p), where one bf16 step exceeds
-        # the fixed tolerance.  The kernel rounds each kept weight P / (1 - p) once to the input
-        # type and O once at the end, so |dO| <= u (sum_j P_ij M_ij / (1 - p) |V_jc| + |O_ic|)
+        # Rows that see few keys have |O| up to about 4 / r (r ~ 1 - p the keep probability),
+        # where one bf16 step exceeds the fixed tolerance.  The kernel rounds each kept weight
+        # P / r once to the input type and O once at the end, so
+        # |dO| <= u (sum_j P_ij M_ij / r |V_jc| + |O_ic|)
         # (u the unit roundoff); elements over the fixed tolerance must be within that bound.
         wabs, _ = oracle.dropout_forward_bh(inp["q64"], inp["k64"], np.abs(inp["v64"]), scale,
                                             causal, window, p, rng_seed, offset, slopes)

@@ -8,11 +8,13 @@
   * the fraction of kept pairs against 1 - p (binomial, 6 sigma) and independence of the
     four words of a call;
   * p = 0 is the plain definition; dropout of an all-ones mask is the plain definition
-    scaled by 1 / (1 - p);
+    scaled by the inverse of the keep probability, and that probability (counted over all
+    2^16 draws of a pair) times the scale is exactly 1, so the drop is unbiased at every p;
   * averaging the dropout output over many seeds approaches the plain output;
   * central differences of the forward with a fixed mask pin the backward.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -88,7 +90,28 @@ def test_zero_probability_is_plain():
     np.testing.assert_allclose(o, ro, rtol=1e-14, atol=1e-14)
     np.testing.assert_array_equal(lse, rl)
     o2, _ = oracle.dropout_forward(q, k, v, 0.5, True, (-1, -1), 0.0, 0.3, np.ones((5, 9), bool))
-    np.testing.assert_allclose(o2, ro / 0.7, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o2 * float(_keep_probability(0.3)), ro, rtol=1e-13, atol=1e-13)
+
+
+def _keep_probability(p):
+    """The probability that a pair is kept, counted over every 16-bit draw u the rule
+    ``u >= floor(p 2^16)`` can see (the draws are uniform: see the keep-fraction test)."""
+    thr = math.floor(p * 2 ** 16)
+    return Fraction(sum(1 for u in range(2 ** 16) if u >= thr), 2 ** 16)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 1 / 3, 0.5, 0.9, 0.99999, 1 - 2 ** -17])
+def test_drop_is_unbiased(p):
+    # E[M * scale] = P(kept) * scale must be exactly 1, also where p 2^16 is far from an
+    # integer (0.99999: keep probability 1/65536, where 1 / (1 - p) would be 1e5)
+    # (up to the float64 rounding of the scale; a factor 1 / (1 - p) is off by 1e-5 at p = 0.1)
+    assert abs(_keep_probability(p) * Fraction(oracle.keep_scale(p)) - 1) <= Fraction(1, 2 ** 52)
+    # and the scale reaches the output: an all-ones mask times the keep probability is the
+    # plain definition
+    q, k, v = _qkv(3, 5, 4, 11)
+    ro, _ = oracle.cross_forward(q, k, v, 0.5, False)
+    o, _ = oracle.dropout_forward(q, k, v, 0.5, False, (-1, -1), 0.0, p, np.ones((3, 5), bool))
+    np.testing.assert_allclose(o * float(_keep_probability(p)), ro, rtol=1e-13, atol=1e-13)
 
 
 def test_mean_over_seeds_approaches_plain_output():
@@ -99,7 +122,7 @@ def test_mean_over_seeds_approaches_plain_output():
     for seed in range(n):
         keep = oracle.dropout_keep(4, 16, 0, 0.3, seed)
         acc += oracle.dropout_forward(q, k, v, 0.5, False, (-1, -1), 0.0, 0.3, keep)[0]
-    # each output is a mean of 16 terms P_ij v_j M_ij / 0.7: its spread is at most
+    # each output is a mean of 16 terms P_ij v_j M_ij / r (r ~ 0.7): its spread is at most
     # max |v| sqrt(0.3 / 0.7); the mean over n seeds must be within 6 sigma of that / sqrt(n)
     bound = 6 * np.abs(v).max() * math.sqrt(0.3 / 0.7) / math.sqrt(n)
     assert np.abs(acc / n - ro).max() < bound
