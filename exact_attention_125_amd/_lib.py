@@ -6,9 +6,13 @@ If the library is missing this module raises on import: there is no fallback pat
 
 Argument names follow the ``flash_attn_fn(q, k, v, dropout_p, softmax_scale, causal,
 window_size, alibi_slopes)`` call listed in "告别OOM和训练慢：用Flash Attention加速你的PyTorch大模型
-（含A100环境配置）" §4.2 (dropout and ALiBi are not supported) and the (batch, num_heads,
-seq_len, head_dim) layout of the SDPA call in "Flash Attention 3.7 核心原理与实战：加速
-Transformer模型训练与推理" §3.2.
+（含A100环境配置）" §4.2 (``fwd_kv`` / ``bwd_kv`` take dropout and ALiBi; ``fwd`` / ``bwd`` do
+not) and the (batch, num_heads, seq_len, head_dim) layout of the SDPA call in "Flash Attention
+3.7 核心原理与实战：加速Transformer模型训练与推理" §3.2.
+
+Caller-supplied outputs (``out``, ``lse``, ``dq``, ``dk``, ``dv``) are checked against the
+inputs before the call: the library sees only their addresses, so an output of the wrong
+size, type or layout would make the kernels write outside it.
 """
 from __future__ import annotations
 
@@ -123,10 +127,44 @@ def _check_tensors(*ts):
             raise ValueError("tensors must be contiguous [B, H, N, d]")
 
 
+def _check_out(t, like, name, dense=True):
+    """An output buffer for a result shaped like ``like``: same device, dtype and shape, last
+    dimension contiguous, no row shared between elements (no zero stride), and dense
+    [B, H, N, d] when the entry point takes no strides (``dense``)."""
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+    if t.dtype != like.dtype:
+        raise ValueError(f"{name} must be {like.dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(like.shape):
+        raise ValueError(f"{name} must have shape {tuple(like.shape)}, got {tuple(t.shape)}")
+    if t.numel() == 0:
+        return
+    if t.stride(-1) != 1 or any(s == 0 for s, n in zip(t.stride(), t.shape) if n > 1):
+        raise ValueError(f"{name} must have a contiguous last dimension and no shared rows")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+
+
+def _check_lse(lse, q, name="lse"):
+    """A float32 [B, H, N_q] contiguous tensor on q's device."""
+    import torch
+    B, H, n = q.shape[0], q.shape[1], q.shape[2]
+    if lse.device != q.device or lse.dtype != torch.float32:
+        raise ValueError(f"{name} must be a float32 tensor on {q.device}")
+    if tuple(lse.shape) != (B, H, n) or not lse.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N_q] = {(B, H, n)} tensor")
+
+
 def _resolve(q, softmax_scale, window_size):
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     wl, wr = (int(window_size[0]), int(window_size[1]))
     return scale, wl, wr
+
+
+def _check_workspace(ws, q):
+    """A contiguous device buffer on q's device (its size is checked by the library)."""
+    if ws.device != q.device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
 
 
 def _check_seqlens(seqlens, q):
@@ -147,11 +185,15 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    if out is not None:
+        _check_out(out, q, "out")
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_lse(lse, q)
     if seqlens is not None:
         _check_seqlens(seqlens, q)
         _check(_lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(seqlens),
@@ -173,12 +215,17 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
     _check_tensors(q, k, v, o, dout)
     B, H, N, d = q.shape
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    _check_lse(lse, q)
+    for g, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if g is not None:
+            _check_out(g, like, name)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     need = _lib.fa_bwd_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check_workspace(workspace, q)
     if seqlens is not None:
         _check_seqlens(seqlens, q)
         _check(_lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
@@ -256,12 +303,16 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    if out is not None:
+        _check_out(out, q, "out", dense=False)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, n_q), device=q.device, dtype=torch.float32) if return_lse else None
     st = (FaStrides * 4)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o)))
     need = fwd_kv_workspace_size(B, H, n_q, n_k, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    if workspace is not None:
+        _check_workspace(workspace, q)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k, d,
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
@@ -289,12 +340,18 @@ def fwd_kv_fp8(q, k, v, k_descale, v_descale, softmax_scale=None, causal=False,
     if tuple(k.shape) != (B, H, n_k, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"k, v must be [B, H, N_k, d] to match q {tuple(q.shape)}")
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    if not q.is_cuda:
+        raise ValueError("q must be on a GPU device")
+    if out is not None:
+        _check_out(out, q, "out", dense=False)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, n_q), device=q.device, dtype=torch.float32) if return_lse else None
     st = (FaStrides * 4)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o)))
     need = fwd_kv_workspace_size(B, H, n_q, n_k, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    if workspace is not None:
+        _check_workspace(workspace, q)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k,
                               d, _dtype_code(q), scale, float(k_descale), float(v_descale),
@@ -318,6 +375,10 @@ def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    _check_lse(lse, q)
+    for g, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if g is not None:
+            _check_out(g, like, name, dense=False)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -327,6 +388,7 @@ def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=
     need = _lib.fa_bwd_workspace_size(B, H, n_q, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check_workspace(workspace, q)
     st = (FaStrides * 8)(*(FaStrides(*t.stride()[:3]) for t in (q, k, v, o, dout, dq, dk, dv)))
     _check(_lib.fa_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), st, _ptr(workspace),

@@ -281,3 +281,32 @@ def test_fwd_kv_fp8_argument_errors(lib):
     assert call(dtype=7) == 4                   # FA_ERR_BAD_DTYPE
     assert lib.fa_fwd_kv_fp8(None, None, None, None, None, None, 0, 1, 1, 1, 64, 1, 0.125, 1.0,
                              1.0, 0, -1, -1, None, 0, None) == 0   # empty batch: no-op
+
+
+def test_binding_rejects_bad_output_buffers():
+    """The Python binding checks caller-supplied outputs before any library call: the library
+    sees only addresses, so a buffer of the wrong size, type or layout would be written past
+    its end (CPU tensors stand in for device ones; only the checks run)."""
+    import torch
+    from exact_attention_125_amd import _lib
+    q = torch.zeros(2, 3, 40, 64, dtype=torch.bfloat16)
+    _lib._check_out(torch.empty_like(q), q, "out")             # a matching buffer passes
+    bad = [torch.zeros(2, 3, 39, 64, dtype=torch.bfloat16),    # too few rows
+           torch.zeros(2, 3, 40, 64, dtype=torch.float32),     # wrong type
+           torch.zeros(2, 3, 40, 128, dtype=torch.bfloat16)[..., ::2],   # strided last dim
+           torch.zeros(2, 3, 40, 64, dtype=torch.bfloat16).transpose(1, 2).contiguous()
+                .transpose(1, 2),                              # not dense [B, H, N, d]
+           torch.zeros(1, 3, 40, 64, dtype=torch.bfloat16).expand(2, 3, 40, 64)]   # shared rows
+    for t in bad:
+        with pytest.raises(ValueError):
+            _lib._check_out(t, q, "out")
+    # strided outputs are fine where the entry point takes strides, shared rows are not
+    _lib._check_out(bad[3], q, "out", dense=False)
+    for t in (bad[2], bad[4]):
+        with pytest.raises(ValueError):
+            _lib._check_out(t, q, "out", dense=False)
+    _lib._check_lse(torch.zeros(2, 3, 40), q)
+    for t in (torch.zeros(2, 3, 40, dtype=torch.float64), torch.zeros(2, 3, 41),
+              torch.zeros(2, 40, 3).transpose(1, 2)):
+        with pytest.raises(ValueError):
+            _lib._check_lse(t, q)

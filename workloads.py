@@ -55,6 +55,14 @@ TRAIN = Workload("train_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1,
 
 ALL = (TINY, BERT, CAUSAL, LONG_4K, LONG_8K, TRAIN)
 
+# Plain causal forward at head dim 128 and N >= 4096 (the long-sequence head dim without the
+# window): the training heads at N = 4096, and half the batch at N = 8192.
+CAUSAL_128_4K = Workload("causal_b8h16n4096d128_bf16", 8, 16, 4096, 128, "bf16", True, (-1, -1),
+                         seed=43)
+CAUSAL_128_8K = Workload("causal_b4h16n8192d128_bf16", 4, 16, 8192, 128, "bf16", True, (-1, -1),
+                         seed=44)
+LONG_128 = (CAUSAL_128_4K, CAUSAL_128_8K)
+
 
 @dataclass(frozen=True)
 class DecodeWorkload:
@@ -106,7 +114,7 @@ BLOCK = BlockWorkload("block_b8h16q1024k4096d64_bf16", 8, 16, 1024, 4096, 64, "b
 # no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
 VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
                   backward=True, padded=True)
-BY_NAME = {w.name: w for w in ALL + (VARLEN,) + DECODES + (BLOCK,)}
+BY_NAME = {w.name: w for w in ALL + LONG_128 + (VARLEN,) + DECODES + (BLOCK,)}
 
 
 def draw_f32(shape, seed: int, count: int):
