@@ -82,31 +82,17 @@ def test_tiny_workload_backward(fa, dtype):
     check_grads(grads, inp, w.softmax_scale, w.causal, w.window, label=f"tiny {dtype}")
 
 
-def test_train_workload_backward(fa):
-    """The full fwd+bwd workload (B=8, H=16, N=4096, d=64, causal, bf16): whole heads at both
-    ends of the batch and two inside against the oracle; exact invariants on every head."""
-    import torch
+def test_train_workload_backward_basic_kernels(fa):
+    """The full fwd+bwd workload (B=8, H=16, N=4096, d=64, causal, bf16) through the four-wave
+    backward kernels, last head against the oracle (the default kernels are checked on every
+    head in test_full_size_gpu.py)."""
     w = W.TRAIN
     inp = W.make_inputs(w)
-    say(f"[train] {w.name}")
+    say(f"[train] {w.name} basic kernels")
     B, H = w.B, w.H
     basic = run(fa, inp, w.softmax_scale, w.causal, w.window, kernel="basic")
     check_grads(basic, inp, w.softmax_scale, w.causal, w.window, heads=[(B - 1, H - 1)],
                 label=w.name + " basic kernels")
-    del basic
-    grads = run(fa, inp, w.softmax_scale, w.causal, w.window)
-    check_grads(grads, inp, w.softmax_scale, w.causal, w.window,
-                heads=[(0, 0), (B - 1, H - 1), (3, 7), (5, 2)], label=w.name)
-    dq, dk, dv = grads
-    for g in grads:
-        assert torch.isfinite(g).all()
-    # every row of P sums to one: sum_j dV_j = sum_i dO_i; every row of dS sums to zero:
-    # sum_j dK_j = 0 (up to the rounding of the stored gradients)
-    sdv = dv.double().sum(dim=2).cpu()
-    sdo = inp["do"].double().sum(dim=2)
-    assert torch.allclose(sdv, sdo, rtol=0, atol=0.05 * float(sdo.abs().max()))
-    sdk = dk.double().sum(dim=2).cpu()
-    assert float(sdk.abs().max()) <= 0.02 * float(dk.double().abs().sum(dim=2).max())
 
 
 # (False, (-1, 64)) and (False, (128, 32)) put band edges on multiples of 32, the case the
