@@ -27,8 +27,9 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA_ERR_BAD_DTYPE", 5: "FA_ERR_BAD_WINDOW", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_BAD_SCALE",
     8: "FA_ERR_WORKSPACE", 9: "FA_ERR_HIP", 10: "FA_ERR_ALIAS", 11: "FA_ERR_BAD_STAGES",
-    12: "FA_ERR_BAD_DROPOUT",
+    12: "FA_ERR_BAD_DROPOUT", 13: "FA_ERR_TOO_LARGE",
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_NOALLOC_SCRATCH_BYTES
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 # Every function include/fa.h declares, with its ctypes signature.
@@ -52,6 +53,8 @@ SIGNATURES = {
                        _I, _I, _I, _P, _P, _F, _U64, _U32, _P]),
     "fa_fwd_kv_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _I, _I,
                            _I, _P, _S, _P]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -239,6 +242,23 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
                               workspace.numel() * workspace.element_size(),
                               B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
                               int(stages), _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale=None, causal=False,
+                window_size=(-1, -1)):
+    """``fa_bwd_noalloc``: ``bwd`` into caller-supplied ``dq``, ``dk``, ``dv`` with the per-query
+    statistics in the library's static device scratch (no allocation by the library or by
+    this wrapper).  Calls that overlap on one device race on that scratch."""
+    _check_tensors(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    _check_lse(lse, q)
+    for g, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_out(g, like, name)
+    _check(_lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _dtype_code(q), scale,
+                               int(bool(causal)), wl, wr, _stream(q.device)))
     return dq, dk, dv
 
 

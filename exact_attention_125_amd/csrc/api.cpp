@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -44,6 +45,45 @@ fa_status hip_status(hipError_t e) {
   return FA_ERR_HIP;
 }
 
+// ---- static scratch of fa_bwd_noalloc
+// One file-scope device array per GPU (each device the library runs on holds its own copy, at
+// its own address, until the process ends).  In host code the array's name is only a host-side
+// stand-in: the device address of a GPU's copy comes from hipGetSymbolAddress, asked once per
+// device with that device current, and only that address is handed to the kernels.  Every
+// call on a device shares its copy; the statistics pass overwrites every slot the later passes
+// read (zeros past the sequence included), so nothing needs clearing, and calls that overlap
+// on one device race on it.
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // device address of each device's `scratch` (null: not asked yet)
+
+// This device's copy (the calling thread's current device), or null after a HIP error.
+void* scratch_of_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_status(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "device ordinal beyond the scratch table";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      hip_status(e);
+      return nullptr;
+    }
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,6 +105,9 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output buffer is also an input buffer";
     case FA_ERR_BAD_STAGES: return "FA_ERR_BAD_STAGES: stage mask empty or unknown bits set";
     case FA_ERR_BAD_DROPOUT: return "FA_ERR_BAD_DROPOUT: dropout_p must be in [0, 1)";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the shape needs more statistics than fa_bwd_noalloc's static "
+             "scratch holds (FA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown fa_status";
 }
@@ -149,7 +192,7 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, const int* seqlens, bool varlen,
                    int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
                    float softmax_scale, int causal, int window_left, int window_right,
-                   unsigned stages, void* stream) {
+                   unsigned stages, void* stream, bool noalloc = false) {
   g_last_error.clear();
   bool empty = false;
   if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_BAD_STAGES;
@@ -161,7 +204,11 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
     return FA_ERR_NULL_PTR;
   if ((reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0) return FA_ERR_MISALIGNED;
   const size_t need = fa_bwd_workspace_size(batch, heads, seqlen, head_dim);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (noalloc) {   // the static scratch replaces the workspace (it aliases no caller buffer)
+    if (need > kScratchBytes) return FA_ERR_TOO_LARGE;
+  } else if (!workspace || workspace_bytes < need) {
+    return FA_ERR_WORKSPACE;
+  }
   const void* ins[] = {q, k, v, o, dout, lse, workspace};
   void* outs[] = {dq, dk, dv};
   for (const void* p : ins)
@@ -198,6 +245,10 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
   p.causal = causal != 0;
   p.window_left = window_left;
   p.window_right = window_right;
+  if (noalloc) {   // validated: only now touch the device
+    p.stats = static_cast<float*>(scratch_of_current_device());
+    if (p.stats == nullptr) return FA_ERR_HIP;
+  }
   return hip_status(fa::launch_bwd(p, stages, static_cast<hipStream_t>(stream)));
 }
 
@@ -224,6 +275,16 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, seqlens, true,
                   batch, heads, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
                   window_right, stages, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                         float softmax_scale, int causal, int window_left, int window_right,
+                         void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, nullptr, false, batch, heads,
+                  seqlen, head_dim, dtype, softmax_scale, causal, window_left, window_right,
+                  FA_BWD_ALL, stream, /*noalloc=*/true);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -67,7 +67,9 @@ typedef enum fa_status {
   FA_ERR_HIP = 9,                 /* the HIP runtime reported an error                  */
   FA_ERR_ALIAS = 10,              /* an output buffer is also an input buffer           */
   FA_ERR_BAD_STAGES = 11,         /* fa_bwd_stages: empty mask or unknown stage bits     */
-  FA_ERR_BAD_DROPOUT = 12         /* dropout_p outside [0, 1)                           */
+  FA_ERR_BAD_DROPOUT = 12,        /* dropout_p outside [0, 1)                           */
+  FA_ERR_TOO_LARGE = 13           /* fa_bwd_noalloc: the shape needs more than its
+                                     static scratch holds                               */
 } fa_status;
 
 typedef enum fa_dtype { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -132,6 +134,27 @@ fa_status fa_bwd_stages(const void* q, const void* k, const void* v, const void*
                         int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
                         float softmax_scale, int causal, int window_left, int window_right,
                         unsigned stages, void* stream);
+
+/* ---- Backward pass without allocation ---------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  fa_bwd_noalloc is fa_bwd
+ * with its per-query statistics kept in a static device array of FA_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on each GPU it runs on until the process ends; it calls no
+ * allocator.  Arguments, results and errors are those of fa_bwd without the workspace
+ * arguments, plus FA_ERR_TOO_LARGE when fa_bwd_workspace_size() of the shape exceeds
+ * FA_NOALLOC_SCRATCH_BYTES (16 MiB: B * H * ceil(N / 32) * 32 <= 2^21 query slots, e.g.
+ * B * H = 128 heads of N = 16384).  The array of the calling thread's current device is used
+ * (the stream must belong to that device); its address is looked up on the first call on each
+ * device.  Every call on one device shares that device's array, so calls that may overlap on
+ * one device (different streams, different host threads) race and must be ordered by the
+ * caller.  Results are bit-identical to fa_bwd's. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
+                         float softmax_scale, int causal, int window_left, int window_right,
+                         void* stream);
 
 /* Padded batches: sequence b is rows 0 .. L_b - 1 of its N rows (every head of batch b), the
  * remaining rows are padding.  This is the per-sample actual length the page "告别OOM和训练慢：

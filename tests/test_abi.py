@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
                             "fa_fwd_kv_workspace_size", "fa_fwd_kv", "fa_bwd_kv",
-                            "fa_fwd_kv_fp8",
+                            "fa_fwd_kv_fp8", "fa_bwd_noalloc",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -82,7 +82,13 @@ def bwd_varlen(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, ws=WS
                              a["wl"], a["wr"], a.get("stages", 7), None)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, fwd_varlen, bwd_varlen])
+def bwd_noalloc(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, a["B"], a["H"], a["N"], a["d"],
+                              a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_varlen, bwd_varlen, bwd_noalloc])
 def test_rejections(lib, call):
     inf = float("inf")
     assert call(lib, dtype=2) == 4
@@ -126,6 +132,24 @@ def test_backward_specific(lib):
     assert bwd(lib, dv=DO) == 10
     assert bwd(lib, dk=DQ) == 10
     assert bwd(lib, ws=DK) == 10
+
+
+def test_noalloc_backward_specific(lib):
+    """fa_bwd_noalloc validates like fa_bwd (no workspace) and refuses shapes whose statistics
+    exceed its static scratch, all before any HIP call."""
+    from exact_attention_125_amd import _lib
+    assert bwd_noalloc(lib, lse=0) == 1
+    assert bwd_noalloc(lib, dv=0) == 1
+    assert bwd_noalloc(lib, dq=Q) == 10
+    assert bwd_noalloc(lib, dk=DQ) == 10
+    # 16 MiB of statistics: 2^21 query slots; one slot more is too large
+    cap = _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.fa_bwd_workspace_size(128, 1, 16384, 64) == cap
+    assert bwd_noalloc(lib, B=128, H=1, N=16384 + 1) == 13
+    assert bwd_noalloc(lib, B=64, H=4, N=8200) == 13
+    assert lib.fa_status_string(13).decode().startswith("FA_ERR_TOO_LARGE")
+    # empty shapes are no-ops
+    assert bwd_noalloc(lib, N=0, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0) == 0
 
 
 def test_padded_batch_specific(lib):
