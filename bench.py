@@ -38,13 +38,15 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
+PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS   # dense FP8 MFMA, published as twice the 16-bit rate
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip",
-                  "api.cpp", "launch.h")
+                  "fwd_fp8.hip", "api.cpp", "launch.h")
 # sources a workload's counters depend on, by workload kind (decode: the few-query kernels)
 DECODE_SOURCES = ("cdna4.h", "fwd_kv.hip", "api.cpp", "launch.h")
 # rocprofv3 kernel names -> the bench's kernel keys
-KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_kernel", "fwd"), ("delta_kernel", "delta"),
+KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_fp8_kernel", "fwd"), ("fwd_kernel", "fwd"),
+               ("delta_kernel", "delta"),
                ("dkdv_main_kernel", "dkdv"), ("dq_main_kernel", "dq"),
                ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"), ("decode_kernel", "decode"),
                ("combine_kernel", "combine"))
@@ -75,6 +77,11 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB device to device three "
                          "times (a plain copy kernel of known traffic, for HBM counter scaling)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of this bench made with the same "
+                         "--workload, --steps, --warmup and --forward-only (and --flush-mib 0): "
+                         "per-kernel durations of the timed dispatches, the warm-up ones apart; "
+                         "updates profiles/kernel_times.json")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench made with --copy-calibration-mib; writes profiles/hbm_traffic.json")
@@ -96,7 +103,7 @@ def allowed_pairs(n, causal, window):
 
 def seqlens_of(w):
     """Per-sample lengths of a padded workload (None for a plain one)."""
-    return [int(x) for x in W.draw_seqlens(w.B, w.N, w.seed)] if w.padded else None
+    return [int(x) for x in W.draw_seqlens(w.B, w.N, w.seed)] if getattr(w, "padded", False) else None
 
 
 def total_pairs(w):
@@ -222,8 +229,83 @@ def pmc_summary(fetch_dir, write_dir, workload, calib_mib):
     return out
 
 
+def pass_name(w, forward_only):
+    return "fwd+bwd" if (getattr(w, "backward", False) and not forward_only) else "fwd"
+
+
+def trace_summary(trace_dir, w, args):
+    """Per-kernel durations from a rocprofv3 kernel trace of this bench: dispatches of each kernel
+    in launch order, the first --warmup of them (the warm-up steps) reported apart, the next
+    --steps averaged; later ones (a cold pass) ignored."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                key = kernel_key(r["Kernel_Name"])
+                if key is None:
+                    continue
+                per.setdefault(key, []).append((int(r["Dispatch_Id"]),
+                                                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for key, rows in per.items():
+        rows.sort()
+        ns = [d for _, d in rows]
+        warm, timed = ns[:args.warmup], ns[args.warmup:args.warmup + args.steps]
+        if not timed:
+            continue
+        out[key] = {"dispatches_timed": len(timed), "avg_us": sum(timed) / len(timed) / 1e3,
+                    "median_us": statistics.median(timed) / 1e3, "min_us": min(timed) / 1e3,
+                    "max_us": max(timed) / 1e3,
+                    "warmup_dispatches": len(warm),
+                    "warmup_avg_us": (sum(warm) / len(warm) / 1e3) if warm else None,
+                    "source_digest": source_digest()}
+    return out
+
+
+def profile_time(kernel, workload, pass_):
+    """Average duration (us) of the kernel's timed dispatches from the committed rocprofv3 trace
+    summary of this workload and pass, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        ent = json.load(f).get(f"{workload}/{pass_}/{kernel}")
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent["avg_us"]
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        w = W.BY_NAME[args.workload]
+        pass_ = pass_name(w, args.forward_only)
+        res = trace_summary(args.trace_summary, w, args)
+        path = os.path.join(ROOT, "profiles", "kernel_times.json")
+        rec = {}
+        if os.path.exists(path):
+            with open(path, encoding="utf-8") as f:
+                rec = json.load(f)
+        for key, ent in res.items():
+            rec[f"{w.name}/{pass_}/{key}"] = ent
+        with open(path, "w", encoding="utf-8") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+        pairs = total_pairs(w)
+        fl = flops(w, pairs)
+        print(f"| kernel | timed dispatches | average us | median us | min us | max us | "
+              f"warm-up average us | TFLOP/s (average) | % of {PEAK_TFLOPS} |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for key in sorted(res, key=lambda k: -res[k]["avg_us"]):
+            e = res[key]
+            kf = {"fwd": fl["fwd"], "dkdv": fl["dkdv"], "dq": fl["dq"]}.get(key)
+            tf = kf / (e["avg_us"] * 1e-6) / 1e12 if kf else None
+            warm = f"{e['warmup_avg_us']:.1f}" if e["warmup_avg_us"] is not None else "-"
+            print(f"| {key} | {e['dispatches_timed']} | {e['avg_us']:.1f} | {e['median_us']:.1f} | "
+                  f"{e['min_us']:.1f} | {e['max_us']:.1f} | {warm} | "
+                  + (f"{tf:.1f} | {100 * tf / PEAK_TFLOPS:.1f}% |" if tf else "- | - |"))
+        return
     if args.pmc_summary:
         w = W.BY_NAME[args.workload]
         path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -249,6 +331,8 @@ def main():
         return bench_decode(args, w)
     if isinstance(w, W.BlockWorkload):
         return bench_block(args, w)
+    if isinstance(w, W.Fp8Workload):
+        return bench_fp8(args, w)
     backward = w.backward and not args.forward_only
 
     # CPU baseline first: the oracle's process pool forks before this process touches the GPU.
@@ -361,6 +445,15 @@ def main():
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(dominant, w.name)}
+    # the same figure from the committed rocprofv3 trace of this workload (null when that trace
+    # was taken on other kernel sources)
+    prof_us = profile_time(dominant, w.name, "fwd+bwd" if backward else "fwd")
+    if prof_us:
+        pa = dom_flops / (prof_us * 1e-6) / 1e12
+        roofline.update(profile_avg_us=round(prof_us, 2), profile_achieved=round(pa, 2),
+                        profile_frac=round(pa / PEAK_TFLOPS, 4))
+    else:
+        roofline.update(profile_avg_us=None, profile_achieved=None, profile_frac=None)
 
     out = {
         "metric": "attention fwd+bwd TFLOP/s on 1 MI355X (fraction of dense bf16 MFMA peak in "
@@ -519,6 +612,96 @@ def bench_decode(args, w):
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("decode", w.name + ("_kvfp8" if fp8 else ""))},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_fp8(args, w):
+    """The forward over FP8 E4M3 queries, keys and values (fa_fwd_fp8): one launch per timed
+    step, TFLOP/s over the visible pairs against the dense FP8 MFMA peak."""
+    import oracle
+    case = W.fp8_attention_case(w.shape, w.seed)
+    desc = (case["q_descale"], case["k_descale"], case["v_descale"])
+    pairs = w.B * w.H * allowed_pairs(w.N, w.causal, w.window)
+    fl = 4.0 * w.d * pairs
+    cpu = None
+    if not args.no_cpu_baseline:   # the oracle on a bounded sample: the first heads' slices
+        from oracle import pool
+        n = args.cpu_sample_heads or 4
+        t0 = time.perf_counter()
+        for i in range(n):
+            b, h = divmod(i, w.H)
+            oracle.fp8_forward(case["q8"][b, h], case["k8"][b, h], case["v8"][b, h],
+                               w.softmax_scale, *desc, w.causal, w.window)
+        secs = time.perf_counter() - t0
+        cpu = {"value": round(n * fl / (w.B * w.H) / secs / 1e12, 6), "unit": "TFLOP/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"{n} of {w.B * w.H} (batch, head) slices of {w.name}, forward, float64 "
+                         f"numpy over the decoded values materialising S and P, {secs:.2f} s "
+                         f"wall, one process ({pool.blas_info()})"}
+    import torch
+    import exact_attention_125_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q, k, v = (torch.from_numpy(case[n + "8"]).to("cuda") for n in "qkv")
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.out_dtype]
+    o = torch.empty(w.shape, device="cuda", dtype=dt)
+    lse = torch.empty(w.B, w.H, w.N, device="cuda", dtype=torch.float32)
+
+    def call():
+        fa.fwd_fp8(q, k, v, *desc, w.softmax_scale, w.causal, w.window, out=o)
+
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a_, b_ in ev:
+        a_.record()
+        call()
+        b_.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [a_.elapsed_time(b_) for a_, b_ in ev]
+    ms = wall / args.steps * 1e3
+    t_mean = sum(times) / len(times)
+    ach = fl / (t_mean * 1e-3) / 1e12
+    entry = {"ms": round(t_mean, 4), "median_ms": round(statistics.median(times), 4),
+             "min_ms": round(min(times), 4), "tflops": round(ach, 2),
+             "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4),
+             "frac_bf16_peak": round(ach / PEAK_TFLOPS, 4)}
+    roofline = {"bound": "mfma", "kernel": "fwd", "achieved": round(ach, 2),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic("fwd", w.name)}
+    prof_us = profile_time("fwd", w.name, "fwd")
+    if prof_us:
+        pa = fl / (prof_us * 1e-6) / 1e12
+        roofline.update(profile_avg_us=round(prof_us, 2), profile_achieved=round(pa, 2),
+                        profile_frac=round(pa / PEAK_FP8_TFLOPS, 4))
+    else:
+        roofline.update(profile_avg_us=None, profile_achieved=None, profile_frac=None)
+    out = {
+        "metric": "attention fwd TFLOP/s on 1 MI355X, FP8 E4M3 Q, K, V (fraction of the dense "
+                  "FP8 MFMA peak in roofline)",
+        "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"fp8_e4m3 q/k/v, {w.out_dtype} o",
+        "data": "synthetic (seeded N(0,1) * 16 as E4M3 codes, descale 1/16 per tensor)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
+                   "head_dim": w.d, "causal": w.causal, "window": list(w.window), "pass": "fwd",
+                   "visible_pairs_per_head": pairs // (w.B * w.H), "flops_per_step": fl},
+        "kernels": {"fwd": entry},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -19,6 +19,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import types
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -53,6 +54,7 @@ SIGNATURES = {
                        _I, _I, _I, _P, _P, _F, _U64, _U32, _P]),
     "fa_fwd_kv_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _I, _I,
                            _I, _P, _S, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I, _I, _I, _P]),
     "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
                             _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -243,6 +245,39 @@ def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1
                               B, H, N, d, _dtype_code(q), scale, int(bool(causal)), wl, wr,
                               int(stages), _stream(q.device)))
     return dq, dk, dv
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, causal=False,
+            window_size=(-1, -1), out_dtype=None, out=None, return_lse=True):
+    """``fa_fwd_fp8``: attention over FP8 E4M3 q, k, v [B, H, N, d] (``torch.float8_e4m3fn`` or
+    their ``uint8`` codes, contiguous, on one device), element value ``descale * value(code)``
+    per tensor.  Returns ``(o, lse)``, ``o`` of ``out_dtype`` (bfloat16 by default, or the dtype
+    of ``out``)."""
+    import torch
+    for t in (q, k, v):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("q, k, v must be float8_e4m3fn or uint8 (E4M3 codes)")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("q, k, v must be on one GPU device")
+        if t.dim() != 4 or tuple(t.shape) != tuple(q.shape) or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors of one shape")
+    B, H, N, d = q.shape
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    like = types.SimpleNamespace(device=q.device, dtype=out_dtype, shape=(B, H, N, d))
+    if out is not None:
+        _check_out(out, like, "out")
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device) if out is None else out
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if return_lse else None
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    _check(_lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                           FA_BF16 if out_dtype == torch.bfloat16 else FA_F16, scale,
+                           float(q_descale), float(k_descale), float(v_descale),
+                           int(bool(causal)), wl, wr, _stream(q.device)))
+    return o, lse
 
 
 def bwd_noalloc(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale=None, causal=False,

@@ -175,6 +175,46 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                   softmax_scale, causal, window_left, window_right, stream);
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads, int seqlen, int head_dim, fa_dtype out_dtype,
+                     float softmax_scale, float q_descale, float k_descale, float v_descale,
+                     int causal, int window_left, int window_right, void* stream) {
+  g_last_error.clear();
+  bool empty = false;
+  fa_status st = check_common(batch, heads, seqlen, head_dim, out_dtype, softmax_scale,
+                              window_left, window_right, &empty);
+  if (st != FA_OK) return st;
+  for (float x : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_BAD_SCALE;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return FA_ERR_MISALIGNED;
+  if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k ||
+      (const void*)lse == v || (void*)lse == o)
+    return FA_ERR_ALIAS;
+  fa::Fp8FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = batch;
+  p.H = heads;
+  p.N = seqlen;
+  p.D = head_dim;
+  p.out_bf16 = out_dtype == FA_BF16;
+  p.scale = softmax_scale;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.causal = causal != 0;
+  p.window_left = window_left;
+  p.window_right = window_right;
+  return hip_status(fa::launch_fwd_fp8(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   bool empty = false;
   if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)

@@ -48,6 +48,24 @@ struct BwdParams {
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 
+// Forward over FP8 E4M3 Q, K, V codes (dense [B, H, N, D], one byte per element) with one
+// descale factor per tensor; O is fp16 or bf16, LSE fp32 (fwd_fp8.hip).
+struct Fp8FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // may be null
+  int B, H, N, D;
+  bool out_bf16;
+  float scale;         // softmax scale
+  float q_descale, k_descale, v_descale;
+  int causal;
+  int window_left;
+  int window_right;
+};
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+
 // Strides of one [B, H, rows, d] operand, in elements (the last dimension is contiguous).
 struct Strides {
   long long b, h, r;

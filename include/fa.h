@@ -317,6 +317,31 @@ fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, fl
                         float k_descale, float v_descale, int causal, int window_left,
                         int window_right, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Forward over FP8 E4M3 queries, keys and values -----------------------------------
+ * fa_fwd with Q, K and V held as E4M3 codes (the format of fa_fwd_kv_fp8 above: the OCP 8-bit
+ * floating-point format, sign / 4 exponent bits with bias 7 / 3 mantissa bits, largest
+ * magnitude 448, 0x7F and 0xFF NaN) and one descale factor per tensor: query element
+ * (b, h, i, c) is q_descale * value(code), and likewise for keys and values.  The attention is
+ * fa_fwd's over those exact values:
+ *     S_ij = softmax_scale * q_descale * k_descale * sum_c value(Q_ic) value(K_jc),
+ *     O_i = v_descale * sum_j softmax_j(S_i) value(V_j),  LSE_i = ln sum_j exp(S_ij),
+ * with fa_fwd's masks.  FP8 support is among the next steps the page "告别OOM和训练慢：用Flash
+ * Attention加速你的PyTorch大模型（含A100环境配置）" lists (§6).  Both products run on gfx950's
+ * FP8 matrix instruction with fp32 accumulation; the probabilities enter the second product
+ * rounded to E4M3 (after an exact power-of-two scaling that keeps them in its normal range),
+ * so each output carries a relative rounding of up to 2^-4 per weight on top of fa_fwd's;
+ * the row sums and LSE use the unrounded probabilities in fp32.
+ *   q, k, v    in:  [B, H, N, head_dim] E4M3 codes, one byte per element, dense, 16-byte aligned
+ *   o          out: [B, H, N, head_dim] of out_dtype (FA_F16 or FA_BF16)
+ *   lse        out: [B, H, N] float32, or NULL
+ *   q_descale, k_descale, v_descale  finite and > 0, else FA_ERR_BAD_SCALE
+ * NaN codes are outside the domain (not checked).  Other arguments, conventions and errors are
+ * those of fa_fwd. */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads, int seqlen, int head_dim, fa_dtype out_dtype,
+                     float softmax_scale, float q_descale, float k_descale, float v_descale,
+                     int causal, int window_left, int window_right, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -32,8 +32,9 @@ Modules
              penalty and block-sparse mask, forward and backward — pinned
   dropout    attention dropout with masks from Philox4x32-10 (a published
              counter-based generator), forward and backward — pinned
-  fp8        decode steps over an FP8 (E4M3) key/value cache: the code values from
-             the OCP definition, then ``cross`` over the descaled values — pinned
+  fp8        decode steps over an FP8 (E4M3) key/value cache, and the forward over
+             FP8 queries, keys and values: the code values from the OCP definition,
+             then ``cross`` / ``attention`` over the descaled values — pinned
   pool       a process pool over (batch, head) for timing the oracle on a
              bounded sample
 
@@ -51,7 +52,7 @@ from .cross import (BLOCK, alibi_bias, block_allowed, cross_allowed_mask, cross_
 
 from .dropout import (dropout_backward, dropout_backward_bh, dropout_forward, dropout_forward_bh,
                       dropout_keep, keep_scale, keep_threshold, philox4x32_10)
-from .fp8 import e4m3_value, fp8_cache_forward, fp8_cache_forward_bh
+from .fp8 import e4m3_value, fp8_cache_forward, fp8_cache_forward_bh, fp8_forward
 
 __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
@@ -62,5 +63,5 @@ __all__ = [
     "cross_backward", "cross_backward_bh", "alibi_bias", "BLOCK", "block_allowed",
     "philox4x32_10", "keep_threshold", "keep_scale", "dropout_keep", "dropout_forward", "dropout_backward",
     "dropout_forward_bh", "dropout_backward_bh",
-    "e4m3_value", "fp8_cache_forward", "fp8_cache_forward_bh",
+    "e4m3_value", "fp8_cache_forward", "fp8_cache_forward_bh", "fp8_forward",
 ]

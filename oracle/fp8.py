@@ -12,11 +12,18 @@ no infinities, and e = 15 with m = 7 is NaN (largest finite magnitude 448).  Eac
 one descale factor: key element = k_descale * value(code), value element = v_descale *
 value(code).  The attention over those exact values is ``cross_forward`` (queries at the last
 N_q key positions).
+
+The FP8 forward (``fp8_forward``) reads queries, keys and values as E4M3 codes, each tensor with
+its own descale: element = descale * value(code).  Its result is the attention of
+``attention.attention_forward`` over those exact values, with the usual masks: the definition
+fixes no intermediate format, so how a kernel rounds the probabilities before the product with V
+is part of its error, not of the reference.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .attention import attention_forward, attention_forward_rows
 from .cross import cross_forward
 
 
@@ -51,3 +58,16 @@ def fp8_cache_forward_bh(q, k_codes, v_codes, scale, k_descale, v_descale, causa
             o[b, h], lse[b, h] = fp8_cache_forward(q[b, h], k_codes[b, h], v_codes[b, h], scale,
                                                    k_descale, v_descale, causal, window)
     return o, lse
+
+
+def fp8_forward(q_codes, k_codes, v_codes, scale, q_descale, k_descale, v_descale, causal=False,
+                window=(-1, -1), rows=None):
+    """One (batch, head) of the FP8 forward: codes [N, d] (uint8) -> (O [N, d], LSE [N]) of the
+    attention over Q = q_descale value(q_codes), K = k_descale value(k_codes),
+    V = v_descale value(v_codes); ``rows`` restricts it to those query rows."""
+    q = float(q_descale) * e4m3_value(q_codes)
+    k = float(k_descale) * e4m3_value(k_codes)
+    v = float(v_descale) * e4m3_value(v_codes)
+    if rows is None:
+        return attention_forward(q, k, v, scale, causal, window)
+    return attention_forward_rows(q, k, v, scale, causal, window, rows=rows)

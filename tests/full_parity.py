@@ -55,6 +55,50 @@ def _ref_head(bh):
     return b, h, out
 
 
+def _init_fp8(name):
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import workloads as W
+    w = W.BY_NAME[name]
+    _G.update(w=w, inp=W.fp8_attention_case(w.shape, w.seed))
+
+
+def _ref_head_fp8(bh):
+    """The FP8 oracle of one head, plus what the kernel's rounding bound needs: the output
+    with |V| (W = sum_j P_ij |V_jc|), the plain sum of |V_jc| over the visible keys, and the
+    per-row bound e_i of the score error."""
+    import oracle
+    b, h = bh
+    w, c = _G["w"], _G["inp"]
+    args = (w.softmax_scale, c["q_descale"], c["k_descale"], c["v_descale"], w.causal, w.window)
+    q8, k8, v8 = c["q8"][b, h], c["k8"][b, h], c["v8"][b, h]
+    o, lse = oracle.fp8_forward(q8, k8, v8, *args)
+    wabs, _ = oracle.fp8_forward(q8, k8, v8 & 0x7F, *args)
+    vis = oracle.allowed_mask(w.N, w.causal, w.window)
+    s1 = vis.astype(np.float64) @ (c["v_descale"] * np.abs(oracle.e4m3_value(v8)))
+    # bound on the score error of the FP8 product's accumulation (see tests/test_fp8_fwd_gpu.py)
+    aq, ak = np.abs(oracle.e4m3_value(q8)), np.abs(oracle.e4m3_value(k8))
+    e_s = 2.0 ** -11 * abs(w.softmax_scale) * c["q_descale"] * c["k_descale"] * np.where(
+        vis, aq @ ak.T, 0.0).max(axis=1)
+    return b, h, [o, lse, wabs, s1, e_s]
+
+
+def oracle_heads_fp8(w, heads, workers=None, progress=None):
+    """Yield (b, h, [O, LSE, W, S1, e]) of ``_ref_head_fp8`` for the listed heads, in any order."""
+    workers = workers or workers_for(len(heads))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_init_fp8, initargs=(w.name,)) as pool:
+        for i, res in enumerate(pool.imap_unordered(_ref_head_fp8, heads, chunksize=1)):
+            if progress and (i + 1) % 16 == 0:
+                progress(f"{w.name}: oracle {i + 1}/{len(heads)} heads")
+            yield res
+
+
 def workers_for(n_heads):
     try:
         cores = len(os.sched_getaffinity(0))

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_version", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
                             "fa_fwd_kv_workspace_size", "fa_fwd_kv", "fa_bwd_kv",
-                            "fa_fwd_kv_fp8", "fa_bwd_noalloc",
+                            "fa_fwd_kv_fp8", "fa_bwd_noalloc", "fa_fwd_fp8",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -334,3 +334,29 @@ def test_binding_rejects_bad_output_buffers():
               torch.zeros(2, 40, 3).transpose(1, 2)):
         with pytest.raises(ValueError):
             _lib._check_lse(t, q)
+
+
+def fwd_fp8(lib, q=Q, k=K, v=V, o=O, lse=L, qd=0.5, kd=0.5, vd=0.5, **kw):
+    a = dict(GOOD, **kw)
+    return lib.fa_fwd_fp8(q, k, v, o, lse, a["B"], a["H"], a["N"], a["d"], a["dtype"], a["scale"],
+                          qd, kd, vd, a["causal"], a["wl"], a["wr"], None)
+
+
+def test_fwd_fp8_rejections(lib):
+    inf, nan = float("inf"), float("nan")
+    assert fwd_fp8(lib, dtype=2) == 4
+    assert fwd_fp8(lib, d=96) == 3
+    assert fwd_fp8(lib, N=-1) == 2
+    assert fwd_fp8(lib, wl=-2) == 5
+    assert fwd_fp8(lib, scale=nan) == 7
+    for bad in (0.0, -1.0, inf, nan):
+        assert fwd_fp8(lib, qd=bad) == 7
+        assert fwd_fp8(lib, kd=bad) == 7
+        assert fwd_fp8(lib, vd=bad) == 7
+    assert fwd_fp8(lib, q=0) == 1
+    assert fwd_fp8(lib, o=0) == 1
+    assert fwd_fp8(lib, v=V + 8) == 6
+    assert fwd_fp8(lib, lse=L + 4) == 6
+    assert fwd_fp8(lib, o=K) == 10
+    assert fwd_fp8(lib, lse=O) == 10
+    assert fwd_fp8(lib, N=0, q=0, k=0, v=0, o=0, lse=0) == 0

@@ -108,13 +108,42 @@ class BlockWorkload:
         return 1.0 / math.sqrt(self.d)
 
 
+@dataclass(frozen=True)
+class Fp8Workload:
+    """A forward over FP8 E4M3 queries, keys and values: codes of N(0, 1) * 16 with descale
+    1/16 per tensor (``fp8_attention_case``), output in ``out_dtype``."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    window: tuple
+    seed: int
+    out_dtype: str = "bf16"
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+# the causal forward shapes at head dims 64 and 128, with FP8 operands
+FP8_64 = Fp8Workload("fp8_causal_b8h16n4096d64", 8, 16, 4096, 64, True, (-1, -1), seed=51)
+FP8_128 = Fp8Workload("fp8_causal_b8h16n4096d128", 8, 16, 4096, 128, True, (-1, -1), seed=52)
+FP8S = (FP8_64, FP8_128)
+
+
 # the training workload's heads, a 1024-query block over 4096 keys
 BLOCK = BlockWorkload("block_b8h16q1024k4096d64_bf16", 8, 16, 1024, 4096, 64, "bf16", seed=9)
 # The training step over a padded batch: sample lengths drawn by draw_seqlens (the pages fix
 # no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
 VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
                   backward=True, padded=True)
-BY_NAME = {w.name: w for w in ALL + LONG_128 + (VARLEN,) + DECODES + (BLOCK,)}
+BY_NAME = {w.name: w for w in ALL + LONG_128 + (VARLEN,) + DECODES + (BLOCK,) + FP8S}
 
 
 def draw_f32(shape, seed: int, count: int):
@@ -206,4 +235,17 @@ def random_case(shape, dtype: str, seed: int, with_grad: bool = False, scale_inp
         t, a64 = round_to(arr * np.float32(scale_inputs), dtype)
         out[name] = t
         out[name + "64"] = a64
+    return out
+
+
+def fp8_attention_case(shape, seed: int, amax: float = 16.0):
+    """Seeded FP8 forward inputs: q, k, v [B, H, N, d] as E4M3 codes (uint8 numpy) of
+    N(0, 1) * amax drawn in that order from one stream and rounded to nearest by torch's
+    float8_e4m3fn conversion, with descale 1 / amax each (so the values are about N(0, 1))."""
+    import torch
+    rng = np.random.default_rng(seed)
+    out = {"q_descale": 1.0 / amax, "k_descale": 1.0 / amax, "v_descale": 1.0 / amax}
+    for name in ("q", "k", "v"):
+        x = torch.from_numpy(rng.standard_normal(tuple(shape), dtype=np.float32) * np.float32(amax))
+        out[name + "8"] = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return out
