@@ -40,12 +40,13 @@ import workloads as W  # noqa: E402
 PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
 PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS   # dense FP8 MFMA, published as twice the 16-bit rate
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip",
+KERNEL_SOURCES = ("cdna4.h", "fwd.hip", "fwd_main.hip", "fwd_split.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip",
                   "fwd_fp8.hip", "api.cpp", "launch.h")
 # sources a workload's counters depend on, by workload kind (decode: the few-query kernels)
 DECODE_SOURCES = ("cdna4.h", "fwd_kv.hip", "api.cpp", "launch.h")
 # rocprofv3 kernel names -> the bench's kernel keys
-KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_fp8_kernel", "fwd"), ("fwd_kernel", "fwd"),
+KERNEL_KEYS = (("fwd_main_kernel", "fwd"), ("fwd_fp8_kernel", "fwd"), ("fwd_split_kernel", "fwd"),
+               ("fwd_kernel", "fwd"),
                ("delta_kernel", "delta"),
                ("dkdv_main_kernel", "dkdv"), ("dq_main_kernel", "dq"),
                ("dkdv_kernel", "dkdv"), ("dq_kernel", "dq"), ("decode_kernel", "decode"),

@@ -480,20 +480,24 @@ int env_kernel_choice() {
   if (e == nullptr) return 0;
   if (std::strcmp(e, "main") == 0) return 1;
   if (std::strcmp(e, "basic") == 0) return 2;
+  if (std::strcmp(e, "split") == 0) return 3;
   return 0;
 }
 
 }  // namespace
 
-// The 8-wave kernel (256 rows per query tile, one workgroup per CU) needs at least one
-// query tile per CU to fill the chip; smaller grids run the four-wave kernel, whose 128-row
-// workgroups are twice as many.
+// The main kernel (128 query rows per workgroup, two workgroups per CU) fills the chip when
+// there are at least two 128-row query tiles per CU, i.e. B H ceil(N / 256) >= 256.  Smaller
+// grids split the key loop over the waves of a workgroup (fwd_split.hip: 64 query rows, 2 to 4
+// key parts), as long as there are keys enough to split (N >= 256); the shortest sequences
+// run the four-wave kernel.  FA_FWD_KERNEL=main|basic|split forces one of them.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const long pp_blocks = (long)p.B * p.H * ((p.N + 255) / 256);
   int choice = env_kernel_choice();
-  if (choice == 0) choice = pp_blocks >= 256 ? 1 : 2;
+  if (choice == 0) choice = pp_blocks >= 256 ? 1 : (p.N >= 256 ? 3 : 2);
   if (p.seqlens != nullptr) choice = 1;   // padded batches always take the main kernel
   if (choice == 1) return launch_fwd_main(p, stream);
+  if (choice == 3) return launch_fwd_split(p, stream);
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
   return p.bf16 ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }

@@ -124,6 +124,9 @@ hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t
 // software pipeline), for grids that fill the chip and for padded batches; launch_fwd chooses
 // between it and the four-wave kernel of fwd.hip.
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream);
+// The forward for grids too small to fill the chip: 64 query rows per workgroup, the key loop
+// split over 2 to 4 parts (one wave pair each) and merged in LDS (fwd_split.hip).
+hipError_t launch_fwd_split(const FwdParams& p, hipStream_t stream);
 // Backward stages, run in this order on one stream: the row statistics (log2(e) * LSE and
 // delta = rowsum(dO * O)) into the workspace, then dK/dV, then dQ (both read them).
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u;

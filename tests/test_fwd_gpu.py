@@ -20,8 +20,8 @@ def fa():
 
 
 def run(fa, inp, scale, causal, window, return_lse=True, kernel=None):
-    """Forward through the C ABI.  ``kernel`` ("main" / "basic") forces the library's kernel
-    choice through its FA_FWD_KERNEL knob; None keeps the library's own heuristic."""
+    """Forward through the C ABI.  ``kernel`` ("main" / "basic" / "split") forces the
+    library's kernel choice through its FA_FWD_KERNEL knob; None keeps its own heuristic."""
     import torch
     q, k, v = (to_dev(inp[n]) for n in "qkv")
     old = os.environ.get("FA_FWD_KERNEL")
@@ -39,7 +39,7 @@ def run(fa, inp, scale, causal, window, return_lse=True, kernel=None):
     return o, lse
 
 
-KERNELS = ["main", "basic"]   # the two forward kernels; the default choice is covered too
+KERNELS = ["main", "basic", "split"]   # the three forward kernels; the default choice too
 
 
 def sampled_rows(n, rng, extra=8):
@@ -60,11 +60,12 @@ def test_tiny_workload(fa, dtype):
     say(f"[tiny] max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}")
 
 
-def test_bert_workload(fa):
+@pytest.mark.parametrize("kernel", [None] + KERNELS)
+def test_bert_workload(fa, kernel):
     w = W.BERT
     inp = W.make_inputs(w)
-    say(f"[bert] {w.name}")
-    o, lse = run(fa, inp, w.softmax_scale, w.causal, w.window)
+    say(f"[bert] {w.name} kernel={kernel or 'default'}")
+    o, lse = run(fa, inp, w.softmax_scale, w.causal, w.window, kernel=kernel)
     err = check_forward(o, lse, inp["q64"], inp["k64"], inp["v64"], w.softmax_scale, w.causal,
                         w.window, w.dtype, label=w.name)
     say(f"[bert] max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}")
