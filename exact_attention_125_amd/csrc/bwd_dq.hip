@@ -508,7 +508,10 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.dlo = (p.causal ? 0 : -wr) - (nk - nq);
   a.dhi = wl - (nk - nq);
   const int half = (a.n_tiles + 1) / 2;
-  a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
+  // pair only where the visible key count of the last query tile is at least twice that of
+  // the first (see the forward): not for a short block of queries over a long cache
+  a.paired = p.causal && p.window_left < 0 && nq >= (nk - nq) + 2 * S::QWG &&
+             (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   const long blocks = (long)a.n_bh * a.n_units;
   if (p.seqlens != nullptr)

@@ -655,8 +655,12 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
   a.heads = p.H;
   a.n_bh = p.B * p.H;
   a.n_qt = (nq + kBr - 1) / kBr;
-  // pairing balances causal rows whose visible key count grows with the query index
-  const bool growing = p.causal && p.window_left < 0;
+  // Pairing balances causal rows whose visible key count grows with the query index.  With the
+  // queries at the end of a longer key sequence (a.off > 0) that count hardly changes: tile t
+  // sees about off + 128 t keys, so the last tile does less than twice the first's work unless
+  // nq >= off + 256.  There pairing would gain nothing and would put twice as many heads in
+  // flight on an XCD, whose K/V then outgrow its L2.
+  const bool growing = p.causal && p.window_left < 0 && nq >= a.off + 2 * kBr;
   a.paired = growing && (long)a.n_bh * ((a.n_qt + 1) / 2) >= 256;
   a.n_units = a.paired ? (a.n_qt + 1) / 2 : a.n_qt;
   // a zero scale becomes a tiny one: every probability is then exactly 1 (as for 0) while
