@@ -35,6 +35,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
+
 import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = 2516.6        # MI355X dense bf16 / fp16 MFMA, published
@@ -359,6 +361,18 @@ def main():
     scale, causal, window = w.softmax_scale, w.causal, w.window
     lens = seqlens_of(w)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda") if lens is not None else None
+    packed = getattr(w, "packed", False)
+    if packed:   # the sequences' rows concatenated per head: [H, total, d], offsets cu
+        cu = torch.tensor([0] + [int(x) for x in np.cumsum(lens)], dtype=torch.int32,
+                          device="cuda")
+
+        def pack(x):
+            return torch.cat([x[b, :, :L] for b, L in enumerate(lens)], dim=1).contiguous()
+        q, k, v = pack(q), pack(k), pack(v)
+        do = pack(do) if do is not None else None
+        o = torch.empty_like(q)
+        lse = torch.empty(w.H, q.shape[1], device="cuda", dtype=torch.float32)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     stages = [("fwd", None)] + ([("delta", fa._lib.BWD_DELTA), ("dkdv", fa._lib.BWD_DKDV),
                                  ("dq", fa._lib.BWD_DQ)] if backward else [])
 
@@ -366,7 +380,12 @@ def main():
         for idx, (name, st) in enumerate(stages):
             if events is not None:
                 events[idx][0].record()
-            if st is None:
+            if packed and st is None:
+                fa.fwd_packed(q, k, v, cu, w.N, scale, causal, window, out=o, lse=lse)
+            elif packed:
+                fa.bwd_packed(do, q, k, v, o, lse, cu, w.N, scale, causal, window, dq=dq, dk=dk,
+                              dv=dv, workspace=ws, stages=st)
+            elif st is None:
                 fa.fwd(q, k, v, scale, causal, window, out=o, lse=lse, seqlens=sl)
             else:
                 fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv,
@@ -463,7 +482,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q, K, V, dO" +
-                                  (", sample lengths uniform in [N/4, N])" if lens else ")"),
+                                  (", sample lengths uniform in [N/4, N]" if lens else "") +
+                                  (", packed per head)" if packed else ")"),
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
                    "head_dim": w.d, "causal": w.causal, "window": list(w.window),
                    "pass": "fwd+bwd" if backward else "fwd",

@@ -47,6 +47,9 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
                            _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
+    "fa_fwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_bwd_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P,
+                           _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P,
                        _F, _U64, _U32, _P, _S, _P]),
@@ -294,6 +297,82 @@ def bwd_noalloc(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale=None, causal=Fa
     _check(_lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _dtype_code(q), scale,
                                int(bool(causal)), wl, wr, _stream(q.device)))
+    return dq, dk, dv
+
+
+def _check_packed(q, cu_seqlens, max_seqlen):
+    """[H, total, d] operands and the offsets of a packed batch; returns (B, H, total, d)."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("packed operands are [H, total, d] tensors")
+    if (not cu_seqlens.is_cuda or cu_seqlens.device != q.device or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1 or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on q's device")
+    if int(max_seqlen) < 0:
+        raise ValueError("max_seqlen must be >= 0")
+    H, total, d = q.shape
+    return cu_seqlens.shape[0] - 1, H, total, d
+
+
+def fwd_packed(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=False,
+               window_size=(-1, -1), out=None, lse=None, return_lse=True):
+    """``fa_fwd_packed``: q, k, v [H, total, d] holding every sequence's rows per head, sequence
+    b at rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32 [B + 1] on the device); ``max_seqlen``
+    the longest sequence.  Returns ``(o, lse)``, ``lse`` [H, total] float32 (rows no sequence
+    covers are left as allocated)."""
+    import torch
+    for t in (q, k, v):
+        if not t.is_cuda or t.device != q.device or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share one GPU device and dtype")
+        if tuple(t.shape) != tuple(q.shape) or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [H, total, d] tensors of one shape")
+    B, H, total, d = _check_packed(q, cu_seqlens, max_seqlen)
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    if out is not None:
+        _check_out(out, q, "out")
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((H, total), device=q.device, dtype=torch.float32)
+    if not return_lse:
+        lse = None
+    if lse is not None and (lse.device != q.device or lse.dtype != torch.float32
+                            or tuple(lse.shape) != (H, total) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 [H, total] = {(H, total)} tensor")
+    _check(_lib.fa_fwd_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                              B, H, total, int(max_seqlen), d, _dtype_code(q), scale,
+                              int(bool(causal)), wl, wr, _stream(q.device)))
+    return o, lse
+
+
+def bwd_packed(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, softmax_scale=None, causal=False,
+               window_size=(-1, -1), dq=None, dk=None, dv=None, workspace=None, stages=BWD_ALL):
+    """``fa_bwd_packed``: gradients ``(dq, dk, dv)`` of ``fwd_packed`` ([H, total, d])."""
+    import torch
+    for t in (k, v, o, dout):
+        if not t.is_cuda or t.device != q.device or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must share one GPU device and dtype")
+        if tuple(t.shape) != tuple(q.shape) or not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous [H, total, d] tensors")
+    B, H, total, d = _check_packed(q, cu_seqlens, max_seqlen)
+    scale, wl, wr = _resolve(q, softmax_scale, window_size)
+    if (lse.device != q.device or lse.dtype != torch.float32 or tuple(lse.shape) != (H, total)
+            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 [H, total] = {(H, total)} tensor")
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if g is not None:
+            _check_out(g, q, name)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = _lib.fa_bwd_workspace_size(B, H, int(max_seqlen), d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check_workspace(workspace, q)
+    _check(_lib.fa_bwd_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(cu_seqlens),
+                              B, H, total, int(max_seqlen), d, _dtype_code(q), scale,
+                              int(bool(causal)), wl, wr, int(stages), _stream(q.device)))
     return dq, dk, dv
 
 

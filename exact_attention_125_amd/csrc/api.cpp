@@ -118,15 +118,28 @@ const char* fa_last_error_detail(void) { return g_last_error.c_str(); }
 
 namespace {
 
+// A packed batch ([H, total, d] arrays, per-sequence offsets): the shape checks of its rows
+// per head (total) besides those of the longest sequence (seqlen).  Sets *empty as
+// check_common does.
+fa_status check_packed(int heads, int total, int head_dim, bool* empty) {
+  if (total < 0) return FA_ERR_BAD_SHAPE;
+  if ((long)total * head_dim >= kMaxRowElems) return FA_ERR_BAD_SHAPE;
+  if ((long)heads * total >= kMaxRows) return FA_ERR_BAD_SHAPE;
+  if (total == 0) *empty = true;
+  return FA_OK;
+}
+
+// `seqlens` is the per-sequence lengths (varlen) or, with `packed`, the offsets cu[B + 1].
 fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                    const int* seqlens, bool varlen, int batch, int heads, int seqlen, int head_dim,
                    fa_dtype dtype, float softmax_scale, int causal, int window_left,
-                   int window_right, void* stream) {
+                   int window_right, void* stream, bool packed = false, int total = 0) {
   g_last_error.clear();
   bool empty = false;
   fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
                               window_right, &empty);
   if (st != FA_OK) return st;
+  if (packed && (st = check_packed(heads, total, head_dim, &empty)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || (varlen && !seqlens)) return FA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -143,7 +156,9 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   p.v = v;
   p.o = o;
   p.lse = lse;
-  p.seqlens = seqlens;
+  p.seqlens = packed ? nullptr : seqlens;
+  p.cu = packed ? seqlens : nullptr;
+  p.total = total;
   p.B = batch;
   p.H = heads;
   p.N = seqlen;
@@ -215,6 +230,15 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
   return hip_status(fa::launch_fwd_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fwd_packed(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int batch, int heads, int total, int max_seqlen,
+                        int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream) {
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, true, batch, heads, max_seqlen, head_dim, dtype,
+                  softmax_scale, causal, window_left, window_right, stream, /*packed=*/true,
+                  total);
+}
+
 size_t fa_bwd_workspace_size(int batch, int heads, int seqlen, int head_dim) {
   bool empty = false;
   if (check_common(batch, heads, seqlen, head_dim, FA_BF16, 1.f, -1, -1, &empty) != FA_OK)
@@ -232,13 +256,15 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, const int* seqlens, bool varlen,
                    int batch, int heads, int seqlen, int head_dim, fa_dtype dtype,
                    float softmax_scale, int causal, int window_left, int window_right,
-                   unsigned stages, void* stream, bool noalloc = false) {
+                   unsigned stages, void* stream, bool noalloc = false, bool packed = false,
+                   int total = 0) {
   g_last_error.clear();
   bool empty = false;
   if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_BAD_STAGES;
   fa_status st = check_common(batch, heads, seqlen, head_dim, dtype, softmax_scale, window_left,
                               window_right, &empty);
   if (st != FA_OK) return st;
+  if (packed && (st = check_packed(heads, total, head_dim, &empty)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (varlen && !seqlens))
     return FA_ERR_NULL_PTR;
@@ -275,7 +301,9 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
   p.dk = dk;
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
-  p.seqlens = seqlens;
+  p.seqlens = packed ? nullptr : seqlens;
+  p.cu = packed ? seqlens : nullptr;
+  p.total = total;
   p.B = batch;
   p.H = heads;
   p.N = seqlen;
@@ -315,6 +343,17 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, seqlens, true,
                   batch, heads, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
                   window_right, stages, stream);
+}
+
+fa_status fa_bwd_packed(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* cu_seqlens, int batch,
+                        int heads, int total, int max_seqlen, int head_dim, fa_dtype dtype,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        unsigned stages, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, cu_seqlens, true,
+                  batch, heads, max_seqlen, head_dim, dtype, softmax_scale, causal, window_left,
+                  window_right, stages, stream, /*noalloc=*/false, /*packed=*/true, total);
 }
 
 fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

@@ -43,6 +43,8 @@ struct BwdArgs {
   char* dv;
   float* stats;   // per-query statistics in 32-query blocks (stat_index)
   const int* seqlens;   // per-batch lengths (device, may be null); only the delta pass reads them
+  const int* cu;        // packed batch: per-batch start rows [B + 1] (device), or null
+  int total;            // packed batch: rows per head
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
   Dropout drop;         // used by the DROPOUT instances only
   const unsigned char* blocks;   // block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks, or null
@@ -90,10 +92,24 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   const int slots = stat_blocks(a.n) * kStatRows;
   for (long bh = blockIdx.y; bh < a.n_bh; bh += gridDim.y) {
     // rows of the sequence; rows len .. n-1 of a padded batch get zeros like the slots past n
+    // (a packed batch: sequence b is rows cu[b] .. cu[b+1]-1 of each head's `total` rows,
+    // offsets clamped to [0, total], at most n rows)
     const int b = (int)(bh / a.heads), h = (int)(bh - (long)b * a.heads);
-    const int len = PADDED ? min(max(a.seqlens[b], 0), a.n) : a.n;
-    const char* orows = a.o + b * a.o_bs + h * a.o_hs + 16 * sub;
-    const char* grows = a.dout + b * a.g_bs + h * a.g_hs + 16 * sub;
+    int len = a.n;
+    long row0 = 0, lrow = bh * a.n;
+    if constexpr (PADDED) {
+      if (a.cu != nullptr) {
+        const int c0 = min(max(a.cu[b], 0), a.total);
+        const int c1 = min(max(a.cu[b + 1], c0), a.total);
+        len = min(c1 - c0, a.n);
+        row0 = c0;
+        lrow = (long)h * a.total + c0;
+      } else {
+        len = min(max(a.seqlens[b], 0), a.n);
+      }
+    }
+    const char* orows = a.o + b * a.o_bs + h * a.o_hs + row0 * a.o_rs + 16 * sub;
+    const char* grows = a.dout + b * a.g_bs + h * a.g_hs + row0 * a.g_rs + 16 * sub;
     u32x4 ov[IT], gv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -122,7 +138,7 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
         const bool in = q < len;
         // a row that sees no key (LSE = -inf; only with fewer keys than queries or a window)
         // gets zeros too: every one of its scores is masked
-        const float lse = in ? a.lse[bh * a.n + q] : 0.f;
+        const float lse = in ? a.lse[lrow + q] : 0.f;
         const bool live = in && lse != -__builtin_inff();
         out[0] = live ? -lse / a.sigma : 0.f;
         out[kStatRows] = live ? -acc : 0.f;
@@ -580,11 +596,16 @@ BwdArgs make_args(const BwdParams& p) {
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
   a.seqlens = p.seqlens;
+  a.cu = p.cu;
+  a.total = p.total;
   a.slopes = nullptr;
   a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
   a.blocks = nullptr;
   a.n_qb = a.n_kb = 0;
-  const long long row = (long long)p.D * 2, head = (long long)p.N * row, batch = p.H * head;
+  // dense [B, H, N, D], or a packed batch's [H, total, D] (sequence b starts at row cu[b])
+  const long long row = (long long)p.D * 2;
+  const long long head = (long long)(p.cu != nullptr ? p.total : p.N) * row;
+  const long long batch = p.cu != nullptr ? 0 : p.H * head;
   a.q_bs = a.k_bs = a.v_bs = a.o_bs = a.g_bs = a.dq_bs = a.dk_bs = a.dv_bs = batch;
   a.q_hs = a.k_hs = a.v_hs = a.o_hs = a.g_hs = a.dq_hs = a.dk_hs = a.dv_hs = head;
   a.q_rs = a.k_rs = a.v_rs = a.o_rs = a.g_rs = a.dq_rs = a.dk_rs = a.dv_rs = (int)row;
@@ -609,14 +630,14 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
   if (stages & kBwdDelta) {
     const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
     const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
-    if (p.seqlens != nullptr)
+    if (p.seqlens != nullptr || p.cu != nullptr)
       hipLaunchKernelGGL((delta_kernel<D, BF16, true>), dim3(gx, gy), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  // padded batches always take the main kernels
-  const bool main_kernels = env_bwd_choice() != 2 || p.seqlens != nullptr;
+  // padded and packed batches always take the main kernels
+  const bool main_kernels = env_bwd_choice() != 2 || p.seqlens != nullptr || p.cu != nullptr;
   if ((stages & kBwdDkDv) && main_kernels) {
     if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDkDv) {
@@ -651,6 +672,8 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.dv = static_cast<char*>(p.dv);
   a.stats = p.stats;
   a.seqlens = nullptr;
+  a.cu = nullptr;
+  a.total = 0;
   a.slopes = p.slopes;
   a.drop = p.drop;
   a.blocks = p.blocks;
@@ -704,6 +727,7 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
     m.dv = p.dv;
     m.stats = p.stats;
     m.seqlens = nullptr;
+    m.cu = nullptr;
     m.B = p.B;
     m.H = p.H;
     m.N = p.Nq;

@@ -67,6 +67,8 @@ struct DkdvArgs {
   char* dk;
   char* dv;
   const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
+  const int* cu;         // packed batch: per-batch start rows [B + 1] (device), or null
+  int total;             // packed batch: rows per head
   int n;                 // query rows per (batch, head) in memory
   int nk;                // key rows per (batch, head) (n for self-attention, padded batches)
   int heads;
@@ -125,12 +127,25 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // rows of the head in memory (nr) and of its sequence (n): rows n .. nr-1 are padding, read
   // as zeros through the buffer resources, with zero gradients
   const int nr = a.n;
-  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  // a packed batch: sequence b is rows cu[b] .. cu[b+1]-1 of each head's `total` rows (offsets
+  // clamped to [0, total], at most nr rows), with no padding rows to write
+  int n = nr, nw = nr;   // sequence rows, rows written
+  long head = (long)bh * nr * RB;                              // Q, dO (and K, V, dK, dV)
+  if constexpr (PADDED) {
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    if (a.cu != nullptr) {
+      const int c0 = min(max(a.cu[b], 0), a.total);
+      const int c1 = min(max(a.cu[b + 1], c0), a.total);
+      n = nw = min(c1 - c0, nr);
+      head = ((long)h * a.total + c0) * RB;
+    } else {
+      n = min(max(a.seqlens[b], 0), nr);
+    }
+  }
   // keys: as many as queries in a padded batch, else nk rows (query i at key position
   // i + nk - n, which the band dlo .. dhi already accounts for)
   const int nkr = PADDED ? n : a.nk;
-  const long head = (long)bh * nr * RB;                        // Q, dO
-  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;     // K, V, dK, dV
+  const long khead = PADDED ? head : (long)bh * a.nk * RB;     // K, V, dK, dV
   const int head_bytes = n * RB;                               // Q, dO bytes
   const auto rq = make_rsrc(a.q + head, head_bytes);
   const auto rk = make_rsrc(a.k + khead, nkr * RB);
@@ -564,7 +579,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw0 + 32 * kb + l32;
-    if (key < (PADDED ? nr : nkr)) {
+    if (key < (PADDED ? nw : nkr)) {
       char* dkrow = a.dk + khead + (long)key * RB;
       char* dvrow = a.dv + khead + (long)key * RB;
       const float sc = a.scale;
@@ -615,6 +630,8 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.dk = static_cast<char*>(p.dk);
   a.dv = static_cast<char*>(p.dv);
   a.seqlens = p.seqlens;
+  a.cu = p.cu;
+  a.total = p.total;
   a.n = nq;
   a.nk = nk;
   a.heads = p.H;
@@ -637,7 +654,7 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr)
+  if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

@@ -57,6 +57,8 @@ struct DqArgs {
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
   char* dq;
   const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
+  const int* cu;         // packed batch: per-batch start rows [B + 1] (device), or null
+  int total;             // packed batch: rows per head
   int n;                 // query rows per (batch, head) in memory
   int nk;                // key rows per (batch, head) (n for self-attention, padded batches)
   int off;               // key position of query 0 (nk - n)
@@ -110,12 +112,25 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // rows of the head in memory (nr) and of its sequence (n): rows n .. nr-1 are padding, read
   // as zeros through the buffer resources, with zero gradients
   const int nr = a.n;
-  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  // a packed batch: sequence b is rows cu[b] .. cu[b+1]-1 of each head's `total` rows (offsets
+  // clamped to [0, total], at most nr rows), with no padding rows to write
+  int n = nr, nw = nr;   // sequence rows, rows written
+  long head = (long)bh * nr * RB;                              // Q, dO, dQ (and K, V)
+  if constexpr (PADDED) {
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    if (a.cu != nullptr) {
+      const int c0 = min(max(a.cu[b], 0), a.total);
+      const int c1 = min(max(a.cu[b + 1], c0), a.total);
+      n = nw = min(c1 - c0, nr);
+      head = ((long)h * a.total + c0) * RB;
+    } else {
+      n = min(max(a.seqlens[b], 0), nr);
+    }
+  }
   // keys: as many as queries in a padded batch, else nk rows, query i at key position i + off
   const int nkr = PADDED ? n : a.nk;
   const int off = PADDED ? 0 : a.off;
-  const long head = (long)bh * nr * RB;                        // Q, dO, dQ
-  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;     // K, V
+  const long khead = PADDED ? head : (long)bh * a.nk * RB;     // K, V
   const int head_bytes = nkr * RB;                             // K, V bytes
   const auto rq = make_rsrc(a.q + head, n * RB);
   const auto rk = make_rsrc(a.k + khead, head_bytes);
@@ -442,7 +457,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + 32 * qb + l32;
-    if (q < (PADDED ? nr : n)) {
+    if (q < (PADDED ? nw : n)) {
       char* row = a.dq + head + (long)q * RB;
       const float sc = a.scale;
 #pragma unroll
@@ -489,6 +504,8 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.stats = p.stats;
   a.dq = static_cast<char*>(p.dq);
   a.seqlens = p.seqlens;
+  a.cu = p.cu;
+  a.total = p.total;
   a.n = nq;
   a.nk = nk;
   a.off = nk - nq;
@@ -514,7 +531,7 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
              (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr)
+  if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

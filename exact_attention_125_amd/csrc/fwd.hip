@@ -495,7 +495,7 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const long pp_blocks = (long)p.B * p.H * ((p.N + 255) / 256);
   int choice = env_kernel_choice();
   if (choice == 0) choice = pp_blocks >= 256 ? 1 : (p.N >= 256 ? 3 : 2);
-  if (p.seqlens != nullptr) choice = 1;   // padded batches always take the main kernel
+  if (p.seqlens != nullptr || p.cu != nullptr) choice = 1;   // padded / packed batches: main kernel
   if (choice == 1) return launch_fwd_main(p, stream);
   if (choice == 3) return launch_fwd_split(p, stream);
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, stream) : launch<64, false>(p, stream);

@@ -75,6 +75,8 @@ struct MainArgs {
   char* o;
   float* lse;
   const int* seqlens;   // per-batch lengths (device, may be null: every sequence has n rows)
+  const int* cu;        // packed batch: per-batch start rows [B + 1] (device), or null
+  int total;            // packed batch: rows per head (the concatenated sequences)
   int n;          // query rows per (batch, head): the sequence length, or the padded one with seqlens
   int nk;         // key rows per (batch, head) (n for self-attention and padded batches)
   int off;        // key position of query 0 (nk - n; 0 for padded batches)
@@ -125,14 +127,29 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
   int bh, unit;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, unit);
   // rows of the head in memory (nr) and of its sequence (n); rows n .. nr-1 are padding, read
-  // as zeros through the buffer resources and written as zeros
+  // as zeros through the buffer resources and written as zeros (a padded batch).  A packed
+  // batch has no padding rows: sequence b is rows cu[b] .. cu[b+1]-1 of each head's `total`
+  // concatenated rows (offsets clamped to [0, total], at most nr rows), and nothing past its
+  // own rows is written.
   const int nr = a.n;
-  const int n = PADDED ? min(max(a.seqlens[bh / a.heads], 0), nr) : nr;
+  int n = nr, nw = nr;   // sequence rows, rows written
+  long head = (long)bh * nr * RB, lrow = (long)bh * nr;   // first byte of Q / O, first LSE index
+  if constexpr (PADDED) {
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    if (a.cu != nullptr) {
+      const int c0 = min(max(a.cu[b], 0), a.total);
+      const int c1 = min(max(a.cu[b + 1], c0), a.total);
+      n = nw = min(c1 - c0, nr);
+      lrow = (long)h * a.total + c0;
+      head = lrow * RB;
+    } else {
+      n = min(max(a.seqlens[b], 0), nr);
+    }
+  }
   // keys: a padded batch has as many as queries; otherwise nk rows, query i at position i + off
   const int nkr = PADDED ? n : a.nk;
   const int off = PADDED ? 0 : a.off;
-  const long head = (long)bh * nr * RB;
-  const long khead = (long)bh * (PADDED ? nr : a.nk) * RB;
+  const long khead = PADDED ? head : (long)bh * a.nk * RB;
   const int head_bytes = nkr * RB;   // K and V bytes of the head's keys
   const auto rq = make_rsrc(a.q + head, n * RB);
   const auto rk = make_rsrc(a.k + khead, head_bytes);
@@ -177,12 +194,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     const int wq0 = q0 + 32 * stripe;
     const int qi = wq0 + l32;
     if (PADDED && q0 >= n) {   // padding rows only: O = 0, LSE = -inf
-      if (qi < nr) {
+      if (qi < nw) {
         char* orow = a.o + head + (long)qi * RB;
 #pragma unroll
         for (int c16 = 0; c16 < RB / 32; ++c16)
           *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
-        if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
+        if (a.lse != nullptr && hi == 0) a.lse[lrow + qi] = NEG_INF;
       }
       continue;
     }
@@ -204,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 #pragma unroll
         for (int c16 = 0; c16 < RB / 32; ++c16)
           *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
-        if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
+        if (a.lse != nullptr && hi == 0) a.lse[lrow + qi] = NEG_INF;
       }
       continue;
     }
@@ -627,13 +644,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
           *reinterpret_cast<u32x2*>(orow + dim * 2) = w;
         }
       if (a.lse != nullptr && hi == 0)
-        a.lse[(long)bh * nr + qi] = live ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : NEG_INF;
-    } else if (PADDED && qi < nr) {   // a padding row
+        a.lse[lrow + qi] = live ? (m_ref + __builtin_log2f(l_tot)) * kLn2 : NEG_INF;
+    } else if (PADDED && qi < nw) {   // a padding row
       char* orow = a.o + head + (long)qi * RB;
 #pragma unroll
       for (int c16 = 0; c16 < RB / 32; ++c16)
         *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
-      if (a.lse != nullptr && hi == 0) a.lse[(long)bh * nr + qi] = NEG_INF;
+      if (a.lse != nullptr && hi == 0) a.lse[lrow + qi] = NEG_INF;
     }
   }
 }
@@ -649,6 +666,8 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
   a.o = static_cast<char*>(p.o);
   a.lse = p.lse;
   a.seqlens = p.seqlens;
+  a.cu = p.cu;
+  a.total = p.total;
   a.n = nq;
   a.nk = nk;
   a.off = nk - nq;
@@ -671,7 +690,7 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr)
+  if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, a);
   else
@@ -695,6 +714,7 @@ hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
   f.o = p.o;
   f.lse = p.lse;
   f.seqlens = nullptr;
+  f.cu = nullptr;
   f.B = p.B;
   f.H = p.H;
   f.N = p.Nq;

@@ -18,6 +18,10 @@ struct FwdParams {
   const int* seqlens = nullptr;   // device int32[B], or null: sequence b is rows
                                   // 0 .. seqlens[b]-1 of its N (values clamped to [0, N]);
                                   // the rest is padding
+  const int* cu = nullptr;        // device int32[B + 1], or null: a packed batch, sequence b is
+                                  // rows cu[b] .. cu[b+1]-1 of each head's `total` rows
+                                  // ([H, total, D] arrays; N is the longest sequence)
+  int total = 0;
   int B, H, N, D;
   bool bf16;
   float scale;         // softmax scale
@@ -38,6 +42,8 @@ struct BwdParams {
   void* dv;
   float* stats;        // workspace: per-query statistics in 32-query blocks (stat_index)
   const int* seqlens = nullptr;   // as in FwdParams
+  const int* cu = nullptr;        // as in FwdParams
+  int total = 0;
   int B, H, N, D;
   bool bf16;
   float scale;

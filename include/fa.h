@@ -184,6 +184,37 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         int causal, int window_left, int window_right, unsigned stages,
                         void* stream);
 
+/* Packed batches: the sequences of a batch concatenated per head, with no padding.  This is
+ * the per-sample actual length of the A100 page (§6) on the (batch, num_heads, seq_len,
+ * head_dim) layout of the FA3.7 page's SDPA call (§3.2) with the batch folded into the
+ * sequence axis:
+ *   q, k, v, o, dout, dq, dk, dv  [H, total, head_dim] of dtype, dense: head h holds the
+ *            `total` rows of every sequence, sequence b being rows cu_seqlens[b] ..
+ *            cu_seqlens[b+1] - 1;
+ *   lse      [H, total] float32;
+ *   cu_seqlens  device int32[B + 1], the sequences' start rows and the end of the last one
+ *            (4-byte aligned, not an output).  Read by the kernels, so not checked on the
+ *            host: each offset is clamped to [0, total], each sequence to [cu[b], cu[b+1])
+ *            and to at most max_seqlen rows.
+ *   max_seqlen  the longest sequence (sizes the grid and the backward workspace,
+ *            fa_bwd_workspace_size(batch, heads, max_seqlen, head_dim) bytes).
+ * Each sequence is attention over its own rows alone, with the masks of fa_fwd; rows no
+ * sequence covers are neither read nor written.  Other arguments, conventions and errors are
+ * those of fa_fwd / fa_bwd_stages (`stages` as there); total < 0, total * head_dim >= 2^30 or
+ * heads * total >= 2^31 give FA_ERR_BAD_SHAPE, and total = 0 is a no-op.  The results are
+ * bit-identical to fa_fwd_varlen / fa_bwd_varlen on the same sequences laid out padded. */
+fa_status fa_fwd_packed(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int batch, int heads, int total, int max_seqlen,
+                        int head_dim, fa_dtype dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream);
+
+fa_status fa_bwd_packed(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* cu_seqlens, int batch,
+                        int heads, int total, int max_seqlen, int head_dim, fa_dtype dtype,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        unsigned stages, void* stream);
+
 /* Queries and keys of different lengths, and operands of any layout.
  *
  * N_q queries attend to N_k keys, and the queries are the LAST N_q positions of the key

@@ -25,7 +25,8 @@ Modules
              closed forms and by ``attention``)
   online     the tiled running-max / running-sum recurrence in the pages'
              order — pinned against ``attention``
-  padded     padded batches (per-sample lengths): the definition over each
+  padded     padded batches (per-sample lengths) and packed ones (sequences concatenated
+             per head, offsets): the definition over each
              sample's own rows, zeros past them — pinned
   cross      N_q queries over N_k keys, the queries being the last N_q positions
              (decode steps, a new block over a cache), optional ALiBi distance
@@ -46,7 +47,8 @@ from .attention import (allowed_mask, attention_forward, attention_backward,
                         allowed_pairs, score_matrix_nbytes)
 from .online import attention_forward_online
 from .brute import attention_forward_brute
-from .padded import clamp_lengths, padded_backward_bh, padded_forward_bh
+from .padded import (clamp_lengths, packed_backward, packed_forward, packed_ranges,
+                     padded_backward_bh, padded_forward_bh)
 from .cross import (BLOCK, alibi_bias, block_allowed, cross_allowed_mask, cross_allowed_pairs, cross_backward,
                     cross_backward_bh, cross_forward, cross_forward_bh)
 
@@ -58,7 +60,8 @@ __all__ = [
     "allowed_mask", "attention_forward", "attention_backward", "attention_forward_rows",
     "attention_forward_bh", "attention_backward_bh", "allowed_pairs", "score_matrix_nbytes",
     "attention_forward_online", "attention_forward_brute",
-    "clamp_lengths", "padded_forward_bh", "padded_backward_bh",
+    "clamp_lengths", "padded_forward_bh", "padded_backward_bh", "packed_ranges",
+    "packed_forward", "packed_backward",
     "cross_allowed_mask", "cross_allowed_pairs", "cross_forward", "cross_forward_bh",
     "cross_backward", "cross_backward_bh", "alibi_bias", "BLOCK", "block_allowed",
     "philox4x32_10", "keep_threshold", "keep_scale", "dropout_keep", "dropout_forward", "dropout_backward",

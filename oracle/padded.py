@@ -48,3 +48,49 @@ def padded_backward_bh(q, k, v, do, seqlens, scale, causal=False, window=(-1, -1
             dq[b, h, :L], dk[b, h, :L], dv[b, h, :L] = attention_backward(
                 q[b, h, :L], k[b, h, :L], v[b, h, :L], do[b, h, :L], scale, causal, window)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------- packed batches
+# Packed batches carry the same sequences without padding: per head, the rows of every sequence
+# concatenated ([H, total, d]), sequence b being rows cu[b] .. cu[b+1] - 1.  Reading: each
+# sequence is attention over its own rows alone, as for a padded batch; rows no sequence covers
+# belong to no sequence (returned as NaN here: the library neither reads nor writes them).
+# Offsets are taken as the kernels read them: each clamped to [0, total], each sequence to
+# [cu[b], cu[b+1]) and to at most max_seqlen rows.
+
+def packed_ranges(cu, total: int, max_seqlen: int):
+    """(start, stop) row range of every sequence, as the packed call reads the offsets."""
+    out = []
+    for b in range(len(cu) - 1):
+        c0 = min(max(int(cu[b]), 0), total)
+        c1 = min(max(int(cu[b + 1]), c0), total)
+        out.append((c0, c0 + min(c1 - c0, max_seqlen)))
+    return out
+
+
+def packed_forward(q, k, v, cu, max_seqlen, scale, causal=False, window=(-1, -1)):
+    """[H, total, d] float64 arrays -> (O [H, total, d], LSE [H, total]), NaN outside every
+    sequence."""
+    H, total, _ = q.shape
+    o = np.full((H, total, v.shape[-1]), np.nan)
+    lse = np.full((H, total), np.nan)
+    for r0, r1 in packed_ranges(cu, total, max_seqlen):
+        if r1 == r0:
+            continue
+        for h in range(H):
+            o[h, r0:r1], lse[h, r0:r1] = attention_forward(q[h, r0:r1], k[h, r0:r1], v[h, r0:r1],
+                                                           scale, causal, window)
+    return o, lse
+
+
+def packed_backward(q, k, v, do, cu, max_seqlen, scale, causal=False, window=(-1, -1)):
+    """[H, total, d] float64 arrays -> (dQ, dK, dV), NaN outside every sequence."""
+    H, total, _ = q.shape
+    dq, dk, dv = (np.full(t.shape, np.nan) for t in (q, k, v))
+    for r0, r1 in packed_ranges(cu, total, max_seqlen):
+        if r1 == r0:
+            continue
+        for h in range(H):
+            dq[h, r0:r1], dk[h, r0:r1], dv[h, r0:r1] = attention_backward(
+                q[h, r0:r1], k[h, r0:r1], v[h, r0:r1], do[h, r0:r1], scale, causal, window)
+    return dq, dk, dv

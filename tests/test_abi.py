@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol(lib):
                             "fa_bwd_stages", "fa_fwd_varlen", "fa_bwd_varlen",
                             "fa_fwd_kv_workspace_size", "fa_fwd_kv", "fa_bwd_kv",
                             "fa_fwd_kv_fp8", "fa_bwd_noalloc", "fa_fwd_fp8",
+                            "fa_fwd_packed", "fa_bwd_packed",
                             "fa_status_string", "fa_last_error_detail"])
     for name in names:
         assert hasattr(lib, name), name
@@ -360,3 +361,28 @@ def test_fwd_fp8_rejections(lib):
     assert fwd_fp8(lib, o=K) == 10
     assert fwd_fp8(lib, lse=O) == 10
     assert fwd_fp8(lib, N=0, q=0, k=0, v=0, o=0, lse=0) == 0
+
+
+def test_packed_rejections(lib):
+    def fwdp(q=Q, k=K, v=V, o=O, lse=L, cu=SL, total=500, mx=100, **kw):
+        a = dict(GOOD, **kw)
+        return lib.fa_fwd_packed(q, k, v, o, lse, cu, a["B"], a["H"], total, mx, a["d"],
+                                 a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+
+    def bwdp(ws=WS, ws_bytes=1 << 20, cu=SL, total=500, mx=100, **kw):
+        a = dict(GOOD, **kw)
+        return lib.fa_bwd_packed(Q, K, V, O, DO, L, DQ, DK, DV, ws, ws_bytes, cu, a["B"], a["H"],
+                                 total, mx, a["d"], a["dtype"], a["scale"], a["causal"], a["wl"],
+                                 a["wr"], 7, None)
+    for call in (fwdp, bwdp):
+        assert call(cu=0) == 1
+        assert call(cu=SL + 2) == 6
+        assert call(total=-1) == 2
+        assert call(total=1 << 24) == 2          # total * d >= 2^30
+        assert call(mx=-1) == 2
+        assert call(d=96) == 3
+        assert call(total=0, cu=0) == 0          # no rows: a no-op
+    assert fwdp(o=Q) == 10
+    assert fwdp(lse=SL) == 10
+    assert bwdp(ws=0) == 8
+    assert bwdp(cu=DQ) == 10

@@ -110,3 +110,75 @@ def test_backward_is_the_derivative_of_the_padded_forward(causal, window):
             num[idx] = (up - loss(*args)) / (2 * eps)
         np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7)
         assert np.all(g[0, :, 3:] == 0.0)
+
+
+# --------------------------------------------------------------------------- packed batches
+def _packed_case(cu, H, d, seed):
+    rng = np.random.default_rng(seed)
+    total = cu[-1]
+    return [rng.standard_normal((H, total, d)) for _ in range(4)]
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (2, 1)),
+                                           (True, (4, 0))])
+def test_packed_is_block_diagonal_attention(causal, window):
+    """Library cross-check: torch CPU SDPA over the whole concatenation of a head's rows, with
+    a mask that lets (i, j) through only within one sequence and under the mask rules taken
+    relative to that sequence's start."""
+    import torch
+    cu = [0, 5, 5, 12, 13, 20]          # an empty sequence and a one-row one
+    H, d = 2, 4
+    q, k, v, _ = _packed_case(cu, H, d, 21)
+    o, lse = oracle.packed_forward(q, k, v, cu, 16, 0.7, causal, window)
+    total = cu[-1]
+    seg = np.zeros(total, dtype=np.int64)
+    pos = np.zeros(total, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        seg[cu[b]:cu[b + 1]] = b
+        pos[cu[b]:cu[b + 1]] = np.arange(cu[b + 1] - cu[b])
+    i, j = pos[:, None], pos[None, :]
+    ok = seg[:, None] == seg[None, :]
+    if causal:
+        ok &= j <= i
+    if window[0] >= 0:
+        ok &= j >= i - window[0]
+    if window[1] >= 0:
+        ok &= j <= i + window[1]
+    m = torch.from_numpy(ok)
+    for h in range(H):
+        t = [torch.from_numpy(x[h])[None] for x in (q, k, v)]
+        ro = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=m, scale=0.7)[0]
+        np.testing.assert_allclose(o[h], ro.numpy(), rtol=1e-12, atol=1e-12)
+        s = (torch.from_numpy(q[h]) @ torch.from_numpy(k[h]).T * 0.7).masked_fill(~m, -np.inf)
+        np.testing.assert_allclose(lse[h], torch.logsumexp(s, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_packed_matches_padded_and_leaves_gaps():
+    """The same sequences laid out padded give the same outputs (forward and backward); rows no
+    sequence covers stay NaN, and offsets beyond the rows are clamped as the kernels clamp them."""
+    cu = [0, 7, 7, 19, 22]
+    H, d, N = 3, 5, 12
+    q, k, v, do = _packed_case(cu, H, d, 22)
+    B = len(cu) - 1
+    lens = [cu[b + 1] - cu[b] for b in range(B)]
+    pad = [np.zeros((B, H, N, d)) for _ in range(4)]
+    for b in range(B):
+        for t, x in zip(pad, (q, k, v, do)):
+            t[b, :, :lens[b]] = x[:, cu[b]:cu[b + 1]]
+    po, pl = oracle.padded_forward_bh(*pad[:3], lens, 0.4, True)
+    pg = oracle.padded_backward_bh(*pad, lens, 0.4, True)
+    o, lse = oracle.packed_forward(q, k, v, cu, N, 0.4, True)
+    g = oracle.packed_backward(q, k, v, do, cu, N, 0.4, True)
+    for b in range(B):
+        r = slice(cu[b], cu[b + 1])
+        np.testing.assert_array_equal(o[:, r], po[b, :, :lens[b]])
+        np.testing.assert_array_equal(lse[:, r], pl[b, :, :lens[b]])
+        for x, y in zip(g, pg):
+            np.testing.assert_array_equal(x[:, r], y[b, :, :lens[b]])
+    # a gap (rows 22 .. 24 covered by no sequence) and clamping: an offset past the end counts
+    # as the end, a sequence longer than max_seqlen keeps its first max_seqlen rows
+    q2 = np.concatenate([q, np.ones((H, 3, d))], axis=1)
+    o2, l2 = oracle.packed_forward(q2, q2, q2, [0, 7, 40], 5, 0.4, False)
+    assert np.isnan(o2[:, 5:7]).all() and np.isnan(o2[:, 12:]).all()
+    assert oracle.packed_ranges([0, 7, 40], 25, 5) == [(0, 5), (7, 12)]
+    assert oracle.packed_ranges([3, -2, 9], 8, 100) == [(3, 3), (0, 8)]

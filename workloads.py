@@ -34,6 +34,7 @@ class Workload:
     backward: bool = False
     scale: float = field(default=float("nan"))
     padded: bool = False     # a padded batch: per-sample lengths from draw_seqlens
+    packed: bool = False     # (with padded) the same sequences packed: [H, total, d], offsets
 
     @property
     def softmax_scale(self) -> float:
@@ -143,7 +144,10 @@ BLOCK = BlockWorkload("block_b8h16q1024k4096d64_bf16", 8, 16, 1024, 4096, 64, "b
 # no length mix; uniform over [N/4, N] is a plain stand-in for a batch of mixed lengths).
 VARLEN = Workload("varlen_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
                   backward=True, padded=True)
-BY_NAME = {w.name: w for w in ALL + LONG_128 + (VARLEN,) + DECODES + (BLOCK,) + FP8S}
+# The same training step over the same sequences packed per head ([H, total, d], offsets).
+PACKED = Workload("packed_b8h16n4096d64_bf16", 8, 16, 4096, 64, "bf16", True, (-1, -1), seed=6,
+                  backward=True, padded=True, packed=True)
+BY_NAME = {w.name: w for w in ALL + LONG_128 + (VARLEN, PACKED) + DECODES + (BLOCK,) + FP8S}
 
 
 def draw_f32(shape, seed: int, count: int):
