@@ -613,7 +613,10 @@ def bench_decode(args, w):
         entry["cold_ms"] = round(sum(cold) / len(cold), 4)
         entry["cold_median_ms"] = round(statistics.median(cold), 4)
         entry["cold_gbs"] = round(nbytes / (entry["cold_ms"] * 1e-3) / 1e9, 1)
-    plan_splits = need // (w.B * w.H * w.n_q * (w.d + 1) * 4) if need else 1
+    # key splits of the 16-bit plan, from its workspace (one partial O and LSE per split); the
+    # FP8 cache's plan, with twice the rows per step, can have fewer, which the library does
+    # not report
+    plan_splits = (need // (w.B * w.H * w.n_q * (w.d + 1) * 4) if need else 1) if not fp8 else None
     out = {
         "metric": "attention decode forward HBM GB/s on 1 MI355X (algorithmic bytes: Q, K, V "
                   "read once, O and LSE written once)",
@@ -625,7 +628,7 @@ def bench_decode(args, w):
                  if fp8 else "synthetic (seeded N(0,1) Q, K, V)"),
         "config": {"workload": w.name + ("_kvfp8" if fp8 else ""), "kv_fp8": fp8, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
                    "head_dim": w.d, "causal": True, "pass": "fwd", "alibi": bool(args.alibi),
-                   "bytes_per_step": nbytes, "key_splits": int(plan_splits)},
+                   "bytes_per_step": nbytes, "key_splits": plan_splits},
         "kernels": {"decode+combine": entry},
         # the call is the decode kernel and the split merge; timing both together
         # understates the decode kernel's own rate slightly

@@ -102,7 +102,9 @@ def test_fp8_cache_decode_shape_sampled(fa, d):
 def test_fp8_cache_matches_the_16_bit_path_on_exact_values(fa):
     """FP8 codes decoded exactly on the host and passed as bf16 (every E4M3 value with a
     power-of-two descale is a bf16 value) give the same attention: both kernels read the same
-    numbers, so the outputs agree to the fp32 summation-order level."""
+    numbers, and their fp32 sums differ only in order (the two kernels split the keys and fold
+    the key descale differently).  So the LSE agrees to 1e-5 and O, rounded to bf16 at the end,
+    to within one bf16 step (an fp32 difference can move a value across a rounding boundary)."""
     import oracle
     import torch
     c = W.fp8_cache_case(2, 2, 2, 3000, 64, "bf16", seed=77)
