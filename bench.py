@@ -297,8 +297,9 @@ def main():
             json.dump(rec, f, indent=1, sort_keys=True)
         pairs = total_pairs(w)
         fl = flops(w, pairs)
+        peak = PEAK_FP8_TFLOPS if isinstance(w, W.Fp8Workload) else PEAK_TFLOPS
         print(f"| kernel | timed dispatches | average us | median us | min us | max us | "
-              f"warm-up average us | TFLOP/s (average) | % of {PEAK_TFLOPS} |")
+              f"warm-up average us | TFLOP/s (average) | % of {peak} |")
         print("|---|---|---|---|---|---|---|---|---|")
         for key in sorted(res, key=lambda k: -res[k]["avg_us"]):
             e = res[key]
@@ -307,7 +308,7 @@ def main():
             warm = f"{e['warmup_avg_us']:.1f}" if e["warmup_avg_us"] is not None else "-"
             print(f"| {key} | {e['dispatches_timed']} | {e['avg_us']:.1f} | {e['median_us']:.1f} | "
                   f"{e['min_us']:.1f} | {e['max_us']:.1f} | {warm} | "
-                  + (f"{tf:.1f} | {100 * tf / PEAK_TFLOPS:.1f}% |" if tf else "- | - |"))
+                  + (f"{tf:.1f} | {100 * tf / peak:.1f}% |" if tf else "- | - |"))
         return
     if args.pmc_summary:
         w = W.BY_NAME[args.workload]
