@@ -52,11 +52,11 @@ SIGNATURES = {
                            _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, ctypes.c_uint, _P]),
     "fa_fwd_kv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "fa_fwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P,
-                       _F, _U64, _U32, _P, _S, _P]),
+                       _P, _F, _U64, _U32, _P, _S, _P]),
     "fa_bwd_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F,
-                       _I, _I, _I, _P, _P, _F, _U64, _U32, _P]),
+                       _I, _I, _I, _P, _P, _P, _F, _U64, _U32, _P]),
     "fa_fwd_kv_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _I, _I,
-                           _I, _P, _S, _P]),
+                           _I, _P, _P, _S, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I, _I, _I, _P]),
     "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
                             _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -420,20 +420,34 @@ def _check_blocks(block_mask, q, n_k):
                          f"= {shape} tensor")
 
 
+def _check_key_padding(key_padding_mask, q, n_k):
+    import torch
+    if key_padding_mask is None:
+        return
+    shape = (q.shape[0], n_k)
+    if (not key_padding_mask.is_cuda or key_padding_mask.device != q.device
+            or key_padding_mask.dtype not in (torch.uint8, torch.bool)):
+        raise ValueError("key_padding_mask must be a uint8 or bool tensor on the device of q")
+    if tuple(key_padding_mask.shape) != shape or not key_padding_mask.is_contiguous():
+        raise ValueError(f"key_padding_mask must be a contiguous [batch, N_k] = {shape} tensor")
+
+
 def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=None,
            return_lse=True, workspace=None, alibi_slopes=None, dropout_p=0.0, dropout_seed=0,
-           dropout_offset=0, block_mask=None):
+           dropout_offset=0, block_mask=None, key_padding_mask=None):
     """``fa_fwd_kv``: q [B, H, N_q, d] over k, v [B, H, N_k, d], the queries being the last N_q
     key positions.  Any strides with a contiguous last dimension (for example transposed
     views of [B, N, H, d] memory).  ``alibi_slopes``: float32 [H] on the device, or None.
     ``dropout_p`` / ``dropout_seed`` / ``dropout_offset``: attention dropout with masks from
     the library's Philox stream (the same three values go to ``bwd_kv``).  ``block_mask``:
     uint8 / bool [H, ceil(N_q/64), ceil(N_k/64)] on the device selecting 64 x 64 blocks.
-    Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
+    ``key_padding_mask``: uint8 / bool [B, N_k] on the device, True (nonzero) where a key is
+    padding.  Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
     import torch
     _check_kv_tensors(q, k, v)
     _check_slopes(alibi_slopes, q)
     _check_blocks(block_mask, q, k.shape[2])
+    _check_key_padding(key_padding_mask, q, k.shape[2])
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
@@ -450,17 +464,20 @@ def fwd_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k, d,
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
-                          _ptr(block_mask), float(dropout_p), int(dropout_seed),
-                          int(dropout_offset), _ptr(workspace), ws_bytes, _stream(q.device)))
+                          _ptr(block_mask), _ptr(key_padding_mask), float(dropout_p),
+                          int(dropout_seed), int(dropout_offset), _ptr(workspace), ws_bytes,
+                          _stream(q.device)))
     return o, lse
 
 
 def fwd_kv_fp8(q, k, v, k_descale, v_descale, softmax_scale=None, causal=False,
-               window_size=(-1, -1), out=None, return_lse=True, workspace=None):
+               window_size=(-1, -1), out=None, return_lse=True, workspace=None,
+               key_padding_mask=None):
     """``fa_fwd_kv_fp8``: a decode step (N_q <= 4) of q [B, H, N_q, d] (fp16 / bf16) over an
     FP8 E4M3 cache k, v [B, H, N_k, d] (``torch.float8_e4m3fn`` or its ``uint8`` codes), key
     element ``k_descale * value``, value element ``v_descale * value``.  Any strides with a
-    contiguous last dimension.  Returns ``(o, lse)``; ``o`` has the strides of ``q``."""
+    contiguous last dimension.  ``key_padding_mask`` as in ``fwd_kv``.  Returns ``(o, lse)``;
+    ``o`` has the strides of ``q``."""
     import torch
     for t in (k, v):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
@@ -476,6 +493,7 @@ def fwd_kv_fp8(q, k, v, k_descale, v_descale, softmax_scale=None, causal=False,
     scale, wl, wr = _resolve(q, softmax_scale, window_size)
     if not q.is_cuda:
         raise ValueError("q must be on a GPU device")
+    _check_key_padding(key_padding_mask, q, n_k)
     if out is not None:
         _check_out(out, q, "out", dense=False)
     o = torch.empty_like(q) if out is None else out
@@ -489,20 +507,21 @@ def fwd_kv_fp8(q, k, v, k_descale, v_descale, softmax_scale=None, causal=False,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.fa_fwd_kv_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, n_q, n_k,
                               d, _dtype_code(q), scale, float(k_descale), float(v_descale),
-                              int(bool(causal)), wl, wr, _ptr(workspace), ws_bytes,
-                              _stream(q.device)))
+                              int(bool(causal)), wl, wr, _ptr(key_padding_mask),
+                              _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, lse
 
 
 def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
            dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None, dropout_p=0.0,
-           dropout_seed=0, dropout_offset=0, block_mask=None):
+           dropout_seed=0, dropout_offset=0, block_mask=None, key_padding_mask=None):
     """``fa_bwd_kv``: gradients ``(dq, dk, dv)`` of ``fwd_kv``.  Any strides with a contiguous
     last dimension; new gradients take the strides of q, k, v."""
     import torch
     _check_kv_tensors(q, k, v)
     _check_slopes(alibi_slopes, q)
     _check_blocks(block_mask, q, k.shape[2])
+    _check_key_padding(key_padding_mask, q, k.shape[2])
     for t in (o, dout):
         if t.dtype != q.dtype or tuple(t.shape) != tuple(q.shape) or t.stride(-1) != 1:
             raise ValueError("o and dout must match q")
@@ -528,6 +547,6 @@ def bwd_kv(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=
                           _ptr(dk), _ptr(dv), st, _ptr(workspace),
                           workspace.numel() * workspace.element_size(), B, H, n_q, n_k, d,
                           _dtype_code(q), scale, int(bool(causal)), wl, wr, _ptr(alibi_slopes),
-                          _ptr(block_mask), float(dropout_p), int(dropout_seed),
-                          int(dropout_offset), _stream(q.device)))
+                          _ptr(block_mask), _ptr(key_padding_mask), float(dropout_p),
+                          int(dropout_seed), int(dropout_offset), _stream(q.device)))
     return dq, dk, dv

@@ -32,9 +32,10 @@ def attention(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), s
 class _AttentionKv(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, softmax_scale, causal, window_size, alibi_slopes, dropout_p,
-                dropout_seed, dropout_offset, block_mask):
+                dropout_seed, dropout_offset, block_mask, key_padding_mask):
         extra = dict(alibi_slopes=alibi_slopes, dropout_p=dropout_p, dropout_seed=dropout_seed,
-                     dropout_offset=dropout_offset, block_mask=block_mask)
+                     dropout_offset=dropout_offset, block_mask=block_mask,
+                     key_padding_mask=key_padding_mask)
         o, lse = _lib.fwd_kv(q, k, v, softmax_scale, causal, window_size, **extra)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.cfg = (softmax_scale, causal, window_size)
@@ -47,16 +48,18 @@ class _AttentionKv(torch.autograd.Function):
         if do.stride(-1) != 1:
             do = do.contiguous()
         dq, dk, dv = _lib.bwd_kv(do, q, k, v, o, lse, *ctx.cfg, **ctx.extra)
-        return (dq, dk, dv) + (None,) * 8
+        return (dq, dk, dv) + (None,) * 9
 
 
 def attention_kv(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
                  alibi_slopes=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0,
-                 block_mask=None):
+                 block_mask=None, key_padding_mask=None):
     """Differentiable ``fa_fwd_kv`` / ``fa_bwd_kv``: q [B, H, N_q, d] over k, v [B, H, N_k, d]
     (the queries being the last N_q key positions), any strides with a contiguous last
     dimension, optional ALiBi slopes, attention dropout (Philox masks from ``dropout_seed`` and
-    ``dropout_offset``; the backward replays the same masks) and a block-sparse mask.  k and v
-    must not share rows (a head stride of 0 would make their gradients overlap)."""
+    ``dropout_offset``; the backward replays the same masks), a block-sparse mask and a key
+    padding mask ([B, N_k], True where a key is padding).  k and v must not share rows (a head
+    stride of 0 would make their gradients overlap)."""
     return _AttentionKv.apply(q, k, v, softmax_scale, causal, tuple(window_size), alibi_slopes,
-                              float(dropout_p), int(dropout_seed), int(dropout_offset), block_mask)
+                              float(dropout_p), int(dropout_seed), int(dropout_offset), block_mask,
+                              key_padding_mask)

@@ -429,9 +429,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    const unsigned char* block_mask, float dropout_p,
-                    unsigned long long dropout_seed, unsigned dropout_offset, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    const unsigned char* block_mask, const unsigned char* key_padding_mask,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -479,14 +479,15 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
   for (const void* out : outs)
     if ((alibi_slopes && out == (const void*)alibi_slopes) ||
-        (block_mask && out == (const void*)block_mask))
+        (block_mask && out == (const void*)block_mask) ||
+        (key_padding_mask && out == (const void*)key_padding_mask))
       return FA_ERR_ALIAS;
 
   // Plain self-attention (equal lengths, dense operands, nothing extra) takes the kernels of
   // fa_fwd, which compute the same function.
   const fa::Strides dq_ = dense_strides(heads, seqlen_q, head_dim);
   if (seqlen_q == seqlen_k && seqlen_q > fa::kDecodeMaxQ && !alibi_slopes && !block_mask &&
-      drop.scale == 1.f && same_strides(p.sq, dq_) && same_strides(p.sk, dq_) &&
+      !key_padding_mask && drop.scale == 1.f && same_strides(p.sq, dq_) && same_strides(p.sk, dq_) &&
       same_strides(p.sv, dq_) && same_strides(p.so, dq_)) {
     fa::FwdParams f;
     f.q = q;
@@ -514,6 +515,7 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
   p.slopes = alibi_slopes;
   p.drop = drop;
   p.blocks = block_mask;
+  p.kpm = has_keys ? key_padding_mask : nullptr;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;
@@ -531,7 +533,8 @@ fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, fl
                         const fa_strides* strides, int batch, int heads, int seqlen_q,
                         int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale,
                         float k_descale, float v_descale, int causal, int window_left,
-                        int window_right, void* workspace, size_t workspace_bytes, void* stream) {
+                        int window_right, const unsigned char* key_padding_mask, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -576,6 +579,8 @@ fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, fl
   if ((lse && (const void*)lse == o) ||
       (outs[2] && ((const void*)outs[2] == o || (const void*)outs[2] == lse)))
     return FA_ERR_ALIAS;
+  for (const void* out : outs)
+    if (key_padding_mask && out == (const void*)key_padding_mask) return FA_ERR_ALIAS;
 
   p.q = q;
   p.k = k;
@@ -583,6 +588,7 @@ fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, fl
   p.o = o;
   p.lse = lse;
   p.ws = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.kpm = has_keys ? key_padding_mask : nullptr;
   p.B = batch;
   p.H = heads;
   p.Nq = seqlen_q;
@@ -608,8 +614,9 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    const unsigned char* block_mask, float dropout_p,
-                    unsigned long long dropout_seed, unsigned dropout_offset, void* stream) {
+                    const unsigned char* block_mask, const unsigned char* key_padding_mask,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
+                    void* stream) {
   g_last_error.clear();
   bool empty_q = false, empty_k = false;
   fa_status st = check_common(batch, heads, seqlen_q, head_dim, dtype, softmax_scale,
@@ -655,7 +662,8 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   if ((reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) != 0) return FA_ERR_MISALIGNED;
   for (void* out : outs)
     if ((alibi_slopes && out == (const void*)alibi_slopes) ||
-        (block_mask && out == (const void*)block_mask))
+        (block_mask && out == (const void*)block_mask) ||
+        (key_padding_mask && out == (const void*)key_padding_mask))
       return FA_ERR_ALIAS;
 
   // Plain self-attention takes the kernels of fa_bwd (the forward took those of fa_fwd).
@@ -664,7 +672,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
     bool dense = seqlen_q == seqlen_k && seqlen_q > fa::kDecodeMaxQ;
     const fa::Strides* all[] = {&p.sq, &p.sk, &p.sv, &p.so, &p.sg, &p.sdq, &p.sdk, &p.sdv};
     for (const fa::Strides* x : all) dense = dense && same_strides(*x, d_);
-    if (dense && !alibi_slopes && !block_mask && dropout_p == 0.f) {
+    if (dense && !alibi_slopes && !block_mask && !key_padding_mask && dropout_p == 0.f) {
       fa::BwdParams b;
       b.q = q;
       b.k = k;
@@ -700,6 +708,7 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
   p.stats = static_cast<float*>(workspace);
   p.slopes = alibi_slopes;
   p.blocks = block_mask;
+  p.kpm = has_k ? key_padding_mask : nullptr;
   if (!dropout_from(dropout_p, dropout_seed, dropout_offset, &p.drop)) return FA_ERR_BAD_DROPOUT;
   p.B = batch;
   p.H = heads;

@@ -48,6 +48,7 @@ struct BwdArgs {
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
   Dropout drop;         // used by the DROPOUT instances only
   const unsigned char* blocks;   // block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks, or null
+  const unsigned char* kpm;      // key padding mask [batch][nk] (nonzero = padding key), or null
   int n_qb, n_kb;
   // batch / head strides (bytes) and row strides (bytes) of q, k, v, o, dout, dq, dk, dv
   long long q_bs, q_hs, k_bs, k_hs, v_bs, v_hs, o_bs, o_hs, g_bs, g_hs;
@@ -190,6 +191,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     kreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rk, key * a.k_rs + (2 * ks + hi) * 16));
     vreg[ks] = __builtin_bit_cast(i16x8, buffer_load16(rv, key * a.v_rs + (2 * ks + hi) * 16));
   }
+  // key padding: this lane's key is hidden from every query (its dK and dV stay zero); a wave
+  // whose keys are all padding (or past the last key) computes nothing
+  const bool kpad = a.kpm != nullptr && key < nk && a.kpm[(long)b * nk + key] != 0;
+  const bool wave_idle = a.kpm != nullptr && __all(kpad || key >= nk);
 
   // queries that see any of the keys: the mask works on positions (index + off), which
   // start at off (negative when there are more queries than keys)
@@ -279,9 +284,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     // block-sparse: this wave's 32 keys and the step's 32 queries lie in one 64 x 64 block;
     // an unselected block contributes nothing (the wave still takes part in the copies)
     // (a wave past the last key has no output: it skips, and reads no mask entry)
-    if (a.blocks == nullptr ||
-        (k_first + 32 * wave < nk &&
-         a.blocks[((long)h * a.n_qb + (s * kQStep) / 64) * a.n_kb + (k_first + 32 * wave) / 64])) {
+    if (!wave_idle &&
+        (a.blocks == nullptr ||
+         (k_first + 32 * wave < nk &&
+          a.blocks[((long)h * a.n_qb + (s * kQStep) / 64) * a.n_kb + (k_first + 32 * wave) / 64]))) {
     // S = Q K^T and dP = dO V^T: C[m = query][n = key], 32 queries x this wave's 32 keys
     f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -315,6 +321,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
           const int qq = q0 + 8 * g + 4 * hi + e;
           pe = (qq < n && mk.visible(qq + off, key)) ? pe : 0.f;
         }
+        pe = kpad ? 0.f : pe;
         if constexpr (DROPOUT) {
           const bool kept = a.drop.keep_half(rw[2 * g + (e >> 1)][e & 1], key & 1);
           p[e] = kept ? pe * a.drop.scale : 0.f;
@@ -452,6 +459,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   for (int db = 0; db < kDb; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
   const float cm = c * mrow;   // -log2(e) LSE
+  // key padding: this batch entry's row of the mask
+  const unsigned char* kpm = a.kpm ? a.kpm + (long)b * nk : nullptr;
 
   // Block-sparse: the workgroup visits only the key tiles that one of its two 64-query block
   // rows selects.
@@ -482,10 +491,15 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const int t_next = next_tile(t + 1);
     if (t_next < t_end) load_tile(t_next);
 
+    // key padding: bit i of pad marks key t * kKStep + i as padding (keys past nk count as
+    // padding here; the sequence mask hides them anyway)
+    unsigned long long pad = 0;
+    if (kpm != nullptr) pad = __ballot(t * kKStep + lane >= nk || kpm[t * kKStep + lane] != 0);
     // block-sparse: this wave's 32 queries and the 64-key tile lie in one 64 x 64 block
     // (a wave past the last query has no output: it skips, and reads no mask entry)
-    if (a.blocks == nullptr ||
-        (q0 + 32 * wave < n && a.blocks[((long)h * a.n_qb + (q0 + 32 * wave) / 64) * a.n_kb + t])) {
+    if (pad != ~0ull &&
+        (a.blocks == nullptr ||
+         (q0 + 32 * wave < n && a.blocks[((long)h * a.n_qb + (q0 + 32 * wave) / 64) * a.n_kb + t]))) {
     // S^T = K Q^T and dP^T = V dO^T: C[m = key][n = query]
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -501,7 +515,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     }
 
     const int j0 = t * kKStep;
-    const bool full = mk.all_visible(q0 + off, q_last + off, j0, j0 + kKStep);
+    const bool full = pad == 0 && mk.all_visible(q0 + off, q_last + off, j0, j0 + kKStep);
     unsigned dsk[2][8];
     unsigned rw[2][4][2];   // DROPOUT: this query's draws for each block's four runs of keys
     if constexpr (DROPOUT) {
@@ -522,8 +536,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
           }
           float p = exp2_fast(x);
           if (!full) {
-            const int j = j0 + 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
-            p = (row_ok && mk.visible(qi + off, j)) ? p : 0.f;
+            const int jt = 32 * mb + 8 * ((i + e) >> 2) + 4 * hi + ((i + e) & 3);
+            p = (row_ok && mk.visible(qi + off, j0 + jt) && ((pad >> jt) & 1ull) == 0) ? p : 0.f;
           }
           if constexpr (DROPOUT) {   // key j: half e of word rw[i >> 2][(i & 3) >> 1]
             const bool kept = a.drop.keep_half(rw[mb][i >> 2][(i & 3) >> 1], e);
@@ -601,6 +615,7 @@ BwdArgs make_args(const BwdParams& p) {
   a.slopes = nullptr;
   a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
   a.blocks = nullptr;
+  a.kpm = nullptr;
   a.n_qb = a.n_kb = 0;
   // dense [B, H, N, D], or a packed batch's [H, total, D] (sequence b starts at row cu[b])
   const long long row = (long long)p.D * 2;
@@ -677,6 +692,7 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.slopes = p.slopes;
   a.drop = p.drop;
   a.blocks = p.blocks;
+  a.kpm = p.kpm;
   a.n_qb = (p.Nq + 63) / 64;
   a.n_kb = (p.Nk + 63) / 64;
   const bool alibi = p.slopes != nullptr, drop = p.drop.scale != 1.f;
@@ -709,7 +725,7 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   }
   // dense operands, nothing extra, and query tiles enough to fill the chip: the dK/dV and dQ
   // kernels of fa_bwd (their band of visible query - key differences shifted by N_k - N_q)
-  if (!alibi && !drop && p.blocks == nullptr && p.Nq > 0 && p.Nk > 0 &&
+  if (!alibi && !drop && p.blocks == nullptr && p.kpm == nullptr && p.Nq > 0 && p.Nk > 0 &&
       (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 && is_dense(p.sq, p.H, p.Nq, p.D) &&
       is_dense(p.so, p.H, p.Nq, p.D) && is_dense(p.sg, p.H, p.Nq, p.D) &&
       is_dense(p.sdq, p.H, p.Nq, p.D) && is_dense(p.sk, p.H, p.Nk, p.D) &&

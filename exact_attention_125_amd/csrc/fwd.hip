@@ -73,6 +73,7 @@ struct FwdArgs {
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
   Dropout drop;          // used by the DROPOUT instances only
   const unsigned char* blocks;   // block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks, or null
+  const unsigned char* kpm;      // key padding mask [batch][nk] (nonzero = padding key), or null
   int n_qb, n_kb;
   float c;        // |softmax_scale| * log2(e)
   unsigned q_sign;  // 0x80008000 to negate Q (negative scale), else 0
@@ -134,6 +135,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   static_assert(32 * QB <= 64 && kBc == 64, "a wave's tile lies in one 64 x 64 block");
   const unsigned char* brow =
       a.blocks ? a.blocks + ((long)h * a.n_qb + wq0 / 64) * a.n_kb : nullptr;
+  // key padding: this batch entry's row of the mask
+  const unsigned char* kpm = a.kpm ? a.kpm + (long)b * nk : nullptr;
 
   // Q^T as the B operand: lane holds query (wq0 + 32 qb + l32), head-dim chunk 2 ks + hi.
   i16x8 qreg[QB][kKs];
@@ -217,8 +220,10 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   const int tr_byte = (tq & 1) * 8;
 
   // One key tile for this wave.  MASKED selects the variant for tiles that straddle an
-  // edge; the common variant has no per-element work beyond the softmax itself.
-  auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0) {
+  // edge or hold padding keys (bit j - j0 of pad set); the common variant has no per-element
+  // work beyond the softmax itself.
+  auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0,
+                  unsigned long long pad) {
     constexpr bool MASKED = decltype(masked_tag)::value;
 
     // ---- S^T = K Q^T: two 32-key blocks x QB query blocks
@@ -259,8 +264,9 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = j0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            s[mb][qb][i] = mk.visible(qpos, j) ? s[mb][qb][i] : NEG_INF;
+            const int t = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool vis = mk.visible(qpos, j0 + t) && ((pad >> t) & 1ull) == 0;
+            s[mb][qb][i] = vis ? s[mb][qb][i] : NEG_INF;
           }
       }
     }
@@ -359,11 +365,16 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     const int t_next = next_tile(t + 1);
     if (t_next < t_end) load_tile(t_next);
     const int j0 = t * kBc;
-    if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo && (brow == nullptr || brow[t])) {
-      if (mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
-        tile(std::false_type{}, kt, vt, j0);
+    // key padding: bit i of pad marks key j0 + i as padding (keys past nk count as padding
+    // here; the sequence mask hides them anyway)
+    unsigned long long pad = 0;
+    if (kpm != nullptr) pad = __ballot(j0 + lane >= nk || kpm[j0 + lane] != 0);
+    if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo && (brow == nullptr || brow[t]) &&
+        pad != ~0ull) {
+      if (pad == 0 && mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
+        tile(std::false_type{}, kt, vt, j0, pad);
       else
-        tile(std::true_type{}, kt, vt, j0);
+        tile(std::true_type{}, kt, vt, j0, pad);
     }
     if (t_next < t_end) store_tile(stage ^ 1);
     __syncthreads();
@@ -459,6 +470,7 @@ hipError_t launch_cfg(const FwdParams& p, hipStream_t stream) {
   a.slopes = nullptr;
   a.drop = Dropout{0u, 0u, 0u, 0u, 1.f};
   a.blocks = nullptr;
+  a.kpm = nullptr;
   a.n_qb = a.n_kb = 0;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);
   return launch_args<D, BF16, WAVES, QB>(a, stream);
@@ -528,6 +540,7 @@ hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t
   a.slopes = p.slopes;
   a.drop = p.drop;
   a.blocks = p.blocks;
+  a.kpm = p.kpm;
   a.n_qb = (p.Nq + 63) / 64;
   a.n_kb = (p.Nk + 63) / 64;
   set_mask_and_scale(a, p.scale, p.causal, p.window_left, p.window_right);

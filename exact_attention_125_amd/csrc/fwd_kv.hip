@@ -56,6 +56,7 @@ struct DecArgs {
   float* plse;
   const float* slopes;   // ALiBi slopes [heads] (device), or null
   const unsigned char* brow0;   // block-sparse mask [heads][n_qb][n_kb] (queries < 64: row 0)
+  const unsigned char* kpm;     // key padding mask [B][nk] (nonzero = padding key), or null
   int n_qb, n_kb;
   float c;        // softmax_scale * log2(e) (* the key descale of an FP8 cache), signed
   float vs;       // the value descale of an FP8 cache (1 otherwise)
@@ -141,9 +142,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   mk.key_range(off, nq - 1 + off, lo, hi);
   lo = max(lo, split * a.split_keys);
   hi = min(hi, (split + 1) * a.split_keys);
-  const bool all_vis = lo < hi && mk.all_visible(off, nq - 1 + off, lo, hi) && a.brow0 == nullptr;
+  const bool all_vis = lo < hi && mk.all_visible(off, nq - 1 + off, lo, hi) && a.brow0 == nullptr &&
+                       a.kpm == nullptr;
   // block-sparse: the (single, nq <= 4 < 64) query block's row of the mask
   const unsigned char* brow = a.brow0 ? a.brow0 + (long)h * a.n_qb * a.n_kb : nullptr;
+  // key padding: this batch entry's row of the mask
+  const unsigned char* kpm = a.kpm ? a.kpm + (long)b * nk : nullptr;
   const int n_steps = lo < hi ? (hi - lo + STEP - 1) / STEP : 0;
 
   // the queries' 8 elements of this lane, times c (so scores come out in base-2 units)
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       for (int qi = 0; qi < NQ; ++qi)
         s[qi][u] = __builtin_fmaf(-b2, __builtin_fabsf((float)(qi + off - r)), s[qi][u]);
       if constexpr (MASKED) {
-        const bool in_block = brow == nullptr || (r < hi && brow[r >> 6]);
+        const bool in_block = (brow == nullptr || (r < hi && brow[r >> 6])) &&
+                              (kpm == nullptr || (r < hi && kpm[r] == 0));
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi)
           s[qi][u] = (r < hi && in_block && mk.visible(qi + off, r)) ? s[qi][u] : NEG_INF;
@@ -421,6 +426,7 @@ hipError_t launch_decode(const KvParams& p, const KvPlan& plan, hipStream_t stre
   a.plse = p.ws ? p.ws + (size_t)plan.n_split * a.n_bh * p.Nq * D : nullptr;
   a.slopes = p.slopes;
   a.brow0 = p.blocks;
+  a.kpm = p.kpm;
   a.n_qb = (p.Nq + 63) / 64;
   a.n_kb = (p.Nk + 63) / 64;
   a.c = (float)((double)p.scale * 1.4426950408889634 * (FP8 ? (double)p.k_descale : 1.0));
@@ -490,7 +496,7 @@ hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stre
   // dense operands, nothing extra, one key split, and query tiles enough to fill the chip:
   // the main forward kernel
   if (!plan.decode && !p.fp8 && plan.n_split == 1 && p.slopes == nullptr && p.blocks == nullptr &&
-      p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
+      p.kpm == nullptr && p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
       is_dense(p.sq, p.H, p.Nq, p.D) && is_dense(p.so, p.H, p.Nq, p.D) &&
       is_dense(p.sk, p.H, p.Nk, p.D) && is_dense(p.sv, p.H, p.Nk, p.D))
     return launch_fwd_main_kv(p, stream);

@@ -93,6 +93,7 @@ struct KvParams {
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Dropout drop{0u, 0u, 0u, 0u, 1.f};   // scale 1: no dropout
   const unsigned char* blocks = nullptr;   // block-sparse mask [H][ceil(Nq/64)][ceil(Nk/64)]
+  const unsigned char* kpm = nullptr;      // key padding mask [B][Nk], nonzero = padding key
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk, D;
   bool bf16;
@@ -122,7 +123,7 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8 = fal
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward kernel (fwd_main.hip) for N_q != N_k over dense operands with no ALiBi,
-// dropout or block mask.
+// dropout, block mask or key padding mask.
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream);
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
 hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);
@@ -153,6 +154,7 @@ struct BwdKvParams {
   const float* slopes = nullptr;   // ALiBi slopes [H] (device), or null
   Dropout drop{0u, 0u, 0u, 0u, 1.f};   // as in the forward call
   const unsigned char* blocks = nullptr;   // as in the forward call
+  const unsigned char* kpm = nullptr;      // as in the forward call
   Strides sq, sk, sv, so, sg, sdq, sdk, sdv;
   int B, H, Nq, Nk, D;
   bool bf16;

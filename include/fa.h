@@ -282,7 +282,17 @@ fa_status fa_bwd_packed(const void* q, const void* k, const void* v, const void*
  * lists among its next steps (§6) and the sparse attention the FA3.7 page names for very long
  * sequences (§6); neither fixes a pattern.  It combines with causal, window, ALiBi and dropout;
  * a query whose row selects no visible key gets O = 0, LSE = -inf.  It must not be an output
- * buffer; fa_bwd_kv must get the forward's mask. */
+ * buffer; fa_bwd_kv must get the forward's mask.
+ *
+ * Key padding mask: key_padding_mask is a device uint8 array [batch][N_k] (dense, C order), or
+ * NULL for none.  Entry (b, j) nonzero marks key j of batch entry b as padding: it is hidden
+ * from every query of that entry in every head (its scores are -inf), as the key_padding_mask
+ * argument of the attention module in §4.2 of the FA3.7 page hides padding keys before the
+ * softmax (the PyTorch-CUDA-v2.9 page, section "如何集成 FlashAttention：从安装到应用", names the
+ * same argument).  Padding keys may sit anywhere, not only at the end of a sequence; it
+ * combines with every other mask, ALiBi and dropout; a query left with no visible key gets
+ * O = 0, LSE = -inf, and a padding key gets dK = dV = 0.  Key tiles made only of padding keys
+ * are skipped.  It must not be an output buffer; fa_bwd_kv must get the forward's mask. */
 typedef struct fa_strides {
   long long batch, head, row;
 } fa_strides;
@@ -293,9 +303,9 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     const fa_strides* strides, int batch, int heads, int seqlen_q, int seqlen_k,
                     int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    const unsigned char* block_mask, float dropout_p,
-                    unsigned long long dropout_seed, unsigned dropout_offset, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    const unsigned char* block_mask, const unsigned char* key_padding_mask,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass of fa_fwd_kv (by recomputation, as fa_bwd): gradients of sum(dout * o) for
  * N_q queries over N_k keys with the queries at the end of the key sequence.
@@ -310,18 +320,20 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
  *                    16-byte aligned; contents on entry do not matter.
  * A row without keys has dQ = 0; with N_q = 0, dK = dV = 0 (and q, o, dout, lse, dq may be
  * NULL); with N_k = 0, dQ = 0 (k, v, dk, dv may be NULL).  Masks, scale, alibi_slopes,
- * block_mask and the dropout arguments must be those of the forward call.  Errors as in fa_bwd and
- * fa_fwd_kv. */
+ * block_mask, key_padding_mask and the dropout arguments must be those of the forward call.
+ * Errors as in fa_bwd and fa_fwd_kv. */
 fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides,
                     void* workspace, size_t workspace_bytes, int batch, int heads, int seqlen_q,
                     int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale, int causal,
                     int window_left, int window_right, const float* alibi_slopes,
-                    const unsigned char* block_mask, float dropout_p,
-                    unsigned long long dropout_seed, unsigned dropout_offset, void* stream);
+                    const unsigned char* block_mask, const unsigned char* key_padding_mask,
+                    float dropout_p, unsigned long long dropout_seed, unsigned dropout_offset,
+                    void* stream);
 
 /* ---- Decode steps over an FP8 key/value cache ------------------------------------------
- * fa_fwd_kv (no ALiBi, dropout or block mask) with K and V held as FP8 E4M3 codes: the OCP
+ * fa_fwd_kv (no ALiBi, dropout or block mask; key_padding_mask as there) with K and V held as
+ * FP8 E4M3 codes: the OCP
  * 8-bit floating-point format of sign, 4 exponent bits (bias 7) and 3 mantissa bits, largest
  * finite magnitude 448, smallest subnormal 2^-9, no infinities, codes 0x7F and 0xFF NaN.
  * Key element (b, h, r, c) is k_descale * value(code), value element v_descale * value(code).
@@ -346,7 +358,8 @@ fa_status fa_fwd_kv_fp8(const void* q, const void* k, const void* v, void* o, fl
                         const fa_strides* strides, int batch, int heads, int seqlen_q,
                         int seqlen_k, int head_dim, fa_dtype dtype, float softmax_scale,
                         float k_descale, float v_descale, int causal, int window_left,
-                        int window_right, void* workspace, size_t workspace_bytes, void* stream);
+                        int window_right, const unsigned char* key_padding_mask, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ---- Forward over FP8 E4M3 queries, keys and values -----------------------------------
  * fa_fwd with Q, K and V held as E4M3 codes (the format of fa_fwd_kv_fp8 above: the OCP 8-bit

@@ -34,6 +34,15 @@ neither fixes the pattern.  Reading: a boolean mask over blocks of BLOCK = 64 qu
 keys (query index i // 64, key index j // 64) selects the blocks that are computed; a pair
 outside the selected blocks is hidden like any masked pair (its score is -inf), so it takes
 no part in the softmax.
+
+Key padding mask: the reference attention module of [FA37] §4.2 takes a ``key_padding_mask``
+of shape (batch, seq_len), True where a key is padding, and sets the scores of those keys to
+-inf before the softmax, broadcast over heads and queries ([PT29], section "如何集成
+FlashAttention：从安装到应用", names the same argument among those the replacement layer keeps):
+a padding key is hidden from every query of its batch entry, in every head.  Reading: the mask may mark any keys
+(holes anywhere, not only a padded tail), it combines with the other masks by AND of the
+visible pairs, and a row left with no visible key follows the rule above (O = 0, LSE = -inf)
+where the page's softmax over a row of -inf would give NaN.
 """
 from __future__ import annotations
 
@@ -76,10 +85,12 @@ def block_allowed(n_q: int, n_k: int, block_mask) -> np.ndarray:
     return bm[np.arange(n_q)[:, None] // BLOCK, np.arange(n_k)[None, :] // BLOCK]
 
 
-def _scores(q, k, scale, causal, window, slope, block_mask=None):
+def _scores(q, k, scale, causal, window, slope, block_mask=None, key_mask=None):
     ok = cross_allowed_mask(q.shape[0], k.shape[0], causal, window)
     if block_mask is not None:
         ok &= block_allowed(q.shape[0], k.shape[0], block_mask)
+    if key_mask is not None:     # True = a padding key, hidden from every query
+        ok &= ~np.asarray(key_mask, dtype=bool)[None, :]
     s = scale * (q @ k.T)
     if slope:
         s = s + alibi_bias(q.shape[0], k.shape[0], slope)
@@ -87,18 +98,18 @@ def _scores(q, k, scale, causal, window, slope, block_mask=None):
 
 
 def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1),
-                  slope: float = 0.0, block_mask=None):
+                  slope: float = 0.0, block_mask=None, key_mask=None):
     """One (batch, head): q float64 [N_q, d], k, v [N_k, d] -> (O [N_q, d], LSE [N_q]).
 
     S = scale * Q K^T (minus the ALiBi distance penalty when slope != 0) is materialised in
     full, masked with -inf (also outside the selected blocks of ``block_mask``
-    [ceil(N_q / 64), ceil(N_k / 64)], if given), and put through the max-shifted softmax;
-    O = P V, LSE = rowmax + ln(rowsum).
+    [ceil(N_q / 64), ceil(N_k / 64)], if given, and at the keys where ``key_mask`` [N_k] is
+    True), and put through the max-shifted softmax; O = P V, LSE = rowmax + ln(rowsum).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    s = _scores(q, k, scale, causal, window, slope, block_mask)
+    s = _scores(q, k, scale, causal, window, slope, block_mask, key_mask)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])     # exp(-inf) = 0 at hidden entries
@@ -111,9 +122,10 @@ def cross_forward(q, k, v, scale: float, causal: bool = False, window=(-1, -1),
 
 
 def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1), slopes=None,
-                     block_mask=None):
+                     block_mask=None, key_padding_mask=None):
     """q [B, H, N_q, d], k, v [B, H, N_k, d] -> (O [B, H, N_q, d], LSE [B, H, N_q]);
-    ``slopes``: the H ALiBi slopes, or None; ``block_mask``: [H, n_qb, n_kb] or None."""
+    ``slopes``: the H ALiBi slopes, or None; ``block_mask``: [H, n_qb, n_kb] or None;
+    ``key_padding_mask``: [B, N_k] (True = padding key) or None."""
     B, H, n_q, _ = q.shape
     o = np.empty((B, H, n_q, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, n_q), dtype=np.float64)
@@ -121,12 +133,14 @@ def cross_forward_bh(q, k, v, scale, causal=False, window=(-1, -1), slopes=None,
         for h in range(H):
             o[b, h], lse[b, h] = cross_forward(q[b, h], k[b, h], v[b, h], scale, causal, window,
                                                0.0 if slopes is None else float(slopes[h]),
-                                               None if block_mask is None else block_mask[h])
+                                               None if block_mask is None else block_mask[h],
+                                               None if key_padding_mask is None
+                                               else key_padding_mask[b])
     return o, lse
 
 
 def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, -1),
-                   slope: float = 0.0, block_mask=None):
+                   slope: float = 0.0, block_mask=None, key_mask=None):
     """One (batch, head): gradients (dQ [N_q, d], dK, dV [N_k, d]) of <dO, O> for
     ``cross_forward``, the ordinary derivative of that definition:
 
@@ -140,7 +154,7 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    s = _scores(q, k, scale, causal, window, slope, block_mask)
+    s = _scores(q, k, scale, causal, window, slope, block_mask, key_mask)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])
@@ -152,7 +166,7 @@ def cross_backward(q, k, v, do, scale: float, causal: bool = False, window=(-1, 
 
 
 def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=None,
-                      block_mask=None):
+                      block_mask=None, key_padding_mask=None):
     """[B, H, N_q, d] q and dO, [B, H, N_k, d] k and v -> (dQ, dK, dV), one head at a time."""
     B, H = q.shape[:2]
     dq, dk, dv = (np.empty(t.shape, dtype=np.float64) for t in (q, k, v))
@@ -161,5 +175,6 @@ def cross_backward_bh(q, k, v, do, scale, causal=False, window=(-1, -1), slopes=
             dq[b, h], dk[b, h], dv[b, h] = cross_backward(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, window,
                 0.0 if slopes is None else float(slopes[h]),
-                None if block_mask is None else block_mask[h])
+                None if block_mask is None else block_mask[h],
+                None if key_padding_mask is None else key_padding_mask[b])
     return dq, dk, dv

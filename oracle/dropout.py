@@ -80,8 +80,8 @@ def dropout_keep(n_q: int, n_k: int, bh: int, p: float, seed: int, offset: int =
     return u >= np.uint64(keep_threshold(p))
 
 
-def _probs(q, k, scale, causal, window, slope):
-    s = _scores(q, k, scale, causal, window, slope)
+def _probs(q, k, scale, causal, window, slope, key_mask=None):
+    s = _scores(q, k, scale, causal, window, slope, key_mask=key_mask)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     live = np.isfinite(m)
     e = np.exp(s - np.where(live, m, 0.0)[:, None])
@@ -92,21 +92,21 @@ def _probs(q, k, scale, causal, window, slope):
     return p, lse
 
 
-def dropout_forward(q, k, v, scale, causal, window, slope, p_drop, keep):
+def dropout_forward(q, k, v, scale, causal, window, slope, p_drop, keep, key_mask=None):
     """One (batch, head) with the keep mask ``keep`` [N_q, N_k]: (O, LSE) with
     O = (P * keep / r) V (1 / r = ``keep_scale(p_drop)``) and LSE of the softmax before
-    dropout."""
+    dropout; ``key_mask`` [N_k] hides padding keys as in ``cross_forward``."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
-    p, lse = _probs(q, k, scale, causal, window, slope)
+    p, lse = _probs(q, k, scale, causal, window, slope, key_mask)
     return (p * keep * keep_scale(p_drop)) @ v, lse
 
 
-def dropout_backward(q, k, v, do, scale, causal, window, slope, p_drop, keep):
+def dropout_backward(q, k, v, do, scale, causal, window, slope, p_drop, keep, key_mask=None):
     """Gradients (dQ, dK, dV) of <dO, O> for ``dropout_forward`` with a fixed mask:
         dV = (P * keep / r)^T dO,   dP = (dO V^T) * keep / r,
         dS = P * (dP - rowsum(P * dP)),   dQ = scale dS K,   dK = scale dS^T Q."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
-    p, _ = _probs(q, k, scale, causal, window, slope)
+    p, _ = _probs(q, k, scale, causal, window, slope, key_mask)
     f = keep * keep_scale(p_drop)
     dv = (p * f).T @ do
     dp = (do @ v.T) * f
@@ -114,8 +114,10 @@ def dropout_backward(q, k, v, do, scale, causal, window, slope, p_drop, keep):
     return scale * (ds @ k), scale * (ds.T @ q), dv
 
 
-def dropout_forward_bh(q, k, v, scale, causal, window, p_drop, seed, offset=0, slopes=None):
-    """[B, H, N_q, d] / [B, H, N_k, d] arrays -> (O, LSE), masks from ``dropout_keep``."""
+def dropout_forward_bh(q, k, v, scale, causal, window, p_drop, seed, offset=0, slopes=None,
+                       key_padding_mask=None):
+    """[B, H, N_q, d] / [B, H, N_k, d] arrays -> (O, LSE), masks from ``dropout_keep``;
+    ``key_padding_mask`` [B, N_k] or None."""
     B, H, n_q, _ = q.shape
     n_k = k.shape[2]
     o = np.empty((B, H, n_q, v.shape[-1]))
@@ -125,11 +127,14 @@ def dropout_forward_bh(q, k, v, scale, causal, window, p_drop, seed, offset=0, s
             keep = dropout_keep(n_q, n_k, b * H + h, p_drop, seed, offset)
             o[b, h], lse[b, h] = dropout_forward(q[b, h], k[b, h], v[b, h], scale, causal, window,
                                                  0.0 if slopes is None else float(slopes[h]),
-                                                 p_drop, keep)
+                                                 p_drop, keep,
+                                                 None if key_padding_mask is None
+                                                 else key_padding_mask[b])
     return o, lse
 
 
-def dropout_backward_bh(q, k, v, do, scale, causal, window, p_drop, seed, offset=0, slopes=None):
+def dropout_backward_bh(q, k, v, do, scale, causal, window, p_drop, seed, offset=0, slopes=None,
+                        key_padding_mask=None):
     B, H, n_q, _ = q.shape
     n_k = k.shape[2]
     dq, dk, dv = (np.empty(t.shape) for t in (q, k, v))
@@ -138,5 +143,6 @@ def dropout_backward_bh(q, k, v, do, scale, causal, window, p_drop, seed, offset
             keep = dropout_keep(n_q, n_k, b * H + h, p_drop, seed, offset)
             dq[b, h], dk[b, h], dv[b, h] = dropout_backward(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, window,
-                0.0 if slopes is None else float(slopes[h]), p_drop, keep)
+                0.0 if slopes is None else float(slopes[h]), p_drop, keep,
+                None if key_padding_mask is None else key_padding_mask[b])
     return dq, dk, dv

@@ -39,24 +39,27 @@ def e4m3_value(codes) -> np.ndarray:
 
 
 def fp8_cache_forward(q, k_codes, v_codes, scale, k_descale, v_descale, causal=False,
-                      window=(-1, -1)):
+                      window=(-1, -1), key_mask=None):
     """One (batch, head): q float64 [N_q, d], k_codes / v_codes uint8 [N_k, d] ->
-    (O [N_q, d], LSE [N_q]) over K = k_descale * value(k_codes), V = v_descale * value(v_codes)."""
+    (O [N_q, d], LSE [N_q]) over K = k_descale * value(k_codes), V = v_descale * value(v_codes);
+    ``key_mask`` [N_k] (True = padding key) as in ``cross_forward``."""
     k = float(k_descale) * e4m3_value(k_codes)
     v = float(v_descale) * e4m3_value(v_codes)
-    return cross_forward(q, k, v, scale, causal, window)
+    return cross_forward(q, k, v, scale, causal, window, key_mask=key_mask)
 
 
 def fp8_cache_forward_bh(q, k_codes, v_codes, scale, k_descale, v_descale, causal=False,
-                         window=(-1, -1)):
-    """[B, H, N_q, d] q, [B, H, N_k, d] codes -> (O [B, H, N_q, d], LSE [B, H, N_q])."""
+                         window=(-1, -1), key_padding_mask=None):
+    """[B, H, N_q, d] q, [B, H, N_k, d] codes -> (O [B, H, N_q, d], LSE [B, H, N_q]);
+    ``key_padding_mask`` [B, N_k] or None."""
     B, H, n_q, d = q.shape
     o = np.empty((B, H, n_q, d))
     lse = np.empty((B, H, n_q))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = fp8_cache_forward(q[b, h], k_codes[b, h], v_codes[b, h], scale,
-                                                   k_descale, v_descale, causal, window)
+            o[b, h], lse[b, h] = fp8_cache_forward(
+                q[b, h], k_codes[b, h], v_codes[b, h], scale, k_descale, v_descale, causal, window,
+                None if key_padding_mask is None else key_padding_mask[b])
     return o, lse
 
 

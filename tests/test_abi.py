@@ -199,7 +199,7 @@ def fwd_kv(lib, q=Q, k=K, v=V, o=O, lse=L, strides=None, nq=5, nk=300, ws=WS, ws
     a = dict(GOOD, **kw)
     return lib.fa_fwd_kv(q, k, v, o, lse, strides, a["B"], a["H"], nq, nk, a["d"], a["dtype"],
                          a["scale"], a["causal"], a["wl"], a["wr"], a.get("slopes"),
-                         a.get("blocks"), a.get("p", 0.0), 0, 0, ws, ws_bytes, None)
+                         a.get("blocks"), a.get("kpm"), a.get("p", 0.0), 0, 0, ws, ws_bytes, None)
 
 
 def test_kv_rejections(lib):
@@ -224,6 +224,9 @@ def test_kv_rejections(lib):
     assert fwd_kv(lib, slopes=L) == 10
     assert fwd_kv(lib, blocks=O) == 10               # block mask: not an output
     assert bwd_kv(lib, blocks=DK) == 10
+    assert fwd_kv(lib, kpm=O) == 10                  # key padding mask: not an output
+    assert fwd_kv(lib, kpm=L) == 10
+    assert bwd_kv(lib, kpm=DV) == 10
     for p in (-0.1, 1.0, 2.0, float("nan"), float("inf")):
         assert fwd_kv(lib, p=p) == 12
         assert bwd_kv(lib, p=p) == 12
@@ -239,7 +242,9 @@ def test_kv_rejections(lib):
         return (_lib.FaStrides * 4)(*(_lib.FaStrides(*r) for r in rows))
     dense = (3 * 300 * 64, 300 * 64, 64)
     qd = (3 * 5 * 64, 5 * 64, 64)
-    assert fwd_kv(lib, strides=st(qd, dense, dense, qd), ws=0, ws_bytes=0) != 2
+    # accepted strides: the call goes on to the next check (an invalid dropout_p, so that no
+    # kernel is launched on the fake addresses)
+    assert fwd_kv(lib, strides=st(qd, dense, dense, qd), p=2.0) == 12
     assert fwd_kv(lib, strides=st(qd, (1, 300 * 64, 64), dense, qd)) == 2
     assert fwd_kv(lib, strides=st(qd, dense, (dense[0], -64, 64), qd)) == 2
     assert fwd_kv(lib, strides=st(qd, dense, dense, (qd[0], qd[1], 60))) == 2
@@ -263,7 +268,8 @@ def bwd_kv(lib, q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, strides=N
     a = dict(GOOD, **kw)
     return lib.fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, strides, ws, ws_bytes, a["B"], a["H"],
                          nq, nk, a["d"], a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"],
-                         a.get("slopes"), a.get("blocks"), a.get("p", 0.0), 0, 0, None)
+                         a.get("slopes"), a.get("blocks"), a.get("kpm"), a.get("p", 0.0), 0, 0,
+                         None)
 
 
 def test_bwd_kv_rejections(lib):
@@ -296,7 +302,7 @@ def test_fwd_kv_fp8_argument_errors(lib):
 
     def call(nq=1, nk=64, d=64, kd=1.0, vd=1.0, dtype=1):
         return lib.fa_fwd_kv_fp8(fake, fake, fake, fake, None, None, 1, 1, nq, nk, d, dtype,
-                                 0.125, kd, vd, 1, -1, -1, None, 0, None)
+                                 0.125, kd, vd, 1, -1, -1, None, None, 0, None)
 
     assert call(nq=5) == 2                      # FA_ERR_BAD_SHAPE: more than 4 queries
     assert call(kd=0.0) == 7                    # FA_ERR_BAD_SCALE
@@ -305,7 +311,7 @@ def test_fwd_kv_fp8_argument_errors(lib):
     assert call(d=96) == 3                      # FA_ERR_UNSUPPORTED_HEAD_DIM
     assert call(dtype=7) == 4                   # FA_ERR_BAD_DTYPE
     assert lib.fa_fwd_kv_fp8(None, None, None, None, None, None, 0, 1, 1, 1, 64, 1, 0.125, 1.0,
-                             1.0, 0, -1, -1, None, 0, None) == 0   # empty batch: no-op
+                             1.0, 0, -1, -1, None, None, 0, None) == 0   # empty batch: no-op
 
 
 def test_binding_rejects_bad_output_buffers():

@@ -403,3 +403,126 @@ def test_block_sparse_backward_central_differences():
         ap[which], am[which] = plus, minus
         num = (loss(*ap) - loss(*am)) / (2 * h)
         assert abs(grad[idx] - num) <= 1e-6 * max(1.0, abs(num))
+
+
+# ---------------------------------------------------------------------------- key padding mask
+def _random_key_mask(n_k, seed, density=0.3):
+    """True = padding key; holes anywhere (not only a padded tail)."""
+    return np.random.default_rng(seed).random(n_k) < density
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (6, 3)),
+                                           (True, (5, -1))])
+@pytest.mark.parametrize("n_q,n_k", [(1, 40), (9, 9), (12, 30), (30, 12)])
+def test_key_padding_torch_bool_mask(causal, window, n_q, n_k):
+    """torch CPU float64 SDPA with the boolean mask ~key_mask broadcast over the queries by
+    torch, ANDed with the position mask written out with tril / triu."""
+    q, k, v = _qkv(n_q, n_k, 4, seed=3 * n_q + n_k)
+    km = _random_key_mask(n_k, seed=n_q * n_k + 1)
+    off = n_k - n_q
+    pos = torch.ones(n_q, n_k, dtype=torch.bool)
+    if causal:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=off)
+    if window[0] >= 0:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).triu(diagonal=off - window[0])
+    if window[1] >= 0:
+        pos &= torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=off + window[1])
+    mask = pos & ~torch.from_numpy(km)[None, :]
+    live = mask.any(dim=1).numpy()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=mask[None], scale=0.55)[0].numpy()
+    o, lse = oracle.cross_forward(q, k, v, 0.55, causal, window, key_mask=km)
+    np.testing.assert_allclose(o[live], ref[live], rtol=1e-12, atol=1e-12)
+    assert np.all(o[~live] == 0.0) and np.all(np.isneginf(lse[~live]))
+
+
+def test_key_padding_is_attention_over_the_other_keys():
+    """Without a position mask, hiding keys is the same as deleting their rows of K and V."""
+    n_q, n_k = 7, 25
+    q, k, v = _qkv(n_q, n_k, 5, seed=17)
+    km = _random_key_mask(n_k, seed=18, density=0.4)
+    o, lse = oracle.cross_forward(q, k, v, 0.7, key_mask=km)
+    ro, rl = oracle.cross_forward(q, k[~km], v[~km], 0.7)
+    np.testing.assert_allclose(o, ro, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_key_padding_all_keys_hidden_and_none_hidden():
+    q, k, v = _qkv(5, 8, 3, seed=19)
+    o, lse = oracle.cross_forward(q, k, v, 0.5, True, key_mask=np.ones(8, bool))
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    a = oracle.cross_forward(q, k, v, 0.5, True, key_mask=np.zeros(8, bool))
+    b = oracle.cross_forward(q, k, v, 0.5, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_key_padding_suffix_is_a_shorter_sequence():
+    """Hiding the last keys of a non-causal call is the call over the first ones (the padded
+    batch of a sequence of that length)."""
+    q, k, v = _qkv(6, 20, 4, seed=20)
+    km = np.arange(20) >= 13
+    o, lse = oracle.cross_forward(q, k, v, 0.4, False, (3, 2), key_mask=km)
+    # the same positions: queries still sit at the last 6 of 20 positions
+    ok = oracle.cross_allowed_mask(6, 20, False, (3, 2)) & ~km[None, :]
+    for i in range(6):
+        js = np.nonzero(ok[i])[0]
+        if len(js) == 0:
+            assert o[i].sum() == 0.0 and np.isneginf(lse[i])
+            continue
+        s = 0.4 * (k[js] @ q[i])
+        z = np.exp(s - s.max())
+        np.testing.assert_allclose(o[i], (z / z.sum()) @ v[js], rtol=1e-13, atol=1e-13)
+
+
+def test_key_padding_backward_torch_autograd():
+    """dQ, dK, dV against torch CPU float64 autograd through SDPA with the same boolean mask
+    (every row keeps a visible key, so torch's softmax has no NaN rows); the hidden keys get
+    zero dK and dV."""
+    n_q, n_k = 10, 16
+    rng = np.random.default_rng(21)
+    q, k, v, do = (rng.standard_normal((r, 4)) for r in (n_q, n_k, n_k, n_q))
+    km = np.zeros(n_k, bool)
+    km[[0, 3, 4, 9, 15]] = True
+    mask = torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=n_k - n_q) & ~torch.from_numpy(km)
+    assert bool(mask.any(dim=1).all())
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None],
+                                                           attn_mask=mask[None], scale=0.65)[0]
+    (out * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = oracle.cross_backward(q, k, v, do, 0.65, True, key_mask=km)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+    assert np.all(dk[km] == 0.0) and np.all(dv[km] == 0.0)
+
+
+def test_key_padding_batch_entries_use_their_own_row():
+    """The [B, N_k] mask: entry b hides its own keys in every head."""
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((2, 3, n, 4)) for n in (5, 9, 9))
+    km = np.zeros((2, 9), bool)
+    km[0, [1, 2]] = True
+    km[1, [7, 8]] = True
+    o, lse = oracle.cross_forward_bh(q, k, v, 0.5, key_padding_mask=km)
+    for b in range(2):
+        for h in range(3):
+            ro, rl = oracle.cross_forward(q[b, h], k[b, h][~km[b]], v[b, h][~km[b]], 0.5)
+            np.testing.assert_allclose(o[b, h], ro, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], rl, rtol=1e-13, atol=1e-13)
+
+
+def test_mutant_query_side_mask_fails_the_deletion_pin():
+    """Applying the mask to the queries instead of the keys is a plausible mistake (a
+    transposed broadcast); the key-deletion pin rejects it."""
+    n = 12
+    q, k, v = _qkv(n, n, 4, seed=23)
+    km = _random_key_mask(n, seed=24, density=0.4)
+    s = 0.5 * (q @ k.T)
+    s = np.where(~km[:, None], s, -np.inf)           # the mistake: rows hidden, not columns
+    live = np.isfinite(s.max(axis=1))
+    e = np.exp(s - np.where(live, s.max(axis=1), 0.0)[:, None])
+    wrong = np.where(live[:, None], (e / np.where(live, e.sum(axis=1), 1.0)[:, None]) @ v, 0.0)
+    ro, _ = oracle.cross_forward(q, k[~km], v[~km], 0.5)
+    assert np.abs(wrong - ro).max() > 1e-2

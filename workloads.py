@@ -207,6 +207,16 @@ def cross_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int
     return out
 
 
+def key_padding_case(B: int, n_k: int, seed: int, density: float = 0.3, runs=()) -> np.ndarray:
+    """A seeded key padding mask, bool [B, n_k] (True = padding key): each key padded with
+    probability ``density`` (holes anywhere), plus the key ranges ``runs`` [(b, start, stop)]
+    padded whole (whole key tiles, a whole batch entry)."""
+    m = np.random.default_rng(seed).random((B, n_k)) < density
+    for b, start, stop in runs:
+        m[b, start:stop] = True
+    return m
+
+
 def fp8_cache_case(B: int, H: int, n_q: int, n_k: int, d: int, dtype: str, seed: int,
                    amax: float = 16.0):
     """Seeded decode inputs over an FP8 cache: q [B, H, n_q, d] N(0, 1) rounded like
