@@ -88,6 +88,7 @@ struct MainArgs {
   float c;        // max(|softmax_scale|, tiny) * log2(e)
   unsigned q_sign;  // 0x80008000 negates Q (negative scale)
   int causal, wl, wr;
+  const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
 };
 
 template <int D>
@@ -107,8 +108,12 @@ struct Shape {
 };
 
 // PADDED: a padded batch (per-batch lengths); a separate instance, so that the plain one
-// carries none of its code
-template <int D, bool BF16, bool PADDED>
+// carries none of its code.
+// ALIBI: every score gets the ALiBi penalty -slope_h |p - j| (p the query's key position, j the
+// key's), in the exponent domain: y = s c - slope log2(e) |p - j|.  The row statistics are
+// taken over y, so y is formed before the row maximum, relative to the row's current reference
+// (0 before its first visible tile), and moved to a new reference only where one is set.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
@@ -157,6 +162,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
   const Mask mk{nkr, a.causal, a.wl, a.wr};
   const float c = a.c;
   const float NEG_INF = -__builtin_inff();
+  const float b2 = ALIBI ? a.slopes[bh % a.heads] * kLog2e : 0.f;   // ALiBi slope, base 2
 
   // With 8 waves, the two waves of a SIMD (w and w + 4) own neighbouring 32-row stripes, so
   // under a causal mask they have nearly the same number of visible keys.
@@ -396,13 +402,92 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 #pragma unroll
       for (int e = LO; e < HI; ++e) sb[X][e / 16][e % 16] = __builtin_fmaf(sb[X][e / 16][e % 16], c, neg_m);
     };
+    // ALIBI: y = s c - b2 |p - j| - base, base the row's reference (0 while it has none).  In key
+    // tile t (keys j0 ..), element (mb, r) holds key j = j0 + 4 hi + Jr, Jr = 32 mb + 8 (r / 4) +
+    // r % 4; with Pl = p - j0 - 4 hi, p - j = Pl - Jr.  Where every key of the tile lies at or
+    // before every query of the wave (B = b2), or at or after every one (B = -b2), the penalty is
+    // linear in Jr: y = s C + (B Jr + L) with C = c, L = -B Pl - base, two instructions per score
+    // with wave-uniform C and B.  Under a causal mask the keys past a query are hidden anyway, so
+    // every tile takes B = b2.  A tile around the diagonal of a non-causal call gets
+    // s c - b2 |p - j| beforehand (the rare branch), and then C = 1, B = 0, L = -base.
+    auto alibi_base = [&]() __attribute__((always_inline)) { return m_ref == kNoRef ? 0.f : m_ref; };
+    auto alibi_pl = [&](int t) __attribute__((always_inline)) {
+      return (float)(qpos - (t_begin + t) * BC - 4 * hi);
+    };
+    auto alibi_straddle = [&](int t) __attribute__((always_inline)) {
+      const int j0 = (t_begin + t) * BC;
+      return !mk.causal && j0 + BC - 1 > wp0 && j0 < wp0 + 31;
+    };
+    auto alibi_fix = [&](auto xb, int t) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value;
+      if (alibi_straddle(t)) {
+        keep_branch();
+        const float pl = alibi_pl(t);
+#pragma unroll
+        for (int e = 0; e < MB * 16; ++e) {
+          const float jr = (float)(32 * (e / 16) + 8 * ((e % 16) >> 2) + (e % 4));
+          sb[X][e / 16][e % 16] =
+              __builtin_fmaf(__builtin_fabsf(pl - jr), -b2, sb[X][e / 16][e % 16] * c);
+        }
+      }
+    };
+    auto alibi_coef = [&](int t, float& cc, float& bb, float& ll) __attribute__((always_inline)) {
+      const bool str = alibi_straddle(t);
+      const bool right = !mk.causal && (t_begin + t) * BC >= wp0 + 31;   // every key >= every query
+      cc = str ? 1.f : c;
+      bb = str ? 0.f : right ? -b2 : b2;
+      ll = __builtin_fmaf(-bb, alibi_pl(t), -alibi_base());
+    };
+    auto alibi_y = [&](auto xb, auto lo_c, auto hi_c, float cc, float bb, float ll)
+                       __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value, LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+#pragma unroll
+      for (int e = LO; e < HI; ++e) {
+        const float jr = (float)(32 * (e / 16) + 8 * ((e % 16) >> 2) + (e % 4));
+        sb[X][e / 16][e % 16] = __builtin_fmaf(sb[X][e / 16][e % 16], cc, __builtin_fmaf(bb, jr, ll));
+      }
+    };
+    // ALIBI: the row statistics of y (relative to base): max, then the reference update with
+    // m_tile = max + base
+    auto update_ref_y = [&](float ext, float base) __attribute__((always_inline)) {
+      ext = max_with_partner(ext);
+      const float m_tile = ext + base;                  // -inf when no key of the tile shows
+      const float g = m_tile - m_ref;                   // +huge on a row's first visible tile
+      const float l_row = sum_with_partner(l_run);
+      const bool heavy = exp2_fast(g + 4.f) > l_row;
+      const bool move = (g > 0.f) & ((g > kTau) | heavy);
+      m_prev = m_ref;
+      m_ref = move ? m_tile : m_ref;
+      moved = move;
+    };
+    // ALIBI: where a reference moved, y relative to the new one (the rare branch)
+    auto alibi_rebase = [&](auto xb, float base) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value;
+      if (__any(moved)) {
+        keep_branch();
+        const float dm = m_ref - base;
+#pragma unroll
+        for (int e = 0; e < MB * 16; ++e) sb[X][e / 16][e % 16] -= dm;
+      }
+    };
     using Z = std::integral_constant<int, 0>;
     using NE = std::integral_constant<int, MB * 16>;
     auto alu0 = [&](auto xb) __attribute__((always_inline)) {
       float ext;
-      row_max(xb, Z{}, NE{}, ext);
-      update_ref(ext);
-      shift(xb, Z{}, NE{});
+      if constexpr (ALIBI) {
+        const float base = alibi_base();
+        float cc, bb, ll;
+        alibi_fix(xb, 0);
+        alibi_coef(0, cc, bb, ll);
+        alibi_y(xb, Z{}, NE{}, cc, bb, ll);
+        row_max(xb, Z{}, NE{}, ext);
+        update_ref_y(ext, base);
+        alibi_rebase(xb, base);
+      } else {
+        row_max(xb, Z{}, NE{}, ext);
+        update_ref(ext);
+        shift(xb, Z{}, NE{});
+      }
     };
     // ALU1 of S_Y, pair pp of its elements: P = 2^x (exp_pair), then l += P (fp32, in four
     // partial sums) and P rounded to the input type (sum_pair)
@@ -485,18 +570,36 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // GEMM1 + ALU0: the row max under the first MFMAs, the reference update under the next,
     // the shift spread over the rest
     // (with the K operand reads of ring stage stk spread over its MFMA slots)
-    auto compute_b = [&](auto xb, auto stk) __attribute__((always_inline)) {
+    // (ALIBI: the ALU0 of key tile t is y first, over the first NT slots, then the row max and
+    // the reference update; the move of y to a new reference follows the phase)
+    auto compute_b = [&](auto xb, auto stk, int t) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
       constexpr int NM = KK * DB, NX = 2;            // NX MFMA slots for the row max
       static_assert(NM >= 8, "ALU0 spread needs eight MFMA slots");
       constexpr int NR = MB * KS;                     // K reads, at most one per slot from slot 0
       static_assert(NR <= NM, "one K read per MFMA slot");
+      constexpr int NT = 4;                           // ALIBI: slots for y
       float ext;
+      float base = 0.f, cc = 0.f, bb = 0.f, ll = 0.f;
+      if constexpr (ALIBI) {
+        base = alibi_base();
+        alibi_coef(t, cc, bb, ll);
+      }
       static_for<NM>([&](auto ec) __attribute__((always_inline)) {
         constexpr int e = decltype(ec)::value;
         pv(ec);
         if constexpr (e < NR) read_k_one(stk, ec);
-        if constexpr (e < NX) {
+        if constexpr (ALIBI) {
+          if constexpr (e < NT) {
+            constexpr int LO = (NE::value * e) / NT, HI = (NE::value * (e + 1)) / NT;
+            alibi_y(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{}, cc, bb, ll);
+          } else if constexpr (e < NT + NX) {
+            constexpr int LO = (NE::value * (e - NT)) / NX, HI = (NE::value * (e - NT + 1)) / NX;
+            row_max(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{}, ext);
+          } else if constexpr (e == NT + NX) {
+            update_ref_y(ext, base);
+          }
+        } else if constexpr (e < NX) {
           constexpr int LO = (NE::value * e) / NX, HI = (NE::value * (e + 1)) / NX;
           row_max(xb, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{}, ext);
         } else if constexpr (e == NX) {
@@ -513,6 +616,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       pin(l_run);
       pin(m_ref);
       pin(m_prev);
+      if constexpr (ALIBI) alibi_rebase(xb, base);
     };
     // The scheduler would otherwise sink the operand reads below the phase's interleaved
     // MFMA/VALU groups, right in front of the wait for them, leaving their latency exposed.
@@ -550,7 +654,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();             // V_i operands have landed (GEMM1_i stays below)
       mask_if_edge(XB{}, i + 1);
-      compute_b(XB{}, std::integral_constant<int, (U + 2) % kNS>{});   // GEMM1_i + ALU0_{i+1}, K_{i+2} reads
+      if constexpr (ALIBI) alibi_fix(XB{}, i + 1);
+      compute_b(XB{}, std::integral_constant<int, (U + 2) % kNS>{}, i + 1);   // GEMM1_i + ALU0_{i+1}, K_{i+2} reads
       rescale();
       wait_lgkmcnt0();
       keep_kop();                        // no register of an in-flight read is reused before the wait
@@ -657,8 +762,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 
 // nq query rows over nk key rows (dense [B, H, rows, D] operands), query i at key position
 // i + nk - nq; nq == nk for self-attention and padded batches
+// slopes: ALiBi slopes [H] (device) or null
 template <int D, bool BF16>
-hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
+hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
+                  const float* slopes = nullptr) {
   MainArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -689,8 +796,12 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream) {
   a.causal = p.causal;
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
+  a.slopes = slopes;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr || p.cu != nullptr)
+  if (slopes != nullptr)   // (no padded batch takes ALiBi)
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
+  else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, a);
   else
@@ -725,8 +836,10 @@ hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
   f.window_left = p.window_left;
   f.window_right = p.window_right;
   if (p.D == 64)
-    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream) : launch<64, false>(f, p.Nq, p.Nk, stream);
-  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream) : launch<128, false>(f, p.Nq, p.Nk, stream);
+    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream, p.slopes)
+                  : launch<64, false>(f, p.Nq, p.Nk, stream, p.slopes);
+  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream, p.slopes)
+                : launch<128, false>(f, p.Nq, p.Nk, stream, p.slopes);
 }
 
 }  // namespace fa

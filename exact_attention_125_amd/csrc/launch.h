@@ -122,8 +122,8 @@ constexpr int kKvMfmaKeyStep = 64;   // key tile of the four-wave MFMA kernel
 KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8 = false);
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
-// The main forward kernel (fwd_main.hip) for N_q != N_k over dense operands with no ALiBi,
-// dropout, block mask or key padding mask.
+// The main forward kernel (fwd_main.hip) for N_q queries over N_k keys, dense operands, with
+// ALiBi slopes or none, and no dropout, block mask or key padding mask.
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream);
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
 hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);
