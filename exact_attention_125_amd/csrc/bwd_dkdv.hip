@@ -80,6 +80,7 @@ struct DkdvArgs {
   float scale;
   int causal, wl, wr;
   int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
+  const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
 };
 
 template <int D>
@@ -111,8 +112,12 @@ __device__ __forceinline__ void slices(F&& f) {
   }
 }
 
-// dK, dV of key tile kt of head bh (the whole workgroup)
-template <int D, bool BF16, bool PADDED>
+// dK, dV of key tile kt of head bh (the whole workgroup).
+// ALIBI (no padded batch; a band with no pair past the diagonal, dlo >= nr - nk, as under a
+// causal mask): P carries the forward's ALiBi penalty -slope log2(e) (p - j), p = i + nk - nr the
+// query's position, linear in the query index: 2^(c S + La - b2 R), R = 8 (r / 4) + r % 4 of
+// accumulator row r, La = -b2 (q0 + 4 hi + nk - nr - j) per key block and step.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false>
 __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int bh, int kt) {
   using S = DShape<D>;
   constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
@@ -154,11 +159,21 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   const int stat_bytes = stat_blocks(nr) * 2 * kStatRows * 4;
   const auto rs = make_rsrc(a.stats + (long)bh * stat_blocks(nr) * 2 * kStatRows, stat_bytes);
   const float c_scale = a.c;
+  const float b2 = ALIBI ? a.slopes[bh % a.heads] * kLog2e : 0.f;   // ALiBi slope, base 2
 
   // ---- this wave's keys: K^T and V^T as B operands (lane: key kw0 + 32 kb + l32, dims of
   // chunk 2 ks + hi), zero beyond the sequence
   const int k_first = kt * S::KWG;
   const int kw0 = k_first + S::KW * wave;
+  // ALIBI: la[kb] for query step t (first query 32 (s_begin + t)), set before its P
+  float la[KB];
+  auto alibi_step = [&](int q0) __attribute__((always_inline)) {
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        la[kb] = -b2 * (float)(q0 + 4 * hi + a.nk - nr - (kw0 + 32 * kb + l32));
+    }
+  };
   i16x8 kreg[KB][KS], vreg[KB][KS];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -365,8 +380,15 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // P = 2^(c S) for query 8 (i/4) + 4 hi + i%4 of the step
   auto p_slice = [&](int c) __attribute__((always_inline)) {
     const int kb = c >> 3, g = c & 7;
-    pv[kb][2 * g] = exp2_fast(sacc[kb][2 * g] * c_scale);
-    pv[kb][2 * g + 1] = exp2_fast(sacc[kb][2 * g + 1] * c_scale);
+    if constexpr (ALIBI) {
+      const float r0 = (float)(8 * ((2 * g) >> 2) + ((2 * g) & 3));
+      pv[kb][2 * g] = exp2_fast(__builtin_fmaf(sacc[kb][2 * g], c_scale, __builtin_fmaf(-b2, r0, la[kb])));
+      pv[kb][2 * g + 1] =
+          exp2_fast(__builtin_fmaf(sacc[kb][2 * g + 1], c_scale, __builtin_fmaf(-b2, r0 + 1.f, la[kb])));
+    } else {
+      pv[kb][2 * g] = exp2_fast(sacc[kb][2 * g] * c_scale);
+      pv[kb][2 * g + 1] = exp2_fast(sacc[kb][2 * g + 1] * c_scale);
+    }
     pk[kb][g] = pack2<BF16>(pv[kb][2 * g], pv[kb][2 * g + 1]);
   };
   // On steps that hold hidden pairs, zero them afterwards: a branch around VALU work only, so
@@ -539,6 +561,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
       keep(mv[g]);
       keep(ndv[g]);
     }
+    alibi_step(s_begin * kBQ);
     slices<0, NSL>(p_slice);
     if (edge_step(0)) mask_step(0);
     pin_phase2();
@@ -555,6 +578,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     phase1(s);
     advance_tr(s);                   // tile s   -> s+1
     advance_rows(s + 1);             // tile s+1 -> s+2
+    alibi_step((s_begin + s + 1) * kBQ);
     phase2();
     if (s + 1 < NSTEP && edge_step(s + 1)) {
       mask_step(s + 1);
@@ -604,7 +628,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 // tile, so tiles t and n_tiles - 1 - t together take the same time for every t: paired, the
 // workgroups are of equal length and fill the chip evenly.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * DShape<D>::STAGE];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
@@ -613,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dkdv_tile<D, BF16, PADDED>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dkdv_tile<D, BF16, PADDED, ALIBI>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -653,8 +677,12 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   const int half = (a.n_tiles + 1) / 2;
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
+  a.slopes = p.slopes;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr || p.cu != nullptr)
+  if (p.slopes != nullptr)   // (no padded batch takes ALiBi)
+    hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
+  else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

@@ -71,6 +71,7 @@ struct DqArgs {
   float scale;
   int causal, wl, wr;
   int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
+  const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
 };
 
 template <int D>
@@ -96,8 +97,12 @@ __device__ __forceinline__ void dq_slices(F&& f) {
   }
 }
 
-// dQ of query tile qt of head bh (the whole workgroup)
-template <int D, bool BF16, bool PADDED>
+// dQ of query tile qt of head bh (the whole workgroup).
+// ALIBI (no padded batch; a band with no pair past the diagonal, as under a causal mask): P
+// carries the forward's ALiBi penalty -slope log2(e) (p - j), p = q + off the query's position,
+// linear in the key index: 2^(c S + Lq + b2 R), R = 8 (r / 4) + r % 4 of accumulator row r,
+// Lq = c m - b2 (p - k0 - 4 hi) per query block and step (keys k0 ..).
+template <int D, bool BF16, bool PADDED, bool ALIBI = false>
 __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int bh, int qt) {
   using S = QShape<D>;
   constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
@@ -138,6 +143,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const auto rg = make_rsrc(a.dout + head, n * RB);
   const Mask mk{nkr, a.causal, a.wl, a.wr};
   const float c_scale = a.c;
+  const float b2 = ALIBI ? a.slopes[bh % a.heads] * kLog2e : 0.f;   // ALiBi slope, base 2
 
   // ---- this wave's queries: Q^T and dO^T as B operands (lane: query qw0 + 32 qb + l32, dims
   // of chunk 2 ks + hi), zero beyond the sequence; their statistics as lane scalars
@@ -146,6 +152,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   i16x8 qreg[QB][KS], greg[QB][KS];
   float lse_in[QB], nd_in[QB];   // statistics as loaded (row 0's beyond the sequence)
   float cm[QB];                  // c m = -log2(e) LSE, set after the prologue copies
+  float lq0[QB], lq[QB];         // ALIBI: c m - b2 (p - 4 hi), and Lq of the current step
   f32x16 ndv[QB];                // -delta, the initial accumulator of dP, likewise
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -270,8 +277,15 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   constexpr int NSL = 8 * QB;
   auto p_slice = [&](int c) __attribute__((always_inline)) {     // P = 2^(c S + c m)
     const int qb = c >> 3, g = c & 7;
-    pv[qb][2 * g] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g], c_scale, cm[qb]));
-    pv[qb][2 * g + 1] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g + 1], c_scale, cm[qb]));
+    if constexpr (ALIBI) {
+      const float r0 = (float)(8 * ((2 * g) >> 2) + ((2 * g) & 3));
+      pv[qb][2 * g] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g], c_scale, __builtin_fmaf(b2, r0, lq[qb])));
+      pv[qb][2 * g + 1] =
+          exp2_fast(__builtin_fmaf(sacc[qb][2 * g + 1], c_scale, __builtin_fmaf(b2, r0 + 1.f, lq[qb])));
+    } else {
+      pv[qb][2 * g] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g], c_scale, cm[qb]));
+      pv[qb][2 * g + 1] = exp2_fast(__builtin_fmaf(sacc[qb][2 * g + 1], c_scale, cm[qb]));
+    }
   };
   auto ds_slice = [&](int c) __attribute__((always_inline)) {    // dS = P (dP - delta)
     const int qb = c >> 3, g = c & 7;
@@ -392,6 +406,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   for (int qb = 0; qb < QB; ++qb) {
     const bool ok = qw0 + 32 * qb + l32 < n;
     cm[qb] = ok ? c_scale * lse_in[qb] : 0.f;
+    if constexpr (ALIBI) lq0[qb] = __builtin_fmaf(-b2, (float)(qw0 + 32 * qb + l32 + off - 4 * hi), cm[qb]);
     const float nd = ok ? nd_in[qb] : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ndv[qb][i] = nd;
@@ -419,6 +434,10 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 
   // ---- steps: one barrier each
   for (int s = 0; s < NSTEP; ++s) {
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lq[qb] = __builtin_fmaf(b2, (float)((s_begin + s) * kBK), lq0[qb]);
+    }
     phase1(s);
     if (edge_step(s)) {
       mask_step(s);
@@ -478,7 +497,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 // tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
 // latest (longest) tiles go first.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
@@ -488,7 +507,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqAr
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dq_tile<D, BF16, PADDED>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dq_tile<D, BF16, PADDED, ALIBI>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -530,8 +549,12 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.paired = p.causal && p.window_left < 0 && nq >= (nk - nq) + 2 * S::QWG &&
              (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
+  a.slopes = p.slopes;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.seqlens != nullptr || p.cu != nullptr)
+  if (p.slopes != nullptr)   // (no padded batch takes ALiBi)
+    hipLaunchKernelGGL((dq_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
+  else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

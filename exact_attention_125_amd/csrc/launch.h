@@ -43,6 +43,9 @@ struct BwdParams {
   float* stats;        // workspace: per-query statistics in 32-query blocks (stat_index)
   const int* seqlens = nullptr;   // as in FwdParams
   const int* cu = nullptr;        // as in FwdParams
+  const float* slopes = nullptr;  // ALiBi slopes [H] (device), or null: the main dK/dV and dQ
+                                  // kernels take them where no visible pair lies past the
+                                  // diagonal (causal, or a right window of 0)
   int total = 0;
   int B, H, N, D;
   bool bf16;

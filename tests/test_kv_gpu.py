@@ -326,6 +326,18 @@ def test_alibi_forward_main_kernel(fa, causal, window, n_q, n_k, d, dtype):
             slopes=sl, edge=True)
 
 
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (300, 0)), (False, (-1, 0)),
+                                           (False, (-1, -1)), (False, (100, 40))])
+@pytest.mark.parametrize("n_q,n_k", [(512, 512), (512, 1500), (300, 1000)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_alibi_backward_main_kernels(fa, causal, window, n_q, n_k, d, dtype):
+    """Full-grid ALiBi backward: the tuned dK/dV and dQ kernels where no visible pair lies past
+    the diagonal (causal, or a right window of 0), the four-wave ones otherwise."""
+    H = 64 if n_q >= 512 else 128
+    run_backward(fa, 2, H, n_q, n_k, d, dtype, causal, window, seed=3 * n_q + n_k,
+                 slopes=alibi_slopes(H))
+
+
 def test_alibi_main_kernel_scales_and_backward(fa):
     """Zero, negative and larger scales on the main kernel's ALiBi instance, and the backward
     (four-wave kernels) from its LSE."""
