@@ -201,9 +201,11 @@ __global__ __launch_bounds__(kT8, 2) void fwd_fp8_kernel(Fp8Args a) {
     float m_ref = NEG_INF;   // reference exponent (base 2)
     float l_run = 0.f;       // sum of 2^(s c - m + kPS) over this lane's keys
 
-    auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0)
+    // One key tile.  Tiles with hidden pairs (edges, and tiles past this wave's keys) have
+    // them set to -inf in a branch around the mask alone, so the accumulators see one code
+    // path (no register copies where paths join); hidden scores then give P'' = 0.
+    auto tile = [&](const char FA_LDS* kt, const char FA_LDS* vt, int j0, bool masked)
         __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
       // ---- S^T = K Q^T: two 32-key blocks
       f32x16 s[2];
 #pragma unroll
@@ -218,7 +220,8 @@ __global__ __launch_bounds__(kT8, 2) void fwd_fp8_kernel(Fp8Args a) {
           s[mb] = mfma_fp8(kop, qop[ks], s[mb]);
         }
       }
-      if constexpr (MASKED) {
+      if (masked) {
+        keep_branch();
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -252,8 +255,8 @@ __global__ __launch_bounds__(kT8, 2) void fwd_fp8_kernel(Fp8Args a) {
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        float x = exp2_fast(__builtin_fmaf(s[e / 16][e % 16], c, neg_m));
-        if constexpr (MASKED) x = s[e / 16][e % 16] == NEG_INF ? 0.f : x;
+        // c > 0 and neg_m finite: a hidden score (-inf) gives 2^-inf = 0
+        const float x = exp2_fast(__builtin_fmaf(s[e / 16][e % 16], c, neg_m));
         p[e] = x;
         part[e & 3] += x;
       }
@@ -287,12 +290,8 @@ __global__ __launch_bounds__(kT8, 2) void fwd_fp8_kernel(Fp8Args a) {
       const char FA_LDS* vt = kt + TILE;
       if (t + 1 < t_end) load_tile(t + 1);
       const int j0 = t * kBc8;
-      if (wave_has_rows && j0 < wkey_hi && j0 + kBc8 > wkey_lo) {
-        if (mk.all_visible(wq0, wq1, j0, j0 + kBc8))
-          tile(std::false_type{}, kt, vt, j0);
-        else
-          tile(std::true_type{}, kt, vt, j0);
-      }
+      const bool live = wave_has_rows && j0 < wkey_hi && j0 + kBc8 > wkey_lo;
+      tile(kt, vt, j0, !(live && mk.all_visible(wq0, wq1, j0, j0 + kBc8)));
       if (t + 1 < t_end) store_tile(stage ^ 1);
       __syncthreads();
       stage ^= 1;
