@@ -222,9 +222,10 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
   // One key tile for this wave.  MASKED selects the variant for tiles that straddle an
   // edge or hold padding keys (bit j - j0 of pad set); the common variant has no per-element
   // work beyond the softmax itself.
-  auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0,
-                  unsigned long long pad) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // (Tiles with hidden pairs have them set to -inf in a branch around the mask alone, so the
+  // accumulators see one code path, with no register copies where paths join.)
+  auto tile = [&](const char FA_LDS* kt, const char FA_LDS* vt, int j0, unsigned long long pad,
+                  bool masked) {
 
     // ---- S^T = K Q^T: two 32-key blocks x QB query blocks
     f32x16 s[2][QB];
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
       }
     }
 
-    if constexpr (MASKED) {
+    if (masked) {
+      keep_branch();
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = wq0 + 32 * qb + l32 + off;
@@ -320,12 +322,10 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
         if constexpr (DROPOUT) a.drop.runs4(bh, wq0 + 32 * qb + l32, j0 + 32 * mb + 4 * hi, rw);
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
+          // hidden scores are -inf: with c > 0 (a zero scale is kept tiny) and a finite
+          // reference shift they give 2^-inf = 0
           float p0 = exp2_fast(__builtin_fmaf(s[mb][qb][i], c, neg_m));
           float p1 = exp2_fast(__builtin_fmaf(s[mb][qb][i + 1], c, neg_m));
-          if constexpr (MASKED) {   // hidden scores are -inf; also right for c == 0
-            p0 = s[mb][qb][i] == NEG_INF ? 0.f : p0;
-            p1 = s[mb][qb][i + 1] == NEG_INF ? 0.f : p1;
-          }
           part[(i >> 1) & 3] += p0 + p1;
           if constexpr (DROPOUT) {   // keys j, j + 1: the low and high half of one word
             const unsigned w = rw[i >> 2][(i & 3) >> 1];
@@ -370,12 +370,8 @@ __global__ __launch_bounds__(64 * WAVES, (D == 64 ? 2 : 1)) void fwd_kernel(FwdA
     unsigned long long pad = 0;
     if (kpm != nullptr) pad = __ballot(j0 + lane >= nk || kpm[j0 + lane] != 0);
     if (wave_has_rows && j0 < wkey_hi && j0 + kBc > wkey_lo && (brow == nullptr || brow[t]) &&
-        pad != ~0ull) {
-      if (pad == 0 && mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc))
-        tile(std::false_type{}, kt, vt, j0, pad);
-      else
-        tile(std::true_type{}, kt, vt, j0, pad);
-    }
+        pad != ~0ull)
+      tile(kt, vt, j0, pad, !(pad == 0 && mk.all_visible(wq0 + off, wq1 + off, j0, j0 + kBc)));
     if (t_next < t_end) store_tile(stage ^ 1);
     __syncthreads();
     stage ^= 1;
@@ -441,7 +437,9 @@ hipError_t launch_args(FwdArgs& a, hipStream_t stream) {
 }
 
 void set_mask_and_scale(FwdArgs& a, float scale, int causal, int wl, int wr) {
-  a.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+  // a zero scale becomes a tiny one: every visible probability is then exactly 1 (as for 0)
+  // while hidden scores (-inf) still give 0 instead of -inf * 0 = NaN
+  a.c = (float)(std::fmax(std::fabs((double)scale), 1e-30) * 1.4426950408889634);
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
   a.causal = causal;
   a.wl = wl;

@@ -153,9 +153,11 @@ __global__ __launch_bounds__(SplitShape<D>::THREADS, 1) void fwd_split_kernel(Sp
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_ref = NEG_INF, l_run = 0.f;
 
-  auto tile = [&](auto masked_tag, const char FA_LDS* kt, const char FA_LDS* vt, int j0)
+  // One key tile.  Tiles with hidden pairs (edges, tiles past this wave's keys) have them set
+  // to -inf in a branch around the mask alone, so the accumulators see one code path (no
+  // register copies where paths join); c > 0 and a finite reference turn -inf into P = 0.
+  auto tile = [&](const char FA_LDS* kt, const char FA_LDS* vt, int j0, bool masked)
       __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(SplitShape<D>::THREADS, 1) void fwd_split_kernel(Sp
             __builtin_bit_cast(i16x8, lds_read16(kt, tile_offset<D>(32 * mb + l32, 2 * ks + hi)));
         s[mb] = mfma32x32x16<BF16>(kop, qreg[ks], s[mb]);
       }
-    if constexpr (MASKED) {
+    if (masked) {
+      keep_branch();
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -197,12 +200,8 @@ __global__ __launch_bounds__(SplitShape<D>::THREADS, 1) void fwd_split_kernel(Sp
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        float p0 = exp2_fast(__builtin_fmaf(s[mb][i], c, neg_m));
-        float p1 = exp2_fast(__builtin_fmaf(s[mb][i + 1], c, neg_m));
-        if constexpr (MASKED) {
-          p0 = s[mb][i] == NEG_INF ? 0.f : p0;
-          p1 = s[mb][i + 1] == NEG_INF ? 0.f : p1;
-        }
+        const float p0 = exp2_fast(__builtin_fmaf(s[mb][i], c, neg_m));
+        const float p1 = exp2_fast(__builtin_fmaf(s[mb][i + 1], c, neg_m));
         part_sum[(i >> 1) & 3] += p0 + p1;
         pk[mb][i >> 1] = pack2<BF16>(p0, p1);
       }
@@ -236,11 +235,9 @@ __global__ __launch_bounds__(SplitShape<D>::THREADS, 1) void fwd_split_kernel(Sp
     const char FA_LDS* vt = kt + TILE;
     if (have_next) load_tile(t + 1);
     const int j0 = t * kBcS;
-    if (have && wave_has_rows && j0 < wkey_hi && j0 + kBcS > wkey_lo) {
-      if (mk.all_visible(wq0, wq1, j0, j0 + kBcS))
-        tile(std::false_type{}, kt, vt, j0);
-      else
-        tile(std::true_type{}, kt, vt, j0);
+    if (have) {   // past the part's tiles the stage holds no tile of it
+      const bool live = wave_has_rows && j0 < wkey_hi && j0 + kBcS > wkey_lo;
+      tile(kt, vt, j0, !(live && mk.all_visible(wq0, wq1, j0, j0 + kBcS)));
     }
     if (have_next) store_tile(stage ^ 1);
     __syncthreads();
