@@ -101,7 +101,7 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
 }
 
 template <int D, bool BF16OUT>
-__global__ __launch_bounds__(kT8, 2) void fwd_fp8_kernel(Fp8Args a) {
+__global__ __launch_bounds__(kT8, D == 64 ? 4 : 3) void fwd_fp8_kernel(Fp8Args a) {
   constexpr int RB = D;                         // bytes per row (one byte per element)
   constexpr int TILE = kBc8 * RB;               // bytes per K or V tile
   constexpr int CPR = D / 16;                   // 16-byte chunks per row
