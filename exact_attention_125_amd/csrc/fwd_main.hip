@@ -89,7 +89,12 @@ struct MainArgs {
   unsigned q_sign;  // 0x80008000 negates Q (negative scale)
   int causal, wl, wr;
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
+  const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
+  int n_qb, n_kb;
 };
+
+// BLK: the list of a query tile's selected key tiles, at most kListMax entries
+constexpr int kListMax = 1024;
 
 template <int D>
 struct Shape {
@@ -113,15 +118,25 @@ struct Shape {
 // key's), in the exponent domain: y = s c - slope log2(e) |p - j|.  The row statistics are
 // taken over y, so y is formed before the row maximum, relative to the row's current reference
 // (0 before its first visible tile), and moved to a new reference only where one is set.
-template <int D, bool BF16, bool PADDED, bool ALIBI = false>
+// BLK: a block-sparse mask.  A query tile's two 64-query blocks select key tiles; the
+// workgroup visits only the tiles one of them selects (a list of them in LDS, built at the
+// start of the tile), and a wave whose block does not select a visited tile sees it hidden.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
   constexpr int TILE = S::TILE, CPT = S::CPT;
 
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE];
+  static_assert(!(ALIBI && BLK), "no instance takes both");
+  constexpr int kListBytes = BLK ? 4 * (kListMax + 8) + 8 * 2 * (kListMax / 64) : 0;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE + kListBytes];
   char FA_LDS* kring = (char FA_LDS*)lds_raw;
   char FA_LDS* vring = kring + kNS * TILE;
+  // BLK: entries r | s0 << 16 | s1 << 17 (r the tile index after t_begin, s0 / s1 whether the
+  // first / second query block selects it), then kPD + 2 sentinels; the count in the last slot.
+  // After the list, per chunk of 64 tiles, the selection bits of each query block.
+  int FA_LDS* tlist = (int FA_LDS*)(lds_raw + 2 * kNS * TILE);
+  unsigned long long FA_LDS* cmask = (unsigned long long FA_LDS*)(tlist + kListMax + 8);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -233,6 +248,73 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     }
     const int t_begin = key_lo / BC;
     const int T = (key_hi + BC - 1) / BC - t_begin;   // key tiles the workgroup visits (>= 1)
+    // BLK: the selected tiles among those T, listed in LDS; TT tiles run through the pipeline
+    int TT = T;
+    if constexpr (BLK) {
+      const unsigned char* bm = a.blocks + (long)(bh % a.heads) * a.n_qb * a.n_kb;
+      const int qb0 = q0 >> 6;
+      const bool two = qb0 + 1 < a.n_qb;
+      const int nch = (T + 63) >> 6;                  // chunks of 64 tiles (at most 16)
+      // per chunk (wave w takes chunks w, w + 4, ...): which tiles each query block selects
+      for (int ch = wave; ch < nch; ch += kWaves) {
+        const int r = 64 * ch + lane;
+        bool s0 = false, s1 = false;
+        if (r < T) {
+          const int kb = ((t_begin + r) * BC) >> 6;
+          s0 = bm[(long)qb0 * a.n_kb + kb] != 0;
+          s1 = two && bm[(long)(qb0 + 1) * a.n_kb + kb] != 0;
+        }
+        const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
+        if (lane == 0) {
+          cmask[2 * ch] = b0;
+          cmask[2 * ch + 1] = b1;
+        }
+      }
+      wg_barrier();
+      // entries of a chunk start after those of the chunks before it
+      int total = 0;
+      for (int ch = 0; ch < nch; ++ch) {
+        const unsigned long long b0 = cmask[2 * ch], b1 = cmask[2 * ch + 1], sel = b0 | b1;
+        if ((ch & (kWaves - 1)) == wave && ((sel >> lane) & 1ull)) {
+          const int pos = total + __builtin_popcountll(sel & ((1ull << lane) - 1ull));
+          tlist[pos] = (64 * ch + lane) | (int)((b0 >> lane) & 1ull) << 16 | (int)((b1 >> lane) & 1ull) << 17;
+        }
+        total += __builtin_popcountll(sel);
+      }
+      // past the last entry: sentinels (a tile index past T: zero-fill copies), and the count
+      if (wave == 0) {
+        if (lane < kPD + 2) tlist[total + lane] = 0xffff;
+        if (lane == 0) tlist[kListMax + 7] = total;
+      }
+      wg_barrier();
+      TT = tlist[kListMax + 7];
+      if (TT == 0) {   // no selected tile: O = 0, LSE = -inf
+        if (qi < n) {
+          char* orow = a.o + head + (long)qi * RB;
+#pragma unroll
+          for (int c16 = 0; c16 < RB / 32; ++c16)
+            *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
+          if (a.lse != nullptr && hi == 0) a.lse[lrow + qi] = NEG_INF;
+        }
+        continue;
+      }
+    }
+    // pipeline step k -> the tile it runs (BLK: list entry; else the index itself) and its
+    // index after t_begin
+    auto ent = [&](int k) __attribute__((always_inline)) {
+      if constexpr (BLK) return __builtin_amdgcn_readfirstlane(tlist[k]);
+      else return k;
+    };
+    auto rel = [&](int e) __attribute__((always_inline)) { return BLK ? (e & 0xffff) : e; };
+    // BLK: the entries of steps i + 1 .. i + 3 of iteration i (scalars, shifted along), and the
+    // one of step i + kPD + 1, read from LDS one iteration ahead
+    int h1 = 0, h2 = 0, h3 = 0, pre = 0;
+    if constexpr (BLK) {
+      h1 = ent(1);
+      h2 = ent(2);
+      h3 = ent(3);
+      pre = tlist[4];
+    }
     // visible key interval of this lane's query (edge tiles), from its key position; a query
     // that sees no key gets an interval past every key
     const int qpos = qi + off;
@@ -241,8 +323,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     if (row_hi < row_lo) row_lo = row_hi = nkr + 2 * BC;
 
     // ring stage of a tile is its index mod kNS; ST is that stage where the caller knows it
-    auto issue_copies = [&](int tk, int tv, int st_k, int st_v) __attribute__((always_inline)) {
+    // (ek, ev: the entries of the K and V tiles, see ent)
+    auto issue_copies = [&](int ek, int ev, int st_k, int st_v) __attribute__((always_inline)) {
       // tiles past the last one read beyond the buffer: zero fills, no memory traffic
+      const int tk = rel(ek), tv = rel(ev);
       const int ok = tk < T ? (t_begin + tk) * TILE : head_bytes;
       const int ov = tv < T ? (t_begin + tv) * TILE : head_bytes;
 #pragma unroll
@@ -342,13 +426,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     const int d_lo = mk.causal ? 0 : mk.wr >= 0 ? -mk.wr : 0;   // q - key >= d_lo (has_lo)
     const bool band32 = (!has_lo || (d_lo & 31) == 0) && (!has_hi || (mk.wl & 31) == 0) &&
                         (off & 31) == 0;
-    auto mask = [&](auto xb, int t) __attribute__((always_inline)) {
+    // (hide: every score of the tile -> -inf)
+    auto mask = [&](auto xb, int t, bool hide) __attribute__((always_inline)) {
       constexpr int X = decltype(xb)::value;
-      if (band32 && (t_begin + t + 1) * BC <= nkr) {
+      if (hide || (band32 && (t_begin + t + 1) * BC <= nkr)) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int x = wp0 - ((t_begin + t) * BC + 32 * mb);   // wave-uniform
-          const int lo = has_lo ? d_lo - x : -32, up = has_hi ? mk.wl - x : 32;
+          const int lo = hide ? 32 : has_lo ? d_lo - x : -32, up = has_hi ? mk.wl - x : 32;
           if (lo >= 32 || up <= -32) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sb[X][mb][r] = NEG_INF;
@@ -631,8 +716,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     auto issue_reads_now = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto mask_if_edge = [&](auto xb, int t) __attribute__((always_inline)) {
-      if (edge(t)) mask(xb, t);
+    // (e: the entry of the tile; BLK: a tile this wave's query block does not select is hidden)
+    auto mask_if_edge = [&](auto xb, int e) __attribute__((always_inline)) {
+      const bool hide = BLK && ((e >> (16 + (stripe >> 1))) & 1) == 0;
+      if (hide || edge(rel(e))) mask(xb, rel(e), hide);
     };
 
     // Iteration i, ring stage U = i mod kNS; buffer (i+1) mod 2 receives S_{i+1}, buffer i mod 2
@@ -648,12 +735,23 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       constexpr int U = decltype(uc)::value;
       using XB = std::integral_constant<int, (U + 1) & 1>;
       using YB = std::integral_constant<int, U & 1>;
-      issue_copies(i + kPD + 1, i + kPD, U, (U + kNS - 1) % kNS);
+      static_assert(kPD == 3, "entries of steps i + 1 .. i + 3 carried, i + 4 read ahead");
+      int e1 = i + 1, ek = i + kPD + 1, ev = i + kPD;
+      if constexpr (BLK) {
+        e1 = h1;
+        ev = h3;
+        ek = __builtin_amdgcn_readfirstlane(pre);
+        pre = tlist[i + kPD + 2];         // the oldest LDS operation of the step
+        h1 = h2;
+        h2 = h3;
+        h3 = ek;
+      }
+      issue_copies(ek, ev, U, (U + kNS - 1) % kNS);
       issue_reads_now();
       compute_a(XB{}, YB{}, std::integral_constant<int, U>{});   // GEMM0_{i+1} + ALU1_i, V_i reads
       wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();             // V_i operands have landed (GEMM1_i stays below)
-      mask_if_edge(XB{}, i + 1);
+      mask_if_edge(XB{}, e1);
       if constexpr (ALIBI) alibi_fix(XB{}, i + 1);
       compute_b(XB{}, std::integral_constant<int, (U + 2) % kNS>{}, i + 1);   // GEMM1_i + ALU0_{i+1}, K_{i+2} reads
       rescale();
@@ -664,10 +762,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // first iteration (i = -1): only S_0 and its row statistics
     auto iteration_first = [&]() __attribute__((always_inline)) {
       using X = std::integral_constant<int, 0>;
-      issue_copies(kPD, kPD - 1, kPD % kNS, (kPD - 1) % kNS);
+      const int e0 = ent(0);
+      issue_copies(ent(kPD), ent(kPD - 1), kPD % kNS, (kPD - 1) % kNS);
       static_for<MB * KS>([&](auto ec) __attribute__((always_inline)) { qk(X{}, ec); });
       wait_vmcnt<2 * CPT * (kPD - 2)>();
-      if (edge(0)) mask(X{}, 0);
+      mask_if_edge(X{}, e0);
       read_k(std::integral_constant<int, 1>{});
       issue_reads_now();
       alu0(X{});
@@ -680,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       constexpr int U = decltype(uc)::value;
       using YB = std::integral_constant<int, U & 1>;
       // beyond the sequence: zero fills, uniform vmcnt
-      issue_copies(T + kPD, T + kPD - 1, U, (U + kNS - 1) % kNS);
+      issue_copies(BLK ? 0xffff : T + kPD, BLK ? 0xffff : T + kPD - 1, U, (U + kNS - 1) % kNS);
       read_v(std::integral_constant<int, U>{});
       issue_reads_now();
       alu1(YB{});
@@ -692,13 +791,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 
     // ---- prologue: copies of K_0..K_{kPD-1} and V_0..V_{kPD-2}, all waited for
 #pragma unroll
-    for (int t = 0; t < kPD - 1; ++t) issue_copies(t, t, t % kNS, t % kNS);
+    for (int t = 0; t < kPD - 1; ++t) {
+      const int e = ent(t);
+      issue_copies(e, e, t % kNS, t % kNS);
+    }
     {
-      const int tk = kPD - 1;
+      const int tk = rel(ent(kPD - 1));
       const int ok = tk < T ? (t_begin + tk) * TILE : head_bytes;
 #pragma unroll
       for (int j = 0; j < CPT; ++j)
-        buffer_load16_lds(rk, kring + (tk % kNS) * TILE + 16 * kThreads * j + 1024 * wave, cp_src + 16 * kThreads * j + ok);
+        buffer_load16_lds(rk, kring + ((kPD - 1) % kNS) * TILE + 16 * kThreads * j + 1024 * wave,
+                          cp_src + 16 * kThreads * j + ok);
     }
     wait_vmcnt<0>();
     wg_barrier();
@@ -712,13 +815,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     static_assert(kNS == 4, "the loop is unrolled over four ring stages");
     iteration_first();
     int i = 0;
-    for (; i + kNS <= T - 1; i += kNS) {
+    for (; i + kNS <= TT - 1; i += kNS) {
       iteration(U0{}, i);
       iteration(U1{}, i + 1);
       iteration(U2{}, i + 2);
       iteration(U3{}, i + 3);
     }
-    const int rem = T - 1 - i;         // 0 .. kNS-1 iterations left, then the last
+    const int rem = TT - 1 - i;        // 0 .. kNS-1 iterations left, then the last
     if (rem > 0) iteration(U0{}, i);
     if (rem > 1) iteration(U1{}, i + 1);
     if (rem > 2) iteration(U2{}, i + 2);
@@ -765,7 +868,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 // slopes: ALiBi slopes [H] (device) or null
 template <int D, bool BF16>
 hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
-                  const float* slopes = nullptr) {
+                  const float* slopes = nullptr, const unsigned char* blocks = nullptr) {
   MainArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -797,15 +900,21 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
   a.slopes = slopes;
-  const long blocks = (long)a.n_bh * a.n_units;
-  if (slopes != nullptr)   // (no padded batch takes ALiBi)
-    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks),
+  a.blocks = blocks;
+  a.n_qb = (nq + 63) / 64;
+  a.n_kb = (nk + 63) / 64;
+  const long wgs = (long)a.n_bh * a.n_units;
+  if (slopes != nullptr)   // (no padded batch takes ALiBi or a block mask)
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, true>), dim3((unsigned)wgs),
+                       dim3(kThreads), 0, stream, a);
+  else if (blocks != nullptr)
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, false, true>), dim3((unsigned)wgs),
                        dim3(kThreads), 0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
-    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)wgs), dim3(kThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(kThreads),
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false>), dim3((unsigned)wgs), dim3(kThreads),
                        0, stream, a);
   return hipGetLastError();
 }
@@ -815,6 +924,11 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
 hipError_t launch_fwd_main(const FwdParams& p, hipStream_t stream) {
   if (p.D == 64) return p.bf16 ? launch<64, true>(p, p.N, p.N, stream) : launch<64, false>(p, p.N, p.N, stream);
   return p.bf16 ? launch<128, true>(p, p.N, p.N, stream) : launch<128, false>(p, p.N, p.N, stream);
+}
+
+bool fwd_main_takes_blocks(int D, int nk) {
+  const int bc = D == 64 ? Shape<64>::BC : Shape<128>::BC;
+  return (nk + bc - 1) / bc <= kListMax;
 }
 
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
@@ -835,11 +949,13 @@ hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
   f.causal = p.causal;
   f.window_left = p.window_left;
   f.window_right = p.window_right;
+  if (p.blocks != nullptr && !fwd_main_takes_blocks(p.D, p.Nk))
+    return hipErrorInvalidValue;   // more key tiles than a tile list holds
   if (p.D == 64)
-    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream, p.slopes)
-                  : launch<64, false>(f, p.Nq, p.Nk, stream, p.slopes);
-  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream, p.slopes)
-                : launch<128, false>(f, p.Nq, p.Nk, stream, p.slopes);
+    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks)
+                  : launch<64, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks);
+  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks)
+                : launch<128, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks);
 }
 
 }  // namespace fa

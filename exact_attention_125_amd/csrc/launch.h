@@ -126,8 +126,10 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8 = fal
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward kernel (fwd_main.hip) for N_q queries over N_k keys, dense operands, with
-// ALiBi slopes or none, and no dropout, block mask or key padding mask.
+// ALiBi slopes or a block mask (not both) or neither, and no dropout or key padding mask.
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream);
+// whether the main forward kernel takes a block-sparse mask over nk keys (its tile list holds them)
+bool fwd_main_takes_blocks(int D, int nk);
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
 hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward (128 query rows per workgroup, direct global->LDS copies, two-phase
