@@ -45,6 +45,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "block_list.h"
 #include "cdna4.h"
 #include "launch.h"
 
@@ -81,6 +82,8 @@ struct DkdvArgs {
   int causal, wl, wr;
   int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
+  const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
+  int n_qb, n_kb;
 };
 
 template <int D>
@@ -117,8 +120,13 @@ __device__ __forceinline__ void slices(F&& f) {
 // causal mask): P carries the forward's ALiBi penalty -slope log2(e) (p - j), p = i + nk - nr the
 // query's position, linear in the query index: 2^(c S + La - b2 R), R = 8 (r / 4) + r % 4 of
 // accumulator row r, La = -b2 (q0 + 4 hi + nk - nr - j) per key block and step.
-template <int D, bool BF16, bool PADDED, bool ALIBI = false>
-__device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int bh, int kt) {
+// BLK: a block-sparse mask.  The workgroup's 64-key blocks (KWG / 64 of them) select query
+// steps; it visits only the steps one of them selects (a list in LDS at `list`, block_list.h),
+// and a wave whose block does not select a visited step sees all of its pairs hidden.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+__device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int FA_LDS* list,
+                                          int bh, int kt) {
+  static_assert(!(ALIBI && BLK), "no instance takes both");
   using S = DShape<D>;
   constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
@@ -199,6 +207,28 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   const int q_hi = min(n, k_last + a.dhi + 1);
   const int s_begin = q_lo / kBQ;
   const int NSTEP = (!PADDED || k_first < n) && q_hi > q_lo ? (q_hi + kBQ - 1) / kBQ - s_begin : 0;
+  // BLK: the visited steps, TS of them (entry k: step rel(k) after s_begin and its selections);
+  // the entries of steps s + 1 .. s + kPD - 1 are carried in scalars (h1 .. h4), those of later
+  // steps read from a window of 64 entries held one per lane
+  constexpr int NBW = S::KWG / 64;   // 64-key blocks of the workgroup
+  static_assert(S::KWG % 64 == 0, "whole key blocks per workgroup");
+  const int own = (S::KW * wave) >> 6;   // this wave's block among them
+  int TS = NSTEP;
+  int win = 0, h0 = 0, h1 = 1, h2 = 2, h3 = 3, h4 = 4;
+  if constexpr (BLK) {
+    if (NSTEP > 0)
+      TS = build_block_list<NBW, kBQ, kPD, 4>(list, a.blocks + (long)(bh % a.heads) * a.n_qb * a.n_kb, 1,
+                                              a.n_kb, k_first >> 6, a.n_kb, s_begin, NSTEP, lane, wave);
+    else   // (the prologue's copies read the sentinels)
+      TS = build_block_list<NBW, kBQ, kPD, 4>(list, a.blocks, 0, 0, 0, 0, 0, 0, lane, wave);
+    win = list[lane];
+    h0 = __builtin_amdgcn_readlane(win, 0);
+    h1 = __builtin_amdgcn_readlane(win, 1);
+    h2 = __builtin_amdgcn_readlane(win, 2);
+    h3 = __builtin_amdgcn_readlane(win, 3);
+    h4 = __builtin_amdgcn_readlane(win, 4);
+  }
+  auto rel = [&](int e) __attribute__((always_inline)) { return BLK ? entry_step(e) : e; };
 
   // ---- per-lane constants
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
@@ -257,11 +287,12 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   const int st_src = lane < 16 ? 128 * (lane >> 3) + 16 * (jl < 4 ? 2 * jl : 2 * (jl - 4) + 1)
                                : stat_bytes;
 
-  // ---- copies of query tile t (relative step) into stage t mod kNS: Q and dO (every wave its
-  // share), and the statistics block; past the last step they read beyond the buffers (zero
-  // fills, no traffic) so every step issues the same copies
-  auto copy_tiles = [&](int t) __attribute__((always_inline)) {
-    const int off = t < NSTEP ? (s_begin + t) * kBQ * RB : head_bytes;
+  // ---- copies of pipeline step t (the query tile of entry e, BLK; else tile t) into stage
+  // t mod kNS: Q and dO (every wave its share), and the statistics block; past the last tile
+  // they read beyond the buffers (zero fills, no traffic) so every step issues the same copies
+  auto copy_tiles = [&](int t, int e) __attribute__((always_inline)) {
+    const int qt = rel(e);
+    const int off = qt < NSTEP ? (s_begin + qt) * kBQ * RB : head_bytes;
     char FA_LDS* st = ring + (t & (kNS - 1)) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -269,13 +300,14 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
       buffer_load16_lds(rg, st + QTILE + 4096 * i + 1024 * wave, cp_src[i] + off);
     }
   };
-  auto copy_stats = [&](int t) __attribute__((always_inline)) {
-    const int off = t < NSTEP ? (s_begin + t) * 2 * kStatRows * 4 : stat_bytes;
+  auto copy_stats = [&](int t, int e) __attribute__((always_inline)) {
+    const int qt = rel(e);
+    const int off = qt < NSTEP ? (s_begin + qt) * 2 * kStatRows * 4 : stat_bytes;
     buffer_load16_lds(rs, ring + (t & (kNS - 1)) * STAGE + 2 * QTILE, st_src + off);
   };
-  auto issue_copies = [&](int t) __attribute__((always_inline)) {
-    copy_stats(t);
-    copy_tiles(t);
+  auto issue_copies = [&](int t, int e) __attribute__((always_inline)) {
+    copy_stats(t, e);
+    copy_tiles(t, e);
   };
   // this wave's copies of tiles up to s+3 have landed (loads complete in order), leaving
   // those of tiles s+4 .. s+kPD in flight (2 CPT tile chunks and one statistics copy each)
@@ -403,14 +435,15 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // wholly hidden or cut along its diagonal: q - key = x - 32 kb + (row - column) with x =
   // q0 - kw0 a multiple of 32 and row - column in [-31, 31].  Those blocks take constant lane
   // masks instead of compares.
-  auto mask_step = [&](int t) __attribute__((always_inline)) {
+  // (hide: every pair of the step hidden)
+  auto mask_step = [&](int t, bool hide) __attribute__((always_inline)) {
     keep_branch();   // not worth running on every step
     const int q0 = (s_begin + t) * kBQ;
     const int x = q0 - kw0;   // wave-uniform
-    if ((a.dlo & 31) == 0 && a.dhi - x >= 31) {
+    if (hide || ((a.dlo & 31) == 0 && a.dhi - x >= 31)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int lo = a.dlo - x + 32 * kb;   // visible iff row - column >= lo
+        const int lo = hide ? 32 : a.dlo - x + 32 * kb;   // visible iff row - column >= lo
         if (lo >= 32) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) pv[kb][i] = 0.f;
@@ -484,7 +517,8 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   //
   // phase 1 of step s: dV_s, S_{s+1} | dS_s; reads Q_s^T, dO_{s+1} rows, -delta_{s+1}; copies
   // of tile s + kPD
-  auto phase1 = [&](int s) __attribute__((always_inline)) {
+  // (ek: the entry of step s + kPD, whose tiles it copies)
+  auto phase1 = [&](int s, int ek) __attribute__((always_inline)) {
     wait_lgkmcnt_fence<KS + 4>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
@@ -496,7 +530,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
         read_one(std::integral_constant<int, m * NR / (NG + NM) + decltype(jc)::value>{}, Z{}, QT{}, O{},
                  qt_lo, qt_hi, ga, ndv);
       });
-      if constexpr (m == 1) copy_tiles(s + kPD);
+      if constexpr (m == 1) copy_tiles(s + kPD, ek);
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_phase1();
@@ -522,7 +556,12 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   };
 
   // ---- prologue: tiles 0..kPD-1, then S_0, dP_0, P_0 and the operands of step 0's phase 1
-  for (int t = 0; t < kPD; ++t) issue_copies(t);
+  static_assert(kPD == 5, "entries of steps 0 .. 4 in h0 .. h4");
+  issue_copies(0, h0);
+  issue_copies(1, h1);
+  issue_copies(2, h2);
+  issue_copies(3, h3);
+  issue_copies(4, h4);
   // K^T, V^T and the accumulators into the AGPRs only now, so that waiting for the K and V rows
   // does not hold back the copies; the wait states after separate those writes from the first
   // product
@@ -543,7 +582,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   mfma_operand_wait();
   wait_vmcnt<0>();
   wg_barrier();
-  if (NSTEP > 0) {
+  if (TS > 0) {
     read_rows(Z{}, Z{}, qa, mv);
     read_rows(QT{}, O{}, ga, ndv);
     wait_lgkmcnt0_fence();
@@ -563,7 +602,8 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
     }
     alibi_step(s_begin * kBQ);
     slices<0, NSL>(p_slice);
-    if (edge_step(0)) mask_step(0);
+    const bool hide = BLK && !entry_selected(h0, own);
+    if (hide || edge_step(rel(h0))) mask_step(rel(h0), hide);
     pin_phase2();
   }
   read_tr(QT{}, gt_lo, gt_hi);       // dO_0^T
@@ -573,15 +613,26 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
   // from here: tr_a at tile s, row_a / st_a at tile s+1 when step s begins
 
   // ---- steps: one barrier each
-  for (int s = 0; s < NSTEP; ++s) {
-    copy_stats(s + kPD);             // before the phase: its branch stays out of the MFMA sequence
-    phase1(s);
+  for (int s = 0; s < TS; ++s) {
+    int ek = s + kPD, e1 = s + 1;
+    if constexpr (BLK) {
+      if (((s + kPD) & 63) == 0) win = list[s + kPD + lane];   // the next window (rare)
+      ek = __builtin_amdgcn_readlane(win, (s + kPD) & 63);
+      e1 = h1;
+      h1 = h2;
+      h2 = h3;
+      h3 = h4;
+      h4 = ek;
+    }
+    copy_stats(s + kPD, ek);         // before the phase: its branch stays out of the MFMA sequence
+    phase1(s, ek);
     advance_tr(s);                   // tile s   -> s+1
     advance_rows(s + 1);             // tile s+1 -> s+2
     alibi_step((s_begin + s + 1) * kBQ);
     phase2();
-    if (s + 1 < NSTEP && edge_step(s + 1)) {
-      mask_step(s + 1);
+    const bool hide = BLK && !entry_selected(e1, own);
+    if (s + 1 < TS && (hide || edge_step(rel(e1)))) {
+      mask_step(rel(e1), hide);
       pin_phase2();
     }
     wait_copies();
@@ -628,16 +679,18 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 // tile, so tiles t and n_tiles - 1 - t together take the same time for every t: paired, the
 // workgroups are of equal length and fill the chip evenly.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED, bool ALIBI = false>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
 __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * DShape<D>::STAGE];
+  constexpr int kRing = kNS * DShape<D>::STAGE;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kRing + (BLK ? block_list_bytes<DShape<D>::KWG / 64>() : 0)];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
+  int FA_LDS* list = (int FA_LDS*)(lds_raw + kRing);
   int bh, t;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, t);
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dkdv_tile<D, BF16, PADDED, ALIBI>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dkdv_tile<D, BF16, PADDED, ALIBI, BLK>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -678,10 +731,16 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.paired = p.causal && p.window_left < 0 && (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   a.slopes = p.slopes;
+  a.blocks = p.blocks;
+  a.n_qb = (nq + 63) / 64;
+  a.n_kb = (nk + 63) / 64;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.slopes != nullptr)   // (no padded batch takes ALiBi)
+  if (p.slopes != nullptr)   // (no padded batch takes ALiBi or a block mask)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, a);
+  else if (p.blocks != nullptr)
+    hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false, false, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else

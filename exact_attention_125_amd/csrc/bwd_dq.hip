@@ -37,6 +37,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "block_list.h"
 #include "cdna4.h"
 #include "launch.h"
 
@@ -72,6 +73,8 @@ struct DqArgs {
   int causal, wl, wr;
   int dlo, dhi;          // key j visible to query i iff dlo <= i - j <= dhi (within the sequence)
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
+  const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
+  int n_qb, n_kb;
 };
 
 template <int D>
@@ -102,8 +105,13 @@ __device__ __forceinline__ void dq_slices(F&& f) {
 // carries the forward's ALiBi penalty -slope log2(e) (p - j), p = q + off the query's position,
 // linear in the key index: 2^(c S + Lq + b2 R), R = 8 (r / 4) + r % 4 of accumulator row r,
 // Lq = c m - b2 (p - k0 - 4 hi) per query block and step (keys k0 ..).
-template <int D, bool BF16, bool PADDED, bool ALIBI = false>
-__device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int bh, int qt) {
+// BLK: a block-sparse mask.  The workgroup's two 64-query blocks select key steps; it visits
+// only the steps one of them selects (a list in LDS at `list`, block_list.h), and a wave whose
+// block does not select a visited step sees all of its pairs hidden.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+__device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int FA_LDS* list, int bh,
+                                        int qt) {
+  static_assert(!(ALIBI && BLK), "no instance takes both");
   using S = QShape<D>;
   constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
@@ -178,6 +186,24 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   mk.key_range(q_first + off, min(q_first + S::QWG, n) - 1 + off, k_lo, k_hi);
   const int s_begin = k_lo / kBK;
   const int NSTEP = (!PADDED || q_first < n) && k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
+  // BLK: the visited steps, TS of them (entry k: step rel(k) after s_begin and its selections);
+  // the entries of steps s .. s + kPD - 1 are carried in scalars (h0 .. h3), those of later
+  // steps read from a window of 64 entries held one per lane
+  int TS = NSTEP;
+  int win = 0, h0 = 0, h1 = 1, h2 = 2, h3 = 3;
+  if constexpr (BLK) {
+    if (NSTEP > 0)
+      TS = build_block_list<2, kBK, kPD, 4>(list, a.blocks + (long)(bh % a.heads) * a.n_qb * a.n_kb,
+                                            a.n_kb, 1, q_first >> 6, a.n_qb, s_begin, NSTEP, lane, wave);
+    else   // (the prologue's copies read the sentinels)
+      TS = build_block_list<2, kBK, kPD, 4>(list, a.blocks, 0, 0, 0, 0, 0, 0, lane, wave);
+    win = list[lane];
+    h0 = __builtin_amdgcn_readlane(win, 0);
+    h1 = __builtin_amdgcn_readlane(win, 1);
+    h2 = __builtin_amdgcn_readlane(win, 2);
+    h3 = __builtin_amdgcn_readlane(win, 3);
+  }
+  auto rel = [&](int e) __attribute__((always_inline)) { return BLK ? entry_step(e) : e; };
 
   // ---- per-lane LDS addresses, moved on by one ring stage per step:
   //   row_a[ks]   A operand rows (key l32, chunk 2 ks + hi) in the stage of tile s+1 (K at
@@ -206,10 +232,12 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
     cp_src[i] = r * RB + ((((p % RB) / 16) ^ chunk_swizzle<D>(r))) * 16;
   }
 
-  // ---- copies of key tile t (relative step) into stage t % kNS; past the last step they
-  // read beyond the buffers (zero fills, no traffic) so every step issues the same copies
-  auto issue_copies = [&](int t) __attribute__((always_inline)) {
-    const int off = t < NSTEP ? (s_begin + t) * kBK * RB : head_bytes;
+  // ---- copies of pipeline step t (the key tile of entry e, BLK; else tile t) into stage
+  // t % kNS; past the last tile they read beyond the buffers (zero fills, no traffic) so every
+  // step issues the same copies
+  auto issue_copies = [&](int t, int e) __attribute__((always_inline)) {
+    const int kt = rel(e);
+    const int off = kt < NSTEP ? (s_begin + kt) * kBK * RB : head_bytes;
     char FA_LDS* st = ring + (t % kNS) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -298,13 +326,14 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // Where only a lower band edge on a multiple of 32 crosses the step, every 32x32 block is
   // wholly visible, wholly hidden or cut along its diagonal: q - key = x + (column - row) with
   // x = qw0 + 32 qb - k0 a multiple of 32.  Those blocks take constant lane masks.
-  auto mask_step = [&](int t) __attribute__((always_inline)) {
+  // (hide: every pair of the step hidden)
+  auto mask_step = [&](int t, bool hide) __attribute__((always_inline)) {
     keep_branch();   // not worth running on every step
     const int k0 = (s_begin + t) * kBK;
-    if ((a.dlo & 31) == 0 && a.dhi - (qw0 + 32 * (QB - 1) - k0) >= 31) {
+    if (hide || ((a.dlo & 31) == 0 && a.dhi - (qw0 + 32 * (QB - 1) - k0) >= 31)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int lo = a.dlo - (qw0 + 32 * qb - k0);   // visible iff column - row >= lo
+        const int lo = hide ? 32 : a.dlo - (qw0 + 32 * qb - k0);   // visible iff column - row >= lo
         if (lo >= 32) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) pv[qb][i] = 0.f;
@@ -344,7 +373,8 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // phase 1 of step s: dQ_{s-1}, dP_s | P_s.  P slices start after the second MFMA: S_s was
   // the last product of the step before.  It starts once the K_{s-1}^T halves have landed
   // (the V_s rows may still be in flight) and runs dP_s once they have too.
-  auto phase1 = [&](int s) __attribute__((always_inline)) {
+  // (ek: the entry of step s + kPD, whose tiles it copies)
+  auto phase1 = [&](int s, int ek) __attribute__((always_inline)) {
     wait_lgkmcnt_fence<KS>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
@@ -359,7 +389,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
           read_one(std::integral_constant<int, h * NR1 / NM + decltype(jc)::value>{});
         });
       }
-      if constexpr (m == 1) copy_tiles(s + kPD);
+      if constexpr (m == 1) copy_tiles(s + kPD, ek);
       __builtin_amdgcn_sched_barrier(0);
     });
     pin_p();
@@ -387,7 +417,11 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 
   // ---- prologue: tiles 0..kPD-1, S_0 and the V_0 rows; dQ_{-1} adds zeros (zero dS and
   // K^T operands)
-  for (int t = 0; t < kPD; ++t) issue_copies(t);
+  static_assert(kPD == 4, "entries of steps 0 .. 3 in h0 .. h3");
+  issue_copies(0, h0);
+  issue_copies(1, h1);
+  issue_copies(2, h2);
+  issue_copies(3, h3);
   // Q^T, dO^T, dQ^T and the statistics are used only now: waiting for the Q and dO rows does
   // not hold back the copies, whose latency overlaps theirs
 #pragma unroll
@@ -424,7 +458,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   read_rows(row_a, Z{}, ka);           // K_0
   read_rows(row_a, KT{}, va);          // V_0
   wait_lgkmcnt0_fence();
-  if (NSTEP > 0) static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
+  if (TS > 0) static_for<NM>([&](auto mc) __attribute__((always_inline)) { mfma_s(mc); });
   pin_ds();
   mfma_result_wait();   // S_0 is read by VALU in step 0
 #pragma unroll
@@ -433,14 +467,25 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   for (int ks = 0; ks < KS; ++ks) row_a[ks] += stage_step(0);   // rows: tile 1
 
   // ---- steps: one barrier each
-  for (int s = 0; s < NSTEP; ++s) {
+  for (int s = 0; s < TS; ++s) {
     if constexpr (ALIBI) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) lq[qb] = __builtin_fmaf(b2, (float)((s_begin + s) * kBK), lq0[qb]);
     }
-    phase1(s);
-    if (edge_step(s)) {
-      mask_step(s);
+    int ek = s + kPD, es = s;
+    if constexpr (BLK) {
+      if (((s + kPD) & 63) == 0) win = list[s + kPD + lane];   // the next window (rare)
+      ek = __builtin_amdgcn_readlane(win, (s + kPD) & 63);
+      es = h0;
+      h0 = h1;
+      h1 = h2;
+      h2 = h3;
+      h3 = ek;
+    }
+    phase1(s, ek);
+    const bool hide = BLK && !entry_selected(es, wave >> 1);
+    if (hide || edge_step(rel(es))) {
+      mask_step(rel(es), hide);
       pin_p();
     }
     phase2();
@@ -459,7 +504,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   }
   wait_lgkmcnt0_fence();
   // dQ of the last step
-  if (NSTEP > 0) {
+  if (TS > 0) {
     static_for<NG>([&](auto mc) __attribute__((always_inline)) {
       mfma_dq(mc);
       __builtin_amdgcn_sched_barrier(0);
@@ -497,17 +542,18 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 // tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
 // latest (longest) tiles go first.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED, bool ALIBI = false>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE + (BLK ? block_list_bytes<2>() : 0)];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
+  int FA_LDS* list = (int FA_LDS*)(lds_raw + kNS * QShape<D>::STAGE);
   int bh, t;
   xcd_tile_order(blockIdx.x, a.n_bh, a.n_units, bh, t);
   t = a.n_tiles - 1 - t;
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dq_tile<D, BF16, PADDED, ALIBI>(a, ring, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dq_tile<D, BF16, PADDED, ALIBI, BLK>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -550,10 +596,16 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
              (long)a.n_bh * half >= 256;
   a.n_units = a.paired ? half : a.n_tiles;
   a.slopes = p.slopes;
+  a.blocks = p.blocks;
+  a.n_qb = (nq + 63) / 64;
+  a.n_kb = (nk + 63) / 64;
   const long blocks = (long)a.n_bh * a.n_units;
-  if (p.slopes != nullptr)   // (no padded batch takes ALiBi)
+  if (p.slopes != nullptr)   // (no padded batch takes ALiBi or a block mask)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, false, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, a);
+  else if (p.blocks != nullptr)
+    hipLaunchKernelGGL((dq_main_kernel<D, BF16, false, false, true>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else

@@ -53,6 +53,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "block_list.h"
 #include "cdna4.h"
 #include "launch.h"
 
@@ -93,9 +94,6 @@ struct MainArgs {
   int n_qb, n_kb;
 };
 
-// BLK: the list of a query tile's selected key tiles, at most kListMax entries
-constexpr int kListMax = 1024;
-
 template <int D>
 struct Shape {
   static constexpr int BC = D == 64 ? 64 : 32;   // keys per tile
@@ -128,15 +126,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
   constexpr int TILE = S::TILE, CPT = S::CPT;
 
   static_assert(!(ALIBI && BLK), "no instance takes both");
-  constexpr int kListBytes = BLK ? 4 * (kListMax + 8) + 8 * 2 * (kListMax / 64) : 0;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE + kListBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE + (BLK ? block_list_bytes<2>() : 0)];
   char FA_LDS* kring = (char FA_LDS*)lds_raw;
   char FA_LDS* vring = kring + kNS * TILE;
-  // BLK: entries r | s0 << 16 | s1 << 17 (r the tile index after t_begin, s0 / s1 whether the
-  // first / second query block selects it), then kPD + 2 sentinels; the count in the last slot.
-  // After the list, per chunk of 64 tiles, the selection bits of each query block.
+  // BLK: the key tiles the query tile's two 64-query blocks select (block_list.h)
   int FA_LDS* tlist = (int FA_LDS*)(lds_raw + 2 * kNS * TILE);
-  unsigned long long FA_LDS* cmask = (unsigned long long FA_LDS*)(tlist + kListMax + 8);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,43 +245,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     // BLK: the selected tiles among those T, listed in LDS; TT tiles run through the pipeline
     int TT = T;
     if constexpr (BLK) {
-      const unsigned char* bm = a.blocks + (long)(bh % a.heads) * a.n_qb * a.n_kb;
-      const int qb0 = q0 >> 6;
-      const bool two = qb0 + 1 < a.n_qb;
-      const int nch = (T + 63) >> 6;                  // chunks of 64 tiles (at most 16)
-      // per chunk (wave w takes chunks w, w + 4, ...): which tiles each query block selects
-      for (int ch = wave; ch < nch; ch += kWaves) {
-        const int r = 64 * ch + lane;
-        bool s0 = false, s1 = false;
-        if (r < T) {
-          const int kb = ((t_begin + r) * BC) >> 6;
-          s0 = bm[(long)qb0 * a.n_kb + kb] != 0;
-          s1 = two && bm[(long)(qb0 + 1) * a.n_kb + kb] != 0;
-        }
-        const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
-        if (lane == 0) {
-          cmask[2 * ch] = b0;
-          cmask[2 * ch + 1] = b1;
-        }
-      }
-      wg_barrier();
-      // entries of a chunk start after those of the chunks before it
-      int total = 0;
-      for (int ch = 0; ch < nch; ++ch) {
-        const unsigned long long b0 = cmask[2 * ch], b1 = cmask[2 * ch + 1], sel = b0 | b1;
-        if ((ch & (kWaves - 1)) == wave && ((sel >> lane) & 1ull)) {
-          const int pos = total + __builtin_popcountll(sel & ((1ull << lane) - 1ull));
-          tlist[pos] = (64 * ch + lane) | (int)((b0 >> lane) & 1ull) << 16 | (int)((b1 >> lane) & 1ull) << 17;
-        }
-        total += __builtin_popcountll(sel);
-      }
-      // past the last entry: sentinels (a tile index past T: zero-fill copies), and the count
-      if (wave == 0) {
-        if (lane < kPD + 2) tlist[total + lane] = 0xffff;
-        if (lane == 0) tlist[kListMax + 7] = total;
-      }
-      wg_barrier();
-      TT = tlist[kListMax + 7];
+      TT = build_block_list<2, BC, kPD + 2, kWaves>(tlist, a.blocks + (long)(bh % a.heads) * a.n_qb * a.n_kb,
+                                                    a.n_kb, 1, q0 >> 6, a.n_qb, t_begin, T, lane, wave);
       if (TT == 0) {   // no selected tile: O = 0, LSE = -inf
         if (qi < n) {
           char* orow = a.o + head + (long)qi * RB;
@@ -305,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       if constexpr (BLK) return __builtin_amdgcn_readfirstlane(tlist[k]);
       else return k;
     };
-    auto rel = [&](int e) __attribute__((always_inline)) { return BLK ? (e & 0xffff) : e; };
+    auto rel = [&](int e) __attribute__((always_inline)) { return BLK ? entry_step(e) : e; };
     // BLK: the entries of steps i + 1 .. i + 3 of iteration i (scalars, shifted along), and the
     // one of step i + kPD + 1, read from LDS one iteration ahead
     int h1 = 0, h2 = 0, h3 = 0, pre = 0;
@@ -718,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     };
     // (e: the entry of the tile; BLK: a tile this wave's query block does not select is hidden)
     auto mask_if_edge = [&](auto xb, int e) __attribute__((always_inline)) {
-      const bool hide = BLK && ((e >> (16 + (stripe >> 1))) & 1) == 0;
+      const bool hide = BLK && !entry_selected(e, stripe >> 1);
       if (hide || edge(rel(e))) mask(xb, rel(e), hide);
     };
 

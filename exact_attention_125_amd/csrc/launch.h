@@ -46,6 +46,8 @@ struct BwdParams {
   const float* slopes = nullptr;  // ALiBi slopes [H] (device), or null: the main dK/dV and dQ
                                   // kernels take them where no visible pair lies past the
                                   // diagonal (causal, or a right window of 0)
+  const unsigned char* blocks = nullptr;   // block-sparse mask [H][ceil(N_q/64)][ceil(N_k/64)]
+                                           // (device), or null; not with slopes
   int total = 0;
   int B, H, N, D;
   bool bf16;
@@ -130,6 +132,9 @@ hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stre
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream);
 // whether the main forward kernel takes a block-sparse mask over nk keys (its tile list holds them)
 bool fwd_main_takes_blocks(int D, int nk);
+// whether the main dK/dV and dQ kernels take a block-sparse mask over nq queries and nk keys
+// (their step lists hold them)
+inline bool bwd_main_takes_blocks(int nq, int nk) { return nq <= 32 * 1024 && nk <= 32 * 1024; }
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
 hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);
 // The main forward (128 query rows per workgroup, direct global->LDS copies, two-phase

@@ -516,10 +516,12 @@ def test_block_sparse_with_alibi_and_structure(fa):
 @pytest.mark.parametrize("n_q,n_k", [(256, 320), (256, 1000), (512, 512), (130, 4096), (300, 2065)])
 @pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
 def test_block_sparse_main_kernel(fa, causal, window, n_q, n_k, d, dtype):
-    """128 heads: query tiles enough for the main forward kernel, which visits only the key
-    tiles a query tile's blocks select.  Head 0 selects nothing (O = 0, LSE = -inf), head 1
-    everything, head 2 the block diagonal, head 3 one key block per query block, the rest
-    random at densities 0.5 and 0.2; sampled heads against the oracle."""
+    """128 heads: query tiles enough for the main forward kernel and the main dK/dV and dQ
+    kernels, which visit only the steps a workgroup's blocks select.  Head 0 selects nothing
+    (O = 0, LSE = -inf, zero gradients), head 1 everything, head 2 the block diagonal, head 3
+    one key block per query block, the rest random at densities 0.5 and 0.2; sampled heads
+    against the oracle (gradients by relative L2)."""
+    import oracle
     import torch
     B, H = 8, 16
     nqb, nkb = -(-n_q // 64), -(-n_k // 64)
@@ -531,22 +533,31 @@ def test_block_sparse_main_kernel(fa, causal, window, n_q, n_k, d, dtype):
     fixed[3][np.arange(nqb), (7 * np.arange(nqb)) % nkb] = True
     blocks = np.concatenate([fixed, blocks])
     inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed=n_q * 7 + n_k)
-    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    g = W.cross_case(B, H, n_q, 1, d, dtype, seed=n_q * 7 + n_k + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
     scale = 1.0 / math.sqrt(d)
     bm = torch.tensor(blocks.astype(np.uint8), device="cuda")
     o, lse = fa.fwd_kv(q, k, v, scale, causal, window, block_mask=bm)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window, block_mask=bm)
     torch.cuda.synchronize()
+    label = f"main blocks nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}"
     heads = [(b, (3 * b + 1) % H) for b in range(B)] + [(0, 0), (1, 1), (2, 2), (3, 3), (B - 1, H - 1)]
-    compare(o, lse, inp, scale, causal, window, dtype,
-            f"main blocks nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}", heads=heads,
-            block_mask=blocks)
+    compare(o, lse, inp, scale, causal, window, dtype, label, heads=heads, block_mask=blocks)
     assert torch.all(torch.isneginf(lse[:, 0])) and torch.all(o[:, 0] == 0)
+    assert all(torch.all(t[:, 0] == 0) for t in (dq, dk, dv)), f"{label}: head 0 gradients"
+    got = [to64(t) for t in (dq, dk, dv)]
+    for b, h in heads:
+        ref = oracle.cross_backward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                    g["q64"][b, h], scale, causal, window, block_mask=blocks[h])
+        floor = 1e-3 * float(np.linalg.norm(g["q64"][b, h]))
+        for name, gt, rf in zip(("dq", "dk", "dv"), got, ref):
+            e = rel_l2(gt[b, h], rf, floor)
+            assert e <= GRAD_REL_L2, f"{label} {name} b={b} h={h}: rel L2 {e:.3e}"
 
 
 def test_block_sparse_main_kernel_block_workload(fa):
     """The block training workload at full size with a density-0.5 block mask (the bench's
-    --block-density 0.5 step): forward on the main kernel, backward; sampled heads against the
-    oracle."""
+    --block-density 0.5 step, all three main kernels); sampled heads against the oracle."""
     import oracle
     import torch
     w = W.BLOCK
