@@ -317,7 +317,7 @@ def main():
         if os.path.exists(path):
             with open(path, encoding="utf-8") as f:
                 rec = json.load(f)
-        name = w.name + ("_kvfp8" if args.kv_fp8 else "")
+        name = variant_name(w, args)
         rec.update(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], name,
                                args.copy_calibration_mib or 256))
         with open(path, "w", encoding="utf-8") as f:
@@ -636,7 +636,7 @@ def bench_decode(args, w):
         "roofline": {"bound": "hbm", "kernel": "decode_kernel (+ combine_kernel)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("decode", w.name + ("_kvfp8" if fp8 else ""))},
+                     "traffic": measured_traffic("decode", variant_name(w, args))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -730,6 +730,19 @@ def bench_fp8(args, w):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def variant_name(w, args):
+    """The name counter summaries file a workload's traffic under: the workload, and the extras
+    that change what its kernels move (an FP8 cache, ALiBi, dropout, a block mask)."""
+    name = w.name + ("_kvfp8" if getattr(args, "kv_fp8", False) else "")
+    if getattr(args, "alibi", False):
+        name += "_alibi"
+    if getattr(args, "dropout", 0.0):
+        name += f"_dropout{args.dropout:g}"
+    if getattr(args, "block_density", 0.0):
+        name += f"_blocks{args.block_density:g}"
+    return name
 
 
 def block_traffic(workload, call):
@@ -844,7 +857,7 @@ def bench_block(args, w):
         # traffic: the HBM bytes of all kernels of that call
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4),
-                     "traffic": block_traffic(w.name, dom)},
+                     "traffic": block_traffic(variant_name(w, args), dom)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
