@@ -377,10 +377,11 @@ def main():
     stages = [("fwd", None)] + ([("delta", fa._lib.BWD_DELTA), ("dkdv", fa._lib.BWD_DKDV),
                                  ("dq", fa._lib.BWD_DQ)] if backward else [])
 
+    # events: one per stage boundary (len(stages) + 1), so that stage i spans events i .. i + 1
     def step(events=None):
+        if events is not None:
+            events[0].record()
         for idx, (name, st) in enumerate(stages):
-            if events is not None:
-                events[idx][0].record()
             if packed and st is None:
                 fa.fwd_packed(q, k, v, cu, w.N, scale, causal, window, out=o, lse=lse)
             elif packed:
@@ -392,7 +393,7 @@ def main():
                 fa.bwd(do, q, k, v, o, lse, scale, causal, window, dq=dq, dk=dk, dv=dv,
                        workspace=ws, stages=st, seqlens=sl)
             if events is not None:
-                events[idx][1].record()
+                events[idx + 1].record()
 
     if args.copy_calibration_mib:
         # contents do not matter: only the bytes moved are counted
@@ -408,8 +409,8 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronised on both sides
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in stages] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -417,7 +418,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_step = {name: [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+    per_step = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
                 for i, (name, _) in enumerate(stages)}
     kernel_ms = {name: sum(t) / len(t) for name, t in per_step.items()}
 
@@ -426,13 +427,13 @@ def main():
     cold = None
     if args.flush_mib > 0:
         flush = torch.empty(args.flush_mib << 20, device="cuda", dtype=torch.uint8)
-        cev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                for _ in stages] for _ in range(args.steps)]
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+               for _ in range(args.steps)]
         for s in range(args.steps):
             flush.fill_(s & 0xFF)
             step(cev[s])
         torch.cuda.synchronize()
-        cold = {name: [cev[s][i][0].elapsed_time(cev[s][i][1]) for s in range(args.steps)]
+        cold = {name: [cev[s][i].elapsed_time(cev[s][i + 1]) for s in range(args.steps)]
                 for i, (name, _) in enumerate(stages)}
         del flush
     pairs = total_pairs(w)
