@@ -72,6 +72,9 @@ def parse():
                     help="decode workloads: keys and values as FP8 E4M3 codes (fa_fwd_kv_fp8)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="block workload: attention dropout probability (seed 1234)")
+    ap.add_argument("--key-padding", type=float, default=0.0,
+                    help="block workload: a key padding mask, each key padding with this "
+                         "probability (holes anywhere)")
     ap.add_argument("--block-density", type=float, default=0.0,
                     help="block workload: a seeded block-sparse mask selecting about this "
                          "fraction of the 64 x 64 blocks (0: no mask)")
@@ -743,6 +746,8 @@ def variant_name(w, args):
         name += f"_dropout{args.dropout:g}"
     if getattr(args, "block_density", 0.0):
         name += f"_blocks{args.block_density:g}"
+    if getattr(args, "key_padding", 0.0):
+        name += f"_kpm{args.key_padding:g}"
     return name
 
 
@@ -754,33 +759,50 @@ def block_traffic(workload, call):
     return None if any(v is None for v in vals) else sum(vals)
 
 
+def block_workload_pairs(w, blocks=None, kpm=None):
+    """Visible (query, key) pairs of the block workload: query i at key position i + n_k - n_q
+    sees keys j <= that position (causal); a block mask [H, n_q/64, n_k/64] and a key padding
+    mask [B, n_k] (True = padding) hide more."""
+    import numpy as np
+    off = w.n_k - w.n_q
+    vis = np.arange(w.n_k)[None, :] <= (np.arange(w.n_q) + off)[:, None]          # [n_q, n_k]
+    per_head = (np.ones(w.H, bool)[:, None, None] & vis[None] if blocks is None else
+                vis[None] & np.asarray(blocks, bool)[:, np.arange(w.n_q)[:, None] // 64,
+                                                      np.arange(w.n_k)[None, :] // 64])
+    if kpm is None:
+        return int(w.B * per_head.sum())
+    keep = ~np.asarray(kpm, bool)                                                 # [B, n_k]
+    # sum over b, h, i, j of per_head[h, i, j] * keep[b, j]
+    return int((per_head.sum(axis=1) @ keep.T.astype(np.int64)).sum())
+
+
 def bench_block(args, w):
     """One training step of a query block over a longer key sequence: fa_fwd_kv then fa_bwd_kv
     (the four-wave kernels), MFMA-bound; `value` is algorithmic TFLOP/s over wall time."""
-    import oracle
     import numpy as np
     inp = W.cross_case(w.B, w.H, w.n_q, w.n_k, w.d, w.dtype, w.seed)
     g = W.cross_case(w.B, w.H, w.n_q, 1, w.d, w.dtype, w.seed + 1000)["q"]
     blocks = None
     if args.block_density > 0:
         blocks = W.draw_blocks(w.H, w.n_q, w.n_k, args.block_density, w.seed)
-        allowed = oracle.cross_allowed_mask(w.n_q, w.n_k, True)
-        pairs = w.B * sum(int((allowed & oracle.block_allowed(w.n_q, w.n_k, blocks[h])).sum())
-                          for h in range(w.H))
-    else:
-        pairs = w.B * w.H * oracle.cross_allowed_pairs(w.n_q, w.n_k, True)
+    kpm = None
+    if args.key_padding > 0:
+        kpm = W.key_padding_case(w.B, w.n_k, w.seed + 7, density=args.key_padding)
+    pairs = block_workload_pairs(w, blocks, kpm)
     fwd_flops, bwd_flops = 4.0 * w.d * pairs, 10.0 * w.d * pairs
     cpu = None
     if not args.no_cpu_baseline:   # the oracle on a bounded sample: the first heads' slices
+        import oracle
         n = args.cpu_sample_heads or 4
         t0 = time.perf_counter()
         for i in range(n):
             b, h = divmod(i, w.H)
             args_ = (inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h])
             bm = None if blocks is None else blocks[h]
-            oracle.cross_forward(*args_, w.softmax_scale, True, block_mask=bm)
+            km = None if kpm is None else kpm[b]
+            oracle.cross_forward(*args_, w.softmax_scale, True, block_mask=bm, key_mask=km)
             oracle.cross_backward(*args_, g.double().numpy()[b, h], w.softmax_scale, True,
-                                  block_mask=bm)
+                                  block_mask=bm, key_mask=km)
         secs = time.perf_counter() - t0
         from oracle import pool
         cpu = {"value": round(n * (fwd_flops + bwd_flops) / (w.B * w.H) / secs / 1e12, 6),
@@ -801,12 +823,14 @@ def bench_block(args, w):
                        dtype=torch.uint8)
     slopes = alibi_slopes(w.H) if args.alibi else None
     bmask = None if blocks is None else torch.tensor(blocks.astype(np.uint8), device="cuda")
+    kmask = None if kpm is None else torch.tensor(kpm.astype(np.uint8), device="cuda")
     state = {}
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        drop = dict(dropout_p=args.dropout, dropout_seed=1234, block_mask=bmask)
+        drop = dict(dropout_p=args.dropout, dropout_seed=1234, block_mask=bmask,
+                    key_padding_mask=kmask)
         _, state["lse"] = fa.fwd_kv(q, k, v, w.softmax_scale, True, out=o, workspace=ws_f,
                                     alibi_slopes=slopes, **drop)
         if ev:
@@ -852,6 +876,7 @@ def bench_block(args, w):
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n_q": w.n_q, "n_k": w.n_k,
                    "head_dim": w.d, "causal": True, "pass": "fwd+bwd", "alibi": bool(args.alibi),
                    "dropout_p": args.dropout, "block_density": args.block_density,
+                   "key_padding": args.key_padding,
                    "visible_pairs": pairs, "flops_per_step": fwd_flops + bwd_flops},
         "kernels": kernels,
         # a call spans several kernels (fwd_kv: one, bwd_kv: delta, dK/dV, dQ), timed together;
