@@ -50,6 +50,7 @@ __device__ __forceinline__ int build_block_list(int FA_LDS* list, const unsigned
       if (lane == 0) words[NB * ch + i] = w;
     }
   }
+  wait_lgkmcnt0();   // (the barrier does not wait for LDS writes)
   wg_barrier();
   int total = 0;
   for (int ch = 0; ch < nch; ++ch) {
@@ -71,6 +72,7 @@ __device__ __forceinline__ int build_block_list(int FA_LDS* list, const unsigned
     if (lane < NSENT) list[total + lane] = 0xffff;
     if (lane == 0) list[kListCount] = total;
   }
+  wait_lgkmcnt0();
   wg_barrier();
   return __builtin_amdgcn_readfirstlane(list[kListCount]);
 }

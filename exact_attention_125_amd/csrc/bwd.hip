@@ -723,13 +723,14 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   }
-  // dense operands, nothing extra but ALiBi or a block mask (not both), and query tiles enough
-  // to fill the chip: the dK/dV and dQ kernels of fa_bwd (their band of visible query - key
+  // dense operands, nothing extra but one of ALiBi, a block mask and a key padding mask, and
+  // query tiles enough to fill the chip: the dK/dV and dQ kernels of fa_bwd (their band of visible query - key
   // differences shifted by N_k - N_q) (ALiBi only where no visible pair lies past the diagonal:
   // those kernels take its penalty as linear in the query - key distance)
   const bool alibi_main = !alibi || p.causal || p.window_right == 0;
-  const bool blocks_main = p.blocks == nullptr || (!alibi && bwd_main_takes_blocks(p.Nq, p.Nk));
-  if (alibi_main && blocks_main && !drop && p.kpm == nullptr && p.Nq > 0 && p.Nk > 0 &&
+  const int extras = alibi + (p.blocks != nullptr) + (p.kpm != nullptr);
+  const bool lists_main = (p.blocks == nullptr && p.kpm == nullptr) || bwd_main_takes_blocks(p.Nq, p.Nk);
+  if (alibi_main && extras <= 1 && lists_main && !drop && p.Nq > 0 && p.Nk > 0 &&
       (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 && is_dense(p.sq, p.H, p.Nq, p.D) &&
       is_dense(p.so, p.H, p.Nq, p.D) && is_dense(p.sg, p.H, p.Nq, p.D) &&
       is_dense(p.sdq, p.H, p.Nq, p.D) && is_dense(p.sk, p.H, p.Nk, p.D) &&
@@ -750,6 +751,7 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
     m.cu = nullptr;
     m.slopes = p.slopes;
     m.blocks = p.blocks;
+    m.kpm = p.kpm;
     m.B = p.B;
     m.H = p.H;
     m.N = p.Nq;

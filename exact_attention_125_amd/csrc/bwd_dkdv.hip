@@ -84,6 +84,7 @@ struct DkdvArgs {
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
   const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
   int n_qb, n_kb;
+  const unsigned char* kpm;      // KPM: key padding mask [batch][nk] (nonzero = padding key)
 };
 
 template <int D>
@@ -123,10 +124,14 @@ __device__ __forceinline__ void slices(F&& f) {
 // BLK: a block-sparse mask.  The workgroup's 64-key blocks (KWG / 64 of them) select query
 // steps; it visits only the steps one of them selects (a list in LDS at `list`, block_list.h),
 // and a wave whose block does not select a visited step sees all of its pairs hidden.
-template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+// KPM: a key padding mask.  A padding key's column of P and dS is computed like any other and
+// touches only its own dK and dV rows, which are written as zeros; a workgroup whose keys are
+// all padding writes its zeros without computing.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false, bool KPM = false>
 __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, int FA_LDS* list,
                                           int bh, int kt) {
   static_assert(!(ALIBI && BLK), "no instance takes both");
+  static_assert(!(KPM && (ALIBI || BLK || PADDED)), "key padding alone");
   using S = DShape<D>;
   constexpr int KB = S::KB, KS = S::KS, DB = S::DB, RB = S::RB, QTILE = S::QTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
@@ -182,6 +187,44 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
         la[kb] = -b2 * (float)(q0 + 4 * hi + a.nk - nr - (kw0 + 32 * kb + l32));
     }
   };
+  // KPM: this lane's keys that are padding (or past the sequence); the workgroup skips its
+  // work when every one of its keys is
+  bool kpad[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) kpad[kb] = false;
+  if constexpr (KPM) {
+    const unsigned char* kp = a.kpm + (long)(bh / a.heads) * nkr;
+    bool all = true;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = kw0 + 32 * kb + l32;
+      kpad[kb] = key >= nkr || kp[key] != 0;
+      all = all && kpad[kb];
+    }
+    int FA_LDS* flags = (int FA_LDS*)list;
+    const bool wave_all = __all(all);   // (a vote of every lane: outside the one-lane store)
+    if (lane == 0) flags[wave] = wave_all ? 1 : 0;
+    wait_lgkmcnt0();   // (the barrier does not wait for LDS writes)
+    wg_barrier();
+    const bool skip = flags[0] && flags[1] && flags[2] && flags[3];
+    wg_barrier();   // every wave has read the flags before a later tile writes them
+    if (skip) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int key = kw0 + 32 * kb + l32;
+        if (key < nkr) {
+          char* dkrow = a.dk + khead + (long)key * RB;
+          char* dvrow = a.dv + khead + (long)key * RB;
+#pragma unroll
+          for (int c16 = 0; c16 < RB / 32; ++c16) {
+            *reinterpret_cast<u32x4*>(dkrow + 32 * c16 + 16 * hi) = u32x4{};
+            *reinterpret_cast<u32x4*>(dvrow + 32 * c16 + 16 * hi) = u32x4{};
+          }
+        }
+      }
+      return;
+    }
+  }
   i16x8 kreg[KB][KS], vreg[KB][KS];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -667,7 +710,7 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
                       pack2<BF16>(dk[kb][db][4 * g + 2] * sc, dk[kb][db][4 * g + 3] * sc)};
           u32x2 wv = {pack2<BF16>(dv[kb][db][4 * g + 0], dv[kb][db][4 * g + 1]),
                       pack2<BF16>(dv[kb][db][4 * g + 2], dv[kb][db][4 * g + 3])};
-          if (PADDED && key >= n) wk = wv = u32x2{};   // padding keys: zero gradients
+          if ((PADDED && key >= n) || (KPM && kpad[kb])) wk = wv = u32x2{};   // padding keys: zero gradients
           *reinterpret_cast<u32x2*>(dkrow + dim * 2) = wk;
           *reinterpret_cast<u32x2*>(dvrow + dim * 2) = wv;
         }
@@ -679,10 +722,11 @@ __device__ __forceinline__ void dkdv_tile(const DkdvArgs& a, char FA_LDS* ring, 
 // tile, so tiles t and n_tiles - 1 - t together take the same time for every t: paired, the
 // workgroups are of equal length and fill the chip evenly.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false, bool KPM = false>
 __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   constexpr int kRing = kNS * DShape<D>::STAGE;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kRing + (BLK ? block_list_bytes<DShape<D>::KWG / 64>() : 0)];
+  constexpr int kExtra = BLK ? block_list_bytes<DShape<D>::KWG / 64>() : KPM ? 16 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kRing + kExtra];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
   int FA_LDS* list = (int FA_LDS*)(lds_raw + kRing);
   int bh, t;
@@ -690,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_main_kernel(DkdvArgs a) {
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dkdv_tile<D, BF16, PADDED, ALIBI, BLK>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dkdv_tile<D, BF16, PADDED, ALIBI, BLK, KPM>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -732,6 +776,7 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.n_units = a.paired ? half : a.n_tiles;
   a.slopes = p.slopes;
   a.blocks = p.blocks;
+  a.kpm = p.kpm;
   a.n_qb = (nq + 63) / 64;
   a.n_kb = (nk + 63) / 64;
   const long blocks = (long)a.n_bh * a.n_units;
@@ -740,6 +785,9 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
                        stream, a);
   else if (p.blocks != nullptr)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false, false, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
+  else if (p.kpm != nullptr)
+    hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, false, false, false, true>), dim3((unsigned)blocks),
                        dim3(kThreads), 0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dkdv_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

@@ -75,6 +75,7 @@ struct DqArgs {
   const float* slopes;   // ALiBi slopes [heads] (device), read by the ALIBI instances only
   const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
   int n_qb, n_kb;
+  const unsigned char* kpm;      // KPM: key padding mask [batch][nk] (nonzero = padding key)
 };
 
 template <int D>
@@ -108,10 +109,15 @@ __device__ __forceinline__ void dq_slices(F&& f) {
 // BLK: a block-sparse mask.  The workgroup's two 64-query blocks select key steps; it visits
 // only the steps one of them selects (a list in LDS at `list`, block_list.h), and a wave whose
 // block does not select a visited step sees all of its pairs hidden.
-template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+// KPM: a key padding mask.  The workgroup gathers one padding word per key step (bit k: key k
+// of the step is padding) into LDS at `list`, drops the leading and trailing steps made only of
+// padding, and zeroes the probabilities of padding keys in the steps that have some, one
+// v_cndmask per element with a scalar lane mask.
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false, bool KPM = false>
 __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int FA_LDS* list, int bh,
                                         int qt) {
   static_assert(!(ALIBI && BLK), "no instance takes both");
+  static_assert(!(KPM && (ALIBI || BLK || PADDED)), "key padding alone");
   using S = QShape<D>;
   constexpr int QB = S::QB, KS = S::KS, DB = S::DB, RB = S::RB, KTILE = S::KTILE;
   constexpr int STAGE = S::STAGE, CPT = S::CPT;
@@ -184,8 +190,45 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // ---- key steps the workgroup's queries can see
   int k_lo, k_hi;
   mk.key_range(q_first + off, min(q_first + S::QWG, n) - 1 + off, k_lo, k_hi);
-  const int s_begin = k_lo / kBK;
-  const int NSTEP = (!PADDED || q_first < n) && k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
+  int s_begin = k_lo / kBK;
+  int NSTEP = (!PADDED || q_first < n) && k_hi > k_lo ? (k_hi + kBK - 1) / kBK - s_begin : 0;
+  // KPM: padding word of step s at pwords[s + pw_off]; the first and past-last steps with a key
+  unsigned FA_LDS* pwords = (unsigned FA_LDS*)list;
+  int pw_off = 0;
+  if constexpr (KPM) {
+    int FA_LDS* ptrim = (int FA_LDS*)(pwords + kListMax + 64);
+    const unsigned char* kp = a.kpm + (long)(bh / a.heads) * nkr;
+    for (int s = wave; s < NSTEP; s += 4) {
+      const int j = (s_begin + s) * kBK + l32;
+      const bool pad = hi != 0 || j >= nkr || kp[j] != 0;
+      const unsigned long long w = __ballot(pad);
+      if (lane == 0) pwords[s] = (unsigned)w;
+    }
+    wait_lgkmcnt0();   // (the barrier does not wait for LDS writes)
+    wg_barrier();
+    if (wave == 0) {
+      int first = NSTEP, last = -1;
+      for (int c = 0; c < NSTEP; c += 64) {
+        const bool live = c + lane < NSTEP && pwords[c + lane] != 0xffffffffu;
+        const unsigned long long b = __ballot(live);
+        if (b != 0) {
+          if (first == NSTEP) first = c + __builtin_ctzll(b);
+          last = c + 63 - __builtin_clzll(b);
+        }
+      }
+      if (lane == 0) {
+        ptrim[0] = first;
+        ptrim[1] = last + 1;
+      }
+    }
+    wait_lgkmcnt0();
+    wg_barrier();
+    const int first = __builtin_amdgcn_readfirstlane(ptrim[0]);
+    const int past = __builtin_amdgcn_readfirstlane(ptrim[1]);
+    s_begin += first;
+    NSTEP = past > first ? past - first : 0;
+    pw_off = first;
+  }
   // BLK: the visited steps, TS of them (entry k: step rel(k) after s_begin and its selections);
   // the entries of steps s .. s + kPD - 1 are carried in scalars (h0 .. h3), those of later
   // steps read from a window of 64 entries held one per lane
@@ -319,6 +362,22 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
     const int qb = c >> 3, g = c & 7;
     dsk[qb][g] = pack2<BF16>(pv[qb][2 * g] * dpacc[qb][2 * g], pv[qb][2 * g + 1] * dpacc[qb][2 * g + 1]);
   };
+  // KPM: padding keys' probabilities -> 0: element i of a lane of half hi holds key
+  // 8 (i / 4) + 4 hi + i % 4 of the step
+  auto pad_zero = [&](unsigned pad) __attribute__((always_inline)) {
+    static_for<16>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int k = 8 * (i >> 2) + (i & 3);
+      // bit k (lanes 0-31) and bit k + 4 (lanes 32-63), each spread over a half of the lane
+      // mask by an arithmetic shift
+      const unsigned lo = (unsigned)((int)(pad << (31 - k)) >> 31);
+      const unsigned hi = (unsigned)((int)(pad << (27 - k)) >> 31);
+      const unsigned long long lanes = (unsigned long long)hi << 32 | lo;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        pv[qb][i] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? 0.f : pv[qb][i];
+    });
+  };
   // Hidden pairs of band-edge steps are zeroed after P is formed (a branch around VALU only).
   // Keys past the sequence need no mask (their K rows are zero fills, so they add nothing to
   // dQ); queries past it are not stored.  q - key - dlo = u - (8 (i/4) + i%4), u per lane.
@@ -370,6 +429,9 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       for (int g = 0; g < 8; ++g) pin(dsk[qb][g]);
   };
 
+  // KPM: the padding word of the current step (scalar, taken in phase 1 once the LDS reads
+  // before it have landed) and the next step's as read from LDS
+  unsigned pad = 0, pwv = 0;
   // phase 1 of step s: dQ_{s-1}, dP_s | P_s.  P slices start after the second MFMA: S_s was
   // the last product of the step before.  It starts once the K_{s-1}^T halves have landed
   // (the V_s rows may still be in flight) and runs dP_s once they have too.
@@ -378,7 +440,13 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
     wait_lgkmcnt_fence<KS>();
     static_for<NG + NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (m == NG) wait_lgkmcnt_fence<0>();   // V_s rows have landed
+      if constexpr (m == NG) {
+        wait_lgkmcnt_fence<0>();   // V_s rows have landed
+        if constexpr (KPM) {       // this step's padding word has too; read the next one's
+          pad = __builtin_amdgcn_readfirstlane(pwv);
+          pwv = pwords[s + 1 + pw_off];
+        }
+      }
       if constexpr (m < NG) mfma_dq(std::integral_constant<int, m>{});
       else mfma_dp(std::integral_constant<int, m - NG>{});
       constexpr int W = NG + NM - 2;
@@ -454,7 +522,11 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) kt_lo[kk][db] = kt_hi[kk][db] = i16x4{};
+    for (int db = 0; db < DB; ++db) {
+      kt_lo[kk][db] = kt_hi[kk][db] = i16x4{};
+      pin(kt_lo[kk][db]);              // zeros held in the operand registers (not rematerialised
+      pin(kt_hi[kk][db]);              // by a VALU write right before the first product)
+    }
   read_rows(row_a, Z{}, ka);           // K_0
   read_rows(row_a, KT{}, va);          // V_0
   wait_lgkmcnt0_fence();
@@ -466,6 +538,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) row_a[ks] += stage_step(0);   // rows: tile 1
 
+  if constexpr (KPM) pwv = pwords[pw_off];   // (landed by step 0's phase-1 fence)
   // ---- steps: one barrier each
   for (int s = 0; s < TS; ++s) {
     if constexpr (ALIBI) {
@@ -484,8 +557,10 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
     }
     phase1(s, ek);
     const bool hide = BLK && !entry_selected(es, wave >> 1);
-    if (hide || edge_step(rel(es))) {
-      mask_step(rel(es), hide);
+    const bool ed = edge_step(rel(es));
+    if (hide || ed || pad != 0) {
+      if (hide || ed) mask_step(rel(es), hide);
+      if constexpr (KPM) pad_zero(pad);
       pin_p();
     }
     phase2();
@@ -542,9 +617,10 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
 // tile: paired as t and n_tiles - 1 - t, the workgroups are of equal length.  Unpaired, the
 // latest (longest) tiles go first.
 // PADDED: a padded batch (per-batch lengths), a separate instance
-template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false, bool KPM = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE + (BLK ? block_list_bytes<2>() : 0)];
+  constexpr int kExtra = BLK ? block_list_bytes<2>() : KPM ? 4 * (kListMax + 64) + 16 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNS * QShape<D>::STAGE + kExtra];
   char FA_LDS* ring = (char FA_LDS*)lds_raw;
   int FA_LDS* list = (int FA_LDS*)(lds_raw + kNS * QShape<D>::STAGE);
   int bh, t;
@@ -553,7 +629,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqAr
   const int n_pass = a.paired && t != a.n_tiles - 1 - t ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     if (pass > 0) wg_barrier();   // every wave is done with the ring before it is refilled
-    dq_tile<D, BF16, PADDED, ALIBI, BLK>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
+    dq_tile<D, BF16, PADDED, ALIBI, BLK, KPM>(a, ring, list, bh, pass == 0 ? t : a.n_tiles - 1 - t);
   }
 }
 
@@ -597,6 +673,7 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.n_units = a.paired ? half : a.n_tiles;
   a.slopes = p.slopes;
   a.blocks = p.blocks;
+  a.kpm = p.kpm;
   a.n_qb = (nq + 63) / 64;
   a.n_kb = (nk + 63) / 64;
   const long blocks = (long)a.n_bh * a.n_units;
@@ -606,6 +683,9 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   else if (p.blocks != nullptr)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, false, false, true>), dim3((unsigned)blocks), dim3(kThreads),
                        0, stream, a);
+  else if (p.kpm != nullptr)
+    hipLaunchKernelGGL((dq_main_kernel<D, BF16, false, false, false, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((dq_main_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else

@@ -244,6 +244,7 @@ __device__ __forceinline__ unsigned lds_addr(const char FA_LDS* p) {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(i16x4& x) { asm volatile("" : "+v"(x)); }
 // Moves x into accumulation registers (AGPRs) at this point; used for values that only
 // register-placed MFMAs read or write afterwards.
 __device__ __forceinline__ void in_agpr(i16x8& x) { asm volatile("" : "+a"(x)); }

@@ -493,11 +493,12 @@ KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8) {
 }
 
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream) {
-  // dense operands, nothing extra but ALiBi or a block mask (not both), one key split, and query
-  // tiles enough to fill the chip: the main forward kernel
-  if (!plan.decode && !p.fp8 && plan.n_split == 1 &&
-      (p.blocks == nullptr || (p.slopes == nullptr && fwd_main_takes_blocks(p.D, p.Nk))) &&
-      p.kpm == nullptr && p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
+  // dense operands, nothing extra but one of ALiBi, a block mask and a key padding mask, one key
+  // split, and query tiles enough to fill the chip: the main forward kernel
+  const int extras = (p.slopes != nullptr) + (p.blocks != nullptr) + (p.kpm != nullptr);
+  if (!plan.decode && !p.fp8 && plan.n_split == 1 && extras <= 1 &&
+      ((p.blocks == nullptr && p.kpm == nullptr) || fwd_main_takes_blocks(p.D, p.Nk)) &&
+      p.drop.scale == 1.f && p.Nk > 0 && (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 &&
       is_dense(p.sq, p.H, p.Nq, p.D) && is_dense(p.so, p.H, p.Nq, p.D) &&
       is_dense(p.sk, p.H, p.Nk, p.D) && is_dense(p.sv, p.H, p.Nk, p.D))
     return launch_fwd_main_kv(p, stream);

@@ -92,6 +92,7 @@ struct MainArgs {
   const float* slopes;  // ALiBi slopes [heads] (device), read by the ALIBI instances only
   const unsigned char* blocks;   // BLK: block-sparse mask [heads][n_qb][n_kb] of 64 x 64 blocks
   int n_qb, n_kb;
+  const unsigned char* kpm;      // KPM: key padding mask [batch][nk] (nonzero = padding key)
 };
 
 template <int D>
@@ -119,18 +120,28 @@ struct Shape {
 // BLK: a block-sparse mask.  A query tile's two 64-query blocks select key tiles; the
 // workgroup visits only the tiles one of them selects (a list of them in LDS, built at the
 // start of the tile), and a wave whose block does not select a visited tile sees it hidden.
-template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false>
+// KPM: a key padding mask.  At the start of a query tile the workgroup gathers one padding
+// word per key tile (bit k: key k of the tile is padding) into LDS and drops the leading and
+// trailing tiles made only of padding; a tile with some padding sets those keys' scores to
+// -inf, one v_cndmask per score with a scalar lane mask (the keys of a score register are the
+// same in every lane of a half-wave).
+template <int D, bool BF16, bool PADDED, bool ALIBI = false, bool BLK = false, bool KPM = false>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs a) {
   using S = Shape<D>;
   constexpr int BC = S::BC, MB = S::MB, KS = S::KS, DB = S::DB, KK = S::KK, RB = S::RB;
   constexpr int TILE = S::TILE, CPT = S::CPT;
 
   static_assert(!(ALIBI && BLK), "no instance takes both");
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE + (BLK ? block_list_bytes<2>() : 0)];
+  static_assert(!(KPM && (ALIBI || BLK || PADDED)), "key padding alone");
+  constexpr int kExtra = BLK ? block_list_bytes<2>() : KPM ? 8 * kListMax + 16 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kNS * TILE + kExtra];
   char FA_LDS* kring = (char FA_LDS*)lds_raw;
   char FA_LDS* vring = kring + kNS * TILE;
   // BLK: the key tiles the query tile's two 64-query blocks select (block_list.h)
   int FA_LDS* tlist = (int FA_LDS*)(lds_raw + 2 * kNS * TILE);
+  // KPM: the padding word of each key tile, then the first and past-last tiles with a key
+  unsigned long long FA_LDS* pwords = (unsigned long long FA_LDS*)(lds_raw + 2 * kNS * TILE);
+  int FA_LDS* ptrim = (int FA_LDS*)(pwords + kListMax);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,8 +251,52 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       }
       continue;
     }
-    const int t_begin = key_lo / BC;
-    const int T = (key_hi + BC - 1) / BC - t_begin;   // key tiles the workgroup visits (>= 1)
+    int t_begin = key_lo / BC;
+    int T = (key_hi + BC - 1) / BC - t_begin;   // key tiles the workgroup visits (>= 1)
+    int pw_off = 0;                             // KPM: padding word of tile t at pwords[t + pw_off]
+    if constexpr (KPM) {
+      const unsigned char* kp = a.kpm + (long)(bh / a.heads) * nkr;
+      for (int t = wave; t < T; t += kWaves) {
+        const int j = (t_begin + t) * BC + lane;
+        const bool pad = lane >= BC || j >= nkr || kp[j] != 0;
+        const unsigned long long w = __ballot(pad);
+        if (lane == 0) pwords[t] = w;
+      }
+      wait_lgkmcnt0();   // (the barrier does not wait for LDS writes)
+      wg_barrier();
+      if (wave == 0) {
+        int first = T, last = -1;
+        for (int c = 0; c < T; c += 64) {
+          const bool live = c + lane < T && pwords[c + lane] != ~0ull;
+          const unsigned long long b = __ballot(live);
+          if (b != 0) {
+            if (first == T) first = c + __builtin_ctzll(b);
+            last = c + 63 - __builtin_clzll(b);
+          }
+        }
+        if (lane == 0) {
+          ptrim[0] = first;
+          ptrim[1] = last + 1;
+        }
+      }
+      wait_lgkmcnt0();
+      wg_barrier();
+      const int first = __builtin_amdgcn_readfirstlane(ptrim[0]);
+      const int past = __builtin_amdgcn_readfirstlane(ptrim[1]);
+      if (past <= first) {   // every key of the tile's range is padding: O = 0, LSE = -inf
+        if (qi < n) {
+          char* orow = a.o + head + (long)qi * RB;
+#pragma unroll
+          for (int c16 = 0; c16 < RB / 32; ++c16)
+            *reinterpret_cast<u32x4*>(orow + 32 * c16 + 16 * hi) = u32x4{};
+          if (a.lse != nullptr && hi == 0) a.lse[lrow + qi] = NEG_INF;
+        }
+        continue;
+      }
+      t_begin += first;
+      T = past - first;
+      pw_off = first;
+    }
     // BLK: the selected tiles among those T, listed in LDS; TT tiles run through the pipeline
     int TT = T;
     if constexpr (BLK) {
@@ -675,10 +730,44 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     auto issue_reads_now = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
     };
-    // (e: the entry of the tile; BLK: a tile this wave's query block does not select is hidden)
-    auto mask_if_edge = [&](auto xb, int e) __attribute__((always_inline)) {
+    // KPM: the padding word of tile t (LDS; read at the start of the step that masks it)
+    auto pad_word = [&](int t) __attribute__((always_inline)) {
+      if constexpr (KPM) return pwords[t + pw_off];
+      else return 0ull;
+    };
+    // padding keys' scores -> -inf: element (mb, r) of a lane of half hi holds key
+    // 32 mb + 8 (r / 4) + 4 hi + r % 4 of the tile
+    auto pad_mask = [&](auto xb, unsigned long long pad) __attribute__((always_inline)) {
+      constexpr int X = decltype(xb)::value;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        static_for<16>([&](auto rc) __attribute__((always_inline)) {
+          constexpr int r = decltype(rc)::value;
+          // bit k of the word (lanes 0-31) and bit k + 4 (lanes 32-63), each spread over a
+          // half of the lane mask by an arithmetic shift
+          const unsigned w = (unsigned)(pad >> (32 * mb));
+          constexpr int k = 8 * (r >> 2) + (r & 3);
+          const unsigned lo = (unsigned)((int)(w << (31 - k)) >> 31);
+          const unsigned hi = (unsigned)((int)(w << (27 - k)) >> 31);
+          const unsigned long long lanes = (unsigned long long)hi << 32 | lo;
+          sb[X][mb][r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? NEG_INF : sb[X][mb][r];
+        });
+    };
+    // (e: the entry of the tile; BLK: a tile this wave's query block does not select is hidden;
+    // pw: KPM, the tile's padding word as read from LDS)
+    auto mask_if_edge = [&](auto xb, int e, unsigned long long pw) __attribute__((always_inline)) {
       const bool hide = BLK && !entry_selected(e, stripe >> 1);
-      if (hide || edge(rel(e))) mask(xb, rel(e), hide);
+      unsigned long long pad = 0;
+      if constexpr (KPM) {
+        // (readfirstlane returns an int: each half goes through unsigned, not sign-extended)
+        pad = (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)pw) |
+              (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(pw >> 32)) << 32;
+      }
+      const bool ed = edge(rel(e));
+      if (hide || ed || pad != 0) {
+        if (hide || ed) mask(xb, rel(e), hide);
+        if constexpr (KPM) pad_mask(xb, pad);
+      }
     };
 
     // Iteration i, ring stage U = i mod kNS; buffer (i+1) mod 2 receives S_{i+1}, buffer i mod 2
@@ -696,6 +785,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       using YB = std::integral_constant<int, U & 1>;
       static_assert(kPD == 3, "entries of steps i + 1 .. i + 3 carried, i + 4 read ahead");
       int e1 = i + 1, ek = i + kPD + 1, ev = i + kPD;
+      const unsigned long long pw1 = pad_word(i + 1);   // (KPM: the oldest LDS read of the step)
       if constexpr (BLK) {
         e1 = h1;
         ev = h3;
@@ -710,7 +800,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
       compute_a(XB{}, YB{}, std::integral_constant<int, U>{});   // GEMM0_{i+1} + ALU1_i, V_i reads
       wait_vmcnt<2 * CPT * (kPD - 2)>();
       wait_lgkmcnt0_fence();             // V_i operands have landed (GEMM1_i stays below)
-      mask_if_edge(XB{}, e1);
+      mask_if_edge(XB{}, e1, pw1);
       if constexpr (ALIBI) alibi_fix(XB{}, i + 1);
       compute_b(XB{}, std::integral_constant<int, (U + 2) % kNS>{}, i + 1);   // GEMM1_i + ALU0_{i+1}, K_{i+2} reads
       rescale();
@@ -722,10 +812,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
     auto iteration_first = [&]() __attribute__((always_inline)) {
       using X = std::integral_constant<int, 0>;
       const int e0 = ent(0);
+      const unsigned long long pw0 = pad_word(0);
       issue_copies(ent(kPD), ent(kPD - 1), kPD % kNS, (kPD - 1) % kNS);
       static_for<MB * KS>([&](auto ec) __attribute__((always_inline)) { qk(X{}, ec); });
       wait_vmcnt<2 * CPT * (kPD - 2)>();
-      mask_if_edge(X{}, e0);
+      mask_if_edge(X{}, e0, pw0);
       read_k(std::integral_constant<int, 1>{});
       issue_reads_now();
       alu0(X{});
@@ -827,7 +918,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_main_kernel(MainArgs
 // slopes: ALiBi slopes [H] (device) or null
 template <int D, bool BF16>
 hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
-                  const float* slopes = nullptr, const unsigned char* blocks = nullptr) {
+                  const float* slopes = nullptr, const unsigned char* blocks = nullptr,
+                  const unsigned char* kpm = nullptr) {
   MainArgs a;
   a.q = static_cast<const char*>(p.q);
   a.k = static_cast<const char*>(p.k);
@@ -860,6 +952,7 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
   a.wr = p.causal ? 0 : p.window_right;
   a.slopes = slopes;
   a.blocks = blocks;
+  a.kpm = kpm;
   a.n_qb = (nq + 63) / 64;
   a.n_kb = (nk + 63) / 64;
   const long wgs = (long)a.n_bh * a.n_units;
@@ -868,6 +961,9 @@ hipError_t launch(const FwdParams& p, int nq, int nk, hipStream_t stream,
                        dim3(kThreads), 0, stream, a);
   else if (blocks != nullptr)
     hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, false, true>), dim3((unsigned)wgs),
+                       dim3(kThreads), 0, stream, a);
+  else if (kpm != nullptr)
+    hipLaunchKernelGGL((fwd_main_kernel<D, BF16, false, false, false, true>), dim3((unsigned)wgs),
                        dim3(kThreads), 0, stream, a);
   else if (p.seqlens != nullptr || p.cu != nullptr)
     hipLaunchKernelGGL((fwd_main_kernel<D, BF16, true>), dim3((unsigned)wgs), dim3(kThreads), 0,
@@ -908,13 +1004,13 @@ hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream) {
   f.causal = p.causal;
   f.window_left = p.window_left;
   f.window_right = p.window_right;
-  if (p.blocks != nullptr && !fwd_main_takes_blocks(p.D, p.Nk))
+  if ((p.blocks != nullptr || p.kpm != nullptr) && !fwd_main_takes_blocks(p.D, p.Nk))
     return hipErrorInvalidValue;   // more key tiles than a tile list holds
   if (p.D == 64)
-    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks)
-                  : launch<64, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks);
-  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks)
-                : launch<128, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks);
+    return p.bf16 ? launch<64, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks, p.kpm)
+                  : launch<64, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks, p.kpm);
+  return p.bf16 ? launch<128, true>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks, p.kpm)
+                : launch<128, false>(f, p.Nq, p.Nk, stream, p.slopes, p.blocks, p.kpm);
 }
 
 }  // namespace fa

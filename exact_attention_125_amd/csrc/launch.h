@@ -48,6 +48,8 @@ struct BwdParams {
                                   // diagonal (causal, or a right window of 0)
   const unsigned char* blocks = nullptr;   // block-sparse mask [H][ceil(N_q/64)][ceil(N_k/64)]
                                            // (device), or null; not with slopes
+  const unsigned char* kpm = nullptr;      // key padding mask [B][N_k] (device), or null; not
+                                           // with slopes or blocks
   int total = 0;
   int B, H, N, D;
   bool bf16;
@@ -127,13 +129,14 @@ constexpr int kKvMfmaKeyStep = 64;   // key tile of the four-wave MFMA kernel
 KvPlan kv_plan(int B, int H, int Nq, int Nk, int D, bool dropout, bool fp8 = false);
 // Runs the plan: the chosen kernel, then (with key splits) the merge of the partial results.
 hipError_t launch_fwd_kv(const KvParams& p, const KvPlan& plan, hipStream_t stream);
-// The main forward kernel (fwd_main.hip) for N_q queries over N_k keys, dense operands, with
-// ALiBi slopes or a block mask (not both) or neither, and no dropout or key padding mask.
+// The main forward kernel (fwd_main.hip) for N_q queries over N_k keys, dense operands, with at
+// most one of ALiBi slopes, a block mask and a key padding mask, and no dropout.
 hipError_t launch_fwd_main_kv(const KvParams& p, hipStream_t stream);
-// whether the main forward kernel takes a block-sparse mask over nk keys (its tile list holds them)
+// whether the main forward kernel takes a block-sparse or key padding mask over nk keys (its
+// per-tile list holds them)
 bool fwd_main_takes_blocks(int D, int nk);
-// whether the main dK/dV and dQ kernels take a block-sparse mask over nq queries and nk keys
-// (their step lists hold them)
+// whether the main dK/dV and dQ kernels take a block-sparse or key padding mask over nq queries
+// and nk keys (their step lists hold them)
 inline bool bwd_main_takes_blocks(int nq, int nk) { return nq <= 32 * 1024 && nk <= 32 * 1024; }
 // The MFMA kernel alone (fwd.hip); with plan.n_split > 1 it leaves partial results in p.ws.
 hipError_t launch_fwd_kv_mfma(const KvParams& p, const KvPlan& plan, hipStream_t stream);

@@ -223,3 +223,61 @@ def test_argument_errors(fa):
         fa.fwd_kv(q, k, k, key_padding_mask=torch.zeros(2, 40, dtype=torch.float32, device="cuda"))
     with pytest.raises(ValueError):
         fa.fwd_kv(q, k, k, key_padding_mask=torch.zeros(2, 40, dtype=torch.uint8))
+
+
+def main_mask(B, n_k, seed):
+    """Per batch entry: 0 holes, two padded 64-key tiles and a padded tail; 1 a padded head of
+    the keys; 2 a padded tail only; 3 no padding; 4 one padding key; B - 1 every key padded;
+    the rest holes of density 0.3."""
+    rng = np.random.default_rng(seed)
+    m = rng.random((B, n_k)) < 0.3
+    m[0, 64:192] = True
+    m[0, n_k - n_k // 5:] = True
+    m[1] = False
+    m[1, :min(n_k, 300)] = True
+    m[2] = False
+    m[2, n_k - n_k // 3:] = True
+    m[3] = False
+    m[4] = False
+    m[4, n_k // 2] = True
+    m[B - 1] = True
+    return m
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (100, 40))])
+@pytest.mark.parametrize("n_q,n_k", [(256, 320), (256, 1000), (512, 512), (130, 4096), (300, 2065)])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f16")])
+def test_key_padding_main_kernels(fa, causal, window, n_q, n_k, d, dtype):
+    """128 heads: query tiles enough for the main forward, dK/dV and dQ kernels; every entry of
+    the batch a different padding pattern (main_mask); sampled heads of every entry against the
+    oracle, forward and backward."""
+    import oracle
+    import torch
+    B, H = 8, 16
+    inp = W.cross_case(B, H, n_q, n_k, d, dtype, seed=n_q * 11 + n_k)
+    g = W.cross_case(B, H, n_q, 1, d, dtype, seed=n_q * 11 + n_k + 1000)
+    q, k, v, do = (to_dev(t) for t in (inp["q"], inp["k"], inp["v"], g["q"]))
+    km = main_mask(B, n_k, seed=n_q + n_k)
+    scale = 1.0 / math.sqrt(d)
+    kpm = torch.tensor(km.astype(np.uint8), device="cuda")
+    o, lse = fa.fwd_kv(q, k, v, scale, causal, window, key_padding_mask=kpm)
+    dq, dk, dv = fa.bwd_kv(do, q, k, v, o, lse, scale, causal, window, key_padding_mask=kpm)
+    torch.cuda.synchronize()
+    label = f"kpm main nq={n_q} nk={n_k} d={d} {dtype} causal={causal} w={window}"
+    got = [to64(t) for t in (dq, dk, dv)]
+    for b in range(B):
+        h = (5 * b + 3) % H
+        ro, rl = oracle.cross_forward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h], scale,
+                                      causal, window, key_mask=km[b])
+        check_forward(o[b, h], lse[b, h], ro, rl, dtype, f"{label} b={b} h={h}")
+        ref = oracle.cross_backward(inp["q64"][b, h], inp["k64"][b, h], inp["v64"][b, h],
+                                    g["q64"][b, h], scale, causal, window, key_mask=km[b])
+        floor = 1e-3 * float(np.linalg.norm(g["q64"][b, h]))
+        for name, gt, rf in zip(("dq", "dk", "dv"), got, ref):
+            e = rel_l2(gt[b, h], rf, floor)
+            assert e <= GRAD_REL_L2, f"{label} {name} b={b} h={h}: rel L2 {e:.3e}"
+    # padding keys get zero gradients, an entry with every key padded zero dQ, O = 0, LSE = -inf
+    pad = torch.tensor(km, device="cuda")
+    assert torch.all(dk.permute(0, 2, 1, 3)[pad] == 0) and torch.all(dv.permute(0, 2, 1, 3)[pad] == 0)
+    assert torch.all(dq[B - 1] == 0) and torch.all(o[B - 1] == 0)
+    assert torch.all(torch.isneginf(lse[B - 1]))
