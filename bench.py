@@ -4,7 +4,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step is one pass of the whole path over one batch of synthetic input: the fused
-forward (fa_fwd) followed by the recomputing backward (delta, dK/dV and dQ kernels).
+forward (fa_fwd) followed by the recomputing backward (dQ with the row statistics, then dK/dV).
 The default workload is B=8, H=16, N=4096, d=64, causal, bf16, with Q, K, V, dO drawn
 N(0, 1) from a fixed seed.  Inputs are resident in device memory before timing starts.
 
@@ -377,8 +377,10 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty(w.H, q.shape[1], device="cuda", dtype=torch.float32)
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    stages = [("fwd", None)] + ([("delta", fa._lib.BWD_DELTA), ("dkdv", fa._lib.BWD_DKDV),
-                                 ("dq", fa._lib.BWD_DQ)] if backward else [])
+    # the backward as fa_bwd runs it: the statistics with dQ (one kernel on the main path), then
+    # dK/dV
+    stages = [("fwd", None)] + ([("dq", fa._lib.BWD_DELTA | fa._lib.BWD_DQ),
+                                 ("dkdv", fa._lib.BWD_DKDV)] if backward else [])
 
     # events: one per stage boundary (len(stages) + 1), so that stage i spans events i .. i + 1
     def step(events=None):

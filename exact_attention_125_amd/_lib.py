@@ -216,8 +216,9 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), out=Non
 def bwd(dout, q, k, v, o, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
         dq=None, dk=None, dv=None, workspace=None, stages=BWD_ALL, seqlens=None):
     """Backward pass.  Returns ``(dq, dk, dv)``.  ``stages`` (a mask of BWD_DELTA, BWD_DKDV,
-    BWD_DQ) runs a subset of the three kernels; later stages need the earlier ones' results
-    in the same ``workspace`` and outputs.  ``seqlens`` (int32 [B] on the device) makes it a
+    BWD_DQ) runs a subset of the three stages; later stages need the earlier ones' results
+    in the same ``workspace`` and outputs (BWD_DELTA with BWD_DQ in one call run as one
+    kernel, before BWD_DKDV).  ``seqlens`` (int32 [B] on the device) makes it a
     padded batch (``fa_bwd_varlen``)."""
     import torch
     _check_tensors(q, k, v, o, dout)

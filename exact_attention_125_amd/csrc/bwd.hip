@@ -123,14 +123,8 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc += to_float<BF16>((unsigned short)(ov[it][w] & 0xffff)) *
-               to_float<BF16>((unsigned short)(gv[it][w] & 0xffff));
-        acc += to_float<BF16>((unsigned short)(ov[it][w] >> 16)) *
-               to_float<BF16>((unsigned short)(gv[it][w] >> 16));
-      }
+      float acc = delta_chunk<BF16>(ov[it], gv[it]);
+      // lanes of a row exchange sums at distance 1, 2, 4 ...: the pairwise order of delta_chunk
 #pragma unroll
       for (int x = 1; x < LPR; x *= 2) acc += __shfl_xor(acc, x);
       const int q = q_base + RPI * it;
@@ -642,7 +636,14 @@ BwdArgs make_args(const BwdParams& p) {
 template <int D, bool BF16>
 hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
   BwdArgs a = make_args(p);
-  if (stages & kBwdDelta) {
+  // padded and packed batches always take the main kernels
+  const bool main_kernels = env_bwd_choice() != 2 || p.seqlens != nullptr || p.cu != nullptr;
+  // statistics and dQ in one call: the main dQ kernel forms the statistics of its own queries
+  // (the same values, bit for bit, as the statistics pass) and runs first
+  const bool fused = (stages & kBwdDelta) && (stages & kBwdDq) && main_kernels;
+  if (fused) {
+    if (hipError_t e = launch_dq_main(p, stream, /*form_stats=*/true); e != hipSuccess) return e;
+  } else if (stages & kBwdDelta) {
     const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
     const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
     if (p.seqlens != nullptr || p.cu != nullptr)
@@ -651,8 +652,6 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
       hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  // padded and packed batches always take the main kernels
-  const bool main_kernels = env_bwd_choice() != 2 || p.seqlens != nullptr || p.cu != nullptr;
   if ((stages & kBwdDkDv) && main_kernels) {
     if (hipError_t e = launch_dkdv_main(p, stream); e != hipSuccess) return e;
   } else if (stages & kBwdDkDv) {
@@ -661,9 +660,9 @@ hipError_t launch(const BwdParams& p, unsigned stages, hipStream_t stream) {
                        dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  if ((stages & kBwdDq) && main_kernels) {
+  if ((stages & kBwdDq) && main_kernels && !fused) {
     if (hipError_t e = launch_dq_main(p, stream); e != hipSuccess) return e;
-  } else if (stages & kBwdDq) {
+  } else if ((stages & kBwdDq) && !fused) {
     a.n_tiles = (a.n + kDqRows - 1) / kDqRows;
     hipLaunchKernelGGL((dq_kernel<D, BF16, false, false>), dim3((unsigned)((long)a.n_bh * a.n_tiles)),
                        dim3(256), 0, stream, a);

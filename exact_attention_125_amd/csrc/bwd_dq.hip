@@ -56,6 +56,12 @@ struct DqArgs {
   const char* v;
   const char* dout;
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
+  // or, with stats_out set (plain and padded self-attention), the kernel forms those statistics
+  // of its own queries from O and LSE and writes them to stats_out for the dK/dV kernel
+  float* stats_out;
+  const char* o;
+  const float* lse;      // [B, H, n] (a packed batch: [H, total])
+  float sigma;           // softmax_scale kept away from zero (softmax_sigma)
   char* dq;
   const int* seqlens;    // per-batch lengths (device, may be null: every sequence has n rows)
   const int* cu;         // packed batch: per-batch start rows [B + 1] (device), or null
@@ -134,7 +140,8 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   // a packed batch: sequence b is rows cu[b] .. cu[b+1]-1 of each head's `total` rows (offsets
   // clamped to [0, total], at most nr rows), with no padding rows to write
   int n = nr, nw = nr;   // sequence rows, rows written
-  long head = (long)bh * nr * RB;                              // Q, dO, dQ (and K, V)
+  long head = (long)bh * nr * RB;                              // Q, dO, O, dQ (and K, V)
+  long lse_row = (long)bh * nr;                                // LSE of query 0
   if constexpr (PADDED) {
     const int b = bh / a.heads, h = bh - b * a.heads;
     if (a.cu != nullptr) {
@@ -142,6 +149,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       const int c1 = min(max(a.cu[b + 1], c0), a.total);
       n = nw = min(c1 - c0, nr);
       head = ((long)h * a.total + c0) * RB;
+      lse_row = (long)h * a.total + c0;
     } else {
       n = min(max(a.seqlens[b], 0), nr);
     }
@@ -165,6 +173,12 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const int qw0 = q_first + S::QW * wave;
   i16x8 qreg[QB][KS], greg[QB][KS];
   float lse_in[QB], nd_in[QB];   // statistics as loaded (row 0's beyond the sequence)
+  // with a.stats_out (plain and padded self-attention) the kernel forms the statistics of its
+  // queries itself: lse_in holds the LSE until then, ov the lane's chunks of the O rows
+  const bool form_stats = !ALIBI && !BLK && !KPM && a.stats_out != nullptr;
+  const auto ro = make_rsrc(a.o + head, n * RB);
+  const auto rl = make_rsrc(a.lse + lse_row, 4 * n);
+  u32x4 ov[QB][KS];
   float cm[QB];                  // c m = -log2(e) LSE, set after the prologue copies
   float lq0[QB], lq[QB];         // ALIBI: c m - b2 (p - 4 hi), and Lq of the current step
   f32x16 ndv[QB];                // -delta, the initial accumulator of dP, likewise
@@ -177,9 +191,15 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       qreg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rq, off));
       greg[qb][ks] = __builtin_bit_cast(i16x8, buffer_load16(rg, off));
     }
-    const long r = stat_index(bh, nr, q < n ? q : 0);
-    lse_in[qb] = a.stats[r];
-    nd_in[qb] = a.stats[r + kStatRows];
+    if (form_stats) {   // O rows (chunks as dO's) and LSE, used once the copies are issued
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ov[qb][ks] = buffer_load16(ro, q * RB + (2 * ks + hi) * 16);
+      lse_in[qb] = buffer_load_f32(rl, 4 * q);   // (zero past the sequence, not used there)
+    } else {
+      const long r = stat_index(bh, nr, q < n ? q : 0);
+      lse_in[qb] = a.stats[r];
+      nd_in[qb] = a.stats[r + kStatRows];
+    }
   }
   f32x16 dqacc[QB][DB];
 #pragma unroll
@@ -492,6 +512,35 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   issue_copies(3, h3);
   // Q^T, dO^T, dQ^T and the statistics are used only now: waiting for the Q and dO rows does
   // not hold back the copies, whose latency overlaps theirs
+  if (form_stats) {
+    // the statistics of the lane's query: m = -LSE / sigma and -delta, zero for a slot past
+    // the sequence and for a row that sees no key (LSE = -inf).  The lane holds the 16-byte
+    // chunks 2 ks + hi of its rows of O and dO; the two halves of the wave trade their chunk
+    // sums and both add all of them in delta_chunk's pairwise order.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float cs[2 * KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float mine = delta_chunk<BF16>(ov[qb][ks], __builtin_bit_cast(u32x4, greg[qb][ks]));
+        const unsigned u = __float_as_uint(mine);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        cs[2 * ks] = __uint_as_float(r[0]);       // chunk 2 ks, from the lower half
+        cs[2 * ks + 1] = __uint_as_float(r[1]);   // chunk 2 ks + 1, from the upper half
+      }
+#pragma unroll
+      for (int w = 1; w < 2 * KS; w *= 2)
+#pragma unroll
+        for (int i = 0; i < 2 * KS; i += 2 * w) cs[i] += cs[i + w];
+      const int q = qw0 + 32 * qb + l32;
+      const float lse = lse_in[qb];
+      const bool live = q < n && lse != -__builtin_inff();
+      lse_in[qb] = live ? -lse / a.sigma : 0.f;
+      nd_in[qb] = live ? -cs[0] : 0.f;
+      // the wave's block of 32 slots: m from the lower half of the wave, -delta from the upper
+      if (qw0 + 32 * qb < nr) a.stats_out[stat_index(bh, nr, q) + hi * kStatRows] = hi ? nd_in[qb] : lse_in[qb];
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -635,7 +684,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dq_main_kernel(DqAr
 
 // nq query rows over nk key rows (dense operands); query i at key position i + nk - nq
 template <int D, bool BF16>
-hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
+hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream, bool form_stats = false) {
   using S = QShape<D>;
   DqArgs a;
   a.q = static_cast<const char*>(p.q);
@@ -643,6 +692,10 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
   a.v = static_cast<const char*>(p.v);
   a.dout = static_cast<const char*>(p.dout);
   a.stats = p.stats;
+  a.stats_out = form_stats ? p.stats : nullptr;
+  a.o = static_cast<const char*>(p.o);
+  a.lse = p.lse;
+  a.sigma = softmax_sigma(p.scale);
   a.dq = static_cast<char*>(p.dq);
   a.seqlens = p.seqlens;
   a.cu = p.cu;
@@ -695,8 +748,12 @@ hipError_t launch(const BwdParams& p, int nq, int nk, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream) {
-  return launch_dq_main_kv(p, p.N, p.N, stream);
+hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream, bool form_stats) {
+  if (p.D == 64)
+    return p.bf16 ? launch<64, true>(p, p.N, p.N, stream, form_stats)
+                  : launch<64, false>(p, p.N, p.N, stream, form_stats);
+  return p.bf16 ? launch<128, true>(p, p.N, p.N, stream, form_stats)
+                : launch<128, false>(p, p.N, p.N, stream, form_stats);
 }
 
 hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream) {

@@ -122,6 +122,21 @@ __device__ __forceinline__ float to_float(unsigned short bits) {
   }
 }
 
+// delta = rowsum(dO * O) of a row, in one order for every kernel that forms it: each 16-byte
+// chunk (8 elements) is summed in element order from zero, then the chunk sums pairwise,
+// neighbours first (((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) ...), so the results
+// agree bit for bit whichever kernel computes them.
+template <bool BF16>
+__device__ __forceinline__ float delta_chunk(const u32x4& o, const u32x4& g) {
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    acc += to_float<BF16>((unsigned short)(o[w] & 0xffff)) * to_float<BF16>((unsigned short)(g[w] & 0xffff));
+    acc += to_float<BF16>((unsigned short)(o[w] >> 16)) * to_float<BF16>((unsigned short)(g[w] >> 16));
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------------------- buffer loads
 // Raw buffer resource over [base, base + bytes).  Loads past the end return zeros, which
 // is how tails of the sequence are read without branches.
@@ -131,6 +146,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
 // ---------------------------------------------------------------------------- async copy

@@ -199,8 +199,10 @@ inline float softmax_sigma(float scale) {
 // dK/dV with key-owned workgroups of one wave per SIMD (bwd_dkdv.hip); launch_bwd chooses
 // between it and the four-wave kernel of bwd.hip.
 hipError_t launch_dkdv_main(const BwdParams& p, hipStream_t stream);
-// dQ with query-owned workgroups of one wave per SIMD (bwd_dq.hip).
-hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream);
+// dQ with query-owned workgroups of one wave per SIMD (bwd_dq.hip).  form_stats: the kernel
+// forms the statistics of its queries itself (from p.o and p.lse) and writes them to p.stats,
+// in place of the statistics pass; the dK/dV kernel then runs after it.
+hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream, bool form_stats = false);
 // The same two kernels for nq query rows over nk key rows of dense [B, H, rows, D] operands
 // (query i at key position i + nk - nq; p.N is ignored, no padded batch).
 hipError_t launch_dkdv_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream);

@@ -113,14 +113,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  float softmax_scale, int causal, int window_left, int window_right,
                  void* stream);
 
-/* The backward pass is three kernels.  fa_bwd runs all of them; fa_bwd_stages runs the
+/* The backward pass has three stages.  fa_bwd runs all of them; fa_bwd_stages runs the
  * subset in `stages` (a bitwise OR of the values below), for callers that time or schedule
  * them one by one.  Same arguments as fa_bwd.  The stages depend on each other through the
  * workspace and the outputs: a call for a later stage must follow (on the same stream, with
  * the same arguments and workspace) the calls for every earlier stage.
  *   FA_BWD_DELTA  workspace <- -lse / sigma and -rowsum(dout * o) per query
  *   FA_BWD_DKDV   dk, dv    (reads workspace)
- *   FA_BWD_DQ     dq        (reads workspace) */
+ *   FA_BWD_DQ     dq        (reads workspace)
+ * A call that holds FA_BWD_DELTA and FA_BWD_DQ (fa_bwd's among them) runs them as one kernel
+ * that forms the statistics of its queries, writes them to the workspace and computes dq;
+ * FA_BWD_DKDV then follows it.  The workspace and every output are the same, bit for bit, as
+ * those of the stages run one by one. */
 typedef enum fa_bwd_stage {
   FA_BWD_DELTA = 1,
   FA_BWD_DKDV = 2,
