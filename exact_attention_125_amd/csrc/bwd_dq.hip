@@ -179,6 +179,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const auto ro = make_rsrc(a.o + head, n * RB);
   const auto rl = make_rsrc(a.lse + lse_row, 4 * n);
   u32x4 ov[QB][KS];
+  float stat_out[QB];   // the lane's value of the wave's statistics block: m (lower half) or -delta
   float cm[QB];                  // c m = -log2(e) LSE, set after the prologue copies
   float lq0[QB], lq[QB];         // ALIBI: c m - b2 (p - 4 hi), and Lq of the current step
   f32x16 ndv[QB];                // -delta, the initial accumulator of dP, likewise
@@ -537,8 +538,7 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
       const bool live = q < n && lse != -__builtin_inff();
       lse_in[qb] = live ? -lse / a.sigma : 0.f;
       nd_in[qb] = live ? -cs[0] : 0.f;
-      // the wave's block of 32 slots: m from the lower half of the wave, -delta from the upper
-      if (qw0 + 32 * qb < nr) a.stats_out[stat_index(bh, nr, q) + hi * kStatRows] = hi ? nd_in[qb] : lse_in[qb];
+      stat_out[qb] = hi ? nd_in[qb] : lse_in[qb];   // stored with dQ, at the end of the tile
     }
   }
 #pragma unroll
@@ -637,6 +637,14 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   wait_vmcnt<0>();   // no copy may land after the workgroup ends
 
   // ---- epilogue: lane holds query qw0 + 32 qb + l32, dims 32 db + 8 g + 4 hi + 0..3
+  // The statistics block of each of the wave's 32-query blocks (slots past the sequence
+  // included), stored here rather than in the prologue, whose final wait would hold the
+  // workgroup for the store's completion.
+  if (form_stats) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (qw0 + 32 * qb < nr) a.stats_out[stat_index(bh, nr, qw0 + 32 * qb + l32) + hi * kStatRows] = stat_out[qb];
+  }
   mfma_result_wait();
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
