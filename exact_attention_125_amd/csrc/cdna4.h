@@ -123,16 +123,22 @@ __device__ __forceinline__ float to_float(unsigned short bits) {
 }
 
 // delta = rowsum(dO * O) of a row, in one order for every kernel that forms it: each 16-byte
-// chunk (8 elements) is summed in element order from zero, then the chunk sums pairwise,
-// neighbours first (((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) ...), so the results
-// agree bit for bit whichever kernel computes them.
+// chunk (8 elements) is summed from zero one element pair (32-bit word) at a time by a packed
+// dot product (the pair's two products, each exact in fp32, added to the running sum), then
+// the chunk sums pairwise, neighbours first (((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7))
+// ...), so the results agree bit for bit whichever kernel computes them.
 template <bool BF16>
 __device__ __forceinline__ float delta_chunk(const u32x4& o, const u32x4& g) {
   float acc = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    acc += to_float<BF16>((unsigned short)(o[w] & 0xffff)) * to_float<BF16>((unsigned short)(g[w] & 0xffff));
-    acc += to_float<BF16>((unsigned short)(o[w] >> 16)) * to_float<BF16>((unsigned short)(g[w] >> 16));
+    // (the words are copied out first: a bit cast of a vector element itself reads element 0)
+    const unsigned ow = o[w], gw = g[w];
+    if constexpr (BF16)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ow), __builtin_bit_cast(bf16x2, gw), acc,
+                                            false);
+    else
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, ow), __builtin_bit_cast(f16x2, gw), acc, false);
   }
   return acc;
 }
