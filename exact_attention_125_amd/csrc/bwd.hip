@@ -714,14 +714,6 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   a.causal = p.causal;
   a.wl = p.window_left;
   a.wr = p.causal ? 0 : p.window_right;
-  // with no query, only dK = dV = 0 is left to write (the dK/dV kernel sees no query step);
-  // with no key, dQ = 0
-  if (p.Nq > 0) {
-    const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
-    const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
-    hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
-    if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
-  }
   // dense operands, nothing extra but one of ALiBi, a block mask and a key padding mask, and
   // query tiles enough to fill the chip: the dK/dV and dQ kernels of fa_bwd (their band of visible query - key
   // differences shifted by N_k - N_q) (ALiBi only where no visible pair lies past the diagonal:
@@ -729,12 +721,22 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
   const bool alibi_main = !alibi || p.causal || p.window_right == 0;
   const int extras = alibi + (p.blocks != nullptr) + (p.kpm != nullptr);
   const bool lists_main = (p.blocks == nullptr && p.kpm == nullptr) || bwd_main_takes_blocks(p.Nq, p.Nk);
-  if (alibi_main && extras <= 1 && lists_main && !drop && p.Nq > 0 && p.Nk > 0 &&
-      (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 && is_dense(p.sq, p.H, p.Nq, p.D) &&
-      is_dense(p.so, p.H, p.Nq, p.D) && is_dense(p.sg, p.H, p.Nq, p.D) &&
-      is_dense(p.sdq, p.H, p.Nq, p.D) && is_dense(p.sk, p.H, p.Nk, p.D) &&
-      is_dense(p.sv, p.H, p.Nk, p.D) && is_dense(p.sdk, p.H, p.Nk, p.D) &&
-      is_dense(p.sdv, p.H, p.Nk, p.D)) {
+  const bool main = alibi_main && extras <= 1 && lists_main && !drop && p.Nq > 0 && p.Nk > 0 &&
+                    (long)p.B * p.H * ((p.Nq + 127) / 128) >= 256 && is_dense(p.sq, p.H, p.Nq, p.D) &&
+                    is_dense(p.so, p.H, p.Nq, p.D) && is_dense(p.sg, p.H, p.Nq, p.D) &&
+                    is_dense(p.sdq, p.H, p.Nq, p.D) && is_dense(p.sk, p.H, p.Nk, p.D) &&
+                    is_dense(p.sv, p.H, p.Nk, p.D) && is_dense(p.sdk, p.H, p.Nk, p.D) &&
+                    is_dense(p.sdv, p.H, p.Nk, p.D);
+  // the row statistics: formed by the main dQ kernel (which then runs first), else by their own
+  // pass.  With no query, only dK = dV = 0 is left to write (the dK/dV kernel sees no query
+  // step); with no key, dQ = 0
+  if (!main && p.Nq > 0) {
+    const unsigned gx = (unsigned)((stat_blocks(a.n) * kStatRows + 255) / 256);
+    const unsigned gy = (unsigned)std::min(a.n_bh, 65535);
+    hipLaunchKernelGGL((delta_kernel<D, BF16, false>), dim3(gx, gy), dim3(256), 0, stream, a);
+    if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+  }
+  if (main) {
     BwdParams m;
     m.q = p.q;
     m.k = p.k;
@@ -760,8 +762,9 @@ hipError_t launch_kv(const BwdKvParams& p, hipStream_t stream) {
     m.causal = p.causal;
     m.window_left = p.window_left;
     m.window_right = p.window_right;
-    if (hipError_t err = launch_dkdv_main_kv(m, p.Nq, p.Nk, stream); err != hipSuccess) return err;
-    return launch_dq_main_kv(m, p.Nq, p.Nk, stream);
+    if (hipError_t err = launch_dq_main_kv(m, p.Nq, p.Nk, stream, /*form_stats=*/true); err != hipSuccess)
+      return err;
+    return launch_dkdv_main_kv(m, p.Nq, p.Nk, stream);
   }
   if (p.Nk > 0) {
     a.n_tiles = (p.Nk + kKvRows - 1) / kKvRows;

@@ -56,8 +56,8 @@ struct DqArgs {
   const char* v;
   const char* dout;
   const float* stats;    // m = -LSE / sigma and -rowsum(dO * O) in 32-query blocks (stat_index)
-  // or, with stats_out set (plain and padded self-attention), the kernel forms those statistics
-  // of its own queries from O and LSE and writes them to stats_out for the dK/dV kernel
+  // or, with stats_out set, the kernel forms those statistics of its own queries from O and
+  // LSE and writes them to stats_out for the dK/dV kernel
   float* stats_out;
   const char* o;
   const float* lse;      // [B, H, n] (a packed batch: [H, total])
@@ -173,9 +173,9 @@ __device__ __forceinline__ void dq_tile(const DqArgs& a, char FA_LDS* ring, int 
   const int qw0 = q_first + S::QW * wave;
   i16x8 qreg[QB][KS], greg[QB][KS];
   float lse_in[QB], nd_in[QB];   // statistics as loaded (row 0's beyond the sequence)
-  // with a.stats_out (plain and padded self-attention) the kernel forms the statistics of its
-  // queries itself: lse_in holds the LSE until then, ov the lane's chunks of the O rows
-  const bool form_stats = !ALIBI && !BLK && !KPM && a.stats_out != nullptr;
+  // with a.stats_out the kernel forms the statistics of its queries itself: lse_in holds the
+  // LSE until then, ov the lane's chunks of the O rows
+  const bool form_stats = a.stats_out != nullptr;
   const auto ro = make_rsrc(a.o + head, n * RB);
   const auto rl = make_rsrc(a.lse + lse_row, 4 * n);
   u32x4 ov[QB][KS];
@@ -764,9 +764,11 @@ hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream, bool form_stat
                 : launch<128, false>(p, p.N, p.N, stream, form_stats);
 }
 
-hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream) {
-  if (p.D == 64) return p.bf16 ? launch<64, true>(p, nq, nk, stream) : launch<64, false>(p, nq, nk, stream);
-  return p.bf16 ? launch<128, true>(p, nq, nk, stream) : launch<128, false>(p, nq, nk, stream);
+hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream, bool form_stats) {
+  if (p.D == 64)
+    return p.bf16 ? launch<64, true>(p, nq, nk, stream, form_stats) : launch<64, false>(p, nq, nk, stream, form_stats);
+  return p.bf16 ? launch<128, true>(p, nq, nk, stream, form_stats)
+                : launch<128, false>(p, nq, nk, stream, form_stats);
 }
 
 }  // namespace fa

@@ -206,6 +206,6 @@ hipError_t launch_dq_main(const BwdParams& p, hipStream_t stream, bool form_stat
 // The same two kernels for nq query rows over nk key rows of dense [B, H, rows, D] operands
 // (query i at key position i + nk - nq; p.N is ignored, no padded batch).
 hipError_t launch_dkdv_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream);
-hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream);
+hipError_t launch_dq_main_kv(const BwdParams& p, int nq, int nk, hipStream_t stream, bool form_stats = false);
 
 }  // namespace fa
