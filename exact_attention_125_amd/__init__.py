@@ -12,11 +12,11 @@ q, k, v: contiguous [batch, heads, seqlen, head_dim] float16 / bfloat16 GPU tens
 head_dim 64 or 128.  The work runs in the HIP kernels of ``libfa.so`` (C ABI in
 include/fa.h); importing this package fails if that library has not been built.
 """
-from ._lib import (FaError, bwd, bwd_kv, bwd_packed, bwd_workspace_size, fwd,  # noqa: F401
-                   fwd_fp8, fwd_kv, fwd_kv_fp8, fwd_kv_workspace_size, fwd_packed, lib)
+from ._lib import (FaError, bwd, bwd_kv, bwd_noalloc, bwd_packed, bwd_workspace_size,  # noqa: F401
+                   fwd, fwd_fp8, fwd_kv, fwd_kv_fp8, fwd_kv_workspace_size, fwd_packed, lib)
 from .autograd import attention, attention_kv  # noqa: F401
 
 __all__ = ["fwd", "bwd", "attention", "attention_kv", "bwd_workspace_size", "fwd_kv",
            "fwd_kv_workspace_size", "fwd_kv_fp8", "fwd_fp8", "fwd_packed", "bwd_packed",
-           "bwd_kv",
+           "bwd_kv", "bwd_noalloc",
            "FaError", "lib"]
