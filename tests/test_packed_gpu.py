@@ -108,3 +108,26 @@ def test_packed_empty_and_errors(fa):
     x = torch.zeros((2, 10, 96), device="cuda", dtype=torch.bfloat16)
     with pytest.raises(fa.FaError, match="UNSUPPORTED_HEAD_DIM"):
         fa.fwd_packed(x, x, x, torch.tensor([0, 10], dtype=torch.int32, device="cuda"), 10)
+
+
+def test_packed_stages_match_single_call(fa):
+    """A packed batch's backward in one call (the dQ kernel forming the row statistics) and as
+    three separate stages give the same gradients, bit for bit."""
+    import torch
+    lens = [37, 0, 1, 300, 129]
+    B, H, N, d = len(lens), 3, max(lens), 64
+    inp = W.random_case((B, H, N, d), "bf16", seed=251, with_grad=True)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    qp, kp, vp, dop = (_pack(t, lens) for t in (q, k, v, do))
+    o, lse = fa.fwd_packed(qp, kp, vp, cu, N, None, True)
+    one = [torch.zeros_like(qp) for _ in range(3)]
+    fa.bwd_packed(dop, qp, kp, vp, o, lse, cu, N, None, True, dq=one[0], dk=one[1], dv=one[2])
+    split = [torch.zeros_like(qp) for _ in range(3)]
+    ws = torch.empty(fa.bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    for st in (fa._lib.BWD_DELTA, fa._lib.BWD_DKDV, fa._lib.BWD_DQ):
+        fa.bwd_packed(dop, qp, kp, vp, o, lse, cu, N, None, True, dq=split[0], dk=split[1], dv=split[2],
+                      workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    for x, y in zip(one, split):
+        assert torch.equal(x, y)

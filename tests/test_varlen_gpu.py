@@ -175,3 +175,25 @@ def test_padded_training_workload_sampled(fa):
     heads = [(b, (5 * b) % w.H) for b in range(w.B)]
     say(f"[varlen] {w.name} lengths {lens}")
     check(fa, inp, lens, w.softmax_scale, w.causal, w.window, w.dtype, w.name, heads=heads)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_padded_stages_match_single_call(fa, d):
+    """A padded batch's backward in one call (the dQ kernel forming the row statistics) and as
+    three separate stages (statistics pass, dK/dV, dQ) give the same gradients, bit for bit,
+    lengths 0 and short ones included."""
+    import torch
+    lens = [300, 0, 1, 257]
+    inp = W.random_case((4, 3, 300, d), "bf16", seed=243 + d, with_grad=True)
+    q, k, v, do = device_inputs(inp, lens, poison=False)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = fa.fwd(q, k, v, None, True, seqlens=sl)
+    one = fa.bwd(do, q, k, v, o, lse, None, True, seqlens=sl)
+    ws = torch.empty(fa.bwd_workspace_size(4, 3, 300, d), dtype=torch.uint8, device="cuda")
+    split = [torch.empty_like(q) for _ in range(3)]
+    for st in (fa._lib.BWD_DELTA, fa._lib.BWD_DKDV, fa._lib.BWD_DQ):
+        fa.bwd(do, q, k, v, o, lse, None, True, dq=split[0], dk=split[1], dv=split[2], workspace=ws,
+               stages=st, seqlens=sl)
+    torch.cuda.synchronize()
+    for x, y in zip(one, split):
+        assert torch.equal(x, y)
