@@ -121,10 +121,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   FA_BWD_DELTA  workspace <- -lse / sigma and -rowsum(dout * o) per query
  *   FA_BWD_DKDV   dk, dv    (reads workspace)
  *   FA_BWD_DQ     dq        (reads workspace)
- * A call that holds FA_BWD_DELTA and FA_BWD_DQ (fa_bwd's among them) runs them as one kernel
- * that forms the statistics of its queries, writes them to the workspace and computes dq;
- * FA_BWD_DKDV then follows it.  The workspace and every output are the same, bit for bit, as
- * those of the stages run one by one. */
+ * A call that holds FA_BWD_DELTA and FA_BWD_DQ (fa_bwd's among them) runs them, on the main
+ * kernels, as one kernel that forms the statistics of its queries, writes them to the workspace
+ * and computes dq; FA_BWD_DKDV then follows it.  The workspace and every output are the same,
+ * bit for bit, as those of the stages run one by one. */
 typedef enum fa_bwd_stage {
   FA_BWD_DELTA = 1,
   FA_BWD_DKDV = 2,
